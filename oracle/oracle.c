@@ -1,0 +1,465 @@
+/*
+ * oracle.c -- plain, slow CPU reference for microscaling-FP4 attention forward.
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by the tests, the smoke check and the
+ * benchmark's CPU-baseline leg; never by the GPU library.  Source titles are
+ * abbreviated as in oracle.h.  Build: gcc -O2 -ffp-contract=off -fno-fast-math.
+ *
+ * Parity status: every function below is pinned by tests/test_oracle_pins.py
+ * (formats, scale rules, quantizers, two-level stretch, PNQ normalisation) and
+ * tests/test_oracle_attention.py (online softmax against brute force, masks,
+ * GQA, packed documents).  The flip budget is a bound, not a result; it is
+ * exercised by the GPU parity tests only.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* E2M1: magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}, sign bit 3 ([MXF4] "NVFP4,  */
+/* not MXFP4"; [MXA] section 2, the E2M1 grid).                               */
+/* ------------------------------------------------------------------------ */
+static const double E2M1_MAG[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double orc_e2m1_value(int code) {
+  double m = E2M1_MAG[code & 7];
+  return (code & 8) ? -m : m;
+}
+
+/* Round to the nearest grid magnitude; on a tie take the even magnitude index
+ * (IEEE round-half-even, the OCP MX convention); magnitudes beyond 6 take 6,
+ * the nearest finite value ([MXA] section 3 describes conversion as nearest
+ * rounding with saturation to the finite range).  The sign is kept, so a negative value
+ * that rounds to zero gives 0x8.  NaN is outside the domain and maps to 0. */
+int orc_e2m1_encode(float x) {
+  int sign = signbit(x) ? 8 : 0;
+  double a = fabs((double)x);
+  int best = 0;
+  if (isnan(x)) return 0;
+  /* beyond the largest magnitude the nearest finite value is 6; testing it
+   * first also keeps huge inputs, whose double distances all tie, exact */
+  if (a >= 6.0) return sign | 7;
+  double bd = a;
+  for (int k = 1; k < 8; k++) {
+    double dist = fabs(a - E2M1_MAG[k]);
+    if (dist < bd || (dist == bd && (k % 2) == 0)) {
+      best = k;
+      bd = dist;
+    }
+  }
+  return sign | best;
+}
+
+/* ------------------------------------------------------------------------ */
+/* E4M3 (OCP FP8): bias 7, 3 mantissa bits, subnormals, no infinity,         */
+/* S.1111.111 is NaN, largest finite 448 ([MXF4] "The probability squeeze").  */
+/* ------------------------------------------------------------------------ */
+double orc_e4m3_value(int b) {
+  int e = (b >> 3) & 15, m = b & 7;
+  double v;
+  if ((b & 0x7f) == 0x7f) return NAN;
+  v = (e == 0) ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+  return (b & 0x80) ? -v : v;
+}
+
+/* Nearest of the 127 finite non-negative magnitudes (codes 0x00..0x7E, which
+ * increase with the code), ties to the even code, beyond 448 -> 448. */
+int orc_e4m3_encode(float x) {
+  int sign = signbit(x) ? 0x80 : 0;
+  double a = fabs((double)x);
+  int lo, hi;
+  if (isnan(x)) return 0x7f;
+  if (a >= 448.0) return sign | 0x7e;
+  /* largest code whose magnitude is <= a */
+  lo = 0;
+  hi = 0x7e;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) / 2;
+    if (orc_e4m3_value(mid) <= a) lo = mid; else hi = mid - 1;
+  }
+  {
+    double below = orc_e4m3_value(lo), above = orc_e4m3_value(lo + 1);
+    double db = a - below, da = above - a;
+    int code = lo;
+    if (da < db || (da == db && ((lo + 1) % 2) == 0)) code = lo + 1;
+    return sign | code;
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* E8M0 shared exponent ([MXA] section 2, section 4.1 and Table 1).           */
+/*   OCP : e = floor(log2 amax) - emax_elem   (emax 2 for E2M1, 8 for E4M3)  */
+/*   CEIL: e = ceil(log2(amax / qmax)), the smallest e with amax <= qmax 2^e  */
+/* amax = 0 gives e = 0: an all-zero block uses sigma = 1 ([MXA] section 2).  */
+/* e is clamped to [-127, 127]; the byte is e + 127 (0xFF, NaN, never used).  */
+/* ------------------------------------------------------------------------ */
+static int elem_emax(int elem) { return elem == ORC_ELEM_E2M1 ? 2 : 8; }
+static double elem_max(int elem) { return elem == ORC_ELEM_E2M1 ? 6.0 : 448.0; }
+
+int orc_e8m0_exponent(float amax, int rule, float qmax, int elem) {
+  int e;
+  if (amax == 0.0f) return 0;
+  if (rule == ORC_RULE_OCP) {
+    e = ilogb(amax) - elem_emax(elem);
+  } else {
+    /* qmax*2^e < amax holds at this start, so the search ends at the smallest e */
+    e = ilogb(amax) - ilogb(qmax) - 1;
+    while ((double)amax > ldexp((double)qmax, e)) e++;
+  }
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  return e;
+}
+
+double orc_scale_value(const orc_fmt* f, int sbyte) {
+  if (f->scale == ORC_SCALE_E8M0) return ldexp(1.0, sbyte - 127);
+  return orc_e4m3_value(sbyte);
+}
+
+static int encode_elem(int elem, float y) {
+  return elem == ORC_ELEM_E2M1 ? orc_e2m1_encode(y) : orc_e4m3_encode(y);
+}
+static double elem_value(int elem, int code) {
+  return elem == ORC_ELEM_E2M1 ? orc_e2m1_value(code) : orc_e4m3_value(code);
+}
+
+/* scale byte for a block maximum */
+static int scale_byte_for(float amax, const orc_fmt* f) {
+  if (f->scale == ORC_SCALE_E8M0)
+    return orc_e8m0_exponent(amax, f->rule, f->qmax, f->elem) + 127;
+  /* NVFP4-style: s = E4M3(amax / 6) with amax/6 a single float division
+   * ([MXF4] "NVFP4, not MXFP4": s = max|X_block|/6; [MPFA] Eq. 1) */
+  return orc_e4m3_encode(amax / (float)elem_max(f->elem));
+}
+
+/* One block: x_hat = round(x / s) with x/s a single float division; a zero
+ * scale (E4M3 underflow) gives zero magnitudes with the sign kept. */
+float orc_quant_block(const float* x, int n, const orc_fmt* f, uint8_t* codes, uint8_t* sbyte) {
+  float amax = 0.0f, s;
+  int sb, i;
+  for (i = 0; i < n; i++) {
+    float a = fabsf(x[i]);
+    if (a > amax) amax = a;
+  }
+  sb = scale_byte_for(amax, f);
+  s = (float)orc_scale_value(f, sb);
+  for (i = 0; i < n; i++) {
+    if (s == 0.0f)
+      codes[i] = (uint8_t)(signbit(x[i]) ? (f->elem == ORC_ELEM_E2M1 ? 0x8 : 0x80) : 0);
+    else
+      codes[i] = (uint8_t)encode_elem(f->elem, x[i] / s);
+  }
+  *sbyte = (uint8_t)sb;
+  return s;
+}
+
+void orc_quantize_rows(const float* x, int64_t rows, int d, const orc_fmt* f, uint8_t* codes,
+                       uint8_t* scales) {
+  int nb = d / f->block;
+  for (int64_t r = 0; r < rows; r++)
+    for (int b = 0; b < nb; b++)
+      orc_quant_block(x + r * d + (int64_t)b * f->block, f->block, f,
+                      codes + r * d + (int64_t)b * f->block, scales + r * nb + b);
+}
+
+void orc_dequant_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows, int d,
+                      const orc_fmt* f, float* out) {
+  int nb = d / f->block;
+  for (int64_t r = 0; r < rows; r++)
+    for (int c = 0; c < d; c++) {
+      double s = orc_scale_value(f, scales[r * nb + c / f->block]);
+      out[r * d + c] = (float)(elem_value(f->elem, codes[r * d + c]) * s);
+    }
+}
+
+/* V role ([SA3] and [MXF4]: V is blocked along the PV contraction axis, the
+ * keys; [FLAMIA] 3.6.1: token blocks stay inside document boundaries). */
+int64_t orc_v_nblocks(int N, const int* doc_off, int ndocs, int block) {
+  int64_t nblk = 0;
+  if (!doc_off || ndocs <= 0) return (N + block - 1) / block;
+  for (int k = 0; k < ndocs; k++) nblk += (doc_off[k + 1] - doc_off[k] + block - 1) / block;
+  return nblk;
+}
+
+void orc_quantize_cols(const float* x, int N, int d, const int* doc_off, int ndocs,
+                       const orc_fmt* f, uint8_t* codes, uint8_t* scales) {
+  int one[2] = {0, N};
+  int64_t nblk = orc_v_nblocks(N, doc_off, ndocs, f->block);
+  float* col = (float*)malloc(sizeof(float) * (size_t)f->block);
+  uint8_t* cc = (uint8_t*)malloc((size_t)f->block);
+  if (!doc_off || ndocs <= 0) {
+    doc_off = one;
+    ndocs = 1;
+  }
+  for (int c = 0; c < d; c++) {
+    int64_t bi = 0;
+    for (int k = 0; k < ndocs; k++) {
+      for (int t0 = doc_off[k]; t0 < doc_off[k + 1]; t0 += f->block) {
+        int n = doc_off[k + 1] - t0 < f->block ? doc_off[k + 1] - t0 : f->block;
+        for (int j = 0; j < n; j++) col[j] = x[(int64_t)(t0 + j) * d + c];
+        orc_quant_block(col, n, f, cc, scales + (int64_t)c * nblk + bi);
+        for (int j = 0; j < n; j++) codes[(int64_t)c * N + t0 + j] = cc[j];
+        bi++;
+      }
+    }
+  }
+  free(col);
+  free(cc);
+}
+
+void orc_dequant_cols(const uint8_t* codes, const uint8_t* scales, int N, int d,
+                      const int* doc_off, int ndocs, const orc_fmt* f, float* out) {
+  int one[2] = {0, N};
+  int64_t nblk = orc_v_nblocks(N, doc_off, ndocs, f->block);
+  if (!doc_off || ndocs <= 0) {
+    doc_off = one;
+    ndocs = 1;
+  }
+  for (int c = 0; c < d; c++) {
+    int64_t bi = 0;
+    for (int k = 0; k < ndocs; k++)
+      for (int t0 = doc_off[k]; t0 < doc_off[k + 1]; t0 += f->block, bi++) {
+        double s = orc_scale_value(f, scales[(int64_t)c * nblk + bi]);
+        int n = doc_off[k + 1] - t0 < f->block ? doc_off[k + 1] - t0 : f->block;
+        for (int j = 0; j < n; j++)
+          out[(int64_t)(t0 + j) * d + c] = (float)(elem_value(f->elem, codes[(int64_t)c * N + t0 + j]) * s);
+      }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Flip budget: rounding decisions within a relative 2^-12 of a threshold   */
+/* may be taken the other way by an implementation whose exp and dot        */
+/* products differ from this one by a few ulps.  For every such decision    */
+/* the budget adds the largest change of the dequantized value it can make. */
+/* ------------------------------------------------------------------------ */
+#define FRAG 0x1p-12
+
+/* alternative code of an element decision, or -1 */
+static int elem_alt(int elem, float y, int code) {
+  double a = fabs((double)y);
+  int mag = elem == ORC_ELEM_E2M1 ? (code & 7) : (code & 0x7f);
+  int top = elem == ORC_ELEM_E2M1 ? 7 : 0x7e;
+  int sign = elem == ORC_ELEM_E2M1 ? (code & 8) : (code & 0x80);
+  for (int nb = -1; nb <= 1; nb += 2) {
+    int other = mag + nb;
+    double mid;
+    if (other < 0 || other > top) continue;
+    mid = 0.5 * (fabs(elem_value(elem, mag)) + fabs(elem_value(elem, other)));
+    if (fabs(a - mid) <= FRAG * mid) return sign | other;
+  }
+  return -1;
+}
+
+/* alternative scale byte of a block decision, or -1 */
+static int scale_alt(float amax, const orc_fmt* f, int sb) {
+  float lo = (float)((double)amax * (1.0 - FRAG)), hi = (float)((double)amax * (1.0 + FRAG));
+  int a = scale_byte_for(lo, f), b = scale_byte_for(hi, f);
+  if (amax == 0.0f) return -1;
+  if (a != sb) return a;
+  if (b != sb) return b;
+  return -1;
+}
+
+/* Quantize-dequantize one P block of n values (n <= 64) and report, per
+ * element, the largest change of its dequantized value that a fragile
+ * decision could make (delta[]).  Returns nothing; deq[] receives code*scale. */
+static void p_block(const float* x, int n, const orc_fmt* f, double* deq, double* delta) {
+  uint8_t codes[64], sb;
+  float s = orc_quant_block(x, n, f, codes, &sb);
+  int alt_sb;
+  for (int j = 0; j < n; j++) {
+    int alt;
+    deq[j] = elem_value(f->elem, codes[j]) * (double)s;
+    delta[j] = 0.0;
+    if (s != 0.0f) {
+      alt = elem_alt(f->elem, x[j] / s, codes[j]);
+      if (alt >= 0) delta[j] = fabs(elem_value(f->elem, alt) - elem_value(f->elem, codes[j])) * (double)s;
+    }
+  }
+  {
+    float amax = 0.0f;
+    for (int j = 0; j < n; j++)
+      if (fabsf(x[j]) > amax) amax = fabsf(x[j]);
+    alt_sb = scale_alt(amax, f, sb);
+  }
+  if (alt_sb >= 0) {
+    float s2 = (float)orc_scale_value(f, alt_sb);
+    for (int j = 0; j < n; j++) {
+      double v2 = 0.0;
+      if (s2 != 0.0f) v2 = elem_value(f->elem, encode_elem(f->elem, x[j] / s2)) * (double)s2;
+      if (fabs(v2 - deq[j]) > delta[j]) delta[j] = fabs(v2 - deq[j]);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention for one query row: FlashAttention-2 form of the online softmax */
+/* ([MXA] section 2 and Algorithm 1; [MPFA] Eqs. 3-6), with the P          */
+/* quantization of the chosen mode applied to each tile's unnormalised     */
+/* exponentials:                                                            */
+/*   DIRECT    P^ = phi(P~), l from P~             ([MXA] 5.2, OCP baseline)*/
+/*   TWO_LEVEL s1 = rowmax(P~)/(448*6) in FP32, P^ = phi(P~/s1), O += s1 P^V */
+/*             ([MXF4] "Two-level scaling"; [SA3] Eq. 5); l from P~        */
+/*   PNQ       P^ = phi(P~) feeds both l and O     ([MXA] 4.2, Algorithm 1) */
+/*   FP8_FIXED c = cast_e4m3(448 P~), O += (c V)/448, l from P~ ([MPFA] 4.1)*/
+/* Tiles of kv_tile keys are aligned to key 0 of the range and walked in   */
+/* ascending order; P blocks are consecutive keys aligned to the tile.     */
+/* ------------------------------------------------------------------------ */
+int orc_attn_row(const float* q, const float* K, const float* V, int nk, int vis, int d,
+                 const orc_attn_params* p, float* o, float* lse, double* fb) {
+  int T = p->kv_tile;
+  float m = -INFINITY, l = 0.0f;
+  float* acc = (float*)calloc((size_t)d, sizeof(float));
+  float* s = (float*)malloc(sizeof(float) * (size_t)T);
+  float* pt = (float*)malloc(sizeof(float) * (size_t)T);
+  float* x2 = (float*)malloc(sizeof(float) * (size_t)T);
+  double* ph = (double*)malloc(sizeof(double) * (size_t)T);
+  double* dl = (double*)malloc(sizeof(double) * (size_t)T);
+  double* col = (double*)malloc(sizeof(double) * (size_t)d);
+  double fb1 = 0.0, fb2 = 0.0; /* flip budget: O part, l part (PNQ) */
+
+  if (vis > nk) vis = nk;
+  for (int t0 = 0; t0 < vis; t0 += T) {
+    int tl = nk - t0 < T ? nk - t0 : T; /* keys in this tile */
+    float mt = -INFINITY, mnew, alpha, mult = 1.0f;
+    double wsum = 0.0, dsum1 = 0.0, dsum2 = 0.0;
+    /* S = Q K^T: exact products of dequantized values summed in double */
+    for (int j = 0; j < tl; j++) {
+      if (t0 + j < vis) {
+        double acc_d = 0.0;
+        for (int c = 0; c < d; c++) acc_d += (double)q[c] * (double)K[(int64_t)(t0 + j) * d + c];
+        s[j] = (float)acc_d;
+        if (s[j] > mt) mt = s[j];
+      } else {
+        s[j] = -INFINITY;
+      }
+    }
+    mnew = m > mt ? m : mt;
+    alpha = (m == -INFINITY) ? 0.0f : (float)exp((double)p->sm_scale * ((double)m - (double)mnew));
+    for (int j = 0; j < tl; j++)
+      pt[j] = (s[j] == -INFINITY) ? 0.0f : (float)exp((double)p->sm_scale * ((double)s[j] - (double)mnew));
+
+    /* P quantization of this tile */
+    for (int j = 0; j < tl; j++) {
+      ph[j] = pt[j];
+      dl[j] = 0.0;
+    }
+    if (p->pmode == ORC_P_TWO_LEVEL) {
+      float r = 0.0f, s1;
+      for (int j = 0; j < tl; j++)
+        if (pt[j] > r) r = pt[j];
+      if (r == 0.0f) { /* nothing visible in this tile */
+        m = mnew;
+        continue;
+      }
+      s1 = r / (448.0f * 6.0f);
+      for (int j = 0; j < tl; j++) x2[j] = pt[j] / s1;
+      for (int b0 = 0; b0 < tl; b0 += p->pfmt.block) {
+        int n = tl - b0 < p->pfmt.block ? tl - b0 : p->pfmt.block;
+        p_block(x2 + b0, n, &p->pfmt, ph + b0, dl + b0);
+      }
+      mult = s1;
+    } else if (p->pmode == ORC_P_DIRECT || p->pmode == ORC_P_PNQ) {
+      for (int b0 = 0; b0 < tl; b0 += p->pfmt.block) {
+        int n = tl - b0 < p->pfmt.block ? tl - b0 : p->pfmt.block;
+        p_block(pt + b0, n, &p->pfmt, ph + b0, dl + b0);
+      }
+    } else if (p->pmode == ORC_P_FP8_FIXED) {
+      for (int j = 0; j < tl; j++) {
+        float y = 448.0f * pt[j];
+        int c = orc_e4m3_encode(y), alt = elem_alt(ORC_ELEM_E4M3, y, c);
+        ph[j] = orc_e4m3_value(c);
+        if (alt >= 0) dl[j] = fabs(orc_e4m3_value(alt) - ph[j]);
+      }
+      mult = 1.0f / 448.0f; /* only scales the flip budget; O divides by 448 */
+    }
+
+    /* l = alpha l + rowsum(w): w = P^ for PNQ, P~ otherwise */
+    for (int j = 0; j < tl; j++) wsum += (p->pmode == ORC_P_PNQ) ? ph[j] : (double)pt[j];
+    l = alpha * l + (float)wsum;
+
+    /* O~ = alpha O~ + P^ V (times s1 or 1/448) */
+    for (int c = 0; c < d; c++) col[c] = 0.0;
+    for (int j = 0; j < tl; j++) {
+      if (ph[j] == 0.0) continue;
+      for (int c = 0; c < d; c++) col[c] += ph[j] * (double)V[(int64_t)(t0 + j) * d + c];
+    }
+    for (int c = 0; c < d; c++) {
+      float t = (float)col[c];
+      if (p->pmode == ORC_P_TWO_LEVEL) t = mult * t;
+      else if (p->pmode == ORC_P_FP8_FIXED) t = t / 448.0f;
+      acc[c] = alpha * acc[c] + t;
+    }
+
+    /* flip budget of this tile, carried with the same alpha as O~ */
+    for (int j = 0; j < tl; j++) {
+      if (dl[j] == 0.0) continue;
+      double vmax = 0.0;
+      for (int c = 0; c < d; c++) {
+        double a = fabs((double)V[(int64_t)(t0 + j) * d + c]);
+        if (a > vmax) vmax = a;
+      }
+      dsum1 += dl[j] * (double)mult * vmax;
+      dsum2 += dl[j] * (double)mult;
+    }
+    fb1 = (double)alpha * fb1 + dsum1;
+    fb2 = (double)alpha * fb2 + dsum2;
+    m = mnew;
+  }
+
+  if (l == 0.0f) {
+    for (int c = 0; c < d; c++) o[c] = 0.0f;
+    if (lse) *lse = -INFINITY;
+    if (fb) *fb = 0.0;
+  } else {
+    double omax = 0.0;
+    for (int c = 0; c < d; c++) {
+      o[c] = acc[c] / l;
+      if (fabs((double)o[c]) > omax) omax = fabs((double)o[c]);
+    }
+    if (lse) *lse = (float)(log((double)l) + (double)p->sm_scale * (double)m);
+    if (fb) *fb = (fb1 + (p->pmode == ORC_P_PNQ ? fb2 * omax : 0.0)) / (double)l;
+  }
+  free(acc);
+  free(s);
+  free(pt);
+  free(x2);
+  free(ph);
+  free(dl);
+  free(col);
+  return 0;
+}
+
+int orc_attention(const float* Q, const float* K, const float* V, int B, int Hq, int Hkv, int N,
+                  int d, const int* doc_off, int ndocs, const orc_attn_params* p,
+                  const int64_t* rows, int64_t nrows, float* O, float* lse, double* fb) {
+  int64_t total = (int64_t)B * Hq * N;
+  if (!rows) nrows = total;
+  if (doc_off && ndocs > 0 && B != 1) return -1;
+  for (int64_t idx = 0; idx < nrows; idx++) {
+    int64_t r = rows ? rows[idx] : idx;
+    int64_t b = r / ((int64_t)Hq * N);
+    int h = (int)((r / N) % Hq);
+    int i = (int)(r % N);
+    int hk = h * Hkv / Hq; /* grouped-query attention: Hq/Hkv query heads per KV head */
+    int ks = 0, ke = N, nk, vis;
+    const float* kb = K + ((b * Hkv + hk) * (int64_t)N) * d;
+    const float* vb = V + ((b * Hkv + hk) * (int64_t)N) * d;
+    if (r < 0 || r >= total) return -2;
+    if (doc_off && ndocs > 0) {
+      for (int k = 0; k < ndocs; k++)
+        if (doc_off[k] <= i && i < doc_off[k + 1]) {
+          ks = doc_off[k];
+          ke = doc_off[k + 1];
+        }
+    }
+    nk = ke - ks;
+    vis = p->causal ? (i - ks + 1) : nk;
+    orc_attn_row(Q + r * d, kb + (int64_t)ks * d, vb + (int64_t)ks * d, nk, vis, d, p,
+                 O + idx * d, lse ? lse + idx : NULL, fb ? fb + idx : NULL);
+  }
+  return 0;
+}

@@ -1,0 +1,118 @@
+/*
+ * oracle.h -- plain, slow CPU reference for microscaling-FP4 attention forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline
+ * leg of the benchmark may load this library.  It shares no code, header, table or
+ * constant with the GPU library; the GPU path never calls it.
+ *
+ * Every routine states the passage it follows.  Sources, by title:
+ *   [MXF4]  "Microscaling FP4 Attention: Why the Softmax Operand Needs Two Scale
+ *           Factors" (blog post on SageAttention3's two-level scaling)
+ *   [MXA]   "MXAttention: Data-Free Optimal Scaling and Pre-Normalization
+ *           Quantization for MXFP4 Attention"
+ *   [SA3]   "SageAttention3 -- L2 Deep Analysis"
+ *   [FLAMIA]"FLAMIA: FLAsh MIcroscaling Attention for Fast and Causally Safe
+ *           Training on Blackwell"
+ *   [MPFA]  "MpFA: Hardware-Efficient Train-Free QK4V8 FlashAttention Kernels on
+ *           Blackwell GPUs"
+ *
+ * Arithmetic conventions (where the pages say FP32 the oracle uses single IEEE
+ * operations in program order; compiled with -ffp-contract=off, no fast-math):
+ *   - dot products: exact products of dequantized values summed in double, then
+ *     rounded once to float;
+ *   - exponentials: exp() in double of sm_scale*(s - m) formed in double from
+ *     float operands, rounded once to float;
+ *   - divisions x/scale, M/6, P/s1, 448*P: single float operations.
+ *
+ * Parity status of every function is recorded next to it ("pinned by ..." names
+ * the test file that fixes it against the pages or mathematics).
+ */
+#ifndef MXATTN_ORACLE_H
+#define MXATTN_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element formats */
+enum { ORC_ELEM_E2M1 = 0, ORC_ELEM_E4M3 = 1 };
+/* block scale formats */
+enum { ORC_SCALE_E8M0 = 0, ORC_SCALE_E4M3 = 1 };
+/* E8M0 exponent rules ([MXA] section 2 and Table 1) */
+enum { ORC_RULE_OCP = 0, ORC_RULE_CEIL = 1 };
+/* how the softmax operand P is quantized inside the loop */
+enum {
+  ORC_P_NONE = 0,      /* unquantized P (textbook online softmax)            */
+  ORC_P_DIRECT = 1,    /* phi(P~), row sum from unquantized P~ ([MXA] 5.2)   */
+  ORC_P_TWO_LEVEL = 2, /* [MXF4] "Two-level scaling", [SA3] Eq. 5            */
+  ORC_P_PNQ = 3,       /* [MXA] section 4.2 and Algorithm 1                  */
+  ORC_P_FP8_FIXED = 4  /* [MPFA] section 4.1: cast_e4m3(448 P~)/448          */
+};
+
+typedef struct {
+  int elem;    /* ORC_ELEM_*                                  */
+  int scale;   /* ORC_SCALE_*                                 */
+  int block;   /* elements sharing one scale (16 or 32)       */
+  int rule;    /* ORC_RULE_* (E8M0 scales only)               */
+  float qmax;  /* CEIL rule boundary: 6, 7.25, 448, ...       */
+} orc_fmt;
+
+typedef struct {
+  int pmode;      /* ORC_P_*                                       */
+  orc_fmt pfmt;   /* block format of P (DIRECT, TWO_LEVEL, PNQ)     */
+  int causal;     /* key j visible to query i iff j <= i            */
+  float sm_scale; /* 1/sqrt(d)                                      */
+  int kv_tile;    /* keys per online-softmax step                   */
+} orc_attn_params;
+
+/* ---- formats ---- */
+double orc_e2m1_value(int code);            /* code: sign<<3 | magnitude index     */
+int orc_e2m1_encode(float x);               /* nearest grid value, ties to even    */
+double orc_e4m3_value(int byte);            /* OCP E4M3 (no inf; S.1111.111 = NaN) */
+int orc_e4m3_encode(float x);               /* nearest finite value, ties to even  */
+int orc_e8m0_exponent(float amax, int rule, float qmax, int elem);
+double orc_scale_value(const orc_fmt* f, int sbyte);
+
+/* Quantize n values that share one scale.  Writes n codes (one per byte) and the
+ * scale byte; returns the scale as a float. */
+float orc_quant_block(const float* x, int n, const orc_fmt* f, uint8_t* codes, uint8_t* sbyte);
+
+/* Q and K role: blocks of f->block consecutive elements along d, per row.
+ * x: [rows][d] (bf16 values widened to float); codes: [rows][d]; scales: [rows][d/block] */
+void orc_quantize_rows(const float* x, int64_t rows, int d, const orc_fmt* f,
+                       uint8_t* codes, uint8_t* scales);
+void orc_dequant_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows, int d,
+                      const orc_fmt* f, float* out);
+
+/* V role: blocks of f->block consecutive tokens per channel, document-local.
+ * x: [N][d]; doc_off: ndocs+1 offsets (NULL -> one document [0,N));
+ * codes: [d][N]; scales: [d][nblk], blocks listed document by document,
+ * nblk = sum over documents of ceil(L/block). */
+int64_t orc_v_nblocks(int N, const int* doc_off, int ndocs, int block);
+void orc_quantize_cols(const float* x, int N, int d, const int* doc_off, int ndocs,
+                       const orc_fmt* f, uint8_t* codes, uint8_t* scales);
+void orc_dequant_cols(const uint8_t* codes, const uint8_t* scales, int N, int d,
+                      const int* doc_off, int ndocs, const orc_fmt* f, float* out /*[N][d]*/);
+
+/* One query row.  K, V: [nk][d] dequantized keys/values of the row's key range
+ * (a document, or the whole sequence); tiles are aligned to key 0 of that range.
+ * vis: number of visible keys (keys 0..vis-1).  Outputs o[d], *lse and the row's
+ * flip budget *fb (bound on |dO| from rounding decisions that lie within a
+ * relative 2^-12 of a threshold).  Returns 0. */
+int orc_attn_row(const float* q, const float* K, const float* V, int nk, int vis, int d,
+                 const orc_attn_params* p, float* o, float* lse, double* fb);
+
+/* Multi-head driver.  Q: [B][Hq][N][d], K,V: [B][Hkv][N][d] dequantized.
+ * doc_off/ndocs: packed documents (requires B == 1), or NULL/0.
+ * rows: flat row ids ((b*Hq + h)*N + i), or NULL for all B*Hq*N rows.
+ * O: [nrows][d]; lse, fb: [nrows] (may be NULL). */
+int orc_attention(const float* Q, const float* K, const float* V, int B, int Hq, int Hkv, int N,
+                  int d, const int* doc_off, int ndocs, const orc_attn_params* p,
+                  const int64_t* rows, int64_t nrows, float* O, float* lse, double* fb);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
