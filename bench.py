@@ -1,0 +1,205 @@
+"""Benchmark of the microscaling-FP4 attention forward on one MI355X.
+
+One step = the whole hot path on one batch of seeded synthetic input already
+resident in HBM: quantize Q, K and V (mxattn_quantize) and run the attention
+forward (mxattn_fwd, bf16 output).  Prints ONE JSON line:
+
+  value      = counted FLOP / step time, in TOPS (4 B H N^2 d for non-causal runs;
+               causal and packed-document runs count the visible half,
+               4 H d sum L(L+1)/2)
+  roofline   = the forward kernel against the dense FP4 MFMA peak (10.1 PFLOP/s),
+               its duration measured with HIP events around each launch
+  cpu_baseline = the CPU oracle timed on a bounded sample of the same workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TOPS (4·B·H·N²·d/t) at N=32K, d=128; % of FP4 MFMA peak"
+FP4_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 MFMA
+BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
+
+# workload -> (Q/K format, V format, P mode, P format, description)
+CONFIGS = {
+    "c1": ("c1_single_head", "mxfp4", "mxfp4", "two_level", "nvfp4",
+           "B1 H1 N1024 d128 non-causal, K with per-channel mean; MXFP4 Q/K/V, two-level P (E4M3/16)"),
+    "c2": ("c2_mha_4k", "mxfp4", "mxfp4", "two_level", "nvfp4",
+           "B2 H16 N4096 d128 non-causal, K mean + 0.1% x20 outliers; MXFP4 Q/K/V, two-level P (E4M3/16)"),
+    "c3": ("c3_video_dit_32k", "mxfp4_uos", "mxfp4_uos", "pnq", "mxfp4_uos",
+           "B1 H24 N32768 d128 non-causal, rank-16 peaked Q/K; MXFP4 UOS (Qmax 7.25) Q/K/V/P, PNQ"),
+    "c4": ("c4_gqa_causal_32k", "nvfp4", "fp8v", "fp8", None,
+           "B1 Hq32 Hkv8 N32768 d128 causal, K mean; QK4PV8: NVFP4 Q/K, FP8 P (scale 448) and V"),
+    "c5": ("c5_varlen_causal_64k", "mxfp4", "mxfp4", "two_level", "nvfp4",
+           "packed 65536 tokens (log-uniform 512..16384), H16 d128 block-diagonal causal, K outliers; "
+           "MXFP4 Q/K/V, two-level P (E4M3/16)"),
+}
+
+
+def counted_flop(B, H, N, d, causal, doc_off):
+    if doc_off is not None:
+        L = np.diff(np.asarray(doc_off, np.int64))
+        pairs = float(np.sum(L * (L + 1) // 2)) if causal else float(np.sum(L * L))
+        return 4.0 * H * d * pairs
+    if causal:
+        return 4.0 * B * H * d * (N * (N + 1) / 2)
+    return 4.0 * B * H * N * N * d
+
+
+def cpu_baseline(wl, x, qf, vf, pm, pf, causal, doc_off, budget_s=12.0):
+    """The oracle (single-threaded C) on a bounded sample: quantize one KV head
+    and run the attention of sampled query rows of one query head."""
+    import oracle
+    import synth
+    from tests.helpers import PM_ORACLE, oracle_quant_qk, oracle_quant_v
+    oracle.build(force=False)
+    B, Hq, Hkv, N = wl["B"], wl["Hq"], wl["Hkv"], wl["N"]
+    q = synth.bf16_to_f32(x["q"][:1, :1])
+    k = synth.bf16_to_f32(x["k"][:1, :1])
+    v = synth.bf16_to_f32(x["v"][:1, :1])
+    t0 = time.perf_counter()
+    _, _, qd = oracle_quant_qk(q, qf)
+    _, _, kd = oracle_quant_qk(k, qf)
+    _, _, vd = oracle_quant_v(v, vf, doc_off)
+    t_quant = time.perf_counter() - t0
+    # rows: last rows first (they see the most keys under a causal mask), then spread
+    rows_all = np.linspace(N - 1, 0, num=min(N, 4096)).astype(np.int64)
+    done, flop, t_att = 0, 0.0, 0.0
+    per = 8
+    while done < len(rows_all) and t_att < budget_s:
+        r = rows_all[done:done + per]
+        t0 = time.perf_counter()
+        oracle.attention(qd, kd, vd, PM_ORACLE[pm], pf, causal=causal, doc_off=doc_off, rows=r)
+        t_att += time.perf_counter() - t0
+        for i in r:
+            if doc_off is not None:
+                kidx = np.searchsorted(doc_off, i, side="right") - 1
+                s = int(doc_off[kidx])
+                vis = (i - s + 1) if causal else int(doc_off[kidx + 1]) - s
+            else:
+                vis = (i + 1) if causal else N
+            flop += 4.0 * 128 * vis
+        done += len(r)
+    tops = flop / t_att / 1e12
+    return {"value": tops, "unit": "TOPS", "cores": 1, "kind": "oracle",
+            "sample": f"{done} query rows of head 0 (attention, {t_att:.1f} s) after quantizing one head of "
+                      f"Q, K and V ({t_quant:.1f} s); value = counted FLOP of those rows / attention time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c3", choices=sorted(CONFIGS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--quiet", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the attention forward is a single-GPU kernel here "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import microscaling_fp4_attention_amd as mx
+
+    name, qf, vf, pm, pf, desc = CONFIGS[args.config]
+    log = (lambda *a: None) if args.quiet else (lambda *a: print(*a, file=sys.stderr, flush=True))
+    t0 = time.time()
+    x = synth.workload(name)
+    log(f"[bench] inputs for {name} generated in {time.time() - t0:.1f} s")
+    B, Hq, Hkv, N = x["B"], x["Hq"], x["Hkv"], x["N"]
+    causal, doc_off = x["causal"], x["doc_off"]
+    dev = torch.device("cuda:0")
+
+    def to_dev(a):
+        return torch.from_numpy(a.astype(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
+    cu = None if doc_off is None else torch.from_numpy(doc_off.astype(np.int32)).to(dev)
+    params = mx.fwd_params(pm, pf, causal=causal, out_fp32=False)
+    ws, nd = None, 0
+    if doc_off is not None:
+        ws = mx.fwd_plan(doc_off, N, causal)
+        nd = len(doc_off) - 1
+    out = torch.empty((B, Hq, N, 128), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    ev = []
+
+    def step(record):
+        Q = mx.quantize(q, mx.ROLE_QK, qf)
+        K = mx.quantize(k, mx.ROLE_QK, qf)
+        V = mx.quantize(v, mx.ROLE_V, vf, cu_seqlens=cu)
+        if record:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        mx.fwd(Q, K, V, params, out=out, workspace=ws, ndocs=nd)
+        if record:
+            e1.record(stream)
+            ev.append((e0, e1))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(args.steps):
+        step(True)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    t_step = g0.elapsed_time(g1) / 1e3 / args.steps
+    t_fwd = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    log(f"[bench] step {t_step * 1e3:.3f} ms (wall {wall / args.steps * 1e3:.3f} ms), fwd {t_fwd * 1e3:.3f} ms")
+
+    flop = counted_flop(B, Hq, N, 128, causal, doc_off)
+    tops = flop / t_step / 1e12
+    fwd_tflops = flop / t_fwd / 1e12
+    peak = FP4_PEAK_TFLOPS
+    res = {
+        "metric": METRIC,
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4" if qf.startswith("mxfp4") else "nvfp4+fp8" if pm == "fp8" else "nvfp4",
+        "data": "synthetic (seeded SplitMix64/Box-Muller bf16 tensors of the workload's shape and structure)",
+        "config": {"workload": f"{name}: {desc}", "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": 128,
+                   "causal": bool(causal), "ndocs": nd, "counted_flop": flop},
+        "pct_fp4_peak": round(100.0 * tops / FP4_PEAK_TFLOPS, 2),
+        "t_fwd_ms": round(t_fwd * 1e3, 4),
+        "t_quant_ms": round((t_step - t_fwd) * 1e3, 4),
+        "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(fwd_tflops / peak, 4), "traffic": None,
+                     "kernel": "fwd_kernel (attention forward)"},
+    }
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(x, x, qf, vf, pm, pf, causal, doc_off)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

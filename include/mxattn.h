@@ -1,0 +1,231 @@
+/*
+ * mxattn.h -- C ABI of the microscaling-FP4 attention forward for AMD MI355X (gfx950).
+ *
+ * The library computes S = Q K^T, P = OnlineSoftmax(S), O = P V (the attention
+ * statement of "SageAttention3 -- L2 Deep Analysis", Q1, and of "MXAttention",
+ * section 2) on block-quantized operands:
+ *   - Q, K and V are quantized once, outside the attention loop, by
+ *     mxattn_quantize() to E2M1 codes with a shared scale per block
+ *     (MXFP4: 1x32 blocks with an E8M0 scale; NVFP4-style: 1x16 blocks with an
+ *     E4M3 scale), or V to E4M3 codes with an E8M0 scale per 32 keys
+ *     ("MpFA", section 4.1 (FP8 V); "FLAMIA", section 3.2 (power-of-two token
+ *     block scales)).
+ *   - mxattn_fwd() runs the tiled FlashAttention-2 recurrence and quantizes the
+ *     softmax operand P inside the loop: directly, with the two-level scheme
+ *     ("Microscaling FP4 Attention" blog, section "Two-level scaling";
+ *     SageAttention3 notes, Q2 Eq. 5), with pre-normalization quantization
+ *     ("MXAttention", section 4.2 and Algorithm 1) or with the fixed FP8 scale
+ *     448 ("MpFA", section 4.1).  PV accumulates in FP32.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are DEVICE pointers unless the parameter name ends in _host.
+ *   - The caller allocates and owns every buffer.  The library never allocates,
+ *     frees or synchronizes; it enqueues work on the caller's HIP stream
+ *     (`stream`, a hipStream_t passed as void*, NULL = default stream) and returns.
+ *     Buffers must stay alive until that work has completed.
+ *   - Every entry point validates its arguments on the host first.  On failure
+ *     it returns a negative mxattn_status and enqueues nothing.  A failed kernel
+ *     launch returns MXATTN_E_HIP; mxattn_last_error() then holds the text.
+ *   - No C++ exception crosses this interface.  Outputs are bitwise
+ *     deterministic for identical inputs and parameters.
+ */
+#ifndef MXATTN_H
+#define MXATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXATTN_ABI_VERSION 1
+
+typedef enum {
+  MXATTN_OK = 0,
+  MXATTN_E_INVALID = -1,     /* bad pointer, shape, enum or stride              */
+  MXATTN_E_UNSUPPORTED = -2, /* valid but not implemented (e.g. d != 128)       */
+  MXATTN_E_ALIGN = -3,       /* a pointer or row is not 16-byte aligned          */
+  MXATTN_E_WORKSPACE = -4,   /* workspace missing or smaller than required       */
+  MXATTN_E_HIP = -5          /* a HIP call failed; see mxattn_last_error()       */
+} mxattn_status;
+
+/* element format of the codes */
+typedef enum {
+  MXATTN_ELEM_E2M1 = 0, /* FP4: magnitudes {0,.5,1,1.5,2,3,4,6}, sign bit 3, 2 codes per
+                           byte with the even element in the low nibble            */
+  MXATTN_ELEM_E4M3 = 1  /* OCP FP8 E4M3: one code per byte, max 448, no infinity   */
+} mxattn_elem;
+
+/* format of the shared block scale */
+typedef enum {
+  MXATTN_SCALE_E8M0 = 0, /* power of two 2^e, byte e + 127 (0xFF never written)  */
+  MXATTN_SCALE_E4M3 = 1  /* OCP E4M3 value s = E4M3(amax / 6)                      */
+} mxattn_scale;
+
+/* how an E8M0 exponent is chosen from the block maximum M ("MXAttention",
+ * section 2 and Table 1) */
+typedef enum {
+  MXATTN_RULE_OCP = 0, /* e = floor(log2 M) - emax(elem); emax = 2 (E2M1), 8 (E4M3) */
+  MXATTN_RULE_CEIL = 1 /* e = smallest integer with M <= qmax * 2^e
+                          (qmax 7.25: UOS; 6: truncation-free; 448: FP8 V)        */
+} mxattn_e8m0_rule;
+
+/* which axis the blocks run along */
+typedef enum {
+  MXATTN_ROLE_QK = 0, /* blocks along the head dimension d, one row per token     */
+  MXATTN_ROLE_V = 1   /* blocks along the tokens (the PV contraction axis), stored
+                         transposed: one row per channel                           */
+} mxattn_role;
+
+/* how the softmax operand P is quantized inside the attention loop */
+typedef enum {
+  MXATTN_P_DIRECT = 1,    /* P^ = phi(P~); row sum l from the unquantized P~         */
+  MXATTN_P_TWO_LEVEL = 2, /* s1 = rowmax_tile(P~)/(448*6) in FP32, P^ = phi(P~/s1),
+                             O += s1 * P^ V; l from P~                              */
+  MXATTN_P_PNQ = 3,       /* P^ = phi(P~) feeds both l and O                         */
+  MXATTN_P_FP8_FIXED = 4  /* c = E4M3(448 P~), O += c V / 448; l from P~             */
+} mxattn_pmode;
+
+/* a block format */
+typedef struct {
+  int32_t elem;  /* mxattn_elem                                   */
+  int32_t scale; /* mxattn_scale                                  */
+  int32_t block; /* elements per scale: 16 or 32                  */
+  int32_t rule;  /* mxattn_e8m0_rule (E8M0 scales only)           */
+  float qmax;    /* boundary of the CEIL rule (ignored for OCP)   */
+} mxattn_qfmt;
+
+/*
+ * A quantized tensor.  The library fills it in mxattn_quantize(); the caller
+ * provides `codes` and `scales` (sized by mxattn_qtensor_bytes()).  Layouts are
+ * dense and row-major:
+ *   role QK: codes  [B][H][N][d * bits / 8]        scales [B][H][N][d / block]
+ *   role V : codes  [B][H][d][n_padded * bits / 8] scales [B][H][d][n_padded / block]
+ * bits = 4 (E2M1) or 8 (E4M3).  For role V the key axis is padded: each document
+ * (the whole sequence when there are no documents) occupies ceil(L / block) whole
+ * blocks starting at a block boundary, in document order, and n_padded rounds
+ * is the size given by mxattn_qtensor_bytes().  Slots after the last document
+ * and inside a document's last block hold code 0; blocks made only of padding
+ * hold the scale of an all-zero block (E8M0 byte 127, E4M3 byte 0).
+ */
+typedef struct {
+  void* codes;
+  void* scales;
+  mxattn_qfmt fmt;
+  int32_t role;
+  int32_t ndocs;    /* documents the V key axis was laid out for (1 = none) */
+  int64_t B, H, N, d;
+  int64_t n_padded; /* role V: padded key count; role QK: N                  */
+} mxattn_qtensor;
+
+/* forward parameters */
+typedef struct {
+  int32_t pmode;    /* mxattn_pmode                                                  */
+  mxattn_qfmt pfmt; /* block format of P (DIRECT, TWO_LEVEL, PNQ; ignored for FP8)    */
+  int32_t causal;   /* 1: key j is visible to query i iff j <= i (within a document)  */
+  float sm_scale;   /* softmax scale applied to the scores, normally 1/sqrt(d)        */
+  int32_t kv_tile;  /* keys per online-softmax step; must be 128                      */
+  int32_t out_fp32; /* 1: O is float32, 0: O is bfloat16 (round to nearest even)      */
+} mxattn_fwd_params;
+
+/* ABI version (MXATTN_ABI_VERSION of the built library). */
+int mxattn_abi_version(void);
+
+/* Static text of a status code. */
+const char* mxattn_status_str(int status);
+
+/* Text of the last MXATTN_E_HIP failure on the calling thread ("" if none). */
+const char* mxattn_last_error(void);
+
+/*
+ * Bytes of the codes and scales buffers of a quantized tensor.
+ *   fmt, role  : format and role as passed to mxattn_quantize()
+ *   B, H, N, d : shape of the bf16 tensor ([B][H][N][d])
+ *   ndocs      : number of packed documents (0 or 1: one sequence)
+ * Writes *code_bytes, *scale_bytes and, if not NULL, *n_padded: role V pads the
+ * key axis to n_padded = round_up(N + ndocs * (block - 1), 128) slots (with
+ * ndocs <= 1: round_up(N, 128)), role QK has n_padded = N.
+ * Errors: MXATTN_E_INVALID, MXATTN_E_UNSUPPORTED.
+ */
+int mxattn_qtensor_bytes(const mxattn_qfmt* fmt, int role, int64_t B, int64_t H, int64_t N, int64_t d,
+                         int ndocs, size_t* code_bytes, size_t* scale_bytes, int64_t* n_padded);
+
+/*
+ * Quantize one bf16 tensor x [B][H][N][d] (element strides x_strides[0..3],
+ * x_strides[3] must be 1; the base and every row must be 16-byte aligned).
+ *   role QK: per token, blocks of fmt->block consecutive channels.
+ *   role V : per channel, blocks of fmt->block consecutive tokens inside one
+ *            document, written transposed (see mxattn_qtensor).
+ * Per block with maximum magnitude M ("MXAttention" section 2; blog "NVFP4, not
+ * MXFP4"):
+ *   E8M0 scale: exponent by fmt->rule, clamped to [-127, 127]; M = 0 gives 2^0.
+ *   E4M3 scale: s = E4M3_rne_sat(fp32(M / 6)).
+ *   element   : code = RNE_sat(fp32(x / scale)) in the element format, sign kept
+ *               (a negative value that rounds to zero encodes as -0); a zero scale
+ *               gives zero magnitudes.
+ * cu_seqlens: DEVICE array of ndocs+1 document offsets (role V with documents;
+ *   requires B == 1), or NULL.  Offsets must start at 0, end at N and never
+ *   decrease; the kernel reads them, the host does not check them.
+ * out: caller-owned descriptor whose codes/scales point to buffers of at least
+ *   the sizes from mxattn_qtensor_bytes(); the library fills the other fields.
+ * Errors: MXATTN_E_INVALID, MXATTN_E_UNSUPPORTED (d != 128, block not 16/32,
+ *   E4M3 elements with an E4M3 scale), MXATTN_E_ALIGN, MXATTN_E_HIP.
+ */
+int mxattn_quantize(const void* x_bf16, const int64_t x_strides[4], int64_t B, int64_t H, int64_t N,
+                    int64_t d, int role, const mxattn_qfmt* fmt, const int32_t* cu_seqlens, int ndocs,
+                    mxattn_qtensor* out, void* stream);
+
+/*
+ * Bytes of workspace a forward over packed documents needs (a document table
+ * and a work list of query tiles): N = total tokens, ndocs = documents.
+ * Returns 0 when ndocs <= 0 (no documents: no workspace is used).
+ */
+size_t mxattn_fwd_workspace_bytes(int64_t N, int ndocs);
+
+/*
+ * Plan a forward over packed documents ("FLAMIA", section 3.6: documents are
+ * packed without padding, attention stays inside each document, and work is
+ * ordered longest first).  From HOST offsets cu_seqlens_host[0..ndocs]
+ * (0 = first, N = last, non-decreasing) it builds, on the host, the document
+ * table and the list of (document, query tile) items in decreasing order of
+ * cost (key tiles visited; ties keep document order), and copies them into
+ * `workspace` on `stream`.  The copy is from pageable host memory, so the call
+ * may block until it is staged; the host array may be reused on return.  A plan
+ * stays valid for every mxattn_fwd() with the same offsets and causal flag.
+ * Errors: MXATTN_E_INVALID, MXATTN_E_WORKSPACE, MXATTN_E_HIP.
+ */
+int mxattn_fwd_plan(const int32_t* cu_seqlens_host, int ndocs, int64_t N, int causal, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
+ * Attention forward on quantized operands.
+ *   q: role QK, [B][Hq][N][d];  k: role QK, [B][Hkv][N][d];  v: role V, [B][Hkv][d][.]
+ *   Hq must be a multiple of Hkv; query head h reads key/value head h*Hkv/Hq.
+ *   params: P mode and format, causal flag, sm_scale, kv_tile (128), output type.
+ *   ndocs: 0 for one sequence per batch entry; otherwise the number of packed
+ *     documents (B == 1), `v` must have been quantized with the same documents
+ *     and `workspace` must hold a plan from mxattn_fwd_plan().  Attention never
+ *     crosses a document, and key tiles start at each document's first token.
+ *   out: [B][Hq][N][d] with element strides out_strides (out_strides[3] == 1,
+ *     16-byte aligned rows), float32 or bfloat16 per params->out_fp32.
+ *   lse: optional float32 [B][Hq][N] log-sum-exp (natural log) of each row, or
+ *     NULL.  Rows that see no key get O = 0 and lse = -inf.
+ * The online softmax walks key tiles of 128 in ascending order; P blocks are
+ * consecutive keys aligned to the tile start.  Quantized-P results depend on
+ * this order, which is part of the contract.
+ * Supported operand routes (others return MXATTN_E_UNSUPPORTED):
+ *   Q/K: MXFP4 (E2M1, E8M0/32) or NVFP4 (E2M1, E4M3/16), the same for both.
+ *   P/V: DIRECT, PNQ or TWO_LEVEL with P in E2M1 (E8M0/32 or E4M3/16) and V in
+ *        E2M1 (E8M0/32 or E4M3/16); FP8_FIXED with V in E4M3 with E8M0/32.
+ * Errors: MXATTN_E_INVALID, MXATTN_E_UNSUPPORTED, MXATTN_E_ALIGN,
+ *   MXATTN_E_WORKSPACE, MXATTN_E_HIP.
+ */
+int mxattn_fwd(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn_qtensor* v,
+               const mxattn_fwd_params* params, int ndocs, void* out, const int64_t out_strides[4],
+               float* lse, const void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MXATTN_H */

@@ -1,0 +1,219 @@
+"""Python binding of libmxattn (include/mxattn.h): argument marshalling only.
+
+Every step of the attention path runs in the HIP kernels of the library; this
+module sizes and allocates buffers with PyTorch (device memory and streams only),
+fills the C structs and calls the C entry points through ctypes.  Importing it
+fails loudly when the built library is missing; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmxattn.so")
+
+# enums of mxattn.h
+OK, E_INVALID, E_UNSUPPORTED, E_ALIGN, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4, -5
+ELEM_E2M1, ELEM_E4M3 = 0, 1
+SCALE_E8M0, SCALE_E4M3 = 0, 1
+RULE_OCP, RULE_CEIL = 0, 1
+ROLE_QK, ROLE_V = 0, 1
+P_DIRECT, P_TWO_LEVEL, P_PNQ, P_FP8_FIXED = 1, 2, 3, 4
+
+
+class QFmt(ctypes.Structure):
+    _fields_ = [("elem", ctypes.c_int32), ("scale", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("rule", ctypes.c_int32), ("qmax", ctypes.c_float)]
+
+
+class QTensorC(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("fmt", QFmt), ("role", ctypes.c_int32),
+                ("ndocs", ctypes.c_int32), ("B", ctypes.c_int64), ("H", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("d", ctypes.c_int64), ("n_padded", ctypes.c_int64)]
+
+
+class FwdParams(ctypes.Structure):
+    _fields_ = [("pmode", ctypes.c_int32), ("pfmt", QFmt), ("causal", ctypes.c_int32), ("sm_scale", ctypes.c_float),
+                ("kv_tile", ctypes.c_int32), ("out_fp32", ctypes.c_int32)]
+
+
+# block formats named as on the pages
+FORMATS = {
+    "mxfp4": (ELEM_E2M1, SCALE_E8M0, 32, RULE_OCP, 0.0),        # OCP MX: E8M0 per 32, floor rule
+    "mxfp4_uos": (ELEM_E2M1, SCALE_E8M0, 32, RULE_CEIL, 7.25),  # MXAttention unified optimal scaling
+    "mxfp4_tfs": (ELEM_E2M1, SCALE_E8M0, 32, RULE_CEIL, 6.0),   # truncation-free scaling
+    "nvfp4": (ELEM_E2M1, SCALE_E4M3, 16, RULE_OCP, 0.0),        # 1x16 blocks, E4M3 scale amax/6
+    "fp8v": (ELEM_E4M3, SCALE_E8M0, 32, RULE_CEIL, 448.0),      # E4M3 values, E8M0 per 32, round up
+}
+PMODES = {"direct": P_DIRECT, "two_level": P_TWO_LEVEL, "pnq": P_PNQ, "fp8": P_FP8_FIXED}
+
+
+def qfmt(f) -> QFmt:
+    if isinstance(f, QFmt):
+        return f
+    return QFmt(*FORMATS[f])
+
+
+class MxattnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        msg = _lib().mxattn_status_str(status).decode()
+        extra = _lib().mxattn_last_error().decode() if status == E_HIP else ""
+        super().__init__(f"{what}: {msg} ({status}) {extra}".strip())
+        self.status = status
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m microscaling_fp4_attention_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        L.mxattn_abi_version.restype = i32
+        L.mxattn_status_str.restype = ctypes.c_char_p
+        L.mxattn_status_str.argtypes = [i32]
+        L.mxattn_last_error.restype = ctypes.c_char_p
+        L.mxattn_qtensor_bytes.restype = i32
+        L.mxattn_qtensor_bytes.argtypes = [P(QFmt), i32, i64, i64, i64, i64, i32, P(ctypes.c_size_t),
+                                           P(ctypes.c_size_t), P(i64)]
+        L.mxattn_quantize.restype = i32
+        L.mxattn_quantize.argtypes = [vp, P(i64), i64, i64, i64, i64, i32, P(QFmt), vp, i32, P(QTensorC), vp]
+        L.mxattn_fwd_workspace_bytes.restype = ctypes.c_size_t
+        L.mxattn_fwd_workspace_bytes.argtypes = [i64, i32]
+        L.mxattn_fwd_plan.restype = i32
+        L.mxattn_fwd_plan.argtypes = [P(ctypes.c_int32), i32, i64, i32, vp, ctypes.c_size_t, vp]
+        L.mxattn_fwd.restype = i32
+        L.mxattn_fwd.argtypes = [P(QTensorC), P(QTensorC), P(QTensorC), P(FwdParams), i32, vp, P(i64), vp, vp,
+                                 ctypes.c_size_t, vp]
+        _LIB = L
+    return _LIB
+
+
+def lib():
+    """The loaded ctypes library (raises ImportError when it is not built)."""
+    return _lib()
+
+
+def _check(rc: int, what: str):
+    if rc != OK:
+        raise MxattnError(rc, what)
+
+
+def _stream(stream=None) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _i64(vals):
+    return (ctypes.c_int64 * len(vals))(*[int(v) for v in vals])
+
+
+@dataclass
+class QTensor:
+    """A quantized tensor: codes and scales (uint8 device tensors) plus its descriptor."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    desc: QTensorC
+
+    @property
+    def n_padded(self) -> int:
+        return int(self.desc.n_padded)
+
+    def codes_view(self) -> torch.Tensor:
+        """role QK: [B, H, N, d*bits/8]; role V: [B, H, d, n_padded*bits/8]."""
+        d = self.desc
+        bits = 4 if d.fmt.elem == ELEM_E2M1 else 8
+        if d.role == ROLE_QK:
+            return self.codes.view(d.B, d.H, d.N, d.d * bits // 8)
+        return self.codes.view(d.B, d.H, d.d, d.n_padded * bits // 8)
+
+    def scales_view(self) -> torch.Tensor:
+        d = self.desc
+        if d.role == ROLE_QK:
+            return self.scales.view(d.B, d.H, d.N, d.d // d.fmt.block)
+        return self.scales.view(d.B, d.H, d.d, d.n_padded // d.fmt.block)
+
+
+def qtensor_bytes(fmt, role: int, B: int, H: int, N: int, d: int = 128, ndocs: int = 0):
+    cb, sb, npad = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_int64(0)
+    f = qfmt(fmt)
+    _check(_lib().mxattn_qtensor_bytes(ctypes.byref(f), role, B, H, N, d, ndocs, ctypes.byref(cb), ctypes.byref(sb),
+                                       ctypes.byref(npad)), "mxattn_qtensor_bytes")
+    return cb.value, sb.value, npad.value
+
+
+def quantize(x: torch.Tensor, role: int, fmt, cu_seqlens: torch.Tensor | None = None, stream=None) -> QTensor:
+    """Quantize a bf16 tensor x [B, H, N, d] (any strides with a unit channel stride).
+
+    cu_seqlens: int32 device tensor of document offsets (role V, B == 1) or None.
+    """
+    if x.dtype != torch.bfloat16 or x.dim() != 4:
+        raise ValueError("x must be a 4-D bfloat16 tensor [B, H, N, d]")
+    B, H, N, d = x.shape
+    ndocs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    cb, sb, _ = qtensor_bytes(fmt, role, B, H, N, d, ndocs)
+    codes = torch.empty(max(cb, 16), dtype=torch.uint8, device=x.device)[:cb]
+    scales = torch.empty(max(sb, 16), dtype=torch.uint8, device=x.device)[:sb]
+    desc = QTensorC()
+    desc.codes = codes.data_ptr() if cb else None
+    desc.scales = scales.data_ptr() if sb else None
+    f = qfmt(fmt)
+    cu = None
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda:
+            raise ValueError("cu_seqlens must be an int32 device tensor")
+        cu = ctypes.c_void_p(cu_seqlens.data_ptr())
+    _check(_lib().mxattn_quantize(ctypes.c_void_p(x.data_ptr()), _i64(x.stride()), B, H, N, d, role,
+                                  ctypes.byref(f), cu, ndocs, ctypes.byref(desc), _stream(stream)), "mxattn_quantize")
+    return QTensor(codes, scales, desc)
+
+
+def fwd_workspace_bytes(N: int, ndocs: int) -> int:
+    return int(_lib().mxattn_fwd_workspace_bytes(N, ndocs))
+
+
+def fwd_plan(cu_seqlens_host, N: int, causal: bool, device="cuda", stream=None) -> torch.Tensor:
+    """Build the work list of a packed-document forward; returns the workspace tensor."""
+    cu = [int(v) for v in cu_seqlens_host]
+    ndocs = len(cu) - 1
+    nbytes = fwd_workspace_bytes(N, ndocs)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    arr = (ctypes.c_int32 * len(cu))(*cu)
+    _check(_lib().mxattn_fwd_plan(arr, ndocs, N, int(bool(causal)), ctypes.c_void_p(ws.data_ptr()), nbytes,
+                                  _stream(stream)), "mxattn_fwd_plan")
+    return ws
+
+
+def fwd_params(pmode, pfmt="mxfp4", causal=False, sm_scale=None, d=128, out_fp32=True, kv_tile=128) -> FwdParams:
+    pm = PMODES[pmode] if isinstance(pmode, str) else int(pmode)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    pf = qfmt(pfmt if pfmt is not None else "mxfp4")
+    return FwdParams(pm, pf, int(bool(causal)), float(sm_scale), kv_tile, int(bool(out_fp32)))
+
+
+def fwd(q: QTensor, k: QTensor, v: QTensor, params: FwdParams, out: torch.Tensor | None = None,
+        lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None, ndocs: int = 0,
+        stream=None) -> torch.Tensor:
+    """Attention forward; returns out [B, Hq, N, 128] (float32 or bfloat16 per params.out_fp32)."""
+    B, Hq, N, d = q.desc.B, q.desc.H, q.desc.N, q.desc.d
+    if out is None:
+        dt = torch.float32 if params.out_fp32 else torch.bfloat16
+        out = torch.empty((B, Hq, N, d), dtype=dt, device=q.codes.device)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = ctypes.c_void_p(workspace.data_ptr()), workspace.numel()
+    lse_ptr = None if lse is None else ctypes.c_void_p(lse.data_ptr())
+    _check(_lib().mxattn_fwd(ctypes.byref(q.desc), ctypes.byref(k.desc), ctypes.byref(v.desc), ctypes.byref(params),
+                             ndocs, ctypes.c_void_p(out.data_ptr()), _i64(out.stride()), lse_ptr, ws_ptr, ws_bytes,
+                             _stream(stream)), "mxattn_fwd")
+    return out

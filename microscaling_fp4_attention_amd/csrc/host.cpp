@@ -1,0 +1,312 @@
+// host.cpp -- the C ABI of libmxattn (include/mxattn.h): argument validation,
+// layout arithmetic, forward plans and kernel launches.  No allocation, no
+// synchronization, no global state apart from a thread-local error text.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "kernels.h"
+#include "mxattn.h"
+
+using namespace mxattn;
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+int hip_fail(hipError_t e, const char* what) {
+  snprintf(g_err, sizeof g_err, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+  return MXATTN_E_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// format checks shared by sizing and quantization
+int check_fmt(const mxattn_qfmt* f, int role) {
+  if (f == nullptr) return MXATTN_E_INVALID;
+  if (f->elem != MXATTN_ELEM_E2M1 && f->elem != MXATTN_ELEM_E4M3) return MXATTN_E_INVALID;
+  if (f->scale != MXATTN_SCALE_E8M0 && f->scale != MXATTN_SCALE_E4M3) return MXATTN_E_INVALID;
+  if (f->block != 16 && f->block != 32) return MXATTN_E_UNSUPPORTED;
+  if (role != MXATTN_ROLE_QK && role != MXATTN_ROLE_V) return MXATTN_E_INVALID;
+  if (f->scale == MXATTN_SCALE_E8M0) {
+    if (f->rule != MXATTN_RULE_OCP && f->rule != MXATTN_RULE_CEIL) return MXATTN_E_INVALID;
+    if (f->rule == MXATTN_RULE_CEIL && !(f->qmax >= 1.0f && f->qmax <= 448.0f)) return MXATTN_E_INVALID;
+  }
+  if (f->elem == MXATTN_ELEM_E4M3 && (f->scale != MXATTN_SCALE_E8M0 || role != MXATTN_ROLE_V))
+    return MXATTN_E_UNSUPPORTED;
+  return MXATTN_OK;
+}
+
+// E8M0 exponent rule as the two integers the kernels use (formats.h)
+E8m0Rule make_rule(const mxattn_qfmt* f) {
+  E8m0Rule r;
+  if (f->rule == MXATTN_RULE_OCP) {
+    r.qe = 127 + (f->elem == MXATTN_ELEM_E2M1 ? 2 : 8);
+    r.qm = 0x7FFFFFu;
+  } else {
+    uint32_t b;
+    memcpy(&b, &f->qmax, 4);
+    r.qe = (int32_t)(b >> 23);
+    r.qm = b & 0x7FFFFFu;
+  }
+  return r;
+}
+
+int64_t v_padded(int64_t N, int ndocs, int block) {
+  int64_t n = ndocs > 1 ? N + (int64_t)ndocs * (block - 1) : N;
+  return (n + 127) / 128 * 128;
+}
+
+int bits_of(int elem) { return elem == MXATTN_ELEM_E2M1 ? 4 : 8; }
+
+bool same_fmt(const mxattn_qfmt& a, const mxattn_qfmt& b) {
+  if (a.elem != b.elem || a.scale != b.scale || a.block != b.block) return false;
+  if (a.scale == MXATTN_SCALE_E8M0 && (a.rule != b.rule || (a.rule == MXATTN_RULE_CEIL && a.qmax != b.qmax)))
+    return false;
+  return true;
+}
+
+bool is_mxfp4(const mxattn_qfmt& f) {
+  return f.elem == MXATTN_ELEM_E2M1 && f.scale == MXATTN_SCALE_E8M0 && f.block == 32;
+}
+bool is_nvfp4(const mxattn_qfmt& f) {
+  return f.elem == MXATTN_ELEM_E2M1 && f.scale == MXATTN_SCALE_E4M3 && f.block == 16;
+}
+bool is_fp8v(const mxattn_qfmt& f) {
+  return f.elem == MXATTN_ELEM_E4M3 && f.scale == MXATTN_SCALE_E8M0 && f.block == 32;
+}
+
+size_t plan_bytes(int64_t N, int ndocs) {
+  if (ndocs <= 0) return 0;
+  int64_t items = (N + 127) / 128 + ndocs;
+  return sizeof(PlanHeader) + sizeof(DocEntry) * (size_t)ndocs + sizeof(WorkItem) * (size_t)items;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mxattn_abi_version(void) { return MXATTN_ABI_VERSION; }
+
+const char* mxattn_status_str(int s) {
+  switch (s) {
+    case MXATTN_OK: return "ok";
+    case MXATTN_E_INVALID: return "invalid argument";
+    case MXATTN_E_UNSUPPORTED: return "unsupported combination";
+    case MXATTN_E_ALIGN: return "misaligned pointer or stride";
+    case MXATTN_E_WORKSPACE: return "workspace missing or too small";
+    case MXATTN_E_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* mxattn_last_error(void) { return g_err; }
+
+int mxattn_qtensor_bytes(const mxattn_qfmt* fmt, int role, int64_t B, int64_t H, int64_t N, int64_t d, int ndocs,
+                         size_t* code_bytes, size_t* scale_bytes, int64_t* n_padded) {
+  int rc = check_fmt(fmt, role);
+  if (rc != MXATTN_OK) return rc;
+  if (code_bytes == nullptr || scale_bytes == nullptr) return MXATTN_E_INVALID;
+  if (B < 0 || H < 0 || N < 0 || d <= 0 || ndocs < 0) return MXATTN_E_INVALID;
+  if (d != 128) return MXATTN_E_UNSUPPORTED;
+  if (ndocs > 1 && B != 1) return MXATTN_E_INVALID;
+  int bits = bits_of(fmt->elem);
+  if (role == MXATTN_ROLE_QK) {
+    *code_bytes = (size_t)(B * H * N * d * bits / 8);
+    *scale_bytes = (size_t)(B * H * N * (d / fmt->block));
+    if (n_padded) *n_padded = N;
+  } else {
+    int64_t np = v_padded(N, ndocs, fmt->block);
+    *code_bytes = (size_t)(B * H * d * np * bits / 8);
+    *scale_bytes = (size_t)(B * H * d * (np / fmt->block));
+    if (n_padded) *n_padded = np;
+  }
+  return MXATTN_OK;
+}
+
+int mxattn_quantize(const void* x_bf16, const int64_t x_strides[4], int64_t B, int64_t H, int64_t N, int64_t d,
+                    int role, const mxattn_qfmt* fmt, const int32_t* cu_seqlens, int ndocs, mxattn_qtensor* out,
+                    void* stream) {
+  size_t cb, sb;
+  int64_t np;
+  int rc = mxattn_qtensor_bytes(fmt, role, B, H, N, d, ndocs, &cb, &sb, &np);
+  if (rc != MXATTN_OK) return rc;
+  if (out == nullptr || x_strides == nullptr) return MXATTN_E_INVALID;
+  if (ndocs > 1 && (cu_seqlens == nullptr || role != MXATTN_ROLE_V)) return MXATTN_E_INVALID;
+  if (x_strides[3] != 1 || x_strides[0] < 0 || x_strides[1] < 0 || x_strides[2] < 0) return MXATTN_E_INVALID;
+  const int64_t nel = B * H * N;
+  if (nel > 0) {
+    if (x_bf16 == nullptr || out->codes == nullptr || out->scales == nullptr) return MXATTN_E_INVALID;
+    if (!aligned16(x_bf16) || !aligned16(out->codes) || !aligned16(out->scales)) return MXATTN_E_ALIGN;
+    if ((x_strides[0] % 8) || (x_strides[1] % 8) || (x_strides[2] % 8)) return MXATTN_E_ALIGN;
+  }
+  out->fmt = *fmt;
+  out->role = role;
+  out->ndocs = ndocs > 1 ? ndocs : 1;
+  out->B = B;
+  out->H = H;
+  out->N = N;
+  out->d = d;
+  out->n_padded = np;
+  if (nel == 0 && !(role == MXATTN_ROLE_V && B * H > 0 && np > 0)) return MXATTN_OK;
+
+  QuantArgs a;
+  a.x = x_bf16;
+  a.sB = x_strides[0];
+  a.sH = x_strides[1];
+  a.sN = x_strides[2];
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.np = np;
+  a.elem = fmt->elem;
+  a.scale = fmt->scale;
+  a.block = fmt->block;
+  a.rule = make_rule(fmt);
+  a.cu = ndocs > 1 ? cu_seqlens : nullptr;
+  a.ndocs = ndocs > 1 ? ndocs : 1;
+  a.codes = out->codes;
+  a.scales = out->scales;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = role == MXATTN_ROLE_QK ? launch_quant_qk(a, st) : launch_quant_v(a, st);
+  if (e != hipSuccess) return hip_fail(e, "mxattn_quantize launch");
+  return MXATTN_OK;
+}
+
+size_t mxattn_fwd_workspace_bytes(int64_t N, int ndocs) { return plan_bytes(N, ndocs); }
+
+int mxattn_fwd_plan(const int32_t* cu_host, int ndocs, int64_t N, int causal, void* workspace, size_t ws_bytes,
+                    void* stream) {
+  if (cu_host == nullptr || ndocs <= 0 || N < 0) return MXATTN_E_INVALID;
+  if (cu_host[0] != 0 || cu_host[ndocs] != N) return MXATTN_E_INVALID;
+  for (int k = 0; k < ndocs; k++)
+    if (cu_host[k + 1] < cu_host[k]) return MXATTN_E_INVALID;
+  size_t need = plan_bytes(N, ndocs);
+  if (workspace == nullptr || ws_bytes < need) return MXATTN_E_WORKSPACE;
+  if (!aligned16(workspace)) return MXATTN_E_ALIGN;
+
+  std::vector<uint8_t> buf(need, 0);
+  PlanHeader* ph = reinterpret_cast<PlanHeader*>(buf.data());
+  DocEntry* docs = reinterpret_cast<DocEntry*>(ph + 1);
+  WorkItem* items = reinterpret_cast<WorkItem*>(docs + ndocs);
+  int64_t v32 = 0, v16 = 0;
+  struct Cand {
+    int64_t cost;
+    int32_t doc, qtile;
+  };
+  std::vector<Cand> cand;
+  for (int k = 0; k < ndocs; k++) {
+    int64_t L = cu_host[k + 1] - cu_host[k];
+    docs[k].start = cu_host[k];
+    docs[k].len = (int32_t)L;
+    docs[k].voff32 = (int32_t)v32;
+    docs[k].voff16 = (int32_t)v16;
+    v32 += (L + 31) / 32 * 32;
+    v16 += (L + 15) / 16 * 16;
+    int64_t nt = (L + 127) / 128;
+    for (int64_t t = 0; t < nt; t++) cand.push_back({causal ? t + 1 : nt, k, (int32_t)t});
+  }
+  // longest first (the key tiles an item visits); ties keep document order
+  std::stable_sort(cand.begin(), cand.end(), [](const Cand& x, const Cand& y) { return x.cost > y.cost; });
+  for (size_t i = 0; i < cand.size(); i++) items[i] = {cand[i].doc, cand[i].qtile};
+  ph->n_items = (int32_t)cand.size();
+  ph->ndocs = ndocs;
+  ph->causal = causal ? 1 : 0;
+  ph->magic = PLAN_MAGIC;
+  hipError_t e = hipMemcpyAsync(workspace, buf.data(), need, hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mxattn_fwd_plan copy");
+  return MXATTN_OK;
+}
+
+int mxattn_fwd(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn_qtensor* v,
+               const mxattn_fwd_params* p, int ndocs, void* out, const int64_t os[4], float* lse,
+               const void* workspace, size_t ws_bytes, void* stream) {
+  if (!q || !k || !v || !p || !os) return MXATTN_E_INVALID;
+  if (q->role != MXATTN_ROLE_QK || k->role != MXATTN_ROLE_QK || v->role != MXATTN_ROLE_V) return MXATTN_E_INVALID;
+  if (q->d != 128 || k->d != 128 || v->d != 128) return MXATTN_E_UNSUPPORTED;
+  if (q->B != k->B || q->B != v->B || q->N != k->N || q->N != v->N || k->H != v->H) return MXATTN_E_INVALID;
+  if (q->H <= 0 || k->H <= 0 || q->H % k->H != 0) return MXATTN_E_INVALID;
+  if (p->kv_tile != 128) return MXATTN_E_UNSUPPORTED;
+  if (!(p->sm_scale > 0.0f) || !isfinite(p->sm_scale)) return MXATTN_E_INVALID;
+  if (ndocs < 0) return MXATTN_E_INVALID;
+  const bool docs = ndocs > 1 || (ndocs == 1 && workspace != nullptr);
+  if (docs && q->B != 1) return MXATTN_E_INVALID;
+  if ((docs ? ndocs : 1) != v->ndocs) return MXATTN_E_INVALID;
+  if (!same_fmt(q->fmt, k->fmt)) return MXATTN_E_UNSUPPORTED;
+  if (os[3] != 1 || os[0] < 0 || os[1] < 0 || os[2] < 0) return MXATTN_E_INVALID;
+
+  // operand routes
+  int qk, pv, psc = SCALE_E8M0, vsc;
+  if (is_mxfp4(q->fmt)) qk = QK_FP4;
+  else if (is_nvfp4(q->fmt)) qk = QK_BF16;
+  else return MXATTN_E_UNSUPPORTED;
+  const int pm = p->pmode;
+  if (pm == MXATTN_P_FP8_FIXED) {
+    if (!is_fp8v(v->fmt)) return MXATTN_E_UNSUPPORTED;
+    pv = PV_FP8;
+    vsc = SCALE_E8M0;
+  } else if (pm == MXATTN_P_DIRECT || pm == MXATTN_P_TWO_LEVEL || pm == MXATTN_P_PNQ) {
+    int prc = check_fmt(&p->pfmt, MXATTN_ROLE_V);
+    if (prc != MXATTN_OK) return prc;
+    if (is_mxfp4(p->pfmt)) psc = SCALE_E8M0;
+    else if (is_nvfp4(p->pfmt)) psc = SCALE_E4M3;
+    else return MXATTN_E_UNSUPPORTED;
+    if (is_mxfp4(v->fmt)) vsc = SCALE_E8M0;
+    else if (is_nvfp4(v->fmt)) vsc = SCALE_E4M3;
+    else return MXATTN_E_UNSUPPORTED;
+    pv = (psc == SCALE_E8M0 && vsc == SCALE_E8M0) ? PV_FP4 : PV_BF16;
+  } else {
+    return MXATTN_E_INVALID;
+  }
+
+  const int64_t B = q->B, Hq = q->H, Hkv = k->H, N = q->N;
+  if (B == 0 || N == 0) return MXATTN_OK;
+  if (!q->codes || !q->scales || !k->codes || !k->scales || !v->codes || !v->scales || !out) return MXATTN_E_INVALID;
+  if (!aligned16(q->codes) || !aligned16(k->codes) || !aligned16(v->codes) || !aligned16(q->scales) ||
+      !aligned16(k->scales) || !aligned16(v->scales) || !aligned16(out))
+    return MXATTN_E_ALIGN;
+  const int esz = p->out_fp32 ? 4 : 2;
+  if ((os[0] * esz) % 16 || (os[1] * esz) % 16 || (os[2] * esz) % 16) return MXATTN_E_ALIGN;
+  if (docs) {
+    if (workspace == nullptr || ws_bytes < plan_bytes(N, ndocs)) return MXATTN_E_WORKSPACE;
+    if (!aligned16(workspace)) return MXATTN_E_ALIGN;
+  }
+
+  FwdArgs a;
+  a.q = static_cast<const uint8_t*>(q->codes);
+  a.qs = static_cast<const uint8_t*>(q->scales);
+  a.k = static_cast<const uint8_t*>(k->codes);
+  a.ks = static_cast<const uint8_t*>(k->scales);
+  a.v = static_cast<const uint8_t*>(v->codes);
+  a.vs = static_cast<const uint8_t*>(v->scales);
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.N = N;
+  a.np = v->n_padded;
+  a.lambda = (float)((double)p->sm_scale * 1.4426950408889634);
+  a.sm_scale = p->sm_scale;
+  a.causal = p->causal ? 1 : 0;
+  a.prule = make_rule(&p->pfmt);
+  a.out = out;
+  a.oB = os[0];
+  a.oH = os[1];
+  a.oN = os[2];
+  a.out_fp32 = p->out_fp32 ? 1 : 0;
+  a.lse = lse;
+  a.plan = docs ? static_cast<const PlanHeader*>(workspace) : nullptr;
+  const int64_t nqt = (N + 127) / 128;
+  a.grid = docs ? Hq * (nqt + ndocs) : B * Hq * nqt;
+  if (a.grid > 0x7FFFFFFF) return MXATTN_E_UNSUPPORTED;
+  hipError_t e = launch_fwd(qk, pv, pm, psc, vsc, a, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return MXATTN_E_UNSUPPORTED;
+  if (e != hipSuccess) return hip_fail(e, "mxattn_fwd launch");
+  return MXATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// kernels.h -- launch arguments shared by the host library and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "formats.h"
+
+namespace mxattn {
+
+// element / scale / P-mode values (the mxattn.h enums)
+enum { ELEM_E2M1 = 0, ELEM_E4M3 = 1 };
+enum { SCALE_E8M0 = 0, SCALE_E4M3 = 1 };
+enum { PM_DIRECT = 1, PM_TWO_LEVEL = 2, PM_PNQ = 3, PM_FP8_FIXED = 4 };
+
+struct QuantArgs {
+  const void* x;
+  int64_t sB, sH, sN;  // element strides of x (the channel stride is 1)
+  int64_t B, H, N;
+  int64_t np;  // role V: padded key count (multiple of 128)
+  int elem, scale, block;
+  E8m0Rule rule;
+  const int32_t* cu;  // role V: device document offsets, or null
+  int ndocs;
+  void* codes;
+  void* scales;
+};
+
+hipError_t launch_quant_qk(const QuantArgs& a, hipStream_t st);
+hipError_t launch_quant_v(const QuantArgs& a, hipStream_t st);
+
+// Operand routes of the forward kernel.
+//   QK_FP4 : Q and K in E2M1 with E8M0/32 scales, scaled FP4 MFMA.
+//   QK_BF16: Q and K in E2M1 with E4M3/16 scales, dequantized (exactly) to bf16,
+//            bf16 MFMA.
+//   PV_FP4 : P in E2M1 with E8M0/32 scales, V in E2M1 with E8M0/32, scaled FP4 MFMA.
+//   PV_BF16: P and V in E2M1 with E8M0/32 or E4M3/16 scales, dequantized to bf16.
+//   PV_FP8 : P as E4M3(448 P~) with unit scale, V in E4M3 with E8M0/32, scaled FP8 MFMA.
+enum { QK_FP4 = 0, QK_BF16 = 1 };
+enum { PV_FP4 = 0, PV_BF16 = 1, PV_FP8 = 2 };
+
+// Document entry of a forward plan (workspace): first token, length, and the first
+// padded key slot of the document in a V layout with blocks of 32 and of 16.
+struct DocEntry {
+  int32_t start, len, voff32, voff16;
+};
+// Work item of a forward plan: document and query tile (128 rows, from the
+// document's first token).
+struct WorkItem {
+  int32_t doc, qtile;
+};
+// Workspace header of a plan.
+struct PlanHeader {
+  int32_t n_items, ndocs, causal, magic;
+};
+constexpr int32_t PLAN_MAGIC = 0x4D585031;  // "MXP1"
+
+struct FwdArgs {
+  // Q codes [B][Hq][N][64 B], scales [B][Hq][N][4 or 8 B]
+  const uint8_t* q;
+  const uint8_t* qs;
+  const uint8_t* k;
+  const uint8_t* ks;
+  // V^T codes [B][Hkv][128][np * bits / 8], scales [B][Hkv][128][np / vblock]
+  const uint8_t* v;
+  const uint8_t* vs;
+  int64_t B, Hq, Hkv, N, np;
+  float lambda;    // sm_scale * log2(e)
+  float sm_scale;  // for the log-sum-exp
+  int causal;
+  E8m0Rule prule;  // E8M0 rule of P (PV_FP4 and PV_BF16 with E8M0 P)
+  void* out;
+  int64_t oB, oH, oN;  // element strides of out
+  int out_fp32;
+  float* lse;
+  const PlanHeader* plan;  // packed documents, or null
+  int64_t grid;            // workgroups launched
+};
+
+// psc: P block scale (SCALE_E8M0 -> blocks of 32, SCALE_E4M3 -> blocks of 16);
+// vsc: V block scale (same meaning).
+hipError_t launch_fwd(int qk, int pv, int pmode, int psc, int vsc, const FwdArgs& a, hipStream_t st);
+
+}  // namespace mxattn

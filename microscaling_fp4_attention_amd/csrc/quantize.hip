@@ -1,0 +1,229 @@
+// quantize.hip -- block quantization of bf16 Q, K and V (gfx950).
+//
+// One memory-bound pass per tensor, as the pages fuse it ahead of the attention
+// kernel (SageAttention3 notes, Q3: the V transpose is fused into quantization;
+// "FLAMIA", section 3.5: one fused quantization launch):
+//   role QK: per token, blocks of 16 or 32 consecutive channels.  Each lane loads
+//            8 channels (one 16-byte load), block maxima are reduced across the 2
+//            or 4 lanes of a block with lane shuffles, and each lane stores its 8
+//            codes as one dword.
+//   role V : per channel, blocks of consecutive tokens inside one document,
+//            written transposed.  A workgroup stages 128 padded key slots x 128
+//            channels in LDS with coalesced row loads, then each lane quantizes
+//            64 keys of one channel and stores them contiguously.
+// Scale rules ("MXAttention", section 2 and Table 1; blog "NVFP4, not MXFP4"):
+//   E8M0: exponent from the block maximum by the OCP or ceiling rule, element
+//         x * 2^-e (exact); E4M3: s = E4M3(fp32(M / 6)), element fp32(x / s).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "formats.h"
+#include "kernels.h"
+
+namespace mxattn {
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return u2f(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return u2f(w & 0xFFFF0000u); }
+
+// code of one element for a block whose scale is given either as 2^-e (E8M0,
+// inv) or as the E4M3 value s (div)
+template <int ELEM, int SCALE>
+__device__ __forceinline__ uint32_t encode_elem(float x, float inv, float s) {
+  uint32_t sign = f2u(x) >> 31;
+  float a = __builtin_fabsf(x);
+  if constexpr (ELEM == ELEM_E2M1) {
+    float y;
+    if constexpr (SCALE == SCALE_E8M0) y = a * inv;
+    else y = (s == 0.0f) ? 0.0f : a / s;
+    return e2m1_mag(y) | (sign << 3);
+  } else {
+    float y = a * inv;  // E4M3 elements only come with E8M0 scales
+    return e4m3_mag(y) | (sign << 7);
+  }
+}
+
+template <int SCALE>
+__device__ __forceinline__ uint32_t block_scale(float M, E8m0Rule rule, float* inv, float* s) {
+  if constexpr (SCALE == SCALE_E8M0) {
+    int e = e8m0_exp(M, rule);
+    *inv = exp2i_neg(e);
+    *s = 0.0f;
+    return (uint32_t)(e + 127);
+  } else {
+    uint32_t c = e4m3_mag(M / 6.0f);
+    *s = e4m3_value(c);
+    *inv = 0.0f;
+    return c;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// role QK: x [B][H][N][128] (strided), codes [B][H][N][64], scales [B][H][N][128/BLOCK]
+// ---------------------------------------------------------------------------
+template <int SCALE, int BLOCK>
+__global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restrict__ x, int64_t sB, int64_t sH,
+                                                       int64_t sN, int64_t H, int64_t N, int64_t rows,
+                                                       E8m0Rule rule, uint32_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales) {
+  int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  int64_t row = gid >> 4;
+  int chunk = (int)(gid & 15);
+  bool live = row < rows;
+  int64_t r = live ? row : rows - 1;
+  int64_t n = r % N, bh = r / N;
+  int64_t h = bh % H, b = bh / H;
+  const uint4 v = *reinterpret_cast<const uint4*>(x + b * sB + h * sH + n * sN + chunk * 8);
+  float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+  float M = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; j++) M = __builtin_fmaxf(M, __builtin_fabsf(f[j]));
+  // lanes of one block are adjacent: 2 (BLOCK 16) or 4 (BLOCK 32)
+  M = __builtin_fmaxf(M, __shfl_xor(M, 1));
+  if constexpr (BLOCK == 32) M = __builtin_fmaxf(M, __shfl_xor(M, 2));
+  float inv, s;
+  uint32_t sb = block_scale<SCALE>(M, rule, &inv, &s);
+  uint32_t w = 0;
+#pragma unroll
+  for (int j = 0; j < 8; j++) w |= encode_elem<ELEM_E2M1, SCALE>(f[j], inv, s) << (4 * j);
+  if (live) {
+    codes[row * 16 + chunk] = w;
+    if ((chunk & (BLOCK / 8 - 1)) == 0) scales[row * (128 / BLOCK) + chunk / (BLOCK / 8)] = (uint8_t)sb;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// role V: x [B][H][N][128] (strided) -> codes [B][H][128][np * bits/8],
+// scales [B][H][128][np / BLOCK].  One workgroup per (b, h, 128 key slots).
+// cu: device document offsets (ndocs + 1) or null for one document [0, N).
+// ---------------------------------------------------------------------------
+constexpr int VQ_ROW = 128 * 2 + 16;  // bytes per staged token row (bf16, padded)
+
+template <int ELEM, int SCALE, int BLOCK>
+__global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict__ x, int64_t sB, int64_t sH,
+                                                      int64_t sN, int64_t H, int64_t N, int64_t np,
+                                                      const int32_t* __restrict__ cu, int ndocs, E8m0Rule rule,
+                                                      uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  __shared__ int32_t tok[128];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[128 * VQ_ROW];
+  const int tid = threadIdx.x;
+  const int64_t ntiles = np / 128;
+  const int64_t bh = blockIdx.x / ntiles;
+  const int64_t t0 = (blockIdx.x % ntiles) * 128;
+  const int64_t b = bh / H, h = bh % H;
+
+  // padded key slot -> token (or -1 for padding)
+  if (tid < 128) {
+    int64_t p = t0 + tid;
+    int32_t t = -1;
+    if (cu == nullptr) {
+      if (p < N) t = (int32_t)p;
+    } else {
+      int64_t voff = 0;
+      for (int k = 0; k < ndocs; k++) {
+        int64_t L = cu[k + 1] - cu[k];
+        int64_t span = (L + BLOCK - 1) / BLOCK * BLOCK;
+        if (p < voff + span) {
+          if (p - voff < L) t = (int32_t)(cu[k] + (p - voff));
+          break;
+        }
+        voff += span;
+      }
+    }
+    tok[tid] = t;
+  }
+  __syncthreads();
+  // stage 128 token rows x 256 bytes: 2048 chunks of 16 bytes
+  const uint16_t* xb = x + b * sB + h * sH;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    int c = tid + 256 * i;
+    int row = c >> 4, part = c & 15;
+    int32_t t = tok[row];
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (t >= 0) v = *reinterpret_cast<const uint4*>(xb + (int64_t)t * sN + part * 8);
+    *reinterpret_cast<uint4*>(tile + row * VQ_ROW + part * 16) = v;
+  }
+  __syncthreads();
+  // lane -> (channel, 64 keys)
+  const int ch = tid & 127, sub = tid >> 7;
+  const int64_t crow = bh * 128 + ch;
+  constexpr int NB = 64 / BLOCK;
+  constexpr int BPE = ELEM == ELEM_E2M1 ? 4 : 8;  // bits per element
+  uint32_t out[64 * BPE / 32];
+#pragma unroll
+  for (int i = 0; i < 64 * BPE / 32; i++) out[i] = 0;
+  uint32_t sbytes = 0;
+#pragma unroll
+  for (int blk = 0; blk < NB; blk++) {
+    float f[BLOCK];
+    float M = 0.0f;
+#pragma unroll
+    for (int j = 0; j < BLOCK; j++) {
+      int key = sub * 64 + blk * BLOCK + j;
+      uint32_t hbits = *reinterpret_cast<const uint16_t*>(tile + key * VQ_ROW + ch * 2);
+      f[j] = u2f(hbits << 16);
+      M = __builtin_fmaxf(M, __builtin_fabsf(f[j]));
+    }
+    float inv, s;
+    uint32_t sb = block_scale<SCALE>(M, rule, &inv, &s);
+    sbytes |= sb << (8 * blk);
+#pragma unroll
+    for (int j = 0; j < BLOCK; j++) {
+      int e = blk * BLOCK + j;  // element index within this lane's 64 keys
+      uint32_t c = encode_elem<ELEM, SCALE>(f[j], inv, s);
+      out[(e * BPE) / 32] |= c << ((e * BPE) % 32);
+    }
+  }
+  uint8_t* cdst = codes + crow * (np * BPE / 8) + (t0 + sub * 64) * BPE / 8;
+#pragma unroll
+  for (int i = 0; i < 64 * BPE / 128; i++)
+    reinterpret_cast<uint4*>(cdst)[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+  uint8_t* sdst = scales + crow * (np / BLOCK) + (t0 + sub * 64) / BLOCK;
+  if constexpr (NB == 2) *reinterpret_cast<uint16_t*>(sdst) = (uint16_t)sbytes;
+  else *reinterpret_cast<uint32_t*>(sdst) = sbytes;
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_quant_qk(const QuantArgs& a, hipStream_t st) {
+  int64_t threads = a.B * a.H * a.N * 16;
+  dim3 grid((unsigned)((threads + 255) / 256));
+  int64_t rows = a.B * a.H * a.N;
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  uint32_t* c = static_cast<uint32_t*>(a.codes);
+  uint8_t* s = static_cast<uint8_t*>(a.scales);
+  if (a.scale == SCALE_E8M0 && a.block == 32)
+    quant_qk_kernel<SCALE_E8M0, 32><<<grid, 256, 0, st>>>(x, a.sB, a.sH, a.sN, a.H, a.N, rows, a.rule, c, s);
+  else if (a.scale == SCALE_E8M0 && a.block == 16)
+    quant_qk_kernel<SCALE_E8M0, 16><<<grid, 256, 0, st>>>(x, a.sB, a.sH, a.sN, a.H, a.N, rows, a.rule, c, s);
+  else if (a.scale == SCALE_E4M3 && a.block == 16)
+    quant_qk_kernel<SCALE_E4M3, 16><<<grid, 256, 0, st>>>(x, a.sB, a.sH, a.sN, a.H, a.N, rows, a.rule, c, s);
+  else if (a.scale == SCALE_E4M3 && a.block == 32)
+    quant_qk_kernel<SCALE_E4M3, 32><<<grid, 256, 0, st>>>(x, a.sB, a.sH, a.sN, a.H, a.N, rows, a.rule, c, s);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_v(const QuantArgs& a, hipStream_t st) {
+  dim3 grid((unsigned)(a.B * a.H * (a.np / 128)));
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  uint8_t* c = static_cast<uint8_t*>(a.codes);
+  uint8_t* s = static_cast<uint8_t*>(a.scales);
+#define MXQV(E, S, BL)                                                                                   \
+  quant_v_kernel<E, S, BL><<<grid, 256, 0, st>>>(x, a.sB, a.sH, a.sN, a.H, a.N, a.np, a.cu, a.ndocs, a.rule, \
+                                                 c, s)
+  if (a.elem == ELEM_E2M1 && a.scale == SCALE_E8M0 && a.block == 32) MXQV(ELEM_E2M1, SCALE_E8M0, 32);
+  else if (a.elem == ELEM_E2M1 && a.scale == SCALE_E8M0 && a.block == 16) MXQV(ELEM_E2M1, SCALE_E8M0, 16);
+  else if (a.elem == ELEM_E2M1 && a.scale == SCALE_E4M3 && a.block == 16) MXQV(ELEM_E2M1, SCALE_E4M3, 16);
+  else if (a.elem == ELEM_E2M1 && a.scale == SCALE_E4M3 && a.block == 32) MXQV(ELEM_E2M1, SCALE_E4M3, 32);
+  else if (a.elem == ELEM_E4M3 && a.scale == SCALE_E8M0 && a.block == 32) MXQV(ELEM_E4M3, SCALE_E8M0, 32);
+  else if (a.elem == ELEM_E4M3 && a.scale == SCALE_E8M0 && a.block == 16) MXQV(ELEM_E4M3, SCALE_E8M0, 16);
+  else return hipErrorInvalidValue;
+#undef MXQV
+  return hipGetLastError();
+}
+
+}  // namespace mxattn

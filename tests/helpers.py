@@ -1,0 +1,140 @@
+"""Shared helpers of the GPU tests: run the HIP path and the CPU oracle on the
+same seeded inputs and compare them.
+
+The oracle side quantizes with its own C routines; the GPU side with
+mxattn_quantize.  Quantized bytes must agree exactly; the forward output (FP32)
+must satisfy |dO| <= 2e-3 * max|O_oracle| + flip budget of the row, where the
+flip budget bounds the effect of rounding decisions that lie within a relative
+2^-12 of a threshold (the oracle reports it per row).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import synth
+
+TOL = 2e-3
+
+
+def gpu_available() -> bool:
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+def unpack_nibbles(b: np.ndarray) -> np.ndarray:
+    """uint8 [..., n] -> uint8 [..., 2n] with the low nibble first."""
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = b & 15
+    out[..., 1::2] = b >> 4
+    return out
+
+
+def v_slots(N, doc_off, block):
+    """token -> padded key slot of the V layout (document-local blocks)."""
+    if doc_off is None:
+        return np.arange(N)
+    slots = np.empty(N, dtype=np.int64)
+    voff = 0
+    for k in range(len(doc_off) - 1):
+        s, e = int(doc_off[k]), int(doc_off[k + 1])
+        slots[s:e] = voff + np.arange(e - s)
+        voff += (e - s + block - 1) // block * block
+    return slots
+
+
+def gpu_codes_qk(qt) -> np.ndarray:
+    """GPU QK codes as one code per byte [B, H, N, d]."""
+    return unpack_nibbles(qt.codes_view().cpu().numpy()) if qt.desc.fmt.elem == 0 else qt.codes_view().cpu().numpy()
+
+
+def gpu_codes_v(qt, N, doc_off) -> tuple[np.ndarray, np.ndarray]:
+    """GPU V codes and scales in the oracle's layout: codes [B, H, d, N] by token,
+    scales [B, H, d, nblk] (document by document)."""
+    c = qt.codes_view().cpu().numpy()
+    if qt.desc.fmt.elem == 0:
+        c = unpack_nibbles(c)
+    slots = v_slots(N, doc_off, qt.desc.fmt.block)
+    nblk = oracle.v_nblocks(N, doc_off, qt.desc.fmt.block)
+    return c[..., slots], qt.scales_view().cpu().numpy()[..., :nblk]
+
+
+def oracle_quant_qk(x: np.ndarray, fmt):
+    codes, scales = oracle.quantize_rows(x, fmt)
+    return codes, scales, oracle.dequant_rows(codes, scales, fmt)
+
+
+def oracle_quant_v(x: np.ndarray, fmt, doc_off=None):
+    """x [B, H, N, d] -> codes [B, H, d, N], scales [B, H, d, nblk], dequantized [B, H, N, d]."""
+    B, H, N, d = x.shape
+    nblk = oracle.v_nblocks(N, doc_off, oracle.fmt(fmt).block)
+    codes = np.zeros((B, H, d, N), np.uint8)
+    scales = np.zeros((B, H, d, nblk), np.uint8)
+    deq = np.zeros_like(x, dtype=np.float32)
+    for b in range(B):
+        for h in range(H):
+            c, s = oracle.quantize_cols(x[b, h], fmt, doc_off)
+            codes[b, h], scales[b, h] = c, s
+            deq[b, h] = oracle.dequant_cols(c, s, fmt, doc_off)
+    return codes, scales, deq
+
+
+PM_ORACLE = {"direct": oracle.P_DIRECT, "two_level": oracle.P_TWO_LEVEL, "pnq": oracle.P_PNQ,
+             "fp8": oracle.P_FP8_FIXED}
+
+
+def run_case(qfmt, vfmt, pmode, pfmt, B, Hq, Hkv, N, causal=False, kind="kmean", seed=0, doc_off=None,
+             rows=None, check_bytes=True, inputs=None):
+    """Run one forward on the GPU and on the oracle; returns a dict of results."""
+    import torch
+    import microscaling_fp4_attention_amd as mx
+
+    x = inputs if inputs is not None else synth.make_inputs(kind, B, Hq, Hkv, N, 128, seed)
+    qf, kf, vf = (synth.bf16_to_f32(x[n]) for n in ("q", "k", "v"))
+    dev = torch.device("cuda:0")
+
+    def to_dev(a):
+        return torch.from_numpy(a.astype(np.int16)).view(torch.bfloat16).to(dev)
+
+    qg, kg, vg = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
+    cu = None if doc_off is None else torch.from_numpy(np.asarray(doc_off, np.int32)).to(dev)
+    Qq = mx.quantize(qg, mx.ROLE_QK, qfmt)
+    Kq = mx.quantize(kg, mx.ROLE_QK, qfmt)
+    Vq = mx.quantize(vg, mx.ROLE_V, vfmt, cu_seqlens=cu)
+    params = mx.fwd_params(pmode, pfmt, causal=causal)
+    ws, nd = None, 0
+    if doc_off is not None:
+        ws = mx.fwd_plan(doc_off, N, causal)
+        nd = len(doc_off) - 1
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    out = mx.fwd(Qq, Kq, Vq, params, lse=lse, workspace=ws, ndocs=nd)
+    torch.cuda.synchronize()
+    O_gpu = out.cpu().numpy().reshape(-1, 128)
+    lse_gpu = lse.cpu().numpy().reshape(-1)
+
+    res = {}
+    # oracle quantization (bytes must match the GPU's)
+    qc, qs, qd = oracle_quant_qk(qf, qfmt)
+    kc, ks, kd = oracle_quant_qk(kf, qfmt)
+    vc, vs, vd = oracle_quant_v(vf, vfmt, doc_off)
+    if check_bytes:
+        assert np.array_equal(gpu_codes_qk(Qq), qc), "Q codes differ"
+        assert np.array_equal(Qq.scales_view().cpu().numpy(), qs), "Q scales differ"
+        assert np.array_equal(gpu_codes_qk(Kq), kc), "K codes differ"
+        assert np.array_equal(Kq.scales_view().cpu().numpy(), ks), "K scales differ"
+        gc, gs = gpu_codes_v(Vq, N, doc_off)
+        assert np.array_equal(gc, vc), "V codes differ"
+        assert np.array_equal(gs, vs), "V scales differ"
+    O_ref, lse_ref, fb = oracle.attention(qd, kd, vd, PM_ORACLE[pmode], pfmt, causal=causal, doc_off=doc_off,
+                                          rows=rows)
+    sel = np.arange(B * Hq * N) if rows is None else np.asarray(rows)
+    Og = O_gpu[sel]
+    err = np.abs(Og - O_ref)
+    amax = np.abs(O_ref).max()
+    bound = TOL * amax + fb[:, None]
+    res.update(err=err, bound=bound, amax=amax, fb=fb, O_ref=O_ref, O_gpu=Og, lse_ref=lse_ref, lse_gpu=lse_gpu[sel],
+               ratio=float((err / bound).max()) if err.size else 0.0, n_fragile=int((fb > 0).sum()))
+    return res

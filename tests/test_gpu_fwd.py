@@ -1,0 +1,120 @@
+"""GPU forward (mxattn_fwd) against the oracle, element by element in FP32:
+|dO| <= 2e-3 * max|O_oracle| + the row's flip budget.  Shapes span several key
+tiles with a ragged tail; the cases cover every operand route, causal masks,
+grouped-query heads and packed documents."""
+import numpy as np
+import pytest
+
+import synth
+from helpers import gpu_available, run_case
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+# (Q/K format, V format, P mode, P format)
+ROUTES = {
+    "mxfp4_direct": ("mxfp4", "mxfp4", "direct", "mxfp4"),
+    "mxfp4_uos_pnq": ("mxfp4_uos", "mxfp4_uos", "pnq", "mxfp4_uos"),
+    "mxfp4_two_level_e8m0": ("mxfp4", "mxfp4", "two_level", "mxfp4"),
+    "mxfp4_two_level_e4m3": ("mxfp4", "mxfp4", "two_level", "nvfp4"),
+    "mxfp4_direct_e4m3p": ("mxfp4", "mxfp4", "direct", "nvfp4"),
+    "nvfp4_direct": ("nvfp4", "nvfp4", "direct", "nvfp4"),
+    "nvfp4_two_level": ("nvfp4", "nvfp4", "two_level", "nvfp4"),
+    "nvfp4_pnq": ("nvfp4", "nvfp4", "pnq", "nvfp4"),
+    "nvfp4_qk_mxfp4_pv": ("nvfp4", "mxfp4", "pnq", "mxfp4"),
+    "qk4pv8": ("nvfp4", "fp8v", "fp8", None),
+    "mxfp4_qk_pv8": ("mxfp4", "fp8v", "fp8", None),
+}
+
+
+def _check(res, name):
+    print(f"{name}: max err/bound {res['ratio']:.3f}, fragile rows {res['n_fragile']}, amax {res['amax']:.3f}")
+    assert np.all(np.isfinite(res["O_gpu"]))
+    assert res["ratio"] <= 1.0, name
+
+
+@pytest.mark.parametrize("route", list(ROUTES))
+def test_fwd_route_noncausal(route):
+    q, v, pm, pf = ROUTES[route]
+    res = run_case(q, v, pm, pf, B=1, Hq=2, Hkv=2, N=300, kind="kmean")
+    _check(res, route)
+
+
+@pytest.mark.parametrize("route", ["mxfp4_direct", "mxfp4_uos_pnq", "mxfp4_two_level_e4m3", "nvfp4_two_level",
+                                   "qk4pv8"])
+def test_fwd_causal_gqa(route):
+    q, v, pm, pf = ROUTES[route]
+    res = run_case(q, v, pm, pf, B=2, Hq=4, Hkv=2, N=257, causal=True, kind="kmean", seed=3)
+    _check(res, route + " causal gqa")
+    lse_ok = np.abs(res["lse_gpu"] - res["lse_ref"]) <= 1e-3 * np.maximum(1.0, np.abs(res["lse_ref"]))
+    assert lse_ok.all()
+
+
+@pytest.mark.parametrize("route", ["mxfp4_uos_pnq", "mxfp4_two_level_e4m3", "mxfp4_two_level_e8m0", "qk4pv8"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_packed_documents(route, causal):
+    q, v, pm, pf = ROUTES[route]
+    doc_off = np.array([0, 100, 101, 357, 490, 700], np.int32)  # includes a 1-token document
+    res = run_case(q, v, pm, pf, B=1, Hq=2, Hkv=2, N=700, causal=causal, kind="outlier", seed=4, doc_off=doc_off)
+    _check(res, route + f" docs causal={causal}")
+
+
+def test_fwd_config1_all_rows():
+    """Single head, N = 1024, K with a per-channel mean: the four direct/two-level
+    modes of the smallest configuration, every row."""
+    x = synth.workload("c1_single_head")
+    for qf, pm in [("nvfp4", "direct"), ("nvfp4", "two_level"), ("mxfp4", "direct"), ("mxfp4", "two_level")]:
+        res = run_case(qf, qf, pm, "nvfp4" if pm == "two_level" else qf, B=1, Hq=1, Hkv=1, N=1024, inputs=x)
+        _check(res, f"c1 {qf} {pm}")
+
+
+def test_fwd_small_and_degenerate_shapes():
+    # one token, one tile exactly, and a tail of one key
+    for N in (1, 128, 129):
+        res = run_case("mxfp4_uos", "mxfp4_uos", "pnq", "mxfp4_uos", B=1, Hq=1, Hkv=1, N=N, kind="plain", seed=5)
+        _check(res, f"N={N}")
+
+
+def test_fwd_deterministic():
+    import torch
+    import microscaling_fp4_attention_amd as mx
+    x = synth.make_inputs("lowrank", 1, 2, 2, 700, 128, 6)
+    dev = "cuda:0"
+    t = {n: torch.from_numpy(x[n].astype(np.int16)).view(torch.bfloat16).to(dev) for n in "qkv"}
+    outs = []
+    for _ in range(2):
+        Q = mx.quantize(t["q"], mx.ROLE_QK, "mxfp4_uos")
+        K = mx.quantize(t["k"], mx.ROLE_QK, "mxfp4_uos")
+        V = mx.quantize(t["v"], mx.ROLE_V, "mxfp4_uos")
+        outs.append(mx.fwd(Q, K, V, mx.fwd_params("pnq", "mxfp4_uos")).cpu())
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_fwd_pnq_rows_sum_to_one():
+    """PNQ (MXAttention Proposition 1): with V = 1 (MXFP4 encodes 1 exactly) every
+    output entry is 1 up to FP32 rounding, whatever the scores."""
+    import torch
+    import microscaling_fp4_attention_amd as mx
+    x = synth.make_inputs("lowrank", 1, 2, 2, 400, 128, 8)
+    dev = "cuda:0"
+    q = torch.from_numpy(x["q"].astype(np.int16)).view(torch.bfloat16).to(dev)
+    k = torch.from_numpy(x["k"].astype(np.int16)).view(torch.bfloat16).to(dev)
+    v = torch.ones((1, 2, 400, 128), dtype=torch.bfloat16, device=dev)
+    Q = mx.quantize(q, mx.ROLE_QK, "mxfp4_uos")
+    K = mx.quantize(k, mx.ROLE_QK, "mxfp4_uos")
+    V = mx.quantize(v, mx.ROLE_V, "mxfp4_uos")
+    o = mx.fwd(Q, K, V, mx.fwd_params("pnq", "mxfp4_uos")).cpu().numpy()
+    assert np.abs(o - 1.0).max() <= 1e-5
+
+
+def test_fwd_bf16_output_matches_fp32():
+    import torch
+    import microscaling_fp4_attention_amd as mx
+    x = synth.make_inputs("kmean", 1, 2, 2, 300, 128, 9)
+    dev = "cuda:0"
+    t = {n: torch.from_numpy(x[n].astype(np.int16)).view(torch.bfloat16).to(dev) for n in "qkv"}
+    Q = mx.quantize(t["q"], mx.ROLE_QK, "mxfp4")
+    K = mx.quantize(t["k"], mx.ROLE_QK, "mxfp4")
+    V = mx.quantize(t["v"], mx.ROLE_V, "mxfp4")
+    o32 = mx.fwd(Q, K, V, mx.fwd_params("direct", "mxfp4", out_fp32=True))
+    o16 = mx.fwd(Q, K, V, mx.fwd_params("direct", "mxfp4", out_fp32=False))
+    assert torch.equal(o32.to(torch.bfloat16), o16)

@@ -1,0 +1,117 @@
+"""GPU quantize pass (mxattn_quantize) against the oracle: every code and scale
+byte must be identical (MXAttention section 2 and Table 1 for the E8M0 rules;
+blog "NVFP4, not MXFP4" for s = E4M3(amax/6); MpFA section 4.1 and FLAMIA
+section 3.2 for E4M3 V with a power-of-two scale per 32 keys)."""
+import numpy as np
+import pytest
+
+import synth
+from helpers import gpu_available, gpu_codes_qk, gpu_codes_v, oracle_quant_qk, oracle_quant_v
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+def _dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).astype(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+
+def _edge_values(n_rows):
+    """Rows that exercise zero blocks, -0, rounding ties at every E2M1 midpoint,
+    saturation, tiny and huge magnitudes, bf16 subnormals and the largest bf16."""
+    rng = np.random.default_rng(7)
+    rows = []
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0, 6.5, 5.5, 0.1, 0.0])
+    for r in range(n_rows):
+        x = np.zeros(128, np.float32)
+        kind = r % 8
+        if kind == 0:
+            pass  # all zero
+        elif kind == 1:
+            x[:] = -0.0
+        elif kind == 2:  # ties relative to a block max of 6 (scale 1 under OCP: M=6 -> e=0)
+            x[:] = np.resize(np.concatenate([mids, -mids]), 128)
+            x[::32] = 6.0
+        elif kind == 3:  # ties at scale 2^-3
+            x[:] = np.resize(np.concatenate([mids, -mids]), 128) * 0.125
+            x[::16] = 0.75
+        elif kind == 4:
+            x[:] = rng.standard_normal(128) * 1e-38  # subnormal range
+        elif kind == 5:
+            x[:] = rng.standard_normal(128) * 1e37
+            x[5] = 3.3895314e38  # largest bf16
+        elif kind == 6:  # block maxima exactly at 7.25 * 2^k and just around it
+            x[:] = rng.uniform(-1, 1, 128)
+            x[0], x[32], x[64], x[96] = 7.25, 7.25 * 2 ** -5, np.nextafter(np.float32(7.25), 9), 3.625
+            x[16], x[48], x[80], x[112] = 6.0, 6.0 * 2 ** 3, np.nextafter(np.float32(6.0), 0), 448.0
+        else:
+            x[:] = rng.standard_normal(128) * 3.0
+        rows.append(x)
+    return synth.f32_to_bf16(np.stack(rows))
+
+
+QK_FMTS = ["mxfp4", "mxfp4_uos", "mxfp4_tfs", "nvfp4"]
+V_FMTS = ["mxfp4", "mxfp4_uos", "nvfp4", "fp8v"]
+
+
+@pytest.mark.parametrize("fmt", QK_FMTS)
+@pytest.mark.parametrize("kind", ["kmean_outlier", "lowrank"])
+def test_quantize_qk_bytes(fmt, kind):
+    import microscaling_fp4_attention_amd as mx
+    x = synth.make_inputs(kind, 2, 3, 3, 300, 128, seed=1)["k"]
+    qt = mx.quantize(_dev(x), mx.ROLE_QK, fmt)
+    c, s, _ = oracle_quant_qk(synth.bf16_to_f32(x), fmt)
+    assert np.array_equal(gpu_codes_qk(qt), c)
+    assert np.array_equal(qt.scales_view().cpu().numpy(), s)
+
+
+@pytest.mark.parametrize("fmt", QK_FMTS)
+def test_quantize_qk_edge_cases(fmt):
+    import microscaling_fp4_attention_amd as mx
+    x = _edge_values(40).reshape(1, 1, 40, 128)
+    qt = mx.quantize(_dev(x), mx.ROLE_QK, fmt)
+    c, s, _ = oracle_quant_qk(synth.bf16_to_f32(x), fmt)
+    assert np.array_equal(gpu_codes_qk(qt), c)
+    assert np.array_equal(qt.scales_view().cpu().numpy(), s)
+
+
+def test_quantize_qk_strided_input():
+    """A [B, N, H, d] tensor viewed as [B, H, N, d] (non-contiguous heads)."""
+    import microscaling_fp4_attention_amd as mx
+    x = synth.make_inputs("plain", 1, 4, 4, 200, 128, seed=3)["q"]
+    g = _dev(x.transpose(0, 2, 1, 3).copy()).permute(0, 2, 1, 3)
+    assert not g.is_contiguous()
+    qt = mx.quantize(g, mx.ROLE_QK, "mxfp4")
+    c, s, _ = oracle_quant_qk(synth.bf16_to_f32(x), "mxfp4")
+    assert np.array_equal(gpu_codes_qk(qt), c)
+    assert np.array_equal(qt.scales_view().cpu().numpy(), s)
+
+
+@pytest.mark.parametrize("fmt", V_FMTS)
+@pytest.mark.parametrize("docs", [None, [0, 37, 100, 229, 300], [0, 300]])
+def test_quantize_v_bytes(fmt, docs):
+    import torch
+    import microscaling_fp4_attention_amd as mx
+    x = synth.make_inputs("plain", 1, 2, 2, 300, 128, seed=2)["v"]
+    doc_off = None if docs is None else np.array(docs, np.int32)
+    cu = None if docs is None else torch.tensor(docs, dtype=torch.int32, device="cuda:0")
+    qt = mx.quantize(_dev(x), mx.ROLE_V, fmt, cu_seqlens=cu)
+    c, s, _ = oracle_quant_v(synth.bf16_to_f32(x), fmt, doc_off)
+    gc, gs = gpu_codes_v(qt, 300, doc_off)
+    assert np.array_equal(gc, c)
+    assert np.array_equal(gs, s)
+    # padding slots hold code 0 and padding-only blocks the all-zero scale
+    full = qt.codes_view().cpu().numpy()
+    nb = qt.n_padded
+    assert full.shape[-1] * (2 if qt.desc.fmt.elem == 0 else 1) == nb
+
+
+@pytest.mark.parametrize("fmt", V_FMTS)
+def test_quantize_v_edge_cases(fmt):
+    import microscaling_fp4_attention_amd as mx
+    x = _edge_values(128).reshape(1, 1, 128, 128)
+    qt = mx.quantize(_dev(x), mx.ROLE_V, fmt)
+    c, s, _ = oracle_quant_v(synth.bf16_to_f32(x), fmt)
+    gc, gs = gpu_codes_v(qt, 128, None)
+    assert np.array_equal(gc, c)
+    assert np.array_equal(gs, s)
