@@ -79,6 +79,18 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 // the other lane half's value (lanes q and q+32 hold the two halves of a row)
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
 
+// max / sum of the two lane halves of a row, in registers: v_permlane32_swap with
+// both operands x leaves x of lanes 0-31 in every lane of the first result and x of
+// lanes 32-63 in every lane of the second
+__device__ __forceinline__ float halves_max(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+  return __builtin_fmaxf(u2f(p[0]), u2f(p[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+  return u2f(p[0]) + u2f(p[1]);
+}
+
 // two floats whose values have at most 8 significant bits -> packed bf16 (exact)
 __device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
   return (f2u(lo) >> 16) | (f2u(hi) & 0xFFFF0000u);
@@ -150,17 +162,26 @@ __device__ __forceinline__ int kpos(int r) {
 
 template <int QK, int PV>
 struct Lds {
-  static constexpr int KROW = QK == QK_FP4 ? 80 : 256;
-  static constexpr int VROW = PV == PV_FP4 ? 80 : PV == PV_BF16 ? 256 : 144;
-  static constexpr int BYTES = 128 * (KROW + VROW);
+  static constexpr int KROW = QK == QK_FP4 ? 80 : 256;  // bytes per staged key row
+  static constexpr int VROW = PV == PV_FP4 ? 80 : PV == PV_BF16 ? 256 : 144;  // per V^T row
+  static constexpr int STAGE = 128 * (KROW + VROW);      // one key tile
+  // Buffers of key tiles: 3 lets the next tile's scores and this tile's PV read
+  // different buffers while a third is refilled (one barrier per tile); 2 needs a
+  // second barrier; 1 (large bf16 tiles) falls back to compute-after-store.  Two
+  // workgroups share a CU's 160 KB.
+  static constexpr int NB = 3 * STAGE <= 80 * 1024 ? 3 : 2 * STAGE <= 80 * 1024 ? 2 : 1;
+  static constexpr int BYTES = NB * STAGE;
 };
 
+// Waves per SIMD the kernel is compiled for (256 registers each).
+template <int QK, int PV>
+constexpr int waves_per_simd() { return 2; }
+
 template <int QK, int PV, int PMODE, int PSC, int VSC>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   using L = Lds<QK, PV>;
-  uint8_t* Ks = smem;
-  uint8_t* Vs = smem + 128 * L::KROW;
+  constexpr int NB = L::NB;
   constexpr int VB = VSC == SCALE_E8M0 ? 32 : 16;  // V block along keys
   constexpr bool SPLIT16 = PV == PV_FP8;            // key permutation of the FP8 MFMA
 
@@ -203,12 +224,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     vstart = 0;
   }
   const int64_t hk = hq * a.Hkv / a.Hq;
-  const int64_t qloc = qt * 128 + 32 * wave + ql;  // this lane's query within its sequence
+  const int qloc = (int)(qt * 128) + 32 * wave + ql;  // this lane's query within its sequence
   const int64_t qrow = (b * a.Hq + hq) * a.N + qstart + (qloc < qlen ? qloc : qlen - 1);
   const int64_t kbase = (b * a.Hkv + hk) * a.N + qstart;  // K row of the sequence's first key
   const int64_t vrow0 = (b * a.Hkv + hk) * 128;           // first V^T row of the head
-  int64_t nkt = (klen + 127) / 128;
-  if (a.causal && nkt > qt + 1) nkt = qt + 1;
+  int nkt = (int)((klen + 127) / 128);
+  if (a.causal && nkt > qt + 1) nkt = (int)qt + 1;
+  const int klen32 = (int)klen;
   const float lam = a.lambda;
 
   // ---------------- Q operand (B operand of S^T = K Q^T), held for the whole loop ----------------
@@ -243,29 +265,28 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   for (int i = 0; i < 4; i++) O[i] = zero16();
   Lacc = zero16();
 
-  // ---------------- staging registers (next tile) ----------------
-  constexpr int NKC = 2;                              // K code chunks of 16 B per thread
+  // ---------------- staging registers (a tile in flight) ----------------
+  constexpr int NKC = 2;                                   // K code chunks of 16 B per thread
   constexpr int NVC = (PV == PV_FP8 || VB == 16) ? 4 : 2;  // V code chunks per thread
   u4 kreg[NKC];
-  uint32_t kscr[NKC];  // QK_FP4: row scales (thread < 128); QK_BF16: 2 scale bytes per chunk
-  u4 vreg[NVC];     // VB == 16 and E2M1: only .x,.y used (8-byte chunks)
-  uint32_t vscr[NVC];  // scales: PV_FP4/PV_FP8 thread >= 128 holds a channel's 4 bytes in [0];
-                       // PV_BF16: the chunk's block scale byte
+  uint32_t kscr[NKC];  // QK_FP4: row scales in [0]; QK_BF16: 2 scale bytes per chunk
+  u4 vreg[NVC];        // VB == 16 with E2M1: only .x, .y used (8-byte chunks)
+  uint32_t vscr[NVC];  // PV_FP4/PV_FP8: a channel's 4 block scales in [0]; PV_BF16: the chunk's scale
 
-  auto load_tile = [&](int64_t kt) __attribute__((always_inline)) {
+  auto load_tile = [&](int kt) __attribute__((always_inline)) {
     // K rows: 512 chunks of 16 bytes
 #pragma unroll
     for (int i = 0; i < NKC; i++) {
       int c = tid + 256 * i, row = c >> 2, part = c & 3;
-      int64_t key = kt * 128 + row;
-      if (key >= klen) key = klen - 1;
+      int key = kt * 128 + row;
+      if (key >= klen32) key = klen32 - 1;
       kreg[i] = *reinterpret_cast<const u4*>(a.k + (kbase + key) * 64 + part * 16);
       if constexpr (QK == QK_BF16)
         kscr[i] = *reinterpret_cast<const uint16_t*>(a.ks + (kbase + key) * 8 + 2 * part);
     }
     if constexpr (QK == QK_FP4) {  // every thread loads (row tid % 128); threads < 128 store
-      int64_t key = kt * 128 + (tid & 127);
-      if (key >= klen) key = klen - 1;
+      int key = kt * 128 + (tid & 127);
+      if (key >= klen32) key = klen32 - 1;
       kscr[0] = *reinterpret_cast<const uint32_t*>(a.ks + (kbase + key) * 4);
     }
     // V^T rows (channels)
@@ -306,7 +327,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     }
   };
 
-  auto store_tile = [&]() __attribute__((always_inline)) {
+  auto store_tile = [&](int buf) __attribute__((always_inline)) {
+    uint8_t* Ks = smem + buf * L::STAGE;
+    uint8_t* Vs = Ks + 128 * L::KROW;
 #pragma unroll
     for (int i = 0; i < NKC; i++) {
       int c = tid + 256 * i, row = c >> 2, part = c & 3;
@@ -357,56 +380,63 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     }
   };
 
-  if (nkt > 0) load_tile(0);
-
-  for (int64_t kt = 0; kt < nkt; kt++) {
-    __syncthreads();  // the previous tile's LDS reads are done
-    store_tile();
-    __syncthreads();
-    // next tile in flight during this tile's math (the last iteration reloads its own
-    // tile: an unconditional load keeps the staging registers out of scratch memory)
-    load_tile(kt + 1 < nkt ? kt + 1 : kt);
-
-    // ---------------- S^T = K Q^T ----------------
-    v16f S[4];
+  // ---------------- S^T = K Q^T of the tile in buffer `buf`, sub-tile bb (32 keys) ----------------
+  auto scores_sub = [&](int buf, int bb, uint32_t after = 0) __attribute__((always_inline)) -> v16f {
+    // `after`: a value this sub-tile's work must wait for.  Routing the LDS offset through
+    // an empty asm that reads it keeps the compiler from hoisting these loads and MFMAs
+    // (pure operations) above the work that produced it.
+    uint32_t boff = (uint32_t)(buf * L::STAGE);
+    asm volatile("" : "+v"(boff) : "v"(after));
+    const uint8_t* Ks = smem + boff;
+    v16f acc = zero16();
+    if constexpr (QK == QK_FP4) {
+      const uint8_t* rp = Ks + (32 * bb + ql) * 80;
+      uint32_t ks4 = *reinterpret_cast<const uint32_t*>(rp + 64);
 #pragma unroll
-    for (int bb = 0; bb < 4; bb++) {
-      S[bb] = zero16();
-      if constexpr (QK == QK_FP4) {
-        const uint8_t* rp = Ks + (32 * bb + ql) * 80;
-        uint32_t ks4 = *reinterpret_cast<const uint32_t*>(rp + 64);
+      for (int c = 0; c < 2; c++) {
+        v8i av = v8_from4(*reinterpret_cast<const u4*>(rp + 32 * c + 16 * hh));
+        int sa = (int)((ks4 >> (8 * (2 * c + hh))) & 0xFF);
+        acc = mfma_fp4(av, qop[c], acc, sa, qsc[c]);
+      }
+    } else {
+      const uint8_t* rp = Ks + (32 * bb + ql) * 256;
 #pragma unroll
-        for (int c = 0; c < 2; c++) {
-          v8i av = v8_from4(*reinterpret_cast<const u4*>(rp + 32 * c + 16 * hh));
-          int sa = (int)((ks4 >> (8 * (2 * c + hh))) & 0xFF);
-          S[bb] = mfma_fp4(av, qop[c], S[bb], sa, qsc[c]);
-        }
-      } else {
-        const uint8_t* rp = Ks + (32 * bb + ql) * 256;
-#pragma unroll
-        for (int s = 0; s < 8; s++) {
-          int chunk = (2 * s + hh) ^ (ql & 15);
-          v8bf av = *reinterpret_cast<const v8bf*>(rp + chunk * 16);
-          S[bb] = mfma_bf16(av, qbf[s], S[bb]);
-        }
+      for (int s = 0; s < 8; s++) {
+        int chunk = (2 * s + hh) ^ (ql & 15);
+        v8bf av = *reinterpret_cast<const v8bf*>(rp + chunk * 16);
+        acc = mfma_bf16(av, qbf[s], acc);
       }
     }
+    return acc;
+  };
+  auto scores = [&](int buf, v16f* S) __attribute__((always_inline)) {
+#pragma unroll
+    for (int bb = 0; bb < 4; bb++) S[bb] = scores_sub(buf, bb);
+  };
 
-    // ---------------- mask (tail keys, causal diagonal) ----------------
-    const int64_t k0 = kt * 128;
-    const bool need_mask = (k0 + 128 > klen) || (a.causal && k0 + 127 > qt * 128 + 32 * wave);
+  // ---------------- softmax, P quantization and PV of one tile ----------------
+  // ---------------- softmax, P quantization and PV of one tile ----------------
+  // S: this tile's scores (consumed).  When NEXT, the scores of the next tile (buffer
+  // nbuf) are computed into S on the matrix cores, one 32-key sub-tile at a time, as
+  // soon as this tile's sub-tile has been exponentiated and quantized, so that only
+  // one tile of scores is live and the MFMAs run between the exponentials.
+  auto softmax_pv = [&](int kt, int buf, v16f* S, bool next, int nbuf) __attribute__((always_inline)) {
+    const uint8_t* Vs = smem + buf * L::STAGE + 128 * L::KROW;
+    // mask (tail keys, causal diagonal): wave-uniform test, per-element select
+    const int k0 = kt * 128;
+    const bool need_mask = (k0 + 128 > klen32) || (a.causal && k0 + 127 > (int)qt * 128 + 32 * wave);
     if (need_mask) {
 #pragma unroll
       for (int bb = 0; bb < 4; bb++)
 #pragma unroll
         for (int j = 0; j < 16; j++) {
-          int64_t key = k0 + key_of<SPLIT16>(bb, hh, j);
-          bool vis = key < klen && (!a.causal || key <= qloc);
+          int key = k0 + key_of<SPLIT16>(bb, hh, j);
+          bool vis = key < klen32 && (!a.causal || key <= qloc);
           S[bb][j] = vis ? S[bb][j] : NEG_INF;
         }
     }
 
-    // ---------------- row max: 16-key block maxima, 32-key block maxima, tile max ----------------
+    // row max: 16-key block maxima, tile max
     float bm16[4];
 #pragma unroll
     for (int bb = 0; bb < 4; bb++) {
@@ -415,8 +445,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       for (int j = 1; j < 16; j++) x = __builtin_fmaxf(x, S[bb][j]);
       bm16[bb] = x;
     }
-    float bm[2] = {__builtin_fmaxf(bm16[0], bm16[1]), __builtin_fmaxf(bm16[2], bm16[3])};
-    float tmax = __builtin_fmaxf(bm[0], bm[1]);
+    float tmax = __builtin_fmaxf(__builtin_fmaxf(bm16[0], bm16[1]), __builtin_fmaxf(bm16[2], bm16[3]));
     tmax = __builtin_fmaxf(tmax, swap_halves(tmax));
     const float mnew = __builtin_fmaxf(m, tmax);
     const float ms = mnew == NEG_INF ? 0.0f : mnew * lam;  // exponent offset of this tile
@@ -424,26 +453,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     const float alpha = m == mnew ? 1.0f : exp2_hw(__builtin_fmaf(m, lam, -ms));
     m = mnew;
 
-    // ---------------- P~ = 2^(lambda (S - m)) ----------------
-#pragma unroll
-    for (int bb = 0; bb < 4; bb++)
-#pragma unroll
-      for (int j = 0; j < 16; j++) S[bb][j] = exp2_hw(__builtin_fmaf(S[bb][j], lam, -ms));
-
     // the maxima of P~ are the exponentials of the maxima of S (same operations, monotone)
     float pm16[4];
 #pragma unroll
     for (int bb = 0; bb < 4; bb++) pm16[bb] = exp2_hw(__builtin_fmaf(bm16[bb], lam, -ms));
-
-    // row sum from the unquantized P~
-    if constexpr (PMODE != PM_PNQ) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int bb = 0; bb < 4; bb++)
-#pragma unroll
-        for (int j = 0; j < 16; j++) acc += S[bb][j];
-      lpart = alpha * lpart + acc;
-    }
 
     // two-level pre-scale s1 = rowmax_tile(P~) / (448 * 6)
     float s1 = 1.0f, k1 = 1.0f;
@@ -453,14 +466,85 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       k1 = r > 0.0f ? 1.0f / s1 : 0.0f;  // a row with nothing visible in this tile adds nothing
       if (r == 0.0f) s1 = 0.0f;
 #pragma unroll
-      for (int bb = 0; bb < 4; bb++) {
+      for (int bb = 0; bb < 4; bb++) pm16[bb] = pm16[bb] * k1;
+    }
+
+    // block scales of P, known before any element is touched
+    float sc16[4], sv16[4], ki16[4];  // per 16-key group: convert scale, dequant factor, multiplier
+    int psc[2];                       // E8M0 byte of each 32-key block (FP4 MFMA operand)
+    if constexpr (PV == PV_FP4 || (PV == PV_BF16 && PSC == SCALE_E8M0)) {
 #pragma unroll
-        for (int j = 0; j < 16; j++) S[bb][j] = S[bb][j] * k1;
-        pm16[bb] = pm16[bb] * k1;
+      for (int p = 0; p < 2; p++) {
+        int e = e8m0_exp(__builtin_fmaxf(pm16[2 * p], pm16[2 * p + 1]), a.prule);
+        e = e < -126 ? -126 : e;
+        float sc = u2f((uint32_t)(e + 127) << 23);
+        psc[p] = e + 127;
+        sc16[2 * p] = sc16[2 * p + 1] = sc;
+        sv16[2 * p] = sv16[2 * p + 1] = sc;
+        ki16[2 * p] = ki16[2 * p + 1] = 1.0f;
+      }
+    } else if constexpr (PV == PV_BF16) {  // E4M3 scale per 16 keys
+#pragma unroll
+      for (int bb = 0; bb < 4; bb++) {
+        float sv = e4m3_value(e4m3_mag(pm16[bb] / 6.0f));
+        sc16[bb] = 1.0f;
+        sv16[bb] = sv;
+        ki16[bb] = sv > 0.0f ? 1.0f / sv : 0.0f;
       }
     }
 
-    // ---------------- rescale the accumulators by alpha (skipped when the max did not move) ----------------
+    // per sub-tile: P~ = 2^(lambda (S - m)), row sum, quantized operand; then the next
+    // tile's scores of that sub-tile
+    float lsum = 0.0f;       // row sum of P~ (or of the dequantized P for PNQ on bf16)
+    uint32_t pc[4][4];       // FP4 codes [sub-tile][dword 0..1] / FP8 codes [sub-tile][dword 0..3]
+    uint32_t pw[4][8];       // bf16 P [sub-tile][dword]
+#pragma unroll
+    for (int bb = 0; bb < 4; bb++) {
+      float y[16];
+#pragma unroll
+      for (int j = 0; j < 16; j++) {
+        float pt = exp2_hw(__builtin_fmaf(S[bb][j], lam, -ms));
+        if constexpr (PMODE != PM_PNQ) lsum += pt;
+        if constexpr (PMODE == PM_TWO_LEVEL) pt *= k1;
+        y[j] = pt;
+      }
+      if constexpr (PV == PV_FP4) {
+        pc[bb][0] = pack8_fp4(y, sc16[bb]);
+        pc[bb][1] = pack8_fp4(y + 8, sc16[bb]);
+      } else if constexpr (PV == PV_BF16) {
+        float z[16];
+#pragma unroll
+        for (int j = 0; j < 16; j++) z[j] = PSC == SCALE_E8M0 ? y[j] : y[j] * ki16[bb];
+        uint32_t ww[2] = {pack8_fp4(z, sc16[bb]), pack8_fp4(z + 8, sc16[bb])};
+#pragma unroll
+        for (int u = 0; u < 2; u++)
+#pragma unroll
+          for (int t = 0; t < 4; t++) {
+            v2f pr = fp4_pair(ww[u], t);
+            float x0 = pr[0] * sv16[bb], x1 = pr[1] * sv16[bb];
+            if constexpr (PMODE == PM_PNQ) lsum += x0 + x1;
+            pw[bb][4 * u + t] = pack_bf16_exact(x0, x1);
+          }
+      } else {  // FP8: c = E4M3(448 P~)
+#pragma unroll
+        for (int dw = 0; dw < 4; dw++) {
+          int x = __builtin_amdgcn_cvt_pk_fp8_f32(448.0f * y[4 * dw], 448.0f * y[4 * dw + 1], 0, false);
+          pc[bb][dw] = __builtin_amdgcn_cvt_pk_fp8_f32(448.0f * y[4 * dw + 2], 448.0f * y[4 * dw + 3], x, true);
+        }
+      }
+      // the next tile's scores of this sub-tile, into the registers just consumed (issued
+      // only after this sub-tile's operand is complete, so that one tile of scores is live)
+      if (next) {
+        uint32_t dep;
+        if constexpr (PV == PV_BF16) dep = pw[bb][7];
+        else if constexpr (PV == PV_FP8) dep = pc[bb][3];
+        else dep = pc[bb][1];
+        S[bb] = scores_sub(nbuf, bb, dep);
+      }
+    }
+    if constexpr (PMODE != PM_PNQ || PV != PV_FP4) lpart = alpha * lpart + lsum;
+
+    // rescale the accumulators by alpha (skipped when no row's max moved)
     const bool any_rescale = __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0;
     if constexpr (PMODE != PM_TWO_LEVEL) {
       if (any_rescale) {
@@ -472,36 +556,17 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       }
     }
 
-    // ---------------- quantize P and run PV ----------------
+    // PV
     v16f D[4];
     if constexpr (PMODE == PM_TWO_LEVEL) {
 #pragma unroll
       for (int i = 0; i < 4; i++) D[i] = zero16();
     }
-    v16f* acc = (PMODE == PM_TWO_LEVEL) ? D : O;
-    float lq = 0.0f;  // PNQ with bf16 PV: sum of the dequantized P of this half
-
     if constexpr (PV == PV_FP4) {
-      // E2M1 codes with an E8M0 scale per 32-key block, the block being the MFMA's scale group
+      // operand of 32-key block p: sub-tiles 2p (keys +0..15) and 2p+1 (keys +16..31)
       v8i bp[2];
-      int psc[2];
 #pragma unroll
-      for (int p = 0; p < 2; p++) {
-        float M = __builtin_fmaxf(pm16[2 * p], pm16[2 * p + 1]);
-        int e = e8m0_exp(M, a.prule);
-        e = e < -126 ? -126 : e;
-        float sc = u2f((uint32_t)(e + 127) << 23);
-        uint32_t w[4];
-#pragma unroll
-        for (int dw = 0; dw < 4; dw++) {
-          float y[8];
-#pragma unroll
-          for (int j = 0; j < 8; j++) y[j] = S[2 * p + (dw >> 1)][8 * (dw & 1) + j];
-          w[dw] = pack8_fp4(y, sc);
-        }
-        bp[p] = v8_from4(mk4(w[0], w[1], w[2], w[3]));
-        psc[p] = e + 127;
-      }
+      for (int p = 0; p < 2; p++) bp[p] = v8_from4(mk4(pc[2 * p][0], pc[2 * p][1], pc[2 * p + 1][0], pc[2 * p + 1][1]));
 #pragma unroll
       for (int db = 0; db < 4; db++) {
         const uint8_t* rp = Vs + (32 * db + ql) * 80;
@@ -510,7 +575,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         for (int kc = 0; kc < 2; kc++) {
           v8i av = v8_from4(*reinterpret_cast<const u4*>(rp + 32 * kc + 16 * hh));
           int sa = (int)((vs4 >> (8 * (2 * kc + hh))) & 0xFF);
-          acc[db] = mfma_fp4(av, bp[kc], acc[db], sa, psc[kc]);
+          if constexpr (PMODE == PM_TWO_LEVEL) D[db] = mfma_fp4(av, bp[kc], D[db], sa, psc[kc]);
+          else O[db] = mfma_fp4(av, bp[kc], O[db], sa, psc[kc]);
         }
       }
       if constexpr (PMODE == PM_PNQ) {
@@ -520,38 +586,6 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         Lacc = mfma_fp4(ones, bp[1], Lacc, 127, psc[1]);
       }
     } else if constexpr (PV == PV_BF16) {
-      // P^ dequantized exactly to bf16; 16-key groups g = bb (one S sub-tile each)
-      uint32_t pw[4][8];  // [bb][dword]: 16 bf16 of sub-tile bb
-#pragma unroll
-      for (int bb = 0; bb < 4; bb++) {
-        float sc, kinv, sval;  // cvt scale (power of two), element multiplier, dequant factor
-        if constexpr (PSC == SCALE_E8M0) {
-          float M = __builtin_fmaxf(pm16[bb & 2], pm16[(bb & 2) + 1]);
-          int e = e8m0_exp(M, a.prule);
-          e = e < -126 ? -126 : e;
-          sc = u2f((uint32_t)(e + 127) << 23);
-          kinv = 1.0f;
-          sval = sc;
-        } else {
-          uint32_t cb = e4m3_mag(pm16[bb] / 6.0f);
-          sval = e4m3_value(cb);
-          sc = 1.0f;
-          kinv = sval > 0.0f ? 1.0f / sval : 0.0f;
-        }
-        float y[16];
-#pragma unroll
-        for (int j = 0; j < 16; j++) y[j] = PSC == SCALE_E8M0 ? S[bb][j] : S[bb][j] * kinv;
-        uint32_t ww[2] = {pack8_fp4(y, sc), pack8_fp4(y + 8, sc)};
-#pragma unroll
-        for (int u = 0; u < 2; u++)
-#pragma unroll
-          for (int t = 0; t < 4; t++) {
-            v2f pr = fp4_pair(ww[u], t);
-            float x0 = pr[0] * sval, x1 = pr[1] * sval;
-            if constexpr (PMODE == PM_PNQ) lq += x0 + x1;
-            pw[bb][4 * u + t] = pack_bf16_exact(x0, x1);
-          }
-      }
 #pragma unroll
       for (int db = 0; db < 4; db++) {
         const uint8_t* rp = Vs + (32 * db + ql) * 256;
@@ -562,21 +596,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
           v8bf av = *reinterpret_cast<const v8bf*>(rp + chunk * 16);
           const int bb = 2 * (s >> 2) + ((s & 3) >> 1), o = 4 * ((s & 3) & 1);
           u4 t = mk4(pw[bb][o], pw[bb][o + 1], pw[bb][o + 2], pw[bb][o + 3]);
-          acc[db] = mfma_bf16(av, __builtin_bit_cast(v8bf, t), acc[db]);
+          if constexpr (PMODE == PM_TWO_LEVEL) D[db] = mfma_bf16(av, __builtin_bit_cast(v8bf, t), D[db]);
+          else O[db] = mfma_bf16(av, __builtin_bit_cast(v8bf, t), O[db]);
         }
       }
-    } else {  // PV_FP8: c = E4M3(448 P~), unit scale; V in E4M3 with E8M0 per 32 keys
+    } else {  // PV_FP8: unit P scale; V in E4M3 with E8M0 per 32 keys
       v8i bp[2];
 #pragma unroll
       for (int kc = 0; kc < 2; kc++) {
 #pragma unroll
-        for (int dw = 0; dw < 8; dw++) {
-          const v16f& src = S[2 * kc + (dw >> 2)];
-          int j0 = 4 * (dw & 3);
-          int x = __builtin_amdgcn_cvt_pk_fp8_f32(448.0f * src[j0], 448.0f * src[j0 + 1], 0, false);
-          x = __builtin_amdgcn_cvt_pk_fp8_f32(448.0f * src[j0 + 2], 448.0f * src[j0 + 3], x, true);
-          bp[kc][dw] = x;
-        }
+        for (int dw = 0; dw < 8; dw++) bp[kc][dw] = (int)pc[2 * kc + (dw >> 2)][dw & 3];
       }
 #pragma unroll
       for (int db = 0; db < 4; db++) {
@@ -589,12 +618,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
           u4 hi = *reinterpret_cast<const u4*>(rp + 64 * kc + 32 + 16 * hh);
           v8i av = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
           int sa = (int)((vs4 >> (8 * (2 * kc + hh))) & 0xFF);
-          acc[db] = mfma_fp8(av, bp[kc], acc[db], sa, 127);
+          O[db] = mfma_fp8(av, bp[kc], O[db], sa, 127);
         }
       }
     }
-
-    if constexpr (PMODE == PM_PNQ && PV != PV_FP4) lpart = alpha * lpart + lq;
 
     if constexpr (PMODE == PM_TWO_LEVEL) {
       // O = alpha O + s1 (P^2 V)
@@ -608,6 +635,48 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         for (int i = 0; i < 4; i++)
 #pragma unroll
           for (int j = 0; j < 16; j++) O[i][j] = __builtin_fmaf(s1, D[i][j], O[i][j]);
+      }
+    }
+  };
+
+  // ---------------- the key-tile loop ----------------
+  if (nkt > 0) {
+    v16f S[4];
+    if constexpr (NB == 1) {
+      // one buffer: store, then compute on it (two barriers per tile)
+      load_tile(0);
+      for (int kt = 0; kt < nkt; kt++) {
+        __syncthreads();  // the previous tile's LDS reads are done
+        store_tile(0);
+        __syncthreads();
+        // next tile in flight during this tile's math (the last iteration reloads its own
+        // tile: an unconditional load keeps the staging registers out of scratch memory)
+        load_tile(kt + 1 < nkt ? kt + 1 : kt);
+        scores(0, S);
+        softmax_pv(kt, 0, S, false, 0);
+      }
+    } else {
+      // software pipeline: the scores of tile kt+1 are computed on the matrix cores
+      // while the softmax of tile kt runs; tile kt+2 is staged behind them
+      load_tile(0);
+      store_tile(0);
+      load_tile(nkt > 1 ? 1 : 0);
+      store_tile(1 % NB);
+      __syncthreads();
+      load_tile(nkt > 2 ? 2 : nkt - 1);
+#ifndef MXATTN_SCORE_PIPELINE
+#define MXATTN_SCORE_PIPELINE 0
+#endif
+      constexpr bool PIPE = MXATTN_SCORE_PIPELINE != 0;
+      if (PIPE) scores(0, S);
+      for (int kt = 0; kt < nkt; kt++) {
+        // the next tile's scores land in S (stale data past the end is never used)
+        if (!PIPE) scores(kt % NB, S);
+        softmax_pv(kt, kt % NB, S, PIPE, (kt + 1) % NB);
+        if constexpr (NB == 2) __syncthreads();  // buffer kt % 2 is free once every PV read it
+        store_tile((kt + 2) % NB);               // tile kt+2 (a repeat of the last tile past the end)
+        load_tile(kt + 3 < nkt ? kt + 3 : nkt - 1);
+        __syncthreads();
       }
     }
   }
@@ -640,7 +709,292 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int g = 0; g < 4; g++) {
           u2 t = mk2(bf16_rne(O[db][4 * g] * inv) | (bf16_rne(O[db][4 * g + 1] * inv) << 16),
-                               bf16_rne(O[db][4 * g + 2] * inv) | (bf16_rne(O[db][4 * g + 3] * inv) << 16));
+                     bf16_rne(O[db][4 * g + 2] * inv) | (bf16_rne(O[db][4 * g + 3] * inv) << 16));
+          *reinterpret_cast<u2*>(op + 32 * db + 8 * g + 4 * hh) = t;
+        }
+    }
+    if (a.lse != nullptr && hh == 0) {
+      float v = l > 0.0f ? __logf(l) + m * a.sm_scale : NEG_INF;
+      a.lse[(b * a.Hq + hq) * a.N + orow] = v;
+    }
+  }
+}
+
+// ===========================================================================
+// Ping-pong form of the all-FP4 route (MXFP4 Q, K, V; P in E2M1 with an E8M0
+// scale per 32 keys): 8 waves own 256 query rows.  Each SIMD holds one wave of
+// group A (waves 0-3) and one of group B (waves 4-7).  Per key tile t a wave runs
+// an MFMA phase M(t) = {PV of tile t-1, S^T of tile t} and a VALU phase V(t) =
+// {mask, max, exp, P quantization, staging of a later tile}; group B runs one
+// phase behind group A, and a workgroup barrier ends every phase, so on every
+// SIMD one wave's matrix-core work overlaps the other wave's vector work.
+// Key tiles sit in 3 LDS buffers; each group stages half of every tile (64 key
+// rows and 64 V^T rows) during its VALU phases, two phases after loading it.
+// ===========================================================================
+template <int PMODE>
+__global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
+  constexpr int ROW = 80;                // staged row: 64 B of codes, 4 B of scales, padding
+  constexpr int KV = 128 * ROW;          // V^T rows follow the 128 key rows of a stage
+  constexpr int STAGE = 2 * KV;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[3 * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, ql = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  const int grp = wave >> 2;  // 0: group A, 1: group B
+  const int gt = tid & 255;   // thread within the group
+
+  // ---------------- work item: 256 query rows of one (batch, head) ----------------
+  const int64_t nqt = (a.N + 255) / 256, BH = a.B * a.Hq, G = a.grid;
+  int64_t id = blockIdx.x, bh, qt;
+  if (a.causal) {  // longest first
+    qt = nqt - 1 - id / BH;
+    bh = id % BH;
+  } else {  // one head's tiles on one XCD (workgroup ids are dealt round-robin to 8 XCDs)
+    if (G % 8 == 0) id = (id % 8) * (G / 8) + id / 8;
+    bh = id / nqt;
+    qt = id % nqt;
+  }
+  const int64_t b = bh / a.Hq, hq = bh % a.Hq, hk = hq * a.Hkv / a.Hq;
+  const int N = (int)a.N;
+  const int qloc = (int)qt * 256 + 32 * wave + ql;
+  const int64_t qrow = (b * a.Hq + hq) * a.N + (qloc < N ? qloc : N - 1);
+  const int64_t kbase = (b * a.Hkv + hk) * a.N;
+  const int64_t vrow0 = (b * a.Hkv + hk) * 128;
+  int nkt = (N + 127) / 128;
+  if (a.causal && nkt > 2 * (int)qt + 2) nkt = 2 * (int)qt + 2;
+  const float lam = a.lambda;
+
+  // ---------------- Q operand and its scales ----------------
+  v8i qop[2];
+  uint32_t qsc;  // byte 2c of (scales >> 8h) is the scale of d-chunk c for this lane half
+  {
+    const uint8_t* qp = a.q + qrow * 64;
+    qsc = *reinterpret_cast<const uint32_t*>(a.qs + qrow * 4) >> (8 * hh);
+    qop[0] = v8_from4(*reinterpret_cast<const u4*>(qp + 16 * hh));
+    qop[1] = v8_from4(*reinterpret_cast<const u4*>(qp + 32 + 16 * hh));
+  }
+
+  // ---------------- staging: this thread's share of a tile ----------------
+  // K code chunk: key row kr = 64 grp + gt/4, 16-byte part gt%4; V^T chunk: channel
+  // vc = 64 grp + gt/4, same part; scales: key row / channel 64 grp + gt%64 (threads
+  // gt < 64 store the K scale, 64 <= gt < 128 the V scale)
+  const int kr = 64 * grp + (gt >> 2), part = gt & 3, sr = 64 * grp + (gt & 63);
+  const uint32_t st_k = (uint32_t)(kpos<false>(kr) * ROW + part * 16);
+  const uint32_t st_v = (uint32_t)(KV + kr * ROW + part * 16);
+  const uint32_t st_s = gt < 64 ? (uint32_t)(kpos<false>(sr) * ROW + 64) : (uint32_t)(KV + sr * ROW + 64);
+  const bool st_s_on = gt < 128;
+  // scalar bases of this head, 32-bit per-lane offsets (saddr + voffset addressing)
+  const uint8_t* hk_codes = a.k + kbase * 64;
+  const uint8_t* hk_scales = a.ks + kbase * 4;
+  const uint8_t* hv_codes = a.v + vrow0 * (a.np / 2);
+  const uint8_t* hv_scales = a.vs + vrow0 * (a.np / 32);
+  const uint32_t vrow_bytes = (uint32_t)(a.np / 2), vsrow_bytes = (uint32_t)(a.np / 32);
+  const uint32_t o_v = (uint32_t)kr * vrow_bytes + part * 16, o_vs = (uint32_t)sr * vsrow_bytes;
+  u4 rk, rv;
+  uint32_t rs;
+  auto load_half = [&](int t) __attribute__((always_inline)) {
+    const int row_k = t * 128 + kr < N ? t * 128 + kr : N - 1;
+    const int row_s = t * 128 + sr < N ? t * 128 + sr : N - 1;
+    rk = *reinterpret_cast<const u4*>(hk_codes + ((uint32_t)row_k * 64 + part * 16));
+    rv = *reinterpret_cast<const u4*>(hv_codes + (o_v + (uint32_t)t * 64));
+    rs = gt < 64 ? *reinterpret_cast<const uint32_t*>(hk_scales + (uint32_t)row_s * 4)
+                 : *reinterpret_cast<const uint32_t*>(hv_scales + (o_vs + (uint32_t)t * 4));
+  };
+  auto store_half = [&](int buf) __attribute__((always_inline)) {
+    uint8_t* base = smem + buf * STAGE;
+    *reinterpret_cast<u4*>(base + st_k) = rk;
+    *reinterpret_cast<u4*>(base + st_v) = rv;
+    if (st_s_on) *reinterpret_cast<uint32_t*>(base + st_s) = rs;
+  };
+
+  // ---------------- state ----------------
+  float m = NEG_INF, lpart = 0.0f, s1prev = 1.0f;
+  v16f O[4], Lacc, S[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) O[i] = zero16();
+  Lacc = zero16();
+  v8i bp[2];
+  uint32_t pscw = 0x7F7F;  // E8M0 bytes of P's two 32-key blocks (byte kc)
+  float bm16[4], tmax;     // 16-key block maxima and the tile max of the scores in S
+  const uint32_t koff = (uint32_t)(ql * ROW + 16 * hh), kso = (uint32_t)(ql * ROW + 64);
+
+  // M(t): PV of tile t-1 (P of that tile in bp/pscw), then S^T of tile t
+  auto phase_m = [&](int t) __attribute__((always_inline)) {
+    if (t >= 1) {
+      const uint8_t* Vs = smem + ((t - 1) % 3) * STAGE + KV;
+#pragma unroll
+      for (int db = 0; db < 4; db++) {
+        const uint8_t* rp = Vs + db * 32 * ROW;
+        uint32_t vs4 = *reinterpret_cast<const uint32_t*>(rp + kso) >> (8 * hh);
+        v8i a0 = v8_from4(*reinterpret_cast<const u4*>(rp + koff));
+        v8i a1 = v8_from4(*reinterpret_cast<const u4*>(rp + koff + 32));
+        O[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, bp[0], O[db], 4, 4, 0, (int)vs4, 0, (int)pscw);
+        O[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, bp[1], O[db], 4, 4, 2, (int)vs4, 1, (int)pscw);
+      }
+      if constexpr (PMODE == PM_PNQ) {
+        const v8i ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};
+        Lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, bp[0], Lacc, 4, 4, 0, 127, 0, (int)pscw);
+        Lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, bp[1], Lacc, 4, 4, 0, 127, 1, (int)pscw);
+      }
+    }
+    if (t < nkt) {
+      const uint8_t* Ks = smem + (t % 3) * STAGE;
+#pragma unroll
+      for (int bb = 0; bb < 4; bb++) {
+        const uint8_t* rp = Ks + bb * 32 * ROW;
+        uint32_t ks4 = *reinterpret_cast<const uint32_t*>(rp + kso) >> (8 * hh);
+        v8i a0 = v8_from4(*reinterpret_cast<const u4*>(rp + koff));
+        v8i a1 = v8_from4(*reinterpret_cast<const u4*>(rp + koff + 32));
+        v16f acc = zero16();
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, qop[0], acc, 4, 4, 0, (int)ks4, 0, (int)qsc);
+        S[bb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, qop[1], acc, 4, 4, 2, (int)ks4, 2, (int)qsc);
+      }
+      // mask (tail keys, causal diagonal) and the maxima, while the other group's wave
+      // on this SIMD runs its exponentials
+      const int k0 = t * 128;
+      if ((k0 + 128 > N) || (a.causal && k0 + 127 > (int)qt * 256 + 32 * wave)) {
+#pragma unroll
+        for (int bb = 0; bb < 4; bb++)
+#pragma unroll
+          for (int j = 0; j < 16; j++) {
+            int key = k0 + key_of<false>(bb, hh, j);
+            bool vis = key < N && (!a.causal || key <= qloc);
+            S[bb][j] = vis ? S[bb][j] : NEG_INF;
+          }
+      }
+#pragma unroll
+      for (int bb = 0; bb < 4; bb++) {
+        float x0 = __builtin_fmaxf(__builtin_fmaxf(S[bb][0], S[bb][1]), S[bb][2]);
+        float x1 = __builtin_fmaxf(__builtin_fmaxf(S[bb][3], S[bb][4]), S[bb][5]);
+        float x2 = __builtin_fmaxf(__builtin_fmaxf(S[bb][6], S[bb][7]), S[bb][8]);
+        float x3 = __builtin_fmaxf(__builtin_fmaxf(S[bb][9], S[bb][10]), S[bb][11]);
+        float x4 = __builtin_fmaxf(__builtin_fmaxf(S[bb][12], S[bb][13]), S[bb][14]);
+        float y0 = __builtin_fmaxf(__builtin_fmaxf(x0, x1), x2);
+        float y1 = __builtin_fmaxf(__builtin_fmaxf(x3, x4), S[bb][15]);
+        bm16[bb] = __builtin_fmaxf(y0, y1);
+      }
+      tmax = halves_max(__builtin_fmaxf(__builtin_fmaxf(bm16[0], bm16[1]), __builtin_fmaxf(bm16[2], bm16[3])));
+    }
+  };
+
+  // V(t): exponentials and P quantization of tile t (its row max came with M(t))
+  auto phase_v = [&](int t) __attribute__((always_inline)) {
+    const float mnew = __builtin_fmaxf(m, tmax);
+    const float ms = mnew == NEG_INF ? 0.0f : mnew * lam;
+    // exactly 1 when the max did not move (keeps the rescale skip exact), 0 while m = -inf
+    const float alpha = m == mnew ? 1.0f : exp2_hw(__builtin_fmaf(m, lam, -ms));
+    m = mnew;
+
+    // two-level: s1 = rowmax_tile(P~)/2688; the accumulator holds O / s1 and is carried
+    // to the new s1 by beta = alpha s1_prev / s1 (a tile whose P~ stays below 2^-64 of
+    // the running maximum adds nothing and keeps s1)
+    float k1 = 1.0f, scale_o = alpha;
+    if constexpr (PMODE == PM_TWO_LEVEL) {
+      float r = exp2_hw(__builtin_fmaf(tmax, lam, -ms));
+      if (r >= 0x1p-64f) {
+        float s1 = r / 2688.0f;
+        k1 = 1.0f / s1;
+        scale_o = alpha * (s1prev / s1);
+        s1prev = s1;
+      } else {
+        k1 = 0.0f;
+      }
+    }
+    const bool any_rescale = __builtin_amdgcn_ballot_w64(scale_o != 1.0f) != 0;
+    if (any_rescale) {
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 16; j++) O[i][j] *= scale_o;
+      Lacc[0] *= alpha;
+    }
+
+    // P~ and its quantization: E8M0 scale per 32-key block from the block maximum
+    int e[2];
+#pragma unroll
+    for (int p = 0; p < 2; p++) {
+      float M = exp2_hw(__builtin_fmaf(__builtin_fmaxf(bm16[2 * p], bm16[2 * p + 1]), lam, -ms)) * k1;
+      int x = e8m0_exp(M, a.prule);
+      e[p] = x < -126 ? -126 : x;
+    }
+    pscw = (uint32_t)(e[0] + 127) | ((uint32_t)(e[1] + 127) << 8);
+    float lsum = 0.0f;
+    uint32_t w[8];
+#pragma unroll
+    for (int bb = 0; bb < 4; bb++) {
+      const float sc = u2f((uint32_t)(e[bb >> 1] + 127) << 23);
+      float y[16];
+#pragma unroll
+      for (int j = 0; j < 16; j++) {
+        float pt = exp2_hw(__builtin_fmaf(S[bb][j], lam, -ms));
+        if constexpr (PMODE != PM_PNQ) lsum += pt;
+        if constexpr (PMODE == PM_TWO_LEVEL) pt *= k1;
+        y[j] = pt;
+      }
+      w[2 * bb] = pack8_fp4(y, sc);
+      w[2 * bb + 1] = pack8_fp4(y + 8, sc);
+    }
+    if constexpr (PMODE != PM_PNQ) lpart = alpha * lpart + lsum;
+    bp[0] = v8_from4(mk4(w[0], w[1], w[2], w[3]));
+    bp[1] = v8_from4(mk4(w[4], w[5], w[6], w[7]));
+  };
+
+  // ---------------- phases ----------------
+  // Every wave runs M(0) V(0) M(1) V(1) ... M(nkt) with a workgroup barrier after each
+  // phase.  Group B passes one extra barrier before M(0) and group A one after the
+  // last phase, so B runs one phase behind A (the barrier counts still match).  In
+  // V(t) a group stores its half of tile t+1+grp (loaded two phases earlier) and
+  // loads its half of tile t+2+grp; tiles past the end repeat the last one into a
+  // buffer that is no longer read.
+  load_half(0);
+  store_half(0);
+  if (grp == 1) {
+    load_half(nkt > 1 ? 1 : 0);
+    store_half(1);
+  }
+  load_half(nkt > 1 + grp ? 1 + grp : nkt - 1);
+  __syncthreads();
+  if (grp == 1) __syncthreads();
+  for (int t = 0; t <= nkt; t++) {
+    phase_m(t);
+    __builtin_amdgcn_sched_barrier(0);  // keep the phase's MFMAs on this side of the barrier
+    __syncthreads();
+    if (t < nkt) {
+      phase_v(t);
+      store_half((t + 1 + grp) % 3);
+      const int nt = t + 2 + grp;
+      load_half(nt < nkt ? nt : nkt - 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+  }
+  if (grp == 0) __syncthreads();
+
+  // ---------------- epilogue ----------------
+  float l;
+  if constexpr (PMODE == PM_PNQ) l = Lacc[0];
+  else l = halves_sum(lpart);
+  float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  if constexpr (PMODE == PM_TWO_LEVEL) inv *= s1prev;
+  if (qloc < N) {
+    const int64_t orow = qloc;
+    if (a.out_fp32) {
+      float* op = static_cast<float*>(a.out) + b * a.oB + hq * a.oH + orow * a.oN;
+#pragma unroll
+      for (int db = 0; db < 4; db++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+          float4 t = make_float4(O[db][4 * g] * inv, O[db][4 * g + 1] * inv, O[db][4 * g + 2] * inv,
+                                 O[db][4 * g + 3] * inv);
+          *reinterpret_cast<float4*>(op + 32 * db + 8 * g + 4 * hh) = t;
+        }
+    } else {
+      uint16_t* op = static_cast<uint16_t*>(a.out) + b * a.oB + hq * a.oH + orow * a.oN;
+#pragma unroll
+      for (int db = 0; db < 4; db++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+          u2 t = mk2(bf16_rne(O[db][4 * g] * inv) | (bf16_rne(O[db][4 * g + 1] * inv) << 16),
+                     bf16_rne(O[db][4 * g + 2] * inv) | (bf16_rne(O[db][4 * g + 3] * inv) << 16));
           *reinterpret_cast<u2*>(op + 32 * db + 8 * g + 4 * hh) = t;
         }
     }
@@ -667,7 +1021,20 @@ static hipError_t launch_one(const FwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int PMODE>
+static hipError_t launch_pp(FwdArgs a, hipStream_t st) {
+  const int64_t nqt = (a.N + 255) / 256;
+  a.grid = a.B * a.Hq * nqt;
+  fwd_pp_kernel<PMODE><<<dim3((unsigned)a.grid), dim3(512), 0, st>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd(int qk, int pv, int pmode, int psc, int vsc, const FwdArgs& a, hipStream_t st) {
+  if (qk == QK_FP4 && pv == PV_FP4 && psc == SCALE_E8M0 && vsc == SCALE_E8M0 && a.plan == nullptr) {
+    if (pmode == PM_DIRECT) return launch_pp<PM_DIRECT>(a, st);
+    if (pmode == PM_PNQ) return launch_pp<PM_PNQ>(a, st);
+    if (pmode == PM_TWO_LEVEL) return launch_pp<PM_TWO_LEVEL>(a, st);
+  }
 #define MXF(QK_, PV_, PM_, PS_, VS_) \
   if (qk == QK_ && pv == PV_ && pmode == PM_ && psc == PS_ && vsc == VS_) return launch_one<QK_, PV_, PM_, PS_, VS_>(a, st)
   // MXFP4 Q/K/V, E8M0/32 P: all on the scaled FP4 MFMA
