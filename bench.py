@@ -29,6 +29,19 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TOPS (4·B·H·N²·d/t) at N=32K, d=128; % of FP4 MFMA peak"
 FP4_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 MFMA
+# HBM bytes per forward launch from rocprofv3 FETCH_SIZE/WRITE_SIZE runs, scaled by a
+# plain-copy calibration; read from the committed profile summaries (None when absent)
+TRAFFIC_FILES = {"c3": "profiles/fwd_pp_kernel_c3_video_dit_32k_traffic.txt"}
+
+
+def profiled_traffic(cfg):
+    path = os.path.join(ROOT, TRAFFIC_FILES.get(cfg, ""))
+    if not os.path.isfile(path):
+        return None
+    for line in open(path):
+        if line.strip().startswith("traffic_bytes_per_launch"):
+            return int(line.split("=")[1])
+    return None
 BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
 
@@ -204,8 +217,8 @@ def main():
         "t_fwd_ms": round(t_fwd * 1e3, 4),
         "t_quant_ms": round((t_step - t_fwd) * 1e3, 4),
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(fwd_tflops / peak, 4), "traffic": None,
-                     "kernel": "fwd_kernel (attention forward)"},
+                     "frac": round(fwd_tflops / peak, 4), "traffic": profiled_traffic(args.config),
+                     "kernel": "attention forward (mxattn_fwd)"},
     }
     if not args.no_cpu:
         log("[bench] timing the CPU oracle on a bounded sample")
