@@ -218,6 +218,8 @@ int mxattn_fwd_plan(const int32_t* cu_seqlens_host, int ndocs, int64_t N, int ca
  *   Q/K: MXFP4 (E2M1, E8M0/32) or NVFP4 (E2M1, E4M3/16), the same for both.
  *   P/V: DIRECT, PNQ or TWO_LEVEL with P in E2M1 (E8M0/32 or E4M3/16) and V in
  *        E2M1 (E8M0/32 or E4M3/16); FP8_FIXED with V in E4M3 with E8M0/32.
+ * Sizes: N and the padded key count of `v` at most 2^24 (MXATTN_E_UNSUPPORTED
+ *   beyond).
  * Errors: MXATTN_E_INVALID, MXATTN_E_UNSUPPORTED, MXATTN_E_ALIGN,
  *   MXATTN_E_WORKSPACE, MXATTN_E_HIP.
  */

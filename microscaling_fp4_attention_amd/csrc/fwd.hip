@@ -721,89 +721,182 @@ __global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(Fw
 }
 
 // ===========================================================================
-// Ping-pong form of the all-FP4 route (MXFP4 Q, K, V; P in E2M1 with an E8M0
-// scale per 32 keys): 8 waves own 256 query rows.  Each SIMD holds one wave of
-// group A (waves 0-3) and one of group B (waves 4-7).  Per key tile t a wave runs
-// an MFMA phase M(t) = {PV of tile t-1, S^T of tile t} and a VALU phase V(t) =
-// {mask, max, exp, P quantization, staging of a later tile}; group B runs one
-// phase behind group A, and a workgroup barrier ends every phase, so on every
-// SIMD one wave's matrix-core work overlaps the other wave's vector work.
-// Key tiles sit in 3 LDS buffers; each group stages half of every tile (64 key
-// rows and 64 V^T rows) during its VALU phases, two phases after loading it.
+// Ping-pong form: 8 waves own 256 query rows.  Each SIMD holds one wave of group A
+// (waves 0-3) and one of group B (waves 4-7).  Per key tile t a wave runs an MFMA
+// phase M(t) = {PV of tile t-1, S^T of tile t and its row maxima} and a VALU phase
+// V(t) = {exponentials, P quantization, staging of a later tile}; group B runs one
+// phase behind group A and a workgroup barrier ends every phase, so on every SIMD
+// one wave's matrix-core work overlaps the other wave's vector work.  Key tiles sit
+// in 3 LDS buffers; each group stages half of every tile (64 key rows and 64 V^T
+// rows) during its VALU phases, two phases after loading it.
+// Routes: QK_FP4 / QK_BF16 x PV_FP4 / PV_FP8 / PV_BF16 (V with E8M0 per 32 keys).
 // ===========================================================================
-template <int PMODE>
+template <int QK, int PV>
+struct PpLds {
+  static constexpr int KROW = QK == QK_FP4 ? 80 : 256;
+  static constexpr int VROW = PV == PV_FP4 ? 80 : PV == PV_FP8 ? 144 : 256;
+  static constexpr int KV = 128 * KROW;  // V^T rows follow the 128 key rows of a stage
+  static constexpr int STAGE = 128 * (KROW + VROW);
+  static constexpr int BYTES = 3 * STAGE;
+};
+
+template <int QK, int PV, int PMODE, int PSC>
 __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
-  constexpr int ROW = 80;                // staged row: 64 B of codes, 4 B of scales, padding
-  constexpr int KV = 128 * ROW;          // V^T rows follow the 128 key rows of a stage
-  constexpr int STAGE = 2 * KV;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[3 * STAGE];
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  using L = PpLds<QK, PV>;
+  constexpr int STAGE = L::STAGE, KV = L::KV;
+  constexpr bool SPLIT16 = PV == PV_FP8;
   const int tid = threadIdx.x, lane = tid & 63, ql = lane & 31, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int grp = wave >> 2;  // 0: group A, 1: group B
   const int gt = tid & 255;   // thread within the group
 
-  // ---------------- work item: 256 query rows of one (batch, head) ----------------
-  const int64_t nqt = (a.N + 255) / 256, BH = a.B * a.Hq, G = a.grid;
-  int64_t id = blockIdx.x, bh, qt;
-  if (a.causal) {  // longest first
-    qt = nqt - 1 - id / BH;
-    bh = id % BH;
-  } else {  // one head's tiles on one XCD (workgroup ids are dealt round-robin to 8 XCDs)
-    if (G % 8 == 0) id = (id % 8) * (G / 8) + id / 8;
-    bh = id / nqt;
-    qt = id % nqt;
+  // ---------------- work item: 256 query rows ----------------
+  int64_t b, hq, qt, qstart, vstart;
+  int klen;
+  if (a.plan != nullptr) {
+    const PlanHeader* ph = a.plan;
+    const DocEntry* docs = reinterpret_cast<const DocEntry*>(ph + 1);
+    const WorkItem* items = reinterpret_cast<const WorkItem*>(docs + ph->ndocs) + ph->cap128;
+    const int64_t item = blockIdx.x / a.Hq;
+    hq = blockIdx.x % a.Hq;
+    b = 0;
+    if (item >= ph->n_items256) return;
+    const WorkItem wi = items[item];
+    const DocEntry de = docs[wi.doc];
+    qt = wi.qtile;
+    qstart = de.start;
+    klen = de.len;
+    vstart = de.voff32;
+  } else {
+    const int64_t nqt = (a.N + 255) / 256, BH = a.B * a.Hq, G = a.grid;
+    int64_t id = blockIdx.x, bh;
+    if (a.causal) {  // longest first
+      qt = nqt - 1 - id / BH;
+      bh = id % BH;
+    } else {  // one head's tiles on one XCD (workgroup ids are dealt round-robin to 8 XCDs)
+      if (G % 8 == 0) id = (id % 8) * (G / 8) + id / 8;
+      bh = id / nqt;
+      qt = id % nqt;
+    }
+    b = bh / a.Hq;
+    hq = bh % a.Hq;
+    qstart = 0;
+    klen = (int)a.N;
+    vstart = 0;
   }
-  const int64_t b = bh / a.Hq, hq = bh % a.Hq, hk = hq * a.Hkv / a.Hq;
-  const int N = (int)a.N;
-  const int qloc = (int)qt * 256 + 32 * wave + ql;
-  const int64_t qrow = (b * a.Hq + hq) * a.N + (qloc < N ? qloc : N - 1);
-  const int64_t kbase = (b * a.Hkv + hk) * a.N;
+  const int64_t hk = hq * a.Hkv / a.Hq;
+  const int qloc = (int)qt * 256 + 32 * wave + ql;  // query within its sequence
+  const int64_t qrow = (b * a.Hq + hq) * a.N + qstart + (qloc < klen ? qloc : klen - 1);
+  const int64_t kbase = (b * a.Hkv + hk) * a.N + qstart;  // K row of the sequence's first key
   const int64_t vrow0 = (b * a.Hkv + hk) * 128;
-  int nkt = (N + 127) / 128;
+  int nkt = (klen + 127) / 128;
   if (a.causal && nkt > 2 * (int)qt + 2) nkt = 2 * (int)qt + 2;
   const float lam = a.lambda;
 
-  // ---------------- Q operand and its scales ----------------
+  // ---------------- Q operand ----------------
   v8i qop[2];
-  uint32_t qsc;  // byte 2c of (scales >> 8h) is the scale of d-chunk c for this lane half
-  {
+  uint32_t qsc = 0;
+  v8bf qbf[8];
+  if constexpr (QK == QK_FP4) {
     const uint8_t* qp = a.q + qrow * 64;
     qsc = *reinterpret_cast<const uint32_t*>(a.qs + qrow * 4) >> (8 * hh);
     qop[0] = v8_from4(*reinterpret_cast<const u4*>(qp + 16 * hh));
     qop[1] = v8_from4(*reinterpret_cast<const u4*>(qp + 32 + 16 * hh));
+  } else {
+    const uint8_t* qp = a.q + qrow * 64;
+    u2 s8 = *reinterpret_cast<const u2*>(a.qs + qrow * 8);
+#pragma unroll
+    for (int s = 0; s < 8; s++) {
+      uint32_t w = *reinterpret_cast<const uint32_t*>(qp + 8 * s + 4 * hh);
+      uint32_t sb = ((s < 4 ? s8.x : s8.y) >> (8 * (s & 3))) & 0xFF;
+      qbf[s] = __builtin_bit_cast(v8bf, dq8_bf16(w, e4m3_value(sb)));
+    }
   }
 
   // ---------------- staging: this thread's share of a tile ----------------
-  // K code chunk: key row kr = 64 grp + gt/4, 16-byte part gt%4; V^T chunk: channel
-  // vc = 64 grp + gt/4, same part; scales: key row / channel 64 grp + gt%64 (threads
-  // gt < 64 store the K scale, 64 <= gt < 128 the V scale)
+  // K: key row kr = 64 grp + gt/4, 16-byte code chunk gt%4 (32 channels); V^T: channel
+  // vc = kr, chunk gt%4 of 32 keys (FP8: two chunks of 16 keys); scales: row / channel
+  // sr = 64 grp + gt%64 (K scales by gt < 64, V scales by 64 <= gt < 128).
   const int kr = 64 * grp + (gt >> 2), part = gt & 3, sr = 64 * grp + (gt & 63);
-  const uint32_t st_k = (uint32_t)(kpos<false>(kr) * ROW + part * 16);
-  const uint32_t st_v = (uint32_t)(KV + kr * ROW + part * 16);
-  const uint32_t st_s = gt < 64 ? (uint32_t)(kpos<false>(sr) * ROW + 64) : (uint32_t)(KV + sr * ROW + 64);
-  const bool st_s_on = gt < 128;
-  // scalar bases of this head, 32-bit per-lane offsets (saddr + voffset addressing)
+  const int kpos_r = kpos<SPLIT16>(kr), kpos_s = kpos<SPLIT16>(sr);
+  // scalar (wave-uniform) bases of this head, 32-bit per-lane offsets (N and np are at
+  // most 2^24).  The V scale bytes of a tile start at block vstart/32 + 4t, a multiple
+  // of 4 unless a document starts inside a group of 4 blocks: two aligned dwords are
+  // loaded and joined when stored (joining them at load time would wait for the loads).
   const uint8_t* hk_codes = a.k + kbase * 64;
-  const uint8_t* hk_scales = a.ks + kbase * 4;
-  const uint8_t* hv_codes = a.v + vrow0 * (a.np / 2);
-  const uint8_t* hv_scales = a.vs + vrow0 * (a.np / 32);
-  const uint32_t vrow_bytes = (uint32_t)(a.np / 2), vsrow_bytes = (uint32_t)(a.np / 32);
-  const uint32_t o_v = (uint32_t)kr * vrow_bytes + part * 16, o_vs = (uint32_t)sr * vsrow_bytes;
-  u4 rk, rv;
-  uint32_t rs;
+  const uint8_t* hk_scales = a.ks + kbase * (QK == QK_FP4 ? 4 : 8);
+  const uint32_t np = (uint32_t)a.np, vrow_bytes = PV == PV_FP8 ? np : np / 2;
+  const uint32_t nvb = np / 32;  // V scale blocks per channel row
+  const uint8_t* hv_codes = a.v + vrow0 * vrow_bytes;
+  const uint8_t* hv_sbase = a.vs + vrow0 * nvb;
+  const uint32_t vblk0 = (uint32_t)(vstart >> 5) & ~3u, vsh = (uint32_t)(vstart >> 5) & 3u;
+  const uint32_t o_v = (uint32_t)kr * vrow_bytes, o_vs = (uint32_t)sr * nvb + vblk0;
+  u4 rk, rv0, rv1;
+  uint32_t rks = 0, rvs = 0, rvs_hi = 0;
   auto load_half = [&](int t) __attribute__((always_inline)) {
-    const int row_k = t * 128 + kr < N ? t * 128 + kr : N - 1;
-    const int row_s = t * 128 + sr < N ? t * 128 + sr : N - 1;
-    rk = *reinterpret_cast<const u4*>(hk_codes + ((uint32_t)row_k * 64 + part * 16));
-    rv = *reinterpret_cast<const u4*>(hv_codes + (o_v + (uint32_t)t * 64));
-    rs = gt < 64 ? *reinterpret_cast<const uint32_t*>(hk_scales + (uint32_t)row_s * 4)
-                 : *reinterpret_cast<const uint32_t*>(hv_scales + (o_vs + (uint32_t)t * 4));
+    const int key = t * 128 + kr < klen ? t * 128 + kr : klen - 1;
+    rk = *reinterpret_cast<const u4*>(hk_codes + ((uint32_t)key * 64 + part * 16));
+    if constexpr (QK == QK_FP4) {
+      if (gt < 64) {  // wave-uniform
+        const int skey = t * 128 + sr < klen ? t * 128 + sr : klen - 1;
+        rks = *reinterpret_cast<const uint32_t*>(hk_scales + (uint32_t)skey * 4);
+      }
+    } else {
+      rks = *reinterpret_cast<const uint16_t*>(hk_scales + ((uint32_t)key * 8 + 2 * part));
+    }
+    const uint32_t key0 = (uint32_t)vstart + (uint32_t)t * 128;  // first padded key slot (< np)
+    if constexpr (PV == PV_FP8) {  // two chunks of 16 keys: parts gt%4 and gt%4 + 4
+      const uint32_t k1 = __builtin_elementwise_min(key0 + 16 * part, np - 16);
+      const uint32_t k2 = __builtin_elementwise_min(key0 + 16 * (part + 4), np - 16);
+      rv0 = *reinterpret_cast<const u4*>(hv_codes + (o_v + k1));
+      rv1 = *reinterpret_cast<const u4*>(hv_codes + (o_v + k2));
+    } else {
+      const uint32_t k1 = __builtin_elementwise_min(key0 + 32 * part, np - 32);
+      rv0 = *reinterpret_cast<const u4*>(hv_codes + (o_v + k1 / 2));
+    }
+    if constexpr (PV == PV_BF16) {  // the chunk's own block scale
+      const uint32_t blk = __builtin_elementwise_min((key0 + 32 * part) / 32, nvb - 1);
+      rvs = hv_sbase[(uint32_t)kr * nvb + blk];
+    } else if (gt >= 64 && gt < 128) {  // a channel's 4 block scales (wave-uniform)
+      // the group of 4 after the tile's first one lies past the row only when the
+      // tile's keys do (vblk0 + 4t <= nvb - 4 since key0 < np and nvb % 4 == 0)
+      const uint32_t lo = o_vs + 4 * (uint32_t)t;
+      const uint32_t hi = vblk0 + 4 * (uint32_t)t + 4 < nvb ? lo + 4 : lo;
+      rvs = *reinterpret_cast<const uint32_t*>(hv_sbase + lo);
+      rvs_hi = *reinterpret_cast<const uint32_t*>(hv_sbase + hi);
+    }
   };
   auto store_half = [&](int buf) __attribute__((always_inline)) {
     uint8_t* base = smem + buf * STAGE;
-    *reinterpret_cast<u4*>(base + st_k) = rk;
-    *reinterpret_cast<u4*>(base + st_v) = rv;
-    if (st_s_on) *reinterpret_cast<uint32_t*>(base + st_s) = rs;
+    if constexpr (QK == QK_FP4) {
+      *reinterpret_cast<u4*>(base + kpos_r * 80 + part * 16) = rk;
+      if (gt < 64) *reinterpret_cast<uint32_t*>(base + kpos_s * 80 + 64) = rks;
+    } else {  // channels 32 part + [0, 32), E4M3 blocks 2 part and 2 part + 1
+      const float s0 = e4m3_value(rks & 0xFF), s1 = e4m3_value((rks >> 8) & 0xFF);
+      const uint32_t w4[4] = {rk.x, rk.y, rk.z, rk.w};
+#pragma unroll
+      for (int u = 0; u < 4; u++)
+        *reinterpret_cast<u4*>(base + kpos_r * 256 + (((4 * part + u) ^ (kpos_r & 15)) * 16)) =
+            dq8_bf16(w4[u], u < 2 ? s0 : s1);
+    }
+    uint8_t* vb = base + KV;
+    if constexpr (PV == PV_FP4) {
+      *reinterpret_cast<u4*>(vb + kr * 80 + part * 16) = rv0;
+      if (gt >= 64 && gt < 128)
+        *reinterpret_cast<uint32_t*>(vb + sr * 80 + 64) = __builtin_amdgcn_alignbyte(rvs_hi, rvs, vsh);
+    } else if constexpr (PV == PV_FP8) {
+      *reinterpret_cast<u4*>(vb + kr * 144 + part * 16) = rv0;
+      *reinterpret_cast<u4*>(vb + kr * 144 + (part + 4) * 16) = rv1;
+      if (gt >= 64 && gt < 128)
+        *reinterpret_cast<uint32_t*>(vb + sr * 144 + 128) = __builtin_amdgcn_alignbyte(rvs_hi, rvs, vsh);
+    } else {  // bf16 row of 128 keys, chunk = key / 8, swizzled by the channel
+      const float sv = scale_value(rvs, SCALE_E8M0);
+      const uint32_t w4[4] = {rv0.x, rv0.y, rv0.z, rv0.w};
+#pragma unroll
+      for (int u = 0; u < 4; u++)
+        *reinterpret_cast<u4*>(vb + kr * 256 + (((4 * part + u) ^ (kr & 15)) * 16)) = dq8_bf16(w4[u], sv);
+    }
   };
 
   // ---------------- state ----------------
@@ -812,52 +905,101 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; i++) O[i] = zero16();
   Lacc = zero16();
-  v8i bp[2];
-  uint32_t pscw = 0x7F7F;  // E8M0 bytes of P's two 32-key blocks (byte kc)
-  float bm16[4], tmax;     // 16-key block maxima and the tile max of the scores in S
-  const uint32_t koff = (uint32_t)(ql * ROW + 16 * hh), kso = (uint32_t)(ql * ROW + 64);
+  float bm16[4], tmax;          // 16-key block maxima and the tile max of the scores in S
+  v8i bp[2];                    // P operand: FP4 codes (4 dwords each) or FP8 codes (8 dwords)
+  uint32_t pscw = 0x7F7F;       // FP4 P: E8M0 bytes of the two 32-key blocks (byte kc)
+  uint32_t pc[8];               // bf16 P route: E2M1 codes [sub-tile][2 dwords] ...
+  float pdq[4];                 // ... and the dequantization factor of each 16-key group
+  const uint32_t koffk = (uint32_t)(ql * L::KROW + 16 * hh), ksok = (uint32_t)(ql * L::KROW + 64);
 
-  // M(t): PV of tile t-1 (P of that tile in bp/pscw), then S^T of tile t
+  // M(t): PV of tile t-1, then S^T of tile t with its mask and maxima
   auto phase_m = [&](int t) __attribute__((always_inline)) {
     if (t >= 1) {
       const uint8_t* Vs = smem + ((t - 1) % 3) * STAGE + KV;
+      if constexpr (PV == PV_FP4) {
 #pragma unroll
-      for (int db = 0; db < 4; db++) {
-        const uint8_t* rp = Vs + db * 32 * ROW;
-        uint32_t vs4 = *reinterpret_cast<const uint32_t*>(rp + kso) >> (8 * hh);
-        v8i a0 = v8_from4(*reinterpret_cast<const u4*>(rp + koff));
-        v8i a1 = v8_from4(*reinterpret_cast<const u4*>(rp + koff + 32));
-        O[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, bp[0], O[db], 4, 4, 0, (int)vs4, 0, (int)pscw);
-        O[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, bp[1], O[db], 4, 4, 2, (int)vs4, 1, (int)pscw);
-      }
-      if constexpr (PMODE == PM_PNQ) {
-        const v8i ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};
-        Lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, bp[0], Lacc, 4, 4, 0, 127, 0, (int)pscw);
-        Lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, bp[1], Lacc, 4, 4, 0, 127, 1, (int)pscw);
+        for (int db = 0; db < 4; db++) {
+          const uint8_t* rp = Vs + (32 * db + ql) * 80;
+          const uint32_t vs4 = *reinterpret_cast<const uint32_t*>(rp + 64) >> (8 * hh);
+          v8i a0 = v8_from4(*reinterpret_cast<const u4*>(rp + 16 * hh));
+          v8i a1 = v8_from4(*reinterpret_cast<const u4*>(rp + 32 + 16 * hh));
+          O[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, bp[0], O[db], 4, 4, 0, (int)vs4, 0, (int)pscw);
+          O[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, bp[1], O[db], 4, 4, 2, (int)vs4, 1, (int)pscw);
+        }
+        if constexpr (PMODE == PM_PNQ) {
+          const v8i ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};
+          Lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, bp[0], Lacc, 4, 4, 0, 127, 0, (int)pscw);
+          Lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, bp[1], Lacc, 4, 4, 0, 127, 1, (int)pscw);
+        }
+      } else if constexpr (PV == PV_FP8) {
+#pragma unroll
+        for (int db = 0; db < 4; db++) {
+          const uint8_t* rp = Vs + (32 * db + ql) * 144;
+          const uint32_t vs4 = *reinterpret_cast<const uint32_t*>(rp + 128) >> (8 * hh);
+#pragma unroll
+          for (int kc = 0; kc < 2; kc++) {
+            // operand element n holds key 64kc + 32(n/16) + 16h + n%16 (see key_of)
+            u4 lo = *reinterpret_cast<const u4*>(rp + 64 * kc + 16 * hh);
+            u4 hi = *reinterpret_cast<const u4*>(rp + 64 * kc + 32 + 16 * hh);
+            v8i av = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            if (kc == 0) O[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bp[0], O[db], 0, 0, 0, (int)vs4, 0, 127);
+            else O[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bp[1], O[db], 0, 0, 2, (int)vs4, 0, 127);
+          }
+        }
+      } else {
+        // P^ of step s (keys 64(s/4) + 32h + 8(s%4) + [0, 8) = sub-tile 2(s/4) + (s%4)/2,
+        // entries 8((s%4)%2) + [0, 8)) dequantized exactly to bf16 from its codes
+        v8bf pb[8];
+#pragma unroll
+        for (int s = 0; s < 8; s++) {
+          const int bb = 2 * (s >> 2) + ((s & 3) >> 1);
+          pb[s] = __builtin_bit_cast(v8bf, dq8_bf16(pc[2 * bb + ((s & 3) & 1)], pdq[bb]));
+        }
+#pragma unroll
+        for (int db = 0; db < 4; db++) {
+          const uint8_t* rp = Vs + (32 * db + ql) * 256;
+#pragma unroll
+          for (int s = 0; s < 8; s++) {
+            const int chunk = (8 * (s >> 2) + 4 * hh + (s & 3)) ^ (ql & 15);
+            v8bf av = *reinterpret_cast<const v8bf*>(rp + chunk * 16);
+            O[db] = mfma_bf16(av, pb[s], O[db]);
+          }
+        }
       }
     }
     if (t < nkt) {
       const uint8_t* Ks = smem + (t % 3) * STAGE;
 #pragma unroll
       for (int bb = 0; bb < 4; bb++) {
-        const uint8_t* rp = Ks + bb * 32 * ROW;
-        uint32_t ks4 = *reinterpret_cast<const uint32_t*>(rp + kso) >> (8 * hh);
-        v8i a0 = v8_from4(*reinterpret_cast<const u4*>(rp + koff));
-        v8i a1 = v8_from4(*reinterpret_cast<const u4*>(rp + koff + 32));
-        v16f acc = zero16();
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, qop[0], acc, 4, 4, 0, (int)ks4, 0, (int)qsc);
-        S[bb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, qop[1], acc, 4, 4, 2, (int)ks4, 2, (int)qsc);
+        if constexpr (QK == QK_FP4) {
+          const uint8_t* rp = Ks + bb * 32 * 80;
+          const uint32_t ks4 = *reinterpret_cast<const uint32_t*>(rp + ksok) >> (8 * hh);
+          v8i a0 = v8_from4(*reinterpret_cast<const u4*>(rp + koffk));
+          v8i a1 = v8_from4(*reinterpret_cast<const u4*>(rp + koffk + 32));
+          v16f acc = zero16();
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, qop[0], acc, 4, 4, 0, (int)ks4, 0, (int)qsc);
+          S[bb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, qop[1], acc, 4, 4, 2, (int)ks4, 2, (int)qsc);
+        } else {
+          const uint8_t* rp = Ks + (32 * bb + ql) * 256;
+          v16f acc = zero16();
+#pragma unroll
+          for (int s = 0; s < 8; s++) {
+            const int chunk = (2 * s + hh) ^ (ql & 15);
+            acc = mfma_bf16(*reinterpret_cast<const v8bf*>(rp + chunk * 16), qbf[s], acc);
+          }
+          S[bb] = acc;
+        }
       }
       // mask (tail keys, causal diagonal) and the maxima, while the other group's wave
       // on this SIMD runs its exponentials
       const int k0 = t * 128;
-      if ((k0 + 128 > N) || (a.causal && k0 + 127 > (int)qt * 256 + 32 * wave)) {
+      if ((k0 + 128 > klen) || (a.causal && k0 + 127 > (int)qt * 256 + 32 * wave)) {
 #pragma unroll
         for (int bb = 0; bb < 4; bb++)
 #pragma unroll
           for (int j = 0; j < 16; j++) {
-            int key = k0 + key_of<false>(bb, hh, j);
-            bool vis = key < N && (!a.causal || key <= qloc);
+            int key = k0 + key_of<SPLIT16>(bb, hh, j);
+            bool vis = key < klen && (!a.causal || key <= qloc);
             S[bb][j] = vis ? S[bb][j] : NEG_INF;
           }
       }
@@ -908,20 +1050,37 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       Lacc[0] *= alpha;
     }
 
-    // P~ and its quantization: E8M0 scale per 32-key block from the block maximum
-    int e[2];
+    // block scales of P from the block maxima of P~ (exponentials of the score maxima)
+    // (exp2_hw is monotone, so the exponential of a block's largest score is the
+    // block's largest P~)
+    float sc16[4], sv16[4], ki16[4];  // per 16 keys: convert scale, dequant factor, multiplier
+    int e[2] = {0, 0};
+    if constexpr (PV == PV_FP4 || (PV == PV_BF16 && PSC == SCALE_E8M0)) {
 #pragma unroll
-    for (int p = 0; p < 2; p++) {
-      float M = exp2_hw(__builtin_fmaf(__builtin_fmaxf(bm16[2 * p], bm16[2 * p + 1]), lam, -ms)) * k1;
-      int x = e8m0_exp(M, a.prule);
-      e[p] = x < -126 ? -126 : x;
+      for (int p = 0; p < 2; p++) {
+        const float bm = __builtin_fmaxf(bm16[2 * p], bm16[2 * p + 1]);
+        int x = e8m0_exp(exp2_hw(__builtin_fmaf(bm, lam, -ms)) * k1, a.prule);
+        e[p] = x < -126 ? -126 : x;
+        const float sc = u2f((uint32_t)(e[p] + 127) << 23);
+        sc16[2 * p] = sc16[2 * p + 1] = sv16[2 * p] = sv16[2 * p + 1] = sc;
+        ki16[2 * p] = ki16[2 * p + 1] = 1.0f;
+      }
+      pscw = (uint32_t)(e[0] + 127) | ((uint32_t)(e[1] + 127) << 8);
+    } else if constexpr (PV == PV_BF16) {  // E4M3 scale per 16 keys
+#pragma unroll
+      for (int bb = 0; bb < 4; bb++) {
+        const float pm = exp2_hw(__builtin_fmaf(bm16[bb], lam, -ms)) * k1;
+        const float sv = e4m3_value(e4m3_mag(pm / 6.0f));
+        sc16[bb] = 1.0f;
+        sv16[bb] = sv;
+        ki16[bb] = sv > 0.0f ? 1.0f / sv : 0.0f;
+      }
     }
-    pscw = (uint32_t)(e[0] + 127) | ((uint32_t)(e[1] + 127) << 8);
+
     float lsum = 0.0f;
     uint32_t w[8];
 #pragma unroll
     for (int bb = 0; bb < 4; bb++) {
-      const float sc = u2f((uint32_t)(e[bb >> 1] + 127) << 23);
       float y[16];
 #pragma unroll
       for (int j = 0; j < 16; j++) {
@@ -930,12 +1089,39 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
         if constexpr (PMODE == PM_TWO_LEVEL) pt *= k1;
         y[j] = pt;
       }
-      w[2 * bb] = pack8_fp4(y, sc);
-      w[2 * bb + 1] = pack8_fp4(y + 8, sc);
+      if constexpr (PV == PV_FP4) {
+        w[2 * bb] = pack8_fp4(y, sc16[bb]);
+        w[2 * bb + 1] = pack8_fp4(y + 8, sc16[bb]);
+      } else if constexpr (PV == PV_FP8) {  // c = E4M3(448 P~): 4 dwords per sub-tile
+#pragma unroll
+        for (int dw = 0; dw < 4; dw++) {
+          int x = __builtin_amdgcn_cvt_pk_fp8_f32(448.0f * y[4 * dw], 448.0f * y[4 * dw + 1], 0, false);
+          x = __builtin_amdgcn_cvt_pk_fp8_f32(448.0f * y[4 * dw + 2], 448.0f * y[4 * dw + 3], x, true);
+          bp[bb >> 1][4 * (bb & 1) + dw] = x;
+        }
+      } else {
+        float z[16];
+#pragma unroll
+        for (int j = 0; j < 16; j++) z[j] = PSC == SCALE_E8M0 ? y[j] : y[j] * ki16[bb];
+        pc[2 * bb] = pack8_fp4(z, sc16[bb]);
+        pc[2 * bb + 1] = pack8_fp4(z + 8, sc16[bb]);
+        pdq[bb] = sv16[bb];
+        if constexpr (PMODE == PM_PNQ) {  // row sum of the dequantized P
+#pragma unroll
+          for (int u = 0; u < 2; u++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+              v2f pr = fp4_pair(pc[2 * bb + u], q);
+              lsum += (pr[0] + pr[1]) * sv16[bb];
+            }
+        }
+      }
     }
-    if constexpr (PMODE != PM_PNQ) lpart = alpha * lpart + lsum;
-    bp[0] = v8_from4(mk4(w[0], w[1], w[2], w[3]));
-    bp[1] = v8_from4(mk4(w[4], w[5], w[6], w[7]));
+    if constexpr (PMODE != PM_PNQ || PV != PV_FP4) lpart = alpha * lpart + lsum;
+    if constexpr (PV == PV_FP4) {
+      bp[0] = v8_from4(mk4(w[0], w[1], w[2], w[3]));
+      bp[1] = v8_from4(mk4(w[4], w[5], w[6], w[7]));
+    }
   };
 
   // ---------------- phases ----------------
@@ -971,21 +1157,22 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
 
   // ---------------- epilogue ----------------
   float l;
-  if constexpr (PMODE == PM_PNQ) l = Lacc[0];
+  if constexpr (PMODE == PM_PNQ && PV == PV_FP4) l = Lacc[0];
   else l = halves_sum(lpart);
   float inv = l > 0.0f ? 1.0f / l : 0.0f;
   if constexpr (PMODE == PM_TWO_LEVEL) inv *= s1prev;
-  if (qloc < N) {
-    const int64_t orow = qloc;
+  if constexpr (PV == PV_FP8) inv = inv / 448.0f;
+  if (qloc < klen) {
+    const int64_t orow = qstart + qloc;
     if (a.out_fp32) {
       float* op = static_cast<float*>(a.out) + b * a.oB + hq * a.oH + orow * a.oN;
 #pragma unroll
       for (int db = 0; db < 4; db++)
 #pragma unroll
         for (int g = 0; g < 4; g++) {
-          float4 t = make_float4(O[db][4 * g] * inv, O[db][4 * g + 1] * inv, O[db][4 * g + 2] * inv,
-                                 O[db][4 * g + 3] * inv);
-          *reinterpret_cast<float4*>(op + 32 * db + 8 * g + 4 * hh) = t;
+          float4 t4 = make_float4(O[db][4 * g] * inv, O[db][4 * g + 1] * inv, O[db][4 * g + 2] * inv,
+                                  O[db][4 * g + 3] * inv);
+          *reinterpret_cast<float4*>(op + 32 * db + 8 * g + 4 * hh) = t4;
         }
     } else {
       uint16_t* op = static_cast<uint16_t*>(a.out) + b * a.oB + hq * a.oH + orow * a.oN;
@@ -993,9 +1180,9 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       for (int db = 0; db < 4; db++)
 #pragma unroll
         for (int g = 0; g < 4; g++) {
-          u2 t = mk2(bf16_rne(O[db][4 * g] * inv) | (bf16_rne(O[db][4 * g + 1] * inv) << 16),
-                     bf16_rne(O[db][4 * g + 2] * inv) | (bf16_rne(O[db][4 * g + 3] * inv) << 16));
-          *reinterpret_cast<u2*>(op + 32 * db + 8 * g + 4 * hh) = t;
+          u2 t2 = mk2(bf16_rne(O[db][4 * g] * inv) | (bf16_rne(O[db][4 * g + 1] * inv) << 16),
+                      bf16_rne(O[db][4 * g + 2] * inv) | (bf16_rne(O[db][4 * g + 3] * inv) << 16));
+          *reinterpret_cast<u2*>(op + 32 * db + 8 * g + 4 * hh) = t2;
         }
     }
     if (a.lse != nullptr && hh == 0) {
@@ -1021,43 +1208,48 @@ static hipError_t launch_one(const FwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int PMODE>
+template <int QK, int PV, int PMODE, int PSC>
 static hipError_t launch_pp(FwdArgs a, hipStream_t st) {
-  const int64_t nqt = (a.N + 255) / 256;
-  a.grid = a.B * a.Hq * nqt;
-  fwd_pp_kernel<PMODE><<<dim3((unsigned)a.grid), dim3(512), 0, st>>>(a);
+  constexpr int bytes = PpLds<QK, PV>::BYTES;
+  auto kern = fwd_pp_kernel<QK, PV, PMODE, PSC>;
+  if (bytes > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+  }
+  if (a.plan == nullptr) a.grid = a.B * a.Hq * ((a.N + 255) / 256);
+  kern<<<dim3((unsigned)a.grid), dim3(512), bytes, st>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd(int qk, int pv, int pmode, int psc, int vsc, const FwdArgs& a, hipStream_t st) {
-  if (qk == QK_FP4 && pv == PV_FP4 && psc == SCALE_E8M0 && vsc == SCALE_E8M0 && a.plan == nullptr) {
-    if (pmode == PM_DIRECT) return launch_pp<PM_DIRECT>(a, st);
-    if (pmode == PM_PNQ) return launch_pp<PM_PNQ>(a, st);
-    if (pmode == PM_TWO_LEVEL) return launch_pp<PM_TWO_LEVEL>(a, st);
-  }
+  // ping-pong kernel: every route whose three key-tile buffers fit in LDS (V with E8M0
+  // scales per 32 keys; not bf16 on both products)
+#define MXP(QK_, PV_, PM_, PS_) \
+  if (qk == QK_ && pv == PV_ && pmode == PM_ && psc == PS_ && vsc == SCALE_E8M0) return launch_pp<QK_, PV_, PM_, PS_>(a, st)
+  MXP(QK_FP4, PV_FP4, PM_DIRECT, SCALE_E8M0);
+  MXP(QK_FP4, PV_FP4, PM_PNQ, SCALE_E8M0);
+  MXP(QK_FP4, PV_FP4, PM_TWO_LEVEL, SCALE_E8M0);
+  MXP(QK_FP4, PV_BF16, PM_DIRECT, SCALE_E4M3);
+  MXP(QK_FP4, PV_BF16, PM_PNQ, SCALE_E4M3);
+  MXP(QK_FP4, PV_BF16, PM_TWO_LEVEL, SCALE_E4M3);
+  MXP(QK_BF16, PV_FP8, PM_FP8_FIXED, SCALE_E8M0);
+  MXP(QK_FP4, PV_FP8, PM_FP8_FIXED, SCALE_E8M0);
+#undef MXP
 #define MXF(QK_, PV_, PM_, PS_, VS_) \
   if (qk == QK_ && pv == PV_ && pmode == PM_ && psc == PS_ && vsc == VS_) return launch_one<QK_, PV_, PM_, PS_, VS_>(a, st)
-  // MXFP4 Q/K/V, E8M0/32 P: all on the scaled FP4 MFMA
-  MXF(QK_FP4, PV_FP4, PM_DIRECT, SCALE_E8M0, SCALE_E8M0);
-  MXF(QK_FP4, PV_FP4, PM_PNQ, SCALE_E8M0, SCALE_E8M0);
-  MXF(QK_FP4, PV_FP4, PM_TWO_LEVEL, SCALE_E8M0, SCALE_E8M0);
-  // MXFP4 Q/K/V, E4M3/16 P: bf16 PV
-  MXF(QK_FP4, PV_BF16, PM_DIRECT, SCALE_E4M3, SCALE_E8M0);
-  MXF(QK_FP4, PV_BF16, PM_PNQ, SCALE_E4M3, SCALE_E8M0);
-  MXF(QK_FP4, PV_BF16, PM_TWO_LEVEL, SCALE_E4M3, SCALE_E8M0);
-  // NVFP4 Q/K/V
+  // the rest (V with E4M3 scales per 16 keys; bf16 scores with FP4 PV): single-buffer kernel
+  MXF(QK_BF16, PV_FP4, PM_DIRECT, SCALE_E8M0, SCALE_E8M0);
+  MXF(QK_BF16, PV_FP4, PM_PNQ, SCALE_E8M0, SCALE_E8M0);
+  MXF(QK_BF16, PV_FP4, PM_TWO_LEVEL, SCALE_E8M0, SCALE_E8M0);
   MXF(QK_BF16, PV_BF16, PM_DIRECT, SCALE_E4M3, SCALE_E4M3);
   MXF(QK_BF16, PV_BF16, PM_PNQ, SCALE_E4M3, SCALE_E4M3);
   MXF(QK_BF16, PV_BF16, PM_TWO_LEVEL, SCALE_E4M3, SCALE_E4M3);
   MXF(QK_BF16, PV_BF16, PM_DIRECT, SCALE_E8M0, SCALE_E4M3);
   MXF(QK_BF16, PV_BF16, PM_TWO_LEVEL, SCALE_E8M0, SCALE_E4M3);
-  // NVFP4 Q/K with MXFP4 P/V
-  MXF(QK_BF16, PV_FP4, PM_DIRECT, SCALE_E8M0, SCALE_E8M0);
-  MXF(QK_BF16, PV_FP4, PM_PNQ, SCALE_E8M0, SCALE_E8M0);
-  MXF(QK_BF16, PV_FP4, PM_TWO_LEVEL, SCALE_E8M0, SCALE_E8M0);
-  // QK4PV8: FP8 P with the fixed scale 448 and FP8 V
-  MXF(QK_BF16, PV_FP8, PM_FP8_FIXED, SCALE_E8M0, SCALE_E8M0);
-  MXF(QK_FP4, PV_FP8, PM_FP8_FIXED, SCALE_E8M0, SCALE_E8M0);
+  MXF(QK_FP4, PV_BF16, PM_DIRECT, SCALE_E4M3, SCALE_E4M3);
+  MXF(QK_FP4, PV_BF16, PM_TWO_LEVEL, SCALE_E4M3, SCALE_E4M3);
+  MXF(QK_FP4, PV_BF16, PM_PNQ, SCALE_E4M3, SCALE_E4M3);
 #undef MXF
   return hipErrorNotSupported;  // no kernel instantiated for this route
 }

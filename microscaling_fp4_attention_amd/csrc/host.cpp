@@ -81,9 +81,11 @@ bool is_fp8v(const mxattn_qfmt& f) {
   return f.elem == MXATTN_ELEM_E4M3 && f.scale == MXATTN_SCALE_E8M0 && f.block == 32;
 }
 
+int64_t plan_cap(int64_t N, int ndocs, int rows) { return (N + rows - 1) / rows + ndocs; }
+
 size_t plan_bytes(int64_t N, int ndocs) {
   if (ndocs <= 0) return 0;
-  int64_t items = (N + 127) / 128 + ndocs;
+  int64_t items = plan_cap(N, ndocs, 128) + plan_cap(N, ndocs, 256);
   return sizeof(PlanHeader) + sizeof(DocEntry) * (size_t)ndocs + sizeof(WorkItem) * (size_t)items;
 }
 
@@ -194,12 +196,14 @@ int mxattn_fwd_plan(const int32_t* cu_host, int ndocs, int64_t N, int causal, vo
   PlanHeader* ph = reinterpret_cast<PlanHeader*>(buf.data());
   DocEntry* docs = reinterpret_cast<DocEntry*>(ph + 1);
   WorkItem* items = reinterpret_cast<WorkItem*>(docs + ndocs);
+  const int64_t cap128 = plan_cap(N, ndocs, 128);
+  WorkItem* items256 = items + cap128;
   int64_t v32 = 0, v16 = 0;
   struct Cand {
     int64_t cost;
     int32_t doc, qtile;
   };
-  std::vector<Cand> cand;
+  std::vector<Cand> cand, cand256;
   for (int k = 0; k < ndocs; k++) {
     int64_t L = cu_host[k + 1] - cu_host[k];
     docs[k].start = cu_host[k];
@@ -208,16 +212,27 @@ int mxattn_fwd_plan(const int32_t* cu_host, int ndocs, int64_t N, int causal, vo
     docs[k].voff16 = (int32_t)v16;
     v32 += (L + 31) / 32 * 32;
     v16 += (L + 15) / 16 * 16;
-    int64_t nt = (L + 127) / 128;
-    for (int64_t t = 0; t < nt; t++) cand.push_back({causal ? t + 1 : nt, k, (int32_t)t});
+    // cost = key tiles of 128 the query tile visits
+    int64_t nkt = (L + 127) / 128;
+    for (int64_t t = 0; t < nkt; t++) cand.push_back({causal ? t + 1 : nkt, k, (int32_t)t});
+    int64_t nt2 = (L + 255) / 256;
+    for (int64_t t = 0; t < nt2; t++) {
+      int64_t c = causal ? std::min<int64_t>(nkt, 2 * t + 2) : nkt;
+      cand256.push_back({c, k, (int32_t)t});
+    }
   }
   // longest first (the key tiles an item visits); ties keep document order
-  std::stable_sort(cand.begin(), cand.end(), [](const Cand& x, const Cand& y) { return x.cost > y.cost; });
+  auto by_cost = [](const Cand& x, const Cand& y) { return x.cost > y.cost; };
+  std::stable_sort(cand.begin(), cand.end(), by_cost);
+  std::stable_sort(cand256.begin(), cand256.end(), by_cost);
   for (size_t i = 0; i < cand.size(); i++) items[i] = {cand[i].doc, cand[i].qtile};
+  for (size_t i = 0; i < cand256.size(); i++) items256[i] = {cand256[i].doc, cand256[i].qtile};
   ph->n_items = (int32_t)cand.size();
   ph->ndocs = ndocs;
   ph->causal = causal ? 1 : 0;
   ph->magic = PLAN_MAGIC;
+  ph->n_items256 = (int32_t)cand256.size();
+  ph->cap128 = (int32_t)cap128;
   hipError_t e = hipMemcpyAsync(workspace, buf.data(), need, hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mxattn_fwd_plan copy");
   return MXATTN_OK;
@@ -266,6 +281,8 @@ int mxattn_fwd(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn_qt
 
   const int64_t B = q->B, Hq = q->H, Hkv = k->H, N = q->N;
   if (B == 0 || N == 0) return MXATTN_OK;
+  // the kernels address one head's K and V with 32-bit offsets
+  if (N > (int64_t(1) << 24) || v->n_padded > (int64_t(1) << 24)) return MXATTN_E_UNSUPPORTED;
   if (!q->codes || !q->scales || !k->codes || !k->scales || !v->codes || !v->scales || !out) return MXATTN_E_INVALID;
   if (!aligned16(q->codes) || !aligned16(k->codes) || !aligned16(v->codes) || !aligned16(q->scales) ||
       !aligned16(k->scales) || !aligned16(v->scales) || !aligned16(out))

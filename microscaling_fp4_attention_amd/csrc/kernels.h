@@ -43,14 +43,17 @@ enum { PV_FP4 = 0, PV_BF16 = 1, PV_FP8 = 2 };
 struct DocEntry {
   int32_t start, len, voff32, voff16;
 };
-// Work item of a forward plan: document and query tile (128 rows, from the
-// document's first token).
+// Work item of a forward plan: document and query tile (from the document's first
+// token).
 struct WorkItem {
   int32_t doc, qtile;
 };
-// Workspace header of a plan.
+// Workspace header of a plan.  After it: DocEntry[ndocs], then the work list of
+// 128-row query tiles (cap128 entries, n_items used), then the work list of 256-row
+// query tiles (n_items256 used); each list longest first.
 struct PlanHeader {
   int32_t n_items, ndocs, causal, magic;
+  int32_t n_items256, cap128, pad0, pad1;
 };
 constexpr int32_t PLAN_MAGIC = 0x4D585031;  // "MXP1"
 
