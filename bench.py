@@ -30,18 +30,34 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TOPS (4·B·H·N²·d/t) at N=32K, d=128; % of FP4 MFMA peak"
 FP4_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 MFMA
 # HBM bytes per forward launch from rocprofv3 FETCH_SIZE/WRITE_SIZE runs, scaled by a
-# plain-copy calibration; read from the committed profile summaries (None when absent)
-TRAFFIC_FILES = {"c3": "profiles/fwd_pp_kernel_c3_video_dit_32k_traffic.txt"}
+# plain-copy calibration; read from the committed profile summaries, which record the
+# SHA-256 of the kernel source they were taken on (None when absent or stale)
+TRAFFIC_FILES = {"c3": "profiles/fwd_pp_kernel_c3_video_dit_32k_traffic.txt",
+                 "c4": "profiles/fwd_pp_kernel_c4_gqa_causal_32k_traffic.txt"}
+KERNEL_SOURCE = "microscaling_fp4_attention_amd/csrc/fwd.hip"
+
+
+def kernel_source_sha256():
+    import hashlib
+    with open(os.path.join(ROOT, KERNEL_SOURCE), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
 
 def profiled_traffic(cfg):
     path = os.path.join(ROOT, TRAFFIC_FILES.get(cfg, ""))
     if not os.path.isfile(path):
         return None
+    fields = {}
     for line in open(path):
-        if line.strip().startswith("traffic_bytes_per_launch"):
-            return int(line.split("=")[1])
-    return None
+        if "=" in line:
+            k, v = line.split("=", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != kernel_source_sha256():
+        return None  # the kernel changed since the counters were taken
+    v = fields.get("traffic_bytes_per_launch")
+    return int(v) if v is not None else None
+
+
 BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
 
