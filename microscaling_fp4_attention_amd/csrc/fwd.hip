@@ -79,12 +79,16 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 // the other lane half's value (lanes q and q+32 hold the two halves of a row)
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
 
+// max that propagates NaN (v_maximum3_f32 on gfx950): unlike fmaxf it needs no
+// quieting of its operands first, and scores are never NaN for finite inputs
+__device__ __forceinline__ float fmaxn(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // max / sum of the two lane halves of a row, in registers: v_permlane32_swap with
 // both operands x leaves x of lanes 0-31 in every lane of the first result and x of
 // lanes 32-63 in every lane of the second
 __device__ __forceinline__ float halves_max(float x) {
   auto p = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
-  return __builtin_fmaxf(u2f(p[0]), u2f(p[1]));
+  return fmaxn(u2f(p[0]), u2f(p[1]));
 }
 __device__ __forceinline__ float halves_sum(float x) {
   auto p = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
@@ -108,8 +112,10 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
 #define CVT_FP4(old, x0, x1, scale, sel) __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, x0, x1, scale, sel)
 
 // 8 floats -> 8 E2M1 codes in one dword (element 2k in the low nibble of byte k)
-__device__ __forceinline__ uint32_t pack8_fp4(const float* x, float scale) {
-  uint32_t w = 0;
+// `old` is any dword: the four converts overwrite every byte of it (passing a dead
+// register saves the instruction that would clear one)
+__device__ __forceinline__ uint32_t pack8_fp4(const float* x, float scale, uint32_t old = 0) {
+  uint32_t w = old;
   w = CVT_FP4(w, x[0], x[1], scale, 0);
   w = CVT_FP4(w, x[2], x[3], scale, 1);
   w = CVT_FP4(w, x[4], x[5], scale, 2);
@@ -742,8 +748,9 @@ struct PpLds {
 
 template <int QK, int PV, int PMODE, int PSC>
 __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   using L = PpLds<QK, PV>;
+  // static LDS: its base is the constant 0, so stage offsets fold into the instructions
+  __shared__ __attribute__((aligned(16))) uint8_t smem[L::BYTES];
   constexpr int STAGE = L::STAGE, KV = L::KV;
   constexpr bool SPLIT16 = PV == PV_FP8;
   const int tid = threadIdx.x, lane = tid & 63, ql = lane & 31, hh = lane >> 5;
@@ -867,11 +874,11 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       rvs_hi = *reinterpret_cast<const uint32_t*>(hv_sbase + hi);
     }
   };
-  auto store_half = [&](int buf) __attribute__((always_inline)) {
-    uint8_t* base = smem + buf * STAGE;
+  auto store_half = [&](uint32_t so) __attribute__((always_inline)) {
+    uint8_t* base = smem + so;
     if constexpr (QK == QK_FP4) {
       *reinterpret_cast<u4*>(base + kpos_r * 80 + part * 16) = rk;
-      if (gt < 64) *reinterpret_cast<uint32_t*>(base + kpos_s * 80 + 64) = rks;
+      if (gt < 64) *reinterpret_cast<u2*>(base + kpos_s * 80 + 64) = mk2(rks, rks >> 8);
     } else {  // channels 32 part + [0, 32), E4M3 blocks 2 part and 2 part + 1
       const float s0 = e4m3_value(rks & 0xFF), s1 = e4m3_value((rks >> 8) & 0xFF);
       const uint32_t w4[4] = {rk.x, rk.y, rk.z, rk.w};
@@ -883,13 +890,17 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     uint8_t* vb = base + KV;
     if constexpr (PV == PV_FP4) {
       *reinterpret_cast<u4*>(vb + kr * 80 + part * 16) = rv0;
-      if (gt >= 64 && gt < 128)
-        *reinterpret_cast<uint32_t*>(vb + sr * 80 + 64) = __builtin_amdgcn_alignbyte(rvs_hi, rvs, vsh);
+      if (gt >= 64 && gt < 128) {
+        const uint32_t w = __builtin_amdgcn_alignbyte(rvs_hi, rvs, vsh);
+        *reinterpret_cast<u2*>(vb + sr * 80 + 64) = mk2(w, w >> 8);
+      }
     } else if constexpr (PV == PV_FP8) {
       *reinterpret_cast<u4*>(vb + kr * 144 + part * 16) = rv0;
       *reinterpret_cast<u4*>(vb + kr * 144 + (part + 4) * 16) = rv1;
-      if (gt >= 64 && gt < 128)
-        *reinterpret_cast<uint32_t*>(vb + sr * 144 + 128) = __builtin_amdgcn_alignbyte(rvs_hi, rvs, vsh);
+      if (gt >= 64 && gt < 128) {
+        const uint32_t w = __builtin_amdgcn_alignbyte(rvs_hi, rvs, vsh);
+        *reinterpret_cast<u2*>(vb + sr * 144 + 128) = mk2(w, w >> 8);
+      }
     } else {  // bf16 row of 128 keys, chunk = key / 8, swizzled by the channel
       const float sv = scale_value(rvs, SCALE_E8M0);
       const uint32_t w4[4] = {rv0.x, rv0.y, rv0.z, rv0.w};
@@ -910,17 +921,20 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   uint32_t pscw = 0x7F7F;       // FP4 P: E8M0 bytes of the two 32-key blocks (byte kc)
   uint32_t pc[8];               // bf16 P route: E2M1 codes [sub-tile][2 dwords] ...
   float pdq[4];                 // ... and the dequantization factor of each 16-key group
-  const uint32_t koffk = (uint32_t)(ql * L::KROW + 16 * hh), ksok = (uint32_t)(ql * L::KROW + 64);
+  // a staged scale dword is followed by a copy shifted right by 8 bits: lane half hh
+  // reads the copy whose low bytes are its blocks' scales
+  const uint32_t koffk = (uint32_t)(ql * L::KROW + 16 * hh), ksok = (uint32_t)(ql * L::KROW + 64 + 4 * hh);
 
-  // M(t): PV of tile t-1, then S^T of tile t with its mask and maxima
-  auto phase_m = [&](int t) __attribute__((always_inline)) {
+  // M(t): PV of tile t-1 (stage offset sv), then S^T of tile t (stage offset sk) with
+  // its mask and maxima
+  auto phase_m = [&](int t, uint32_t sk, uint32_t sv) __attribute__((always_inline)) {
     if (t >= 1) {
-      const uint8_t* Vs = smem + ((t - 1) % 3) * STAGE + KV;
+      const uint8_t* Vs = smem + sv + KV;
       if constexpr (PV == PV_FP4) {
 #pragma unroll
         for (int db = 0; db < 4; db++) {
           const uint8_t* rp = Vs + (32 * db + ql) * 80;
-          const uint32_t vs4 = *reinterpret_cast<const uint32_t*>(rp + 64) >> (8 * hh);
+          const uint32_t vs4 = *reinterpret_cast<const uint32_t*>(rp + 64 + 4 * hh);
           v8i a0 = v8_from4(*reinterpret_cast<const u4*>(rp + 16 * hh));
           v8i a1 = v8_from4(*reinterpret_cast<const u4*>(rp + 32 + 16 * hh));
           O[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, bp[0], O[db], 4, 4, 0, (int)vs4, 0, (int)pscw);
@@ -935,7 +949,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
 #pragma unroll
         for (int db = 0; db < 4; db++) {
           const uint8_t* rp = Vs + (32 * db + ql) * 144;
-          const uint32_t vs4 = *reinterpret_cast<const uint32_t*>(rp + 128) >> (8 * hh);
+          const uint32_t vs4 = *reinterpret_cast<const uint32_t*>(rp + 128 + 4 * hh);
 #pragma unroll
           for (int kc = 0; kc < 2; kc++) {
             // operand element n holds key 64kc + 32(n/16) + 16h + n%16 (see key_of)
@@ -968,12 +982,12 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       }
     }
     if (t < nkt) {
-      const uint8_t* Ks = smem + (t % 3) * STAGE;
+      const uint8_t* Ks = smem + sk;
 #pragma unroll
       for (int bb = 0; bb < 4; bb++) {
         if constexpr (QK == QK_FP4) {
           const uint8_t* rp = Ks + bb * 32 * 80;
-          const uint32_t ks4 = *reinterpret_cast<const uint32_t*>(rp + ksok) >> (8 * hh);
+          const uint32_t ks4 = *reinterpret_cast<const uint32_t*>(rp + ksok);
           v8i a0 = v8_from4(*reinterpret_cast<const u4*>(rp + koffk));
           v8i a1 = v8_from4(*reinterpret_cast<const u4*>(rp + koffk + 32));
           v16f acc = zero16();
@@ -1005,22 +1019,22 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       }
 #pragma unroll
       for (int bb = 0; bb < 4; bb++) {
-        float x0 = __builtin_fmaxf(__builtin_fmaxf(S[bb][0], S[bb][1]), S[bb][2]);
-        float x1 = __builtin_fmaxf(__builtin_fmaxf(S[bb][3], S[bb][4]), S[bb][5]);
-        float x2 = __builtin_fmaxf(__builtin_fmaxf(S[bb][6], S[bb][7]), S[bb][8]);
-        float x3 = __builtin_fmaxf(__builtin_fmaxf(S[bb][9], S[bb][10]), S[bb][11]);
-        float x4 = __builtin_fmaxf(__builtin_fmaxf(S[bb][12], S[bb][13]), S[bb][14]);
-        float y0 = __builtin_fmaxf(__builtin_fmaxf(x0, x1), x2);
-        float y1 = __builtin_fmaxf(__builtin_fmaxf(x3, x4), S[bb][15]);
-        bm16[bb] = __builtin_fmaxf(y0, y1);
+        float x0 = fmaxn(fmaxn(S[bb][0], S[bb][1]), S[bb][2]);
+        float x1 = fmaxn(fmaxn(S[bb][3], S[bb][4]), S[bb][5]);
+        float x2 = fmaxn(fmaxn(S[bb][6], S[bb][7]), S[bb][8]);
+        float x3 = fmaxn(fmaxn(S[bb][9], S[bb][10]), S[bb][11]);
+        float x4 = fmaxn(fmaxn(S[bb][12], S[bb][13]), S[bb][14]);
+        float y0 = fmaxn(fmaxn(x0, x1), x2);
+        float y1 = fmaxn(fmaxn(x3, x4), S[bb][15]);
+        bm16[bb] = fmaxn(y0, y1);
       }
-      tmax = halves_max(__builtin_fmaxf(__builtin_fmaxf(bm16[0], bm16[1]), __builtin_fmaxf(bm16[2], bm16[3])));
+      tmax = halves_max(fmaxn(fmaxn(bm16[0], bm16[1]), fmaxn(bm16[2], bm16[3])));
     }
   };
 
   // V(t): exponentials and P quantization of tile t (its row max came with M(t))
   auto phase_v = [&](int t) __attribute__((always_inline)) {
-    const float mnew = __builtin_fmaxf(m, tmax);
+    const float mnew = fmaxn(m, tmax);
     const float ms = mnew == NEG_INF ? 0.0f : mnew * lam;
     // exactly 1 when the max did not move (keeps the rescale skip exact), 0 while m = -inf
     const float alpha = m == mnew ? 1.0f : exp2_hw(__builtin_fmaf(m, lam, -ms));
@@ -1058,7 +1072,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     if constexpr (PV == PV_FP4 || (PV == PV_BF16 && PSC == SCALE_E8M0)) {
 #pragma unroll
       for (int p = 0; p < 2; p++) {
-        const float bm = __builtin_fmaxf(bm16[2 * p], bm16[2 * p + 1]);
+        const float bm = fmaxn(bm16[2 * p], bm16[2 * p + 1]);
         int x = e8m0_exp(exp2_hw(__builtin_fmaf(bm, lam, -ms)) * k1, a.prule);
         e[p] = x < -126 ? -126 : x;
         const float sc = u2f((uint32_t)(e[p] + 127) << 23);
@@ -1089,9 +1103,9 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
         if constexpr (PMODE == PM_TWO_LEVEL) pt *= k1;
         y[j] = pt;
       }
-      if constexpr (PV == PV_FP4) {
-        w[2 * bb] = pack8_fp4(y, sc16[bb]);
-        w[2 * bb + 1] = pack8_fp4(y + 8, sc16[bb]);
+      if constexpr (PV == PV_FP4) {  // into the registers of the previous tile's P
+        w[2 * bb] = pack8_fp4(y, sc16[bb], (uint32_t)bp[bb >> 1][2 * (bb & 1)]);
+        w[2 * bb + 1] = pack8_fp4(y + 8, sc16[bb], (uint32_t)bp[bb >> 1][2 * (bb & 1) + 1]);
       } else if constexpr (PV == PV_FP8) {  // c = E4M3(448 P~): 4 dwords per sub-tile
 #pragma unroll
         for (int dw = 0; dw < 4; dw++) {
@@ -1131,27 +1145,34 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   // V(t) a group stores its half of tile t+1+grp (loaded two phases earlier) and
   // loads its half of tile t+2+grp; tiles past the end repeat the last one into a
   // buffer that is no longer read.
+  // Stage offsets rotate through 0, STAGE, 2 STAGE as scalars: sk holds tile t, sv
+  // tile t-1, ss the tile this group stores next (t+1+grp).
   load_half(0);
   store_half(0);
   if (grp == 1) {
     load_half(nkt > 1 ? 1 : 0);
-    store_half(1);
+    store_half(STAGE);
   }
   load_half(nkt > 1 + grp ? 1 + grp : nkt - 1);
   __syncthreads();
   if (grp == 1) __syncthreads();
+  auto rot = [](uint32_t o) { return o == 2 * STAGE ? 0u : o + STAGE; };
+  uint32_t sk = 0, sv = 2 * STAGE, ss = grp == 0 ? STAGE : 2 * STAGE;
   for (int t = 0; t <= nkt; t++) {
-    phase_m(t);
+    phase_m(t, sk, sv);
     __builtin_amdgcn_sched_barrier(0);  // keep the phase's MFMAs on this side of the barrier
     __syncthreads();
     if (t < nkt) {
       phase_v(t);
-      store_half((t + 1 + grp) % 3);
+      store_half(ss);
       const int nt = t + 2 + grp;
       load_half(nt < nkt ? nt : nkt - 1);
     }
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
+    sv = sk;
+    sk = __builtin_amdgcn_readfirstlane(rot(sk));
+    ss = __builtin_amdgcn_readfirstlane(rot(ss));
   }
   if (grp == 0) __syncthreads();
 
@@ -1210,15 +1231,8 @@ static hipError_t launch_one(const FwdArgs& a, hipStream_t st) {
 
 template <int QK, int PV, int PMODE, int PSC>
 static hipError_t launch_pp(FwdArgs a, hipStream_t st) {
-  constexpr int bytes = PpLds<QK, PV>::BYTES;
-  auto kern = fwd_pp_kernel<QK, PV, PMODE, PSC>;
-  if (bytes > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e != hipSuccess) return e;
-  }
   if (a.plan == nullptr) a.grid = a.B * a.Hq * ((a.N + 255) / 256);
-  kern<<<dim3((unsigned)a.grid), dim3(512), bytes, st>>>(a);
+  fwd_pp_kernel<QK, PV, PMODE, PSC><<<dim3((unsigned)a.grid), dim3(512), 0, st>>>(a);
   return hipGetLastError();
 }
 
