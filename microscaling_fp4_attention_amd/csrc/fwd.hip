@@ -777,8 +777,16 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     vstart = de.voff32;
   } else {
     const int64_t nqt = (a.N + 255) / 256, BH = a.B * a.Hq, G = a.grid;
+    const int64_t groups = a.B * a.Hkv, gsz = a.Hq / a.Hkv;  // KV heads, query heads per KV head
     int64_t id = blockIdx.x, bh;
-    if (a.causal) {  // longest first
+    if (a.causal && groups % 8 == 0) {
+      // Workgroup ids are dealt round-robin to the 8 XCDs: XCD id % 8 gets whole KV-head
+      // groups (their K/V stay in its L2), and runs its items longest first.
+      const int64_t ng = groups / 8, slot = id / 8;
+      qt = nqt - 1 - slot / (ng * gsz);
+      const int64_t rem = slot % (ng * gsz), grp_id = (id % 8) * ng + rem / gsz;
+      bh = (grp_id / a.Hkv) * a.Hq + (grp_id % a.Hkv) * gsz + rem % gsz;
+    } else if (a.causal) {  // longest first
       qt = nqt - 1 - id / BH;
       bh = id % BH;
     } else {  // one head's tiles on one XCD (workgroup ids are dealt round-robin to 8 XCDs)
