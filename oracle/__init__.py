@@ -81,6 +81,14 @@ def lib():
         L.orc_v_nblocks.argtypes = [ctypes.c_int, i32p, ctypes.c_int, ctypes.c_int]
         L.orc_quantize_cols.argtypes = [f32p, ctypes.c_int, ctypes.c_int, i32p, ctypes.c_int, P(Fmt), u8p, u8p]
         L.orc_dequant_cols.argtypes = [u8p, u8p, ctypes.c_int, ctypes.c_int, i32p, ctypes.c_int, P(Fmt), f32p]
+        L.orc_attention_bias.restype = ctypes.c_int
+        L.orc_attention_bias.argtypes = [f32p, f32p, f32p, f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, i32p, ctypes.c_int, P(AttnParams), i64p,
+                                         ctypes.c_int64, f32p, f32p, f64p]
+        L.orc_channel_mean.argtypes = [f32p, ctypes.c_int, ctypes.c_int, i32p, ctypes.c_int, f32p]
+        L.orc_preprocess_rows.argtypes = [f32p, ctypes.c_int, ctypes.c_int, f32p, i32p, ctypes.c_int,
+                                          ctypes.c_int, f32p]
+        L.orc_center_comp.argtypes = [f32p, f32p, f32p, ctypes.c_int, ctypes.c_int, i32p, ctypes.c_int, f32p]
         L.orc_attention.restype = ctypes.c_int
         L.orc_attention.argtypes = [f32p, f32p, f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_int, i32p, ctypes.c_int, P(AttnParams), i64p, ctypes.c_int64,
@@ -189,8 +197,9 @@ def dequant_cols(codes, scales, f, doc_off=None):
 
 
 def attention(Q, K, V, pmode, pfmt=None, causal=False, sm_scale=None, kv_tile=128, doc_off=None,
-              rows=None):
-    """Q [B,Hq,N,d], K/V [B,Hkv,N,d] float32 (dequantized).  Returns (O [nrows,d], lse, fb)."""
+              rows=None, bias=None):
+    """Q [B,Hq,N,d], K/V [B,Hkv,N,d] float32 (dequantized); bias: None or float32 [B,Hq,N]
+    added to each key's scores.  Returns (O [nrows,d], lse, fb)."""
     Q = np.ascontiguousarray(Q, dtype=np.float32)
     K = np.ascontiguousarray(K, dtype=np.float32)
     V = np.ascontiguousarray(V, dtype=np.float32)
@@ -206,10 +215,54 @@ def attention(Q, K, V, pmode, pfmt=None, causal=False, sm_scale=None, kv_tile=12
     lse = np.zeros(nrows, dtype=np.float32)
     fb = np.zeros(nrows, dtype=np.float64)
     dd = None if doc_off is None else np.ascontiguousarray(doc_off, dtype=np.int32)
-    rc = lib().orc_attention(_ptr(Q, ctypes.c_float), _ptr(K, ctypes.c_float), _ptr(V, ctypes.c_float), B, Hq,
-                             Hkv, N, d, _ptr(dd, ctypes.c_int32), 0 if dd is None else len(dd) - 1,
-                             ctypes.byref(p), _ptr(r, ctypes.c_int64), nrows, _ptr(O, ctypes.c_float),
-                             _ptr(lse, ctypes.c_float), _ptr(fb, ctypes.c_double))
+    bb = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    if bb is not None and bb.shape != (B, Hq, N):
+        raise ValueError("bias must be [B, Hq, N]")
+    rc = lib().orc_attention_bias(_ptr(Q, ctypes.c_float), _ptr(K, ctypes.c_float), _ptr(V, ctypes.c_float),
+                                  _ptr(bb, ctypes.c_float), B, Hq, Hkv, N, d, _ptr(dd, ctypes.c_int32),
+                                  0 if dd is None else len(dd) - 1, ctypes.byref(p), _ptr(r, ctypes.c_int64),
+                                  nrows, _ptr(O, ctypes.c_float), _ptr(lse, ctypes.c_float),
+                                  _ptr(fb, ctypes.c_double))
     if rc != 0:
         raise ValueError(f"orc_attention failed with {rc}")
     return O, lse, fb
+
+
+# ---- outlier pre-processing (one head at a time) ----
+def _docs(doc_off):
+    dd = None if doc_off is None else np.ascontiguousarray(doc_off, dtype=np.int32)
+    return dd, (0 if dd is None else len(dd) - 1)
+
+
+def channel_mean(x, doc_off=None):
+    """x: float32 [N, d] -> per-document channel means float32 [max(ndocs,1), d]."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    N, d = x.shape
+    dd, nd = _docs(doc_off)
+    mean = np.zeros((max(nd, 1), d), dtype=np.float32)
+    lib().orc_channel_mean(_ptr(x, ctypes.c_float), N, d, _ptr(dd, ctypes.c_int32), nd, _ptr(mean, ctypes.c_float))
+    return mean
+
+
+def preprocess_rows(x, mean=None, doc_off=None, hadamard=False):
+    """x: float32 [N, d] -> fl32(((x - mean[doc]) H) / sqrt(d)) (rotation optional), [N, d]."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    N, d = x.shape
+    dd, nd = _docs(doc_off)
+    m = None if mean is None else np.ascontiguousarray(mean, dtype=np.float32)
+    out = np.zeros((N, d), dtype=np.float32)
+    lib().orc_preprocess_rows(_ptr(x, ctypes.c_float), N, d, _ptr(m, ctypes.c_float), _ptr(dd, ctypes.c_int32), nd,
+                              int(bool(hadamard)), _ptr(out, ctypes.c_float))
+    return out
+
+
+def center_comp(qmean, K, kmean, doc_off=None):
+    """qmean, kmean: float32 [max(ndocs,1), d]; K: float32 [N, d] -> delta float32 [N]."""
+    K = np.ascontiguousarray(K, dtype=np.float32)
+    N, d = K.shape
+    dd, nd = _docs(doc_off)
+    delta = np.zeros(N, dtype=np.float32)
+    lib().orc_center_comp(_ptr(np.ascontiguousarray(qmean, dtype=np.float32), ctypes.c_float),
+                          _ptr(K, ctypes.c_float), _ptr(np.ascontiguousarray(kmean, dtype=np.float32), ctypes.c_float),
+                          N, d, _ptr(dd, ctypes.c_int32), nd, _ptr(delta, ctypes.c_float))
+    return delta

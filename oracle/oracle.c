@@ -308,8 +308,18 @@ static void p_block(const float* x, int n, const orc_fmt* f, double* deq, double
 /* Tiles of kv_tile keys are aligned to key 0 of the range and walked in   */
 /* ascending order; P blocks are consecutive keys aligned to the tile.     */
 /* ------------------------------------------------------------------------ */
+static int attn_row_bias(const float* q, const float* K, const float* V, const float* sbias, int nk,
+                         int vis, int d, const orc_attn_params* p, float* o, float* lse, double* fb);
+
 int orc_attn_row(const float* q, const float* K, const float* V, int nk, int vis, int d,
                  const orc_attn_params* p, float* o, float* lse, double* fb) {
+  return attn_row_bias(q, K, V, NULL, nk, vis, d, p, o, lse, fb);
+}
+
+/* sbias: NULL, or the score bias of keys 0..nk-1 of this range ([MPFA] Eq. 10: added
+ * to the exact dot product before the mask and the running maximum) */
+static int attn_row_bias(const float* q, const float* K, const float* V, const float* sbias, int nk,
+                         int vis, int d, const orc_attn_params* p, float* o, float* lse, double* fb) {
   int T = p->kv_tile;
   float m = -INFINITY, l = 0.0f;
   float* acc = (float*)calloc((size_t)d, sizeof(float));
@@ -331,6 +341,7 @@ int orc_attn_row(const float* q, const float* K, const float* V, int nk, int vis
       if (t0 + j < vis) {
         double acc_d = 0.0;
         for (int c = 0; c < d; c++) acc_d += (double)q[c] * (double)K[(int64_t)(t0 + j) * d + c];
+        if (sbias) acc_d += (double)sbias[t0 + j];
         s[j] = (float)acc_d;
         if (s[j] > mt) mt = s[j];
       } else {
@@ -436,6 +447,13 @@ int orc_attn_row(const float* q, const float* K, const float* V, int nk, int vis
 int orc_attention(const float* Q, const float* K, const float* V, int B, int Hq, int Hkv, int N,
                   int d, const int* doc_off, int ndocs, const orc_attn_params* p,
                   const int64_t* rows, int64_t nrows, float* O, float* lse, double* fb) {
+  return orc_attention_bias(Q, K, V, NULL, B, Hq, Hkv, N, d, doc_off, ndocs, p, rows, nrows, O, lse, fb);
+}
+
+int orc_attention_bias(const float* Q, const float* K, const float* V, const float* bias, int B,
+                       int Hq, int Hkv, int N, int d, const int* doc_off, int ndocs,
+                       const orc_attn_params* p, const int64_t* rows, int64_t nrows, float* O,
+                       float* lse, double* fb) {
   int64_t total = (int64_t)B * Hq * N;
   if (!rows) nrows = total;
   if (doc_off && ndocs > 0 && B != 1) return -1;
@@ -458,8 +476,69 @@ int orc_attention(const float* Q, const float* K, const float* V, int B, int Hq,
     }
     nk = ke - ks;
     vis = p->causal ? (i - ks + 1) : nk;
-    orc_attn_row(Q + r * d, kb + (int64_t)ks * d, vb + (int64_t)ks * d, nk, vis, d, p,
-                 O + idx * d, lse ? lse + idx : NULL, fb ? fb + idx : NULL);
+    attn_row_bias(Q + r * d, kb + (int64_t)ks * d, vb + (int64_t)ks * d,
+                  bias ? bias + (b * Hq + h) * (int64_t)N + ks : NULL, nk, vis, d, p, O + idx * d,
+                  lse ? lse + idx : NULL, fb ? fb + idx : NULL);
   }
   return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Outlier pre-processing ([MPFA] section 4.2-4.3, [FLAMIA] section 3.4 and   */
+/* appendix A.2, [MXF4] "Smooth-K is the smaller lever").                     */
+/* ------------------------------------------------------------------------ */
+static int doc_of(int t, const int* doc_off, int ndocs) {
+  if (!doc_off || ndocs <= 0) return 0;
+  for (int k = 0; k < ndocs; k++)
+    if (doc_off[k] <= t && t < doc_off[k + 1]) return k;
+  return ndocs - 1;
+}
+
+void orc_channel_mean(const float* x, int N, int d, const int* doc_off, int ndocs, float* mean) {
+  int nd = (doc_off && ndocs > 0) ? ndocs : 1;
+  for (int k = 0; k < nd; k++) {
+    int t0 = (doc_off && ndocs > 0) ? doc_off[k] : 0;
+    int t1 = (doc_off && ndocs > 0) ? doc_off[k + 1] : N;
+    for (int c = 0; c < d; c++) {
+      double sum = 0.0;
+      for (int t = t0; t < t1; t++) sum += (double)x[(int64_t)t * d + c];
+      mean[(int64_t)k * d + c] = (t1 > t0) ? (float)(sum / (double)(t1 - t0)) : 0.0f;
+    }
+  }
+}
+
+static int hadamard_sign(int i, int j) { return __builtin_popcount((unsigned)(i & j)) & 1 ? -1 : 1; }
+
+void orc_preprocess_rows(const float* x, int N, int d, const float* mean, const int* doc_off,
+                         int ndocs, int hadamard, float* out) {
+  double* y = (double*)malloc(sizeof(double) * (size_t)d);
+  const double c = 1.0 / sqrt((double)d);
+  for (int t = 0; t < N; t++) {
+    const float* mu = mean ? mean + (int64_t)doc_of(t, doc_off, ndocs) * d : NULL;
+    for (int i = 0; i < d; i++) y[i] = (double)x[(int64_t)t * d + i] - (mu ? (double)mu[i] : 0.0);
+    for (int j = 0; j < d; j++) {
+      double z;
+      if (hadamard) {
+        z = 0.0;
+        for (int i = 0; i < d; i++) z += hadamard_sign(i, j) > 0 ? y[i] : -y[i];
+        z = z * c;
+      } else {
+        z = y[j];
+      }
+      out[(int64_t)t * d + j] = (float)z;
+    }
+  }
+  free(y);
+}
+
+void orc_center_comp(const float* qmean, const float* K, const float* kmean, int N, int d,
+                     const int* doc_off, int ndocs, float* delta) {
+  for (int j = 0; j < N; j++) {
+    int k = doc_of(j, doc_off, ndocs);
+    double acc = 0.0;
+    for (int c = 0; c < d; c++)
+      acc += (double)qmean[(int64_t)k * d + c] *
+             ((double)K[(int64_t)j * d + c] - (double)kmean[(int64_t)k * d + c]);
+    delta[j] = (float)acc;
+  }
 }

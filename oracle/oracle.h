@@ -112,6 +112,44 @@ int orc_attention(const float* Q, const float* K, const float* V, int B, int Hq,
                   int d, const int* doc_off, int ndocs, const orc_attn_params* p,
                   const int64_t* rows, int64_t nrows, float* O, float* lse, double* fb);
 
+/* As orc_attention, plus an optional per-key score bias: bias [B][Hq][N] (NULL for
+ * none) is added to every score of its key before masking and before the running
+ * maximum, s = fl32(exact dot + bias) ([MPFA] section 4.3, Eq. 10). */
+int orc_attention_bias(const float* Q, const float* K, const float* V, const float* bias, int B,
+                       int Hq, int Hkv, int N, int d, const int* doc_off, int ndocs,
+                       const orc_attn_params* p, const int64_t* rows, int64_t nrows, float* O,
+                       float* lse, double* fb);
+
+/* ---- outlier pre-processing of Q and K (before quantization) ---- */
+
+/* Per-channel mean over the tokens of each document of one head ([MPFA] section
+ * 4.2, Eq. 7; [MXF4] "Smooth-K is the smaller lever": K.mean over tokens).
+ * x: [N][d]; doc_off/ndocs as above (NULL/0: one document [0, N)).
+ * mean: [max(ndocs,1)][d], mean = fl32(sum / L) with the sum over the document's
+ * tokens taken in double in token order (exact for bf16 inputs whose magnitudes
+ * span less than 2^38) and the division in double; an empty document gets 0.
+ * Pinned by tests/test_oracle_preproc.py. */
+void orc_channel_mean(const float* x, int N, int d, const int* doc_off, int ndocs, float* mean);
+
+/* Pre-processed rows y = fl32(((x - mu) H) c) of one head: mu is the channel mean of
+ * the token's document (mean may be NULL: mu = 0), H the d x d Sylvester Hadamard
+ * matrix H[i][j] = (-1)^popcount(i & j) when hadamard != 0 (else the identity) and
+ * c = fl64(1/sqrt(d)) with the rotation, 1 without it.  The normalized rotation is
+ * orthogonal, so it keeps every Q.K dot product ([FLAMIA] section 3.4 and appendix
+ * A.2); centering follows [MPFA] section 4.2.  x - mu and the +-1 sum are formed
+ * exactly in double (bf16 x, float mu), then multiplied by c in double and rounded
+ * once to float.  out: [N][d].  Pinned by tests/test_oracle_preproc.py. */
+void orc_preprocess_rows(const float* x, int N, int d, const float* mean, const int* doc_off,
+                         int ndocs, int hadamard, float* out);
+
+/* Centering compensation of one query head ([MPFA] section 4.3, Eq. 9):
+ * delta[j] = fl32(sum_c qmean[doc(j)][c] * (K[j][c] - kmean[doc(j)][c])), the
+ * products and the sum in double in channel order.  K: [N][d] of the query head's
+ * KV head; qmean, kmean: [max(ndocs,1)][d]; delta: [N].
+ * Pinned by tests/test_oracle_preproc.py. */
+void orc_center_comp(const float* qmean, const float* K, const float* kmean, int N, int d,
+                     const int* doc_off, int ndocs, float* delta);
+
 #ifdef __cplusplus
 }
 #endif
