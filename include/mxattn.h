@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MXATTN_ABI_VERSION 1
+#define MXATTN_ABI_VERSION 2
 
 typedef enum {
   MXATTN_OK = 0,
@@ -127,6 +127,10 @@ typedef struct {
   float sm_scale;   /* softmax scale applied to the scores, normally 1/sqrt(d)        */
   int32_t kv_tile;  /* keys per online-softmax step; must be 128                      */
   int32_t out_fp32; /* 1: O is float32, 0: O is bfloat16 (round to nearest even)      */
+  const float* score_bias; /* DEVICE [B][Hq][N] float32 added to the scores of each key
+                              before the mask and the running maximum (the centering
+                              compensation of mxattn_center_comp()), or NULL; 16-byte
+                              aligned                                                  */
 } mxattn_fwd_params;
 
 /* ABI version (MXATTN_ABI_VERSION of the built library). */
@@ -175,6 +179,68 @@ int mxattn_qtensor_bytes(const mxattn_qfmt* fmt, int role, int64_t B, int64_t H,
 int mxattn_quantize(const void* x_bf16, const int64_t x_strides[4], int64_t B, int64_t H, int64_t N,
                     int64_t d, int role, const mxattn_qfmt* fmt, const int32_t* cu_seqlens, int ndocs,
                     mxattn_qtensor* out, void* stream);
+
+/*
+ * Outlier pre-processing of Q and K ("MpFA" section 4.2, Eq. 7: sequence
+ * centering; blog "Microscaling FP4 Attention ...", "Smooth-K is the smaller
+ * lever": subtract K's per-channel mean; "FLAMIA" section 3.4 and appendix A.2:
+ * a normalized Hadamard rotation of the head channels before quantization).
+ *
+ * mxattn_channel_mean: per-channel means of a bf16 tensor x [B][H][N][d] (strides
+ *   as for mxattn_quantize) over the tokens of each document:
+ *   mean[b][h][k][c] = fl32(sum / L_k), the sum over document k's tokens taken in
+ *   double (exact for realistic bf16 spans, so the result does not depend on the
+ *   summation order) and divided in double; an empty document gives 0.
+ *   mean: DEVICE float32 [B][H][max(ndocs,1)][d], 16-byte aligned.
+ *   cu_seqlens/ndocs: DEVICE document offsets as for mxattn_quantize (ndocs <= 1
+ *   or cu_seqlens NULL: one document [0, N)).
+ *   Errors: MXATTN_E_INVALID, MXATTN_E_UNSUPPORTED (d != 128), MXATTN_E_ALIGN,
+ *   MXATTN_E_HIP.
+ */
+int mxattn_channel_mean(const void* x_bf16, const int64_t x_strides[4], int64_t B, int64_t H, int64_t N,
+                        int64_t d, const int32_t* cu_seqlens, int ndocs, float* mean, void* stream);
+
+/* Pre-processing applied by mxattn_quantize_pre() before the block quantization. */
+typedef struct {
+  const float* mean; /* DEVICE [B][H][max(ndocs,1)][d] channel means to subtract (from
+                        mxattn_channel_mean), or NULL                                  */
+  int32_t hadamard;  /* 1: rotate each token by H / sqrt(d), H the Sylvester Hadamard
+                        matrix H[i][j] = (-1)^popcount(i & j); 0: no rotation          */
+} mxattn_preproc;
+
+/*
+ * Quantize Q or K (role QK only) after pre-processing: each token becomes
+ * y = fl32(((x - mean[doc]) H) c), c = fl64(1 / fl64(sqrt(128))) with the rotation
+ * and 1 without it, the difference and the +-1 sums exact in double, then y is
+ * quantized exactly as mxattn_quantize() quantizes x.  Rotating Q and K alike
+ * keeps Q.K; subtracting K's mean alone changes each softmax row by a constant
+ * (smooth-K); subtracting both means needs the compensation of
+ * mxattn_center_comp() as the forward's score_bias.
+ *   pre: NULL (plain quantization) or the pre-processing to apply.
+ *   cu_seqlens/ndocs: DEVICE document offsets selecting each token's mean row
+ *   (the qtensor is laid out as without documents: role QK has no padding).
+ * Errors: as mxattn_quantize(), plus MXATTN_E_INVALID for role V.
+ */
+int mxattn_quantize_pre(const void* x_bf16, const int64_t x_strides[4], int64_t B, int64_t H, int64_t N,
+                        int64_t d, int role, const mxattn_qfmt* fmt, const mxattn_preproc* pre,
+                        const int32_t* cu_seqlens, int ndocs, mxattn_qtensor* out, void* stream);
+
+/*
+ * Centering compensation ("MpFA" section 4.3, Eqs. 8-9): with Q and K both
+ * centered, S = Q_c K_c^T + 1 (qmean K_c^T) + (Q kmean^T) 1^T; the last term is
+ * constant along each softmax row and cancels, the middle one is restored as
+ *   delta[b][hq][j] = fl32(sum_c qmean[b][hq][doc(j)][c] * (k[b][hk][j][c] - kmean[b][hk][doc(j)][c]))
+ * with hk = hq * Hkv / Hq, products and sums in double (within one float ulp of
+ * the exactly rounded value).  Pass delta as mxattn_fwd_params.score_bias.
+ *   qmean: DEVICE [B][Hq][max(ndocs,1)][d]; kmean: DEVICE [B][Hkv][max(ndocs,1)][d]
+ *   k: bf16 [B][Hkv][N][d] with element strides k_strides (the unquantized K);
+ *   delta: DEVICE float32 [B][Hq][N].
+ * Errors: MXATTN_E_INVALID, MXATTN_E_UNSUPPORTED (d != 128), MXATTN_E_ALIGN,
+ *   MXATTN_E_HIP.
+ */
+int mxattn_center_comp(const float* qmean, const void* k_bf16, const int64_t k_strides[4], const float* kmean,
+                       int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, const int32_t* cu_seqlens,
+                       int ndocs, float* delta, void* stream);
 
 /*
  * Bytes of workspace a forward over packed documents needs (a document table

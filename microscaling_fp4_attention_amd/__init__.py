@@ -26,6 +26,9 @@ ROLE_QK, ROLE_V = 0, 1
 P_DIRECT, P_TWO_LEVEL, P_PNQ, P_FP8_FIXED = 1, 2, 3, 4
 
 
+ABI_VERSION = 2  # MXATTN_ABI_VERSION of include/mxattn.h
+
+
 class QFmt(ctypes.Structure):
     _fields_ = [("elem", ctypes.c_int32), ("scale", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("rule", ctypes.c_int32), ("qmax", ctypes.c_float)]
@@ -39,7 +42,11 @@ class QTensorC(ctypes.Structure):
 
 class FwdParams(ctypes.Structure):
     _fields_ = [("pmode", ctypes.c_int32), ("pfmt", QFmt), ("causal", ctypes.c_int32), ("sm_scale", ctypes.c_float),
-                ("kv_tile", ctypes.c_int32), ("out_fp32", ctypes.c_int32)]
+                ("kv_tile", ctypes.c_int32), ("out_fp32", ctypes.c_int32), ("score_bias", ctypes.c_void_p)]
+
+
+class PreProc(ctypes.Structure):
+    _fields_ = [("mean", ctypes.c_void_p), ("hadamard", ctypes.c_int32)]
 
 
 # block formats named as on the pages
@@ -79,6 +86,8 @@ def _lib():
         P = ctypes.POINTER
         i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         L.mxattn_abi_version.restype = i32
+        if L.mxattn_abi_version() != ABI_VERSION:
+            raise ImportError(f"{LIB_PATH} has ABI {L.mxattn_abi_version()}, this binding needs {ABI_VERSION}; rebuild")
         L.mxattn_status_str.restype = ctypes.c_char_p
         L.mxattn_status_str.argtypes = [i32]
         L.mxattn_last_error.restype = ctypes.c_char_p
@@ -87,6 +96,13 @@ def _lib():
                                            P(ctypes.c_size_t), P(i64)]
         L.mxattn_quantize.restype = i32
         L.mxattn_quantize.argtypes = [vp, P(i64), i64, i64, i64, i64, i32, P(QFmt), vp, i32, P(QTensorC), vp]
+        L.mxattn_channel_mean.restype = i32
+        L.mxattn_channel_mean.argtypes = [vp, P(i64), i64, i64, i64, i64, vp, i32, vp, vp]
+        L.mxattn_quantize_pre.restype = i32
+        L.mxattn_quantize_pre.argtypes = [vp, P(i64), i64, i64, i64, i64, i32, P(QFmt), P(PreProc), vp, i32,
+                                          P(QTensorC), vp]
+        L.mxattn_center_comp.restype = i32
+        L.mxattn_center_comp.argtypes = [vp, vp, P(i64), vp, i64, i64, i64, i64, i64, vp, i32, vp, vp]
         L.mxattn_fwd_workspace_bytes.restype = ctypes.c_size_t
         L.mxattn_fwd_workspace_bytes.argtypes = [i64, i32]
         L.mxattn_fwd_plan.restype = i32
@@ -151,14 +167,74 @@ def qtensor_bytes(fmt, role: int, B: int, H: int, N: int, d: int = 128, ndocs: i
     return cb.value, sb.value, npad.value
 
 
-def quantize(x: torch.Tensor, role: int, fmt, cu_seqlens: torch.Tensor | None = None, stream=None) -> QTensor:
+def _cu(cu_seqlens):
+    if cu_seqlens is None:
+        return None, 0
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda:
+        raise ValueError("cu_seqlens must be an int32 device tensor")
+    return ctypes.c_void_p(cu_seqlens.data_ptr()), cu_seqlens.numel() - 1
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def channel_mean(x: torch.Tensor, cu_seqlens: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Per-channel means of a bf16 tensor x [B, H, N, d] over each document's tokens:
+    float32 [B, H, max(ndocs, 1), d] (mxattn_channel_mean)."""
+    if x.dtype != torch.bfloat16 or x.dim() != 4:
+        raise ValueError("x must be a 4-D bfloat16 tensor [B, H, N, d]")
+    B, H, N, d = x.shape
+    cu, ndocs = _cu(cu_seqlens)
+    mean = torch.empty((B, H, max(ndocs, 1), d), dtype=torch.float32, device=x.device)
+    _check(_lib().mxattn_channel_mean(_ptr(x), _i64(x.stride()), B, H, N, d, cu, ndocs, _ptr(mean),
+                                      _stream(stream)), "mxattn_channel_mean")
+    return mean
+
+
+def center_comp(qmean: torch.Tensor, k: torch.Tensor, kmean: torch.Tensor, cu_seqlens: torch.Tensor | None = None,
+                stream=None) -> torch.Tensor:
+    """Centering compensation delta [B, Hq, N] (float32) for the forward's score_bias
+    (mxattn_center_comp): qmean [B, Hq, nd, d], k bf16 [B, Hkv, N, d], kmean [B, Hkv, nd, d]."""
+    B, Hkv, N, d = k.shape
+    Hq = qmean.shape[1]
+    cu, ndocs = _cu(cu_seqlens)
+    delta = torch.empty((B, Hq, N), dtype=torch.float32, device=k.device)
+    _check(_lib().mxattn_center_comp(_ptr(qmean.contiguous()), _ptr(k), _i64(k.stride()), _ptr(kmean.contiguous()),
+                                     B, Hq, Hkv, N, d, cu, ndocs, _ptr(delta), _stream(stream)), "mxattn_center_comp")
+    return delta
+
+
+def quantize(x: torch.Tensor, role: int, fmt, cu_seqlens: torch.Tensor | None = None, stream=None,
+             mean: torch.Tensor | None = None, hadamard: bool = False) -> QTensor:
     """Quantize a bf16 tensor x [B, H, N, d] (any strides with a unit channel stride).
 
-    cu_seqlens: int32 device tensor of document offsets (role V, B == 1) or None.
+    cu_seqlens: int32 device tensor of document offsets (role V: the document layout;
+    role QK with a mean: each token's mean row), or None.
+    mean / hadamard (role QK only): subtract the per-document channel means (from
+    channel_mean) and/or rotate by the normalized Hadamard matrix before quantizing
+    (mxattn_quantize_pre).
     """
     if x.dtype != torch.bfloat16 or x.dim() != 4:
         raise ValueError("x must be a 4-D bfloat16 tensor [B, H, N, d]")
     B, H, N, d = x.shape
+    if mean is not None or hadamard:
+        if role != ROLE_QK:
+            raise ValueError("pre-processing applies to role QK only")
+        cb, sb, _ = qtensor_bytes(fmt, role, B, H, N, d, 0)
+        codes = torch.empty(max(cb, 16), dtype=torch.uint8, device=x.device)[:cb]
+        scales = torch.empty(max(sb, 16), dtype=torch.uint8, device=x.device)[:sb]
+        desc = QTensorC()
+        desc.codes = codes.data_ptr() if cb else None
+        desc.scales = scales.data_ptr() if sb else None
+        f = qfmt(fmt)
+        mean_c = None if mean is None else mean.contiguous()
+        pre = PreProc(None if mean_c is None else mean_c.data_ptr(), int(bool(hadamard)))
+        cu, ndocs = _cu(cu_seqlens)
+        _check(_lib().mxattn_quantize_pre(_ptr(x), _i64(x.stride()), B, H, N, d, role, ctypes.byref(f),
+                                          ctypes.byref(pre), cu, ndocs, ctypes.byref(desc), _stream(stream)),
+               "mxattn_quantize_pre")
+        return QTensor(codes, scales, desc)
     ndocs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
     cb, sb, _ = qtensor_bytes(fmt, role, B, H, N, d, ndocs)
     codes = torch.empty(max(cb, 16), dtype=torch.uint8, device=x.device)[:cb]
@@ -193,12 +269,20 @@ def fwd_plan(cu_seqlens_host, N: int, causal: bool, device="cuda", stream=None) 
     return ws
 
 
-def fwd_params(pmode, pfmt="mxfp4", causal=False, sm_scale=None, d=128, out_fp32=True, kv_tile=128) -> FwdParams:
+def fwd_params(pmode, pfmt="mxfp4", causal=False, sm_scale=None, d=128, out_fp32=True, kv_tile=128,
+               score_bias: torch.Tensor | None = None) -> FwdParams:
+    """score_bias: float32 device tensor [B, Hq, N] added to each key's scores (the
+    centering compensation from center_comp), or None.  The params keep a reference."""
     pm = PMODES[pmode] if isinstance(pmode, str) else int(pmode)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
     pf = qfmt(pfmt if pfmt is not None else "mxfp4")
-    return FwdParams(pm, pf, int(bool(causal)), float(sm_scale), kv_tile, int(bool(out_fp32)))
+    if score_bias is not None and (score_bias.dtype != torch.float32 or not score_bias.is_contiguous()):
+        raise ValueError("score_bias must be a contiguous float32 tensor [B, Hq, N]")
+    p = FwdParams(pm, pf, int(bool(causal)), float(sm_scale), kv_tile, int(bool(out_fp32)),
+                  None if score_bias is None else score_bias.data_ptr())
+    p._score_bias_ref = score_bias
+    return p
 
 
 def fwd(q: QTensor, k: QTensor, v: QTensor, params: FwdParams, out: torch.Tensor | None = None,

@@ -59,6 +59,15 @@ __device__ __forceinline__ v16f zero16() {
   return z;
 }
 
+// 16 consecutive floats from LDS (a lane's score bias of one 32-key block: its 16
+// scores belong to 16 consecutive keys)
+__device__ __forceinline__ v16f bias16(const uint8_t* p) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 16),
+               c = *reinterpret_cast<const float4*>(p + 32), d = *reinterpret_cast<const float4*>(p + 48);
+  v16f r = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w, c.x, c.y, c.z, c.w, d.x, d.y, d.z, d.w};
+  return r;
+}
+
 __device__ __forceinline__ v8i v8_from4(u4 t) {
   v8i r = {(int)t.x, (int)t.y, (int)t.z, (int)t.w, 0, 0, 0, 0};
   return r;
@@ -166,11 +175,12 @@ __device__ __forceinline__ int kpos(int r) {
   return 32 * b + 8 * (t >> 2) + 4 * hh + (t & 3);
 }
 
-template <int QK, int PV>
+template <int QK, int PV, bool BIAS = false>
 struct Lds {
   static constexpr int KROW = QK == QK_FP4 ? 80 : 256;  // bytes per staged key row
   static constexpr int VROW = PV == PV_FP4 ? 80 : PV == PV_BF16 ? 256 : 144;  // per V^T row
-  static constexpr int STAGE = 128 * (KROW + VROW);      // one key tile
+  static constexpr int BOFF = 128 * (KROW + VROW);       // then the score bias of the 128 keys
+  static constexpr int STAGE = BOFF + (BIAS ? 512 : 0);  // one key tile
   // Buffers of key tiles: 3 lets the next tile's scores and this tile's PV read
   // different buffers while a third is refilled (one barrier per tile); 2 needs a
   // second barrier; 1 (large bf16 tiles) falls back to compute-after-store.  Two
@@ -183,10 +193,10 @@ struct Lds {
 template <int QK, int PV>
 constexpr int waves_per_simd() { return 2; }
 
-template <int QK, int PV, int PMODE, int PSC, int VSC>
+template <int QK, int PV, int PMODE, int PSC, int VSC, bool BIAS>
 __global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  using L = Lds<QK, PV>;
+  using L = Lds<QK, PV, BIAS>;
   constexpr int NB = L::NB;
   constexpr int VB = VSC == SCALE_E8M0 ? 32 : 16;  // V block along keys
   constexpr bool SPLIT16 = PV == PV_FP8;            // key permutation of the FP8 MFMA
@@ -279,7 +289,17 @@ __global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(Fw
   u4 vreg[NVC];        // VB == 16 with E2M1: only .x, .y used (8-byte chunks)
   uint32_t vscr[NVC];  // PV_FP4/PV_FP8: a channel's 4 block scales in [0]; PV_BF16: the chunk's scale
 
+  // score bias of this query head (threads < 128 stage one key each)
+  const float* hbias = BIAS ? a.bias + (b * a.Hq + hq) * a.N + qstart : nullptr;
+  float rbias = 0.0f;
   auto load_tile = [&](int kt) __attribute__((always_inline)) {
+    if constexpr (BIAS) {
+      if (tid < 128) {
+        int key = kt * 128 + tid;
+        if (key >= klen32) key = klen32 - 1;
+        rbias = hbias[key];
+      }
+    }
     // K rows: 512 chunks of 16 bytes
 #pragma unroll
     for (int i = 0; i < NKC; i++) {
@@ -336,6 +356,9 @@ __global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(Fw
   auto store_tile = [&](int buf) __attribute__((always_inline)) {
     uint8_t* Ks = smem + buf * L::STAGE;
     uint8_t* Vs = Ks + 128 * L::KROW;
+    if constexpr (BIAS) {
+      if (tid < 128) *reinterpret_cast<float*>(Ks + L::BOFF + 4 * tid) = rbias;
+    }
 #pragma unroll
     for (int i = 0; i < NKC; i++) {
       int c = tid + 256 * i, row = c >> 2, part = c & 3;
@@ -394,7 +417,7 @@ __global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(Fw
     uint32_t boff = (uint32_t)(buf * L::STAGE);
     asm volatile("" : "+v"(boff) : "v"(after));
     const uint8_t* Ks = smem + boff;
-    v16f acc = zero16();
+    v16f acc = BIAS ? bias16(Ks + L::BOFF + 4 * key_of<SPLIT16>(bb, hh, 0)) : zero16();
     if constexpr (QK == QK_FP4) {
       const uint8_t* rp = Ks + (32 * bb + ql) * 80;
       uint32_t ks4 = *reinterpret_cast<const uint32_t*>(rp + 64);
@@ -737,18 +760,19 @@ __global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(Fw
 // rows) during its VALU phases, two phases after loading it.
 // Routes: QK_FP4 / QK_BF16 x PV_FP4 / PV_FP8 / PV_BF16 (V with E8M0 per 32 keys).
 // ===========================================================================
-template <int QK, int PV>
+template <int QK, int PV, bool BIAS>
 struct PpLds {
   static constexpr int KROW = QK == QK_FP4 ? 80 : 256;
   static constexpr int VROW = PV == PV_FP4 ? 80 : PV == PV_FP8 ? 144 : 256;
-  static constexpr int KV = 128 * KROW;  // V^T rows follow the 128 key rows of a stage
-  static constexpr int STAGE = 128 * (KROW + VROW);
+  static constexpr int KV = 128 * KROW;             // V^T rows follow the 128 key rows of a stage
+  static constexpr int BOFF = 128 * (KROW + VROW);  // then the score bias of the 128 keys
+  static constexpr int STAGE = BOFF + (BIAS ? 512 : 0);
   static constexpr int BYTES = 3 * STAGE;
 };
 
-template <int QK, int PV, int PMODE, int PSC>
+template <int QK, int PV, int PMODE, int PSC, bool BIAS>
 __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
-  using L = PpLds<QK, PV>;
+  using L = PpLds<QK, PV, BIAS>;
   // static LDS: its base is the constant 0, so stage offsets fold into the instructions
   __shared__ __attribute__((aligned(16))) uint8_t smem[L::BYTES];
   constexpr int STAGE = L::STAGE, KV = L::KV;
@@ -847,9 +871,19 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   const uint8_t* hv_sbase = a.vs + vrow0 * nvb;
   const uint32_t vblk0 = (uint32_t)(vstart >> 5) & ~3u, vsh = (uint32_t)(vstart >> 5) & 3u;
   const uint32_t o_v = (uint32_t)kr * vrow_bytes, o_vs = (uint32_t)sr * nvb + vblk0;
+  // score bias of this query head: wave 2 of each group stages its half's 64 keys
+  const float* hbias = BIAS ? a.bias + (b * a.Hq + hq) * a.N + qstart : nullptr;
+  const int bkey = 64 * grp + (gt & 63);
   u4 rk, rv0, rv1;
   uint32_t rks = 0, rvs = 0, rvs_hi = 0;
+  float rb = 0.0f;
   auto load_half = [&](int t) __attribute__((always_inline)) {
+    if constexpr (BIAS) {
+      if (gt >= 128 && gt < 192) {  // wave-uniform
+        const int k = t * 128 + bkey < klen ? t * 128 + bkey : klen - 1;
+        rb = hbias[k];
+      }
+    }
     const int key = t * 128 + kr < klen ? t * 128 + kr : klen - 1;
     rk = *reinterpret_cast<const u4*>(hk_codes + ((uint32_t)key * 64 + part * 16));
     if constexpr (QK == QK_FP4) {
@@ -884,6 +918,9 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   };
   auto store_half = [&](uint32_t so) __attribute__((always_inline)) {
     uint8_t* base = smem + so;
+    if constexpr (BIAS) {
+      if (gt >= 128 && gt < 192) *reinterpret_cast<float*>(base + L::BOFF + 4 * bkey) = rb;
+    }
     if constexpr (QK == QK_FP4) {
       *reinterpret_cast<u4*>(base + kpos_r * 80 + part * 16) = rk;
       if (gt < 64) *reinterpret_cast<u2*>(base + kpos_s * 80 + 64) = mk2(rks, rks >> 8);
@@ -998,12 +1035,12 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
           const uint32_t ks4 = *reinterpret_cast<const uint32_t*>(rp + ksok);
           v8i a0 = v8_from4(*reinterpret_cast<const u4*>(rp + koffk));
           v8i a1 = v8_from4(*reinterpret_cast<const u4*>(rp + koffk + 32));
-          v16f acc = zero16();
+          v16f acc = BIAS ? bias16(Ks + L::BOFF + 4 * key_of<SPLIT16>(bb, hh, 0)) : zero16();
           acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, qop[0], acc, 4, 4, 0, (int)ks4, 0, (int)qsc);
           S[bb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, qop[1], acc, 4, 4, 2, (int)ks4, 2, (int)qsc);
         } else {
           const uint8_t* rp = Ks + (32 * bb + ql) * 256;
-          v16f acc = zero16();
+          v16f acc = BIAS ? bias16(Ks + L::BOFF + 4 * key_of<SPLIT16>(bb, hh, 0)) : zero16();
 #pragma unroll
           for (int s = 0; s < 8; s++) {
             const int chunk = (2 * s + hh) ^ (ql & 15);
@@ -1224,10 +1261,10 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
 // ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
-template <int QK, int PV, int PMODE, int PSC, int VSC>
-static hipError_t launch_one(const FwdArgs& a, hipStream_t st) {
-  constexpr int bytes = Lds<QK, PV>::BYTES;
-  auto kern = fwd_kernel<QK, PV, PMODE, PSC, VSC>;
+template <int QK, int PV, int PMODE, int PSC, int VSC, bool BIAS>
+static hipError_t launch_one_b(const FwdArgs& a, hipStream_t st) {
+  constexpr int bytes = Lds<QK, PV, BIAS>::BYTES;
+  auto kern = fwd_kernel<QK, PV, PMODE, PSC, VSC, BIAS>;
   if (bytes > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
@@ -1237,10 +1274,17 @@ static hipError_t launch_one(const FwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int QK, int PV, int PMODE, int PSC, int VSC>
+static hipError_t launch_one(const FwdArgs& a, hipStream_t st) {
+  if (a.bias != nullptr) return launch_one_b<QK, PV, PMODE, PSC, VSC, true>(a, st);
+  return launch_one_b<QK, PV, PMODE, PSC, VSC, false>(a, st);
+}
+
 template <int QK, int PV, int PMODE, int PSC>
 static hipError_t launch_pp(FwdArgs a, hipStream_t st) {
   if (a.plan == nullptr) a.grid = a.B * a.Hq * ((a.N + 255) / 256);
-  fwd_pp_kernel<QK, PV, PMODE, PSC><<<dim3((unsigned)a.grid), dim3(512), 0, st>>>(a);
+  if (a.bias != nullptr) fwd_pp_kernel<QK, PV, PMODE, PSC, true><<<dim3((unsigned)a.grid), dim3(512), 0, st>>>(a);
+  else fwd_pp_kernel<QK, PV, PMODE, PSC, false><<<dim3((unsigned)a.grid), dim3(512), 0, st>>>(a);
   return hipGetLastError();
 }
 

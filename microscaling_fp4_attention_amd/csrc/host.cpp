@@ -180,6 +180,113 @@ int mxattn_quantize(const void* x_bf16, const int64_t x_strides[4], int64_t B, i
   return MXATTN_OK;
 }
 
+int mxattn_channel_mean(const void* x_bf16, const int64_t x_strides[4], int64_t B, int64_t H, int64_t N, int64_t d,
+                        const int32_t* cu_seqlens, int ndocs, float* mean, void* stream) {
+  if (x_strides == nullptr || B < 0 || H < 0 || N < 0 || ndocs < 0) return MXATTN_E_INVALID;
+  if (d != 128) return MXATTN_E_UNSUPPORTED;
+  if (ndocs > 1 && cu_seqlens == nullptr) return MXATTN_E_INVALID;
+  if (x_strides[3] != 1 || x_strides[0] < 0 || x_strides[1] < 0 || x_strides[2] < 0) return MXATTN_E_INVALID;
+  if (B * H == 0) return MXATTN_OK;
+  if (mean == nullptr || (N > 0 && x_bf16 == nullptr)) return MXATTN_E_INVALID;
+  if (!aligned16(mean) || (N > 0 && !aligned16(x_bf16))) return MXATTN_E_ALIGN;
+  if ((x_strides[0] % 8) || (x_strides[1] % 8) || (x_strides[2] % 8)) return MXATTN_E_ALIGN;
+  QuantArgs a{};
+  a.x = x_bf16;
+  a.sB = x_strides[0];
+  a.sH = x_strides[1];
+  a.sN = x_strides[2];
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.cu = ndocs > 1 ? cu_seqlens : nullptr;
+  a.ndocs = ndocs > 1 ? ndocs : 1;
+  hipError_t e = launch_channel_mean(a, mean, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mxattn_channel_mean launch");
+  return MXATTN_OK;
+}
+
+int mxattn_quantize_pre(const void* x_bf16, const int64_t x_strides[4], int64_t B, int64_t H, int64_t N, int64_t d,
+                        int role, const mxattn_qfmt* fmt, const mxattn_preproc* pre, const int32_t* cu_seqlens,
+                        int ndocs, mxattn_qtensor* out, void* stream) {
+  if (role != MXATTN_ROLE_QK) return MXATTN_E_INVALID;
+  if (pre == nullptr) return mxattn_quantize(x_bf16, x_strides, B, H, N, d, role, fmt, nullptr, 0, out, stream);
+  if (pre->hadamard != 0 && pre->hadamard != 1) return MXATTN_E_INVALID;
+  if (ndocs < 0 || (ndocs > 1 && cu_seqlens == nullptr)) return MXATTN_E_INVALID;
+  size_t cb, sb;
+  int64_t np;
+  int rc = mxattn_qtensor_bytes(fmt, role, B, H, N, d, 0, &cb, &sb, &np);
+  if (rc != MXATTN_OK) return rc;
+  if (out == nullptr || x_strides == nullptr) return MXATTN_E_INVALID;
+  if (x_strides[3] != 1 || x_strides[0] < 0 || x_strides[1] < 0 || x_strides[2] < 0) return MXATTN_E_INVALID;
+  const int64_t nel = B * H * N;
+  if (nel > 0) {
+    if (x_bf16 == nullptr || out->codes == nullptr || out->scales == nullptr) return MXATTN_E_INVALID;
+    if (!aligned16(x_bf16) || !aligned16(out->codes) || !aligned16(out->scales)) return MXATTN_E_ALIGN;
+    if ((x_strides[0] % 8) || (x_strides[1] % 8) || (x_strides[2] % 8)) return MXATTN_E_ALIGN;
+    if (pre->mean != nullptr && !aligned16(pre->mean)) return MXATTN_E_ALIGN;
+  }
+  out->fmt = *fmt;
+  out->role = role;
+  out->ndocs = 1;
+  out->B = B;
+  out->H = H;
+  out->N = N;
+  out->d = d;
+  out->n_padded = np;
+  if (nel == 0) return MXATTN_OK;
+  QuantArgs a{};
+  a.x = x_bf16;
+  a.sB = x_strides[0];
+  a.sH = x_strides[1];
+  a.sN = x_strides[2];
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.np = np;
+  a.elem = fmt->elem;
+  a.scale = fmt->scale;
+  a.block = fmt->block;
+  a.rule = make_rule(fmt);
+  a.cu = ndocs > 1 ? cu_seqlens : nullptr;
+  a.ndocs = ndocs > 1 ? ndocs : 1;
+  a.codes = out->codes;
+  a.scales = out->scales;
+  hipError_t e = launch_quant_qk_pre(a, pre->mean, pre->hadamard, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mxattn_quantize_pre launch");
+  return MXATTN_OK;
+}
+
+int mxattn_center_comp(const float* qmean, const void* k_bf16, const int64_t k_strides[4], const float* kmean,
+                       int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, const int32_t* cu_seqlens,
+                       int ndocs, float* delta, void* stream) {
+  if (k_strides == nullptr || B < 0 || N < 0 || ndocs < 0) return MXATTN_E_INVALID;
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return MXATTN_E_INVALID;
+  if (d != 128) return MXATTN_E_UNSUPPORTED;
+  if (ndocs > 1 && cu_seqlens == nullptr) return MXATTN_E_INVALID;
+  if (k_strides[3] != 1 || k_strides[0] < 0 || k_strides[1] < 0 || k_strides[2] < 0) return MXATTN_E_INVALID;
+  if (B * N == 0) return MXATTN_OK;
+  if (qmean == nullptr || kmean == nullptr || k_bf16 == nullptr || delta == nullptr) return MXATTN_E_INVALID;
+  if (!aligned16(qmean) || !aligned16(kmean) || !aligned16(k_bf16) || !aligned16(delta)) return MXATTN_E_ALIGN;
+  if ((k_strides[0] % 8) || (k_strides[1] % 8) || (k_strides[2] % 8)) return MXATTN_E_ALIGN;
+  CompArgs a{};
+  a.qmean = qmean;
+  a.k = k_bf16;
+  a.sB = k_strides[0];
+  a.sH = k_strides[1];
+  a.sN = k_strides[2];
+  a.kmean = kmean;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.N = N;
+  a.cu = ndocs > 1 ? cu_seqlens : nullptr;
+  a.ndocs = ndocs > 1 ? ndocs : 1;
+  a.delta = delta;
+  hipError_t e = launch_center_comp(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mxattn_center_comp launch");
+  return MXATTN_OK;
+}
+
 size_t mxattn_fwd_workspace_bytes(int64_t N, int ndocs) { return plan_bytes(N, ndocs); }
 
 int mxattn_fwd_plan(const int32_t* cu_host, int ndocs, int64_t N, int causal, void* workspace, size_t ws_bytes,
@@ -317,6 +424,8 @@ int mxattn_fwd(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn_qt
   a.out_fp32 = p->out_fp32 ? 1 : 0;
   a.lse = lse;
   a.plan = docs ? static_cast<const PlanHeader*>(workspace) : nullptr;
+  a.bias = p->score_bias;
+  if (a.bias != nullptr && !aligned16(a.bias)) return MXATTN_E_ALIGN;
   const int64_t nqt = (N + 127) / 128;
   a.grid = docs ? Hq * (nqt + ndocs) : B * Hq * nqt;
   if (a.grid > 0x7FFFFFFF) return MXATTN_E_UNSUPPORTED;

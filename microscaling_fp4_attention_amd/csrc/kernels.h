@@ -28,6 +28,24 @@ struct QuantArgs {
 hipError_t launch_quant_qk(const QuantArgs& a, hipStream_t st);
 hipError_t launch_quant_v(const QuantArgs& a, hipStream_t st);
 
+// outlier pre-processing (preproc.hip)
+// mean: [B][H][nd][128] float, nd = max(ndocs, 1); a.cu/a.ndocs give the documents
+hipError_t launch_channel_mean(const QuantArgs& a, float* mean, hipStream_t st);
+// role QK quantization of fl32(((x - mean) H) c); mean may be null, hadamard 0/1
+hipError_t launch_quant_qk_pre(const QuantArgs& a, const float* mean, int hadamard, hipStream_t st);
+
+struct CompArgs {
+  const float* qmean;  // [B][Hq][nd][128]
+  const void* k;       // bf16 [B][Hkv][N][128], element strides sB, sH, sN
+  int64_t sB, sH, sN;
+  const float* kmean;  // [B][Hkv][nd][128]
+  int64_t B, Hq, Hkv, N;
+  const int32_t* cu;   // device document offsets, or null
+  int ndocs;
+  float* delta;        // [B][Hq][N]
+};
+hipError_t launch_center_comp(const CompArgs& a, hipStream_t st);
+
 // Operand routes of the forward kernel.
 //   QK_FP4 : Q and K in E2M1 with E8M0/32 scales, scaled FP4 MFMA.
 //   QK_BF16: Q and K in E2M1 with E4M3/16 scales, dequantized (exactly) to bf16,
@@ -77,6 +95,7 @@ struct FwdArgs {
   float* lse;
   const PlanHeader* plan;  // packed documents, or null
   int64_t grid;            // workgroups launched
+  const float* bias;       // per-key score bias [B][Hq][N] (centering compensation), or null
 };
 
 // psc: P block scale (SCALE_E8M0 -> blocks of 32, SCALE_E4M3 -> blocks of 16);

@@ -86,9 +86,47 @@ PM_ORACLE = {"direct": oracle.P_DIRECT, "two_level": oracle.P_TWO_LEVEL, "pnq": 
              "fp8": oracle.P_FP8_FIXED}
 
 
+def oracle_preproc(xf, doc_off, mean_on, hadamard):
+    """Oracle pre-processing of Q or K [B, H, N, d] head by head: (means or None, y)."""
+    B, H, N, d = xf.shape
+    nd = 1 if doc_off is None else len(doc_off) - 1
+    means = np.zeros((B, H, nd, d), np.float32) if mean_on else None
+    y = np.empty_like(xf)
+    for b in range(B):
+        for h in range(H):
+            m = oracle.channel_mean(xf[b, h], doc_off) if mean_on else None
+            if mean_on:
+                means[b, h] = m
+            y[b, h] = oracle.preprocess_rows(xf[b, h], m, doc_off, hadamard)
+    return means, y
+
+
+def oracle_comp(qmeans, kf, kmeans, Hq, doc_off):
+    B, Hkv, N, d = kf.shape
+    delta = np.zeros((B, Hq, N), np.float32)
+    for b in range(B):
+        for h in range(Hq):
+            hk = h * Hkv // Hq
+            delta[b, h] = oracle.center_comp(qmeans[b, h], kf[b, hk], kmeans[b, hk], doc_off)
+    return delta
+
+
+def ulp_diff(a: np.ndarray, b: np.ndarray) -> int:
+    """largest distance in float32 units in the last place (finite values)"""
+    ia = a.astype(np.float32).view(np.int32).astype(np.int64)
+    ib = b.astype(np.float32).view(np.int32).astype(np.int64)
+    ia = np.where(ia < 0, -(ia & 0x7FFFFFFF), ia)
+    ib = np.where(ib < 0, -(ib & 0x7FFFFFFF), ib)
+    return int(np.abs(ia - ib).max()) if ia.size else 0
+
+
 def run_case(qfmt, vfmt, pmode, pfmt, B, Hq, Hkv, N, causal=False, kind="kmean", seed=0, doc_off=None,
-             rows=None, check_bytes=True, inputs=None):
-    """Run one forward on the GPU and on the oracle; returns a dict of results."""
+             rows=None, check_bytes=True, inputs=None, pre=None):
+    """Run one forward on the GPU and on the oracle; returns a dict of results.
+
+    pre: None, or a dict of outlier pre-processing for Q and K: {"center": both means
+    subtracted and the compensation passed as score bias, "smoothk": K's mean only,
+    "hadamard": normalized rotation} (keys absent = off)."""
     import torch
     import microscaling_fp4_attention_amd as mx
 
@@ -101,10 +139,19 @@ def run_case(qfmt, vfmt, pmode, pfmt, B, Hq, Hkv, N, causal=False, kind="kmean",
 
     qg, kg, vg = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
     cu = None if doc_off is None else torch.from_numpy(np.asarray(doc_off, np.int32)).to(dev)
-    Qq = mx.quantize(qg, mx.ROLE_QK, qfmt)
-    Kq = mx.quantize(kg, mx.ROLE_QK, qfmt)
+    pre = pre or {}
+    center, smoothk, had = bool(pre.get("center")), bool(pre.get("smoothk")), bool(pre.get("hadamard"))
+    qmean_g = mx.channel_mean(qg, cu) if center else None
+    kmean_g = mx.channel_mean(kg, cu) if (center or smoothk) else None
+    if center or smoothk or had:
+        Qq = mx.quantize(qg, mx.ROLE_QK, qfmt, cu_seqlens=cu, mean=qmean_g, hadamard=had)
+        Kq = mx.quantize(kg, mx.ROLE_QK, qfmt, cu_seqlens=cu, mean=kmean_g, hadamard=had)
+    else:
+        Qq = mx.quantize(qg, mx.ROLE_QK, qfmt)
+        Kq = mx.quantize(kg, mx.ROLE_QK, qfmt)
     Vq = mx.quantize(vg, mx.ROLE_V, vfmt, cu_seqlens=cu)
-    params = mx.fwd_params(pmode, pfmt, causal=causal)
+    delta_g = mx.center_comp(qmean_g, kg, kmean_g, cu) if center else None
+    params = mx.fwd_params(pmode, pfmt, causal=causal, score_bias=delta_g)
     ws, nd = None, 0
     if doc_off is not None:
         ws = mx.fwd_plan(doc_off, N, causal)
@@ -116,9 +163,24 @@ def run_case(qfmt, vfmt, pmode, pfmt, B, Hq, Hkv, N, causal=False, kind="kmean",
     lse_gpu = lse.cpu().numpy().reshape(-1)
 
     res = {}
+    # oracle pre-processing (means bit-exact, compensation within one float ulp)
+    bias = None
+    if center or smoothk or had:
+        qmeans, qf_in = oracle_preproc(qf, doc_off, center, had)
+        kmeans, kf_in = oracle_preproc(kf, doc_off, center or smoothk, had)
+        if center:
+            assert np.array_equal(qmean_g.cpu().numpy(), qmeans), "Q means differ"
+        if center or smoothk:
+            assert np.array_equal(kmean_g.cpu().numpy(), kmeans), "K means differ"
+        if center:
+            bias = oracle_comp(qmeans, kf, kmeans, Hq, doc_off)
+            res["delta_ulp"] = ulp_diff(delta_g.cpu().numpy(), bias)
+            assert res["delta_ulp"] <= 1, f"compensation differs by {res['delta_ulp']} ulp"
+    else:
+        qf_in, kf_in = qf, kf
     # oracle quantization (bytes must match the GPU's)
-    qc, qs, qd = oracle_quant_qk(qf, qfmt)
-    kc, ks, kd = oracle_quant_qk(kf, qfmt)
+    qc, qs, qd = oracle_quant_qk(qf_in, qfmt)
+    kc, ks, kd = oracle_quant_qk(kf_in, qfmt)
     vc, vs, vd = oracle_quant_v(vf, vfmt, doc_off)
     if check_bytes:
         assert np.array_equal(gpu_codes_qk(Qq), qc), "Q codes differ"
@@ -129,7 +191,7 @@ def run_case(qfmt, vfmt, pmode, pfmt, B, Hq, Hkv, N, causal=False, kind="kmean",
         assert np.array_equal(gc, vc), "V codes differ"
         assert np.array_equal(gs, vs), "V scales differ"
     O_ref, lse_ref, fb = oracle.attention(qd, kd, vd, PM_ORACLE[pmode], pfmt, causal=causal, doc_off=doc_off,
-                                          rows=rows)
+                                          rows=rows, bias=bias)
     sel = np.arange(B * Hq * N) if rows is None else np.asarray(rows)
     Og = O_gpu[sel]
     err = np.abs(Og - O_ref)
