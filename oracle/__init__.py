@@ -85,6 +85,11 @@ def lib():
         L.orc_attention_bias.argtypes = [f32p, f32p, f32p, f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_int, ctypes.c_int, i32p, ctypes.c_int, P(AttnParams), i64p,
                                          ctypes.c_int64, f32p, f32p, f64p]
+        L.orc_attention_ex.restype = ctypes.c_int
+        L.orc_attention_ex.argtypes = [f32p, f32p, f32p, f32p, f32p, i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int, i32p, ctypes.c_int, P(AttnParams), i64p,
+                                       ctypes.c_int64, f32p, f32p, f64p]
+        L.orc_quantize_keys.argtypes = [f32p, ctypes.c_int, ctypes.c_int, P(Fmt), u8p, i32p]
         L.orc_channel_mean.argtypes = [f32p, ctypes.c_int, ctypes.c_int, i32p, ctypes.c_int, f32p]
         L.orc_preprocess_rows.argtypes = [f32p, ctypes.c_int, ctypes.c_int, f32p, i32p, ctypes.c_int,
                                           ctypes.c_int, f32p]
@@ -197,9 +202,10 @@ def dequant_cols(codes, scales, f, doc_off=None):
 
 
 def attention(Q, K, V, pmode, pfmt=None, causal=False, sm_scale=None, kv_tile=128, doc_off=None,
-              rows=None, bias=None):
+              rows=None, bias=None, vkey=None, vkey_exp=None):
     """Q [B,Hq,N,d], K/V [B,Hkv,N,d] float32 (dequantized); bias: None or float32 [B,Hq,N]
-    added to each key's scores.  Returns (O [nrows,d], lse, fb)."""
+    added to each key's scores; vkey [B,Hkv,N,d] / vkey_exp [B,Hkv,N]: the per-key form
+    of V used on each row's diagonal tile (causal only).  Returns (O [nrows,d], lse, fb)."""
     Q = np.ascontiguousarray(Q, dtype=np.float32)
     K = np.ascontiguousarray(K, dtype=np.float32)
     V = np.ascontiguousarray(V, dtype=np.float32)
@@ -218,11 +224,15 @@ def attention(Q, K, V, pmode, pfmt=None, causal=False, sm_scale=None, kv_tile=12
     bb = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
     if bb is not None and bb.shape != (B, Hq, N):
         raise ValueError("bias must be [B, Hq, N]")
-    rc = lib().orc_attention_bias(_ptr(Q, ctypes.c_float), _ptr(K, ctypes.c_float), _ptr(V, ctypes.c_float),
-                                  _ptr(bb, ctypes.c_float), B, Hq, Hkv, N, d, _ptr(dd, ctypes.c_int32),
-                                  0 if dd is None else len(dd) - 1, ctypes.byref(p), _ptr(r, ctypes.c_int64),
-                                  nrows, _ptr(O, ctypes.c_float), _ptr(lse, ctypes.c_float),
-                                  _ptr(fb, ctypes.c_double))
+    vk = None if vkey is None else np.ascontiguousarray(vkey, dtype=np.float32)
+    ek = None if vkey_exp is None else np.ascontiguousarray(vkey_exp, dtype=np.int32)
+    if (vk is None) != (ek is None):
+        raise ValueError("vkey and vkey_exp go together")
+    rc = lib().orc_attention_ex(_ptr(Q, ctypes.c_float), _ptr(K, ctypes.c_float), _ptr(V, ctypes.c_float),
+                                _ptr(bb, ctypes.c_float), _ptr(vk, ctypes.c_float), _ptr(ek, ctypes.c_int32), B, Hq,
+                                Hkv, N, d, _ptr(dd, ctypes.c_int32), 0 if dd is None else len(dd) - 1,
+                                ctypes.byref(p), _ptr(r, ctypes.c_int64), nrows, _ptr(O, ctypes.c_float),
+                                _ptr(lse, ctypes.c_float), _ptr(fb, ctypes.c_double))
     if rc != 0:
         raise ValueError(f"orc_attention failed with {rc}")
     return O, lse, fb
@@ -266,3 +276,23 @@ def center_comp(qmean, K, kmean, doc_off=None):
                           _ptr(K, ctypes.c_float), _ptr(np.ascontiguousarray(kmean, dtype=np.float32), ctypes.c_float),
                           N, d, _ptr(dd, ctypes.c_int32), nd, _ptr(delta, ctypes.c_float))
     return delta
+
+
+# ---- causally safe per-key form of a 4-bit V ----
+def quantize_keys(x, f):
+    """x float32 [N, d] -> (codes uint8 [N, d], exponents int32 [N]): one E8M0 scale per
+    token over its d channels (f's rule), element codes of x / 2^e."""
+    f = fmt(f)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    N, d = x.shape
+    codes = np.zeros((N, d), np.uint8)
+    ek = np.zeros(N, np.int32)
+    lib().orc_quantize_keys(_ptr(x, ctypes.c_float), N, d, ctypes.byref(f), _ptr(codes, ctypes.c_uint8),
+                            _ptr(ek, ctypes.c_int32))
+    return codes, ek
+
+
+def e2m1_values(codes):
+    """E2M1 codes -> their values (unit scale), float32"""
+    table = np.array([e2m1_value(c) for c in range(16)], np.float32)
+    return table[np.asarray(codes) & 15]

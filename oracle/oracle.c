@@ -308,18 +308,26 @@ static void p_block(const float* x, int n, const orc_fmt* f, double* deq, double
 /* Tiles of kv_tile keys are aligned to key 0 of the range and walked in   */
 /* ascending order; P blocks are consecutive keys aligned to the tile.     */
 /* ------------------------------------------------------------------------ */
-static int attn_row_bias(const float* q, const float* K, const float* V, const float* sbias, int nk,
-                         int vis, int d, const orc_attn_params* p, float* o, float* lse, double* fb);
+static int attn_row_bias(const float* q, const float* K, const float* V, const float* sbias,
+                         const float* Vk, const int* ek, int diag_t0, int nk, int vis, int d,
+                         const orc_attn_params* p, float* o, float* lse, double* fb);
 
 int orc_attn_row(const float* q, const float* K, const float* V, int nk, int vis, int d,
                  const orc_attn_params* p, float* o, float* lse, double* fb) {
-  return attn_row_bias(q, K, V, NULL, nk, vis, d, p, o, lse, fb);
+  return attn_row_bias(q, K, V, NULL, NULL, NULL, -1, nk, vis, d, p, o, lse, fb);
 }
 
 /* sbias: NULL, or the score bias of keys 0..nk-1 of this range ([MPFA] Eq. 10: added
- * to the exact dot product before the mask and the running maximum) */
-static int attn_row_bias(const float* q, const float* K, const float* V, const float* sbias, int nk,
-                         int vis, int d, const orc_attn_params* p, float* o, float* lse, double* fb) {
+ * to the exact dot product before the mask and the running maximum).
+ * Vk, ek, diag_t0: causally safe V scales ([FLAMIA] section 3.2): on the tile that
+ * starts at key diag_t0 the row uses the per-key form of V -- E2M1 values Vk[j][c]
+ * with unit scale and a power-of-two scale 2^ek[j] per key -- and folds that scale
+ * into P, P'_j = P~_j * 2^ek[j] (exact float ldexp), which is then quantized as P
+ * normally is; O takes P^' Vk, and the PNQ row sum takes deq(P^'_j) 2^-ek[j].
+ * Vk == NULL: no tile uses the per-key form. */
+static int attn_row_bias(const float* q, const float* K, const float* V, const float* sbias,
+                         const float* Vk, const int* ek, int diag_t0, int nk, int vis, int d,
+                         const orc_attn_params* p, float* o, float* lse, double* fb) {
   int T = p->kv_tile;
   float m = -INFINITY, l = 0.0f;
   float* acc = (float*)calloc((size_t)d, sizeof(float));
@@ -352,22 +360,29 @@ static int attn_row_bias(const float* q, const float* K, const float* V, const f
     alpha = (m == -INFINITY) ? 0.0f : (float)exp((double)p->sm_scale * ((double)m - (double)mnew));
     for (int j = 0; j < tl; j++)
       pt[j] = (s[j] == -INFINITY) ? 0.0f : (float)exp((double)p->sm_scale * ((double)s[j] - (double)mnew));
+    /* per-key fold of the diagonal tile: the quantizer sees P' = P~ 2^ek */
+    const int fold = Vk != NULL && t0 == diag_t0;
+    float* pq = pt;
+    if (fold) {
+      for (int j = 0; j < tl; j++) x2[j] = ldexpf(pt[j], ek[t0 + j]);
+      pq = x2;
+    }
 
     /* P quantization of this tile */
     for (int j = 0; j < tl; j++) {
-      ph[j] = pt[j];
+      ph[j] = pq[j];
       dl[j] = 0.0;
     }
     if (p->pmode == ORC_P_TWO_LEVEL) {
       float r = 0.0f, s1;
       for (int j = 0; j < tl; j++)
-        if (pt[j] > r) r = pt[j];
+        if (pq[j] > r) r = pq[j];
       if (r == 0.0f) { /* nothing visible in this tile */
         m = mnew;
         continue;
       }
       s1 = r / (448.0f * 6.0f);
-      for (int j = 0; j < tl; j++) x2[j] = pt[j] / s1;
+      for (int j = 0; j < tl; j++) x2[j] = pq[j] / s1; /* in place when folded */
       for (int b0 = 0; b0 < tl; b0 += p->pfmt.block) {
         int n = tl - b0 < p->pfmt.block ? tl - b0 : p->pfmt.block;
         p_block(x2 + b0, n, &p->pfmt, ph + b0, dl + b0);
@@ -376,7 +391,7 @@ static int attn_row_bias(const float* q, const float* K, const float* V, const f
     } else if (p->pmode == ORC_P_DIRECT || p->pmode == ORC_P_PNQ) {
       for (int b0 = 0; b0 < tl; b0 += p->pfmt.block) {
         int n = tl - b0 < p->pfmt.block ? tl - b0 : p->pfmt.block;
-        p_block(pt + b0, n, &p->pfmt, ph + b0, dl + b0);
+        p_block(pq + b0, n, &p->pfmt, ph + b0, dl + b0);
       }
     } else if (p->pmode == ORC_P_FP8_FIXED) {
       for (int j = 0; j < tl; j++) {
@@ -389,14 +404,16 @@ static int attn_row_bias(const float* q, const float* K, const float* V, const f
     }
 
     /* l = alpha l + rowsum(w): w = P^ for PNQ, P~ otherwise */
-    for (int j = 0; j < tl; j++) wsum += (p->pmode == ORC_P_PNQ) ? ph[j] : (double)pt[j];
+    for (int j = 0; j < tl; j++)
+      wsum += (p->pmode == ORC_P_PNQ) ? (fold ? ldexp(ph[j], -ek[t0 + j]) : ph[j]) : (double)pt[j];
     l = alpha * l + (float)wsum;
 
-    /* O~ = alpha O~ + P^ V (times s1 or 1/448) */
+    /* O~ = alpha O~ + P^ V (times s1 or 1/448); the folded tile takes the per-key V */
+    const float* Vt = fold ? Vk : V;
     for (int c = 0; c < d; c++) col[c] = 0.0;
     for (int j = 0; j < tl; j++) {
       if (ph[j] == 0.0) continue;
-      for (int c = 0; c < d; c++) col[c] += ph[j] * (double)V[(int64_t)(t0 + j) * d + c];
+      for (int c = 0; c < d; c++) col[c] += ph[j] * (double)Vt[(int64_t)(t0 + j) * d + c];
     }
     for (int c = 0; c < d; c++) {
       float t = (float)col[c];
@@ -410,11 +427,11 @@ static int attn_row_bias(const float* q, const float* K, const float* V, const f
       if (dl[j] == 0.0) continue;
       double vmax = 0.0;
       for (int c = 0; c < d; c++) {
-        double a = fabs((double)V[(int64_t)(t0 + j) * d + c]);
+        double a = fabs((double)Vt[(int64_t)(t0 + j) * d + c]);
         if (a > vmax) vmax = a;
       }
       dsum1 += dl[j] * (double)mult * vmax;
-      dsum2 += dl[j] * (double)mult;
+      dsum2 += dl[j] * (double)mult * (fold ? ldexp(1.0, -ek[t0 + j]) : 1.0);
     }
     fb1 = (double)alpha * fb1 + dsum1;
     fb2 = (double)alpha * fb2 + dsum2;
@@ -454,7 +471,16 @@ int orc_attention_bias(const float* Q, const float* K, const float* V, const flo
                        int Hq, int Hkv, int N, int d, const int* doc_off, int ndocs,
                        const orc_attn_params* p, const int64_t* rows, int64_t nrows, float* O,
                        float* lse, double* fb) {
+  return orc_attention_ex(Q, K, V, bias, NULL, NULL, B, Hq, Hkv, N, d, doc_off, ndocs, p, rows, nrows, O,
+                          lse, fb);
+}
+
+int orc_attention_ex(const float* Q, const float* K, const float* V, const float* bias, const float* Vk,
+                     const int* ek, int B, int Hq, int Hkv, int N, int d, const int* doc_off, int ndocs,
+                     const orc_attn_params* p, const int64_t* rows, int64_t nrows, float* O, float* lse,
+                     double* fb) {
   int64_t total = (int64_t)B * Hq * N;
+  if (Vk && !p->causal) return -3; /* the per-key form serves causal diagonal tiles */
   if (!rows) nrows = total;
   if (doc_off && ndocs > 0 && B != 1) return -1;
   for (int64_t idx = 0; idx < nrows; idx++) {
@@ -476,9 +502,13 @@ int orc_attention_bias(const float* Q, const float* K, const float* V, const flo
     }
     nk = ke - ks;
     vis = p->causal ? (i - ks + 1) : nk;
+    const float* vkb = Vk ? Vk + ((b * Hkv + hk) * (int64_t)N + ks) * d : NULL;
+    const int* ekb = ek ? ek + (b * Hkv + hk) * (int64_t)N + ks : NULL;
+    /* the row's diagonal tile: the kv_tile keys from kv_tile * floor((i - ks) / kv_tile) */
+    int diag = Vk ? ((i - ks) / p->kv_tile) * p->kv_tile : -1;
     attn_row_bias(Q + r * d, kb + (int64_t)ks * d, vb + (int64_t)ks * d,
-                  bias ? bias + (b * Hq + h) * (int64_t)N + ks : NULL, nk, vis, d, p, O + idx * d,
-                  lse ? lse + idx : NULL, fb ? fb + idx : NULL);
+                  bias ? bias + (b * Hq + h) * (int64_t)N + ks : NULL, vkb, ekb, diag, nk, vis, d, p,
+                  O + idx * d, lse ? lse + idx : NULL, fb ? fb + idx : NULL);
   }
   return 0;
 }
@@ -540,5 +570,20 @@ void orc_center_comp(const float* qmean, const float* K, const float* kmean, int
       acc += (double)qmean[(int64_t)k * d + c] *
              ((double)K[(int64_t)j * d + c] - (double)kmean[(int64_t)k * d + c]);
     delta[j] = (float)acc;
+  }
+}
+
+/* Per-key form of V ([FLAMIA] section 3.2: a per-key power-of-two scale for a 4-bit
+ * V on diagonal tiles): for each token j the block is its d channels, the E8M0
+ * exponent ek[j] follows f's rule from the block maximum, and the codes are the
+ * element codes of V[j][c] / 2^ek[j].  x: [N][d]; codes: [N][d]; ek: [N].
+ * E8M0 formats only.  Pinned by tests/test_oracle_causal_safe.py. */
+void orc_quantize_keys(const float* x, int N, int d, const orc_fmt* f, uint8_t* codes, int* ek) {
+  orc_fmt fk = *f;
+  fk.block = d;
+  for (int j = 0; j < N; j++) {
+    uint8_t sb;
+    orc_quant_block(x + (int64_t)j * d, d, &fk, codes + (int64_t)j * d, &sb);
+    ek[j] = (int)sb - 127;
   }
 }

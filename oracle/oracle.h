@@ -120,6 +120,22 @@ int orc_attention_bias(const float* Q, const float* K, const float* V, const flo
                        const orc_attn_params* p, const int64_t* rows, int64_t nrows, float* O,
                        float* lse, double* fb);
 
+/* As orc_attention_bias, plus the causally safe form of a 4-bit V ([FLAMIA] section
+ * 3.2): Vk [B][Hkv][N][d] holds the E2M1 values of V's per-key form (unit scale)
+ * and ek [B][Hkv][N] its per-key exponents (orc_quantize_keys).  On each row's
+ * diagonal tile -- the kv_tile keys from kv_tile * floor((i - start) / kv_tile) of
+ * its sequence or document -- P~_j is multiplied by 2^ek[j] before it is quantized
+ * and multiplies Vk; every other tile uses V.  Requires a causal mask (returns -3
+ * otherwise); Vk/ek NULL: as orc_attention_bias. */
+int orc_attention_ex(const float* Q, const float* K, const float* V, const float* bias, const float* Vk,
+                     const int* ek, int B, int Hq, int Hkv, int N, int d, const int* doc_off, int ndocs,
+                     const orc_attn_params* p, const int64_t* rows, int64_t nrows, float* O, float* lse,
+                     double* fb);
+
+/* Per-key form of V: per token j, one E8M0 scale 2^ek[j] for its d channels by f's
+ * rule and the element codes of V[j][c] / 2^ek[j].  x, codes: [N][d]; ek: [N]. */
+void orc_quantize_keys(const float* x, int N, int d, const orc_fmt* f, uint8_t* codes, int* ek);
+
 /* ---- outlier pre-processing of Q and K (before quantization) ---- */
 
 /* Per-channel mean over the tokens of each document of one head ([MPFA] section
