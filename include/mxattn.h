@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MXATTN_ABI_VERSION 2
+#define MXATTN_ABI_VERSION 3
 
 typedef enum {
   MXATTN_OK = 0,
@@ -74,8 +74,13 @@ typedef enum {
 /* which axis the blocks run along */
 typedef enum {
   MXATTN_ROLE_QK = 0, /* blocks along the head dimension d, one row per token     */
-  MXATTN_ROLE_V = 1   /* blocks along the tokens (the PV contraction axis), stored
+  MXATTN_ROLE_V = 1,  /* blocks along the tokens (the PV contraction axis), stored
                          transposed: one row per channel                           */
+  MXATTN_ROLE_VKEY = 2 /* the per-key form of a 4-bit V for causally safe diagonal
+                          tiles ("FLAMIA" section 3.2): one E8M0 scale per key over
+                          its d channels (fmt's rule), E2M1 codes stored transposed
+                          in role V's slot layout (fmt->block fixes that layout);
+                          scales are [B][H][n_padded], one byte per key slot      */
 } mxattn_role;
 
 /* how the softmax operand P is quantized inside the attention loop */
@@ -131,6 +136,15 @@ typedef struct {
                               before the mask and the running maximum (the centering
                               compensation of mxattn_center_comp()), or NULL; 16-byte
                               aligned                                                  */
+  const mxattn_qtensor* vkey; /* causally safe V scales ("FLAMIA" section 3.2), or NULL: a
+                        mxattn_qtensor of role VKEY quantized from the same V with the
+                        same documents.  On the key tile that holds a row's own
+                        position (the 128 keys from 128 floor(i / 128) of its sequence
+                        or document) the row uses this per-key form and multiplies
+                        P~_j by the key's scale 2^e_j before quantizing P; every other
+                        tile uses v.  Needs a causal mask and a V in E2M1 with E8M0
+                        scales per 32 keys (an FP8 V with round-up exponents needs no
+                        per-key form).                                                 */
 } mxattn_fwd_params;
 
 /* ABI version (MXATTN_ABI_VERSION of the built library). */

@@ -22,11 +22,11 @@ OK, E_INVALID, E_UNSUPPORTED, E_ALIGN, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4, -
 ELEM_E2M1, ELEM_E4M3 = 0, 1
 SCALE_E8M0, SCALE_E4M3 = 0, 1
 RULE_OCP, RULE_CEIL = 0, 1
-ROLE_QK, ROLE_V = 0, 1
+ROLE_QK, ROLE_V, ROLE_VKEY = 0, 1, 2
 P_DIRECT, P_TWO_LEVEL, P_PNQ, P_FP8_FIXED = 1, 2, 3, 4
 
 
-ABI_VERSION = 2  # MXATTN_ABI_VERSION of include/mxattn.h
+ABI_VERSION = 3  # MXATTN_ABI_VERSION of include/mxattn.h
 
 
 class QFmt(ctypes.Structure):
@@ -42,7 +42,8 @@ class QTensorC(ctypes.Structure):
 
 class FwdParams(ctypes.Structure):
     _fields_ = [("pmode", ctypes.c_int32), ("pfmt", QFmt), ("causal", ctypes.c_int32), ("sm_scale", ctypes.c_float),
-                ("kv_tile", ctypes.c_int32), ("out_fp32", ctypes.c_int32), ("score_bias", ctypes.c_void_p)]
+                ("kv_tile", ctypes.c_int32), ("out_fp32", ctypes.c_int32), ("score_bias", ctypes.c_void_p),
+                ("vkey", ctypes.c_void_p)]
 
 
 class PreProc(ctypes.Structure):
@@ -153,9 +154,12 @@ class QTensor:
         return self.codes.view(d.B, d.H, d.d, d.n_padded * bits // 8)
 
     def scales_view(self) -> torch.Tensor:
+        """role QK: [B, H, N, d/block]; role V: [B, H, d, n_padded/block]; role VKEY: [B, H, n_padded]."""
         d = self.desc
         if d.role == ROLE_QK:
             return self.scales.view(d.B, d.H, d.N, d.d // d.fmt.block)
+        if d.role == ROLE_VKEY:
+            return self.scales.view(d.B, d.H, d.n_padded)
         return self.scales.view(d.B, d.H, d.d, d.n_padded // d.fmt.block)
 
 
@@ -270,9 +274,11 @@ def fwd_plan(cu_seqlens_host, N: int, causal: bool, device="cuda", stream=None) 
 
 
 def fwd_params(pmode, pfmt="mxfp4", causal=False, sm_scale=None, d=128, out_fp32=True, kv_tile=128,
-               score_bias: torch.Tensor | None = None) -> FwdParams:
+               score_bias: torch.Tensor | None = None, vkey: "QTensor | None" = None) -> FwdParams:
     """score_bias: float32 device tensor [B, Hq, N] added to each key's scores (the
-    centering compensation from center_comp), or None.  The params keep a reference."""
+    centering compensation from center_comp), or None.  vkey: the role-VKEY quantization
+    of the same V (causally safe V scales on the diagonal tiles), or None.  The params
+    keep references to both."""
     pm = PMODES[pmode] if isinstance(pmode, str) else int(pmode)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
@@ -280,8 +286,10 @@ def fwd_params(pmode, pfmt="mxfp4", causal=False, sm_scale=None, d=128, out_fp32
     if score_bias is not None and (score_bias.dtype != torch.float32 or not score_bias.is_contiguous()):
         raise ValueError("score_bias must be a contiguous float32 tensor [B, Hq, N]")
     p = FwdParams(pm, pf, int(bool(causal)), float(sm_scale), kv_tile, int(bool(out_fp32)),
-                  None if score_bias is None else score_bias.data_ptr())
+                  None if score_bias is None else score_bias.data_ptr(),
+                  None if vkey is None else ctypes.addressof(vkey.desc))
     p._score_bias_ref = score_bias
+    p._vkey_ref = vkey
     return p
 
 

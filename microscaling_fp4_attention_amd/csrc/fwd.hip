@@ -760,19 +760,26 @@ __global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(Fw
 // rows) during its VALU phases, two phases after loading it.
 // Routes: QK_FP4 / QK_BF16 x PV_FP4 / PV_FP8 / PV_BF16 (V with E8M0 per 32 keys).
 // ===========================================================================
-template <int QK, int PV, bool BIAS>
+template <int QK, int PV, bool BIAS, bool SAFE>
 struct PpLds {
   static constexpr int KROW = QK == QK_FP4 ? 80 : 256;
   static constexpr int VROW = PV == PV_FP4 ? 80 : PV == PV_FP8 ? 144 : 256;
   static constexpr int KV = 128 * KROW;             // V^T rows follow the 128 key rows of a stage
   static constexpr int BOFF = 128 * (KROW + VROW);  // then the score bias of the 128 keys
   static constexpr int STAGE = BOFF + (BIAS ? 512 : 0);
-  static constexpr int BYTES = 3 * STAGE;
+  // after the 3 stages, with causally safe V scales: the per-key form of the two
+  // diagonal tiles of the workgroup (128 channel rows of 80 bytes, E2M1 codes, then
+  // the 128 per-key E8M0 bytes in key order)
+  static constexpr int KEYR = 3 * STAGE;
+  static constexpr int KEYX = 128 * 80;
+  static constexpr int KEYT = KEYX + 128;
+  static constexpr int BYTES = KEYR + (SAFE ? 2 * KEYT : 0);
 };
 
-template <int QK, int PV, int PMODE, int PSC, bool BIAS>
+template <int QK, int PV, int PMODE, int PSC, bool BIAS, bool SAFE>
 __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
-  using L = PpLds<QK, PV, BIAS>;
+  static_assert(!SAFE || PV == PV_FP4 || PV == PV_BF16, "the per-key form serves a 4-bit V");
+  using L = PpLds<QK, PV, BIAS, SAFE>;
   // static LDS: its base is the constant 0, so stage offsets fold into the instructions
   __shared__ __attribute__((aligned(16))) uint8_t smem[L::BYTES];
   constexpr int STAGE = L::STAGE, KV = L::KV;
@@ -957,6 +964,9 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
 
   // ---------------- state ----------------
   float m = NEG_INF, lpart = 0.0f, s1prev = 1.0f;
+  float lfix = 0.0f;  // PNQ with causally safe V: this lane's share of the folded tile's row sum
+  // causally safe V: the key tile holding this group's rows (256-row query tile qt)
+  const int tdiag = SAFE ? 2 * (int)qt + grp : -1;
   v16f O[4], Lacc, S[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) O[i] = zero16();
@@ -972,23 +982,29 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
 
   // M(t): PV of tile t-1 (stage offset sv), then S^T of tile t (stage offset sk) with
   // its mask and maxima
-  auto phase_m = [&](int t, uint32_t sk, uint32_t sv) __attribute__((always_inline)) {
+  auto phase_m = [&](int t, uint32_t sk, uint32_t sv, bool can_fold) __attribute__((always_inline)) {
     if (t >= 1) {
+      // the folded tile takes the per-key form of V (unit block scales)
+      const bool fold = SAFE && can_fold && t - 1 == tdiag;
       const uint8_t* Vs = smem + sv + KV;
       if constexpr (PV == PV_FP4) {
+        const uint8_t* Vr = fold ? smem + L::KEYR + grp * L::KEYT : Vs;
 #pragma unroll
         for (int db = 0; db < 4; db++) {
-          const uint8_t* rp = Vs + (32 * db + ql) * 80;
-          const uint32_t vs4 = *reinterpret_cast<const uint32_t*>(rp + 64 + 4 * hh);
+          const uint8_t* rp = Vr + (32 * db + ql) * 80;
+          uint32_t vs4 = *reinterpret_cast<const uint32_t*>(rp + 64 + 4 * hh);
+          if constexpr (SAFE) vs4 = fold ? 0x7F7F7F7Fu : vs4;
           v8i a0 = v8_from4(*reinterpret_cast<const u4*>(rp + 16 * hh));
           v8i a1 = v8_from4(*reinterpret_cast<const u4*>(rp + 32 + 16 * hh));
           O[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, bp[0], O[db], 4, 4, 0, (int)vs4, 0, (int)pscw);
           O[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, bp[1], O[db], 4, 4, 2, (int)vs4, 1, (int)pscw);
         }
         if constexpr (PMODE == PM_PNQ) {
-          const v8i ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};
-          Lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, bp[0], Lacc, 4, 4, 0, 127, 0, (int)pscw);
-          Lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, bp[1], Lacc, 4, 4, 0, 127, 1, (int)pscw);
+          if (!fold) {  // the folded tile's row sum is formed in its V phase
+            const v8i ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};
+            Lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, bp[0], Lacc, 4, 4, 0, 127, 0, (int)pscw);
+            Lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, bp[1], Lacc, 4, 4, 0, 127, 1, (int)pscw);
+          }
         }
       } else if constexpr (PV == PV_FP8) {
 #pragma unroll
@@ -1014,14 +1030,28 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
           const int bb = 2 * (s >> 2) + ((s & 3) >> 1);
           pb[s] = __builtin_bit_cast(v8bf, dq8_bf16(pc[2 * bb + ((s & 3) & 1)], pdq[bb]));
         }
+        if (SAFE && fold) {  // per-key E2M1 codes, dequantized (unit scale) on the fly
+          const uint8_t* Kr = smem + L::KEYR + grp * L::KEYT;
 #pragma unroll
-        for (int db = 0; db < 4; db++) {
-          const uint8_t* rp = Vs + (32 * db + ql) * 256;
+          for (int db = 0; db < 4; db++) {
+            const uint8_t* rp = Kr + (32 * db + ql) * 80;
 #pragma unroll
-          for (int s = 0; s < 8; s++) {
-            const int chunk = (8 * (s >> 2) + 4 * hh + (s & 3)) ^ (ql & 15);
-            v8bf av = *reinterpret_cast<const v8bf*>(rp + chunk * 16);
-            O[db] = mfma_bf16(av, pb[s], O[db]);
+            for (int s = 0; s < 8; s++) {
+              const int lc = 8 * (s >> 2) + 4 * hh + (s & 3);  // keys 8 lc + [0, 8)
+              v8bf av = __builtin_bit_cast(v8bf, dq8_bf16(*reinterpret_cast<const uint32_t*>(rp + 4 * lc), 1.0f));
+              O[db] = mfma_bf16(av, pb[s], O[db]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int db = 0; db < 4; db++) {
+            const uint8_t* rp = Vs + (32 * db + ql) * 256;
+#pragma unroll
+            for (int s = 0; s < 8; s++) {
+              const int chunk = (8 * (s >> 2) + 4 * hh + (s & 3)) ^ (ql & 15);
+              v8bf av = *reinterpret_cast<const v8bf*>(rp + chunk * 16);
+              O[db] = mfma_bf16(av, pb[s], O[db]);
+            }
           }
         }
       }
@@ -1107,6 +1137,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
 #pragma unroll
         for (int j = 0; j < 16; j++) O[i][j] *= scale_o;
       Lacc[0] *= alpha;
+      if constexpr (SAFE) lfix *= alpha;
     }
 
     // block scales of P from the block maxima of P~ (exponentials of the score maxima)
@@ -1183,6 +1214,117 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     }
   };
 
+  // V phase of the group's diagonal tile with causally safe V scales ("FLAMIA" section
+  // 3.2): P'_j = P~_j 2^e_j with the key's per-key exponent (exact ldexp), quantized as
+  // P is; block maxima and the two-level row maximum come from the P' values.  The row
+  // sum takes P~ (DIRECT, TWO_LEVEL) or deq(P^'_j) 2^-e_j (PNQ).
+  auto phase_v_fold = [&](int t) __attribute__((always_inline)) {
+    const float mnew = fmaxn(m, tmax);
+    const float ms = mnew == NEG_INF ? 0.0f : mnew * lam;
+    const float alpha = m == mnew ? 1.0f : exp2_hw(__builtin_fmaf(m, lam, -ms));
+    m = mnew;
+    const uint8_t* kx = smem + L::KEYR + grp * L::KEYT + L::KEYX;  // per-key bytes, key order
+    // exponent of the lane's key j of sub-tile bb (re-read where needed, not held)
+    auto kexp = [&](int bb, int j) __attribute__((always_inline)) -> int {
+      return (int)kx[key_of<false>(bb, hh, 0) + j] - 127;
+    };
+    float lsum = 0.0f, pm16[4];
+#pragma unroll
+    for (int bb = 0; bb < 4; bb++) {
+      const u4 eb = *reinterpret_cast<const u4*>(kx + key_of<false>(bb, hh, 0));
+      const uint32_t ew[4] = {eb.x, eb.y, eb.z, eb.w};
+      float mx = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 16; j++) {
+        const float pt = exp2_hw(__builtin_fmaf(S[bb][j], lam, -ms));
+        if constexpr (PMODE != PM_PNQ) lsum += pt;
+        const float pp = __builtin_ldexpf(pt, (int)((ew[j >> 2] >> (8 * (j & 3))) & 0xFFu) - 127);
+        S[bb][j] = pp;
+        mx = fmaxn(mx, pp);
+      }
+      pm16[bb] = mx;
+    }
+    float k1 = 1.0f, scale_o = alpha;
+    if constexpr (PMODE == PM_TWO_LEVEL) {
+      // s1 from the largest P' of the row; a tile whose P' stays below 2^-100 adds
+      // nothing and keeps s1 (keeps 1/s1 and the carried O/s1 finite)
+      const float r = halves_max(fmaxn(fmaxn(pm16[0], pm16[1]), fmaxn(pm16[2], pm16[3])));
+      if (r >= 0x1p-100f) {
+        const float s1 = r / 2688.0f;
+        k1 = 1.0f / s1;
+        scale_o = alpha * (s1prev / s1);
+        s1prev = s1;
+      } else {
+        k1 = 0.0f;
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(scale_o != 1.0f) != 0) {
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 16; j++) O[i][j] *= scale_o;
+      Lacc[0] *= alpha;
+      lfix *= alpha;
+    }
+    float lq = 0.0f;  // PNQ: deq(P^') 2^-e of this lane's keys
+    if constexpr (PV == PV_FP4) {
+      int e[2];
+#pragma unroll
+      for (int p = 0; p < 2; p++) {
+        const int x = e8m0_exp(fmaxn(pm16[2 * p], pm16[2 * p + 1]) * k1, a.prule);
+        e[p] = x < -126 ? -126 : x;
+      }
+      pscw = (uint32_t)(e[0] + 127) | ((uint32_t)(e[1] + 127) << 8);
+      uint32_t w[8];
+#pragma unroll
+      for (int bb = 0; bb < 4; bb++) {
+        const float sc = u2f((uint32_t)(e[bb >> 1] + 127) << 23);
+        float y[16];
+#pragma unroll
+        for (int j = 0; j < 16; j++) y[j] = PMODE == PM_TWO_LEVEL ? S[bb][j] * k1 : S[bb][j];
+        w[2 * bb] = pack8_fp4(y, sc);
+        w[2 * bb + 1] = pack8_fp4(y + 8, sc);
+        if constexpr (PMODE == PM_PNQ) {
+#pragma unroll
+          for (int u = 0; u < 2; u++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+              const v2f pr = fp4_pair(w[2 * bb + u], q);
+              lq += __builtin_ldexpf(pr[0] * sc, -kexp(bb, 8 * u + 2 * q)) +
+                    __builtin_ldexpf(pr[1] * sc, -kexp(bb, 8 * u + 2 * q + 1));
+            }
+        }
+      }
+      bp[0] = v8_from4(mk4(w[0], w[1], w[2], w[3]));
+      bp[1] = v8_from4(mk4(w[4], w[5], w[6], w[7]));
+    } else {  // PV_BF16: E4M3 scale per 16 keys
+#pragma unroll
+      for (int bb = 0; bb < 4; bb++) {
+        const float sv = e4m3_value(e4m3_mag(pm16[bb] * k1 / 6.0f));
+        const float ki = sv > 0.0f ? 1.0f / sv : 0.0f;
+        float z[16];
+#pragma unroll
+        for (int j = 0; j < 16; j++) z[j] = (PMODE == PM_TWO_LEVEL ? S[bb][j] * k1 : S[bb][j]) * ki;
+        pc[2 * bb] = pack8_fp4(z, 1.0f);
+        pc[2 * bb + 1] = pack8_fp4(z + 8, 1.0f);
+        pdq[bb] = sv;
+        if constexpr (PMODE == PM_PNQ) {
+#pragma unroll
+          for (int u = 0; u < 2; u++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+              const v2f pr = fp4_pair(pc[2 * bb + u], q);
+              lq += __builtin_ldexpf(pr[0] * sv, -kexp(bb, 8 * u + 2 * q)) +
+                    __builtin_ldexpf(pr[1] * sv, -kexp(bb, 8 * u + 2 * q + 1));
+            }
+        }
+      }
+    }
+    if constexpr (PMODE == PM_PNQ && PV == PV_FP4) lfix += lq;
+    else if constexpr (PMODE == PM_PNQ) lpart = alpha * lpart + lq;
+    else lpart = alpha * lpart + lsum;
+  };
+
   // ---------------- phases ----------------
   // Every wave runs M(0) V(0) M(1) V(1) ... M(nkt) with a workgroup barrier after each
   // phase.  Group B passes one extra barrier before M(0) and group A one after the
@@ -1192,6 +1334,25 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   // buffer that is no longer read.
   // Stage offsets rotate through 0, STAGE, 2 STAGE as scalars: sk holds tile t, sv
   // tile t-1, ss the tile this group stores next (t+1+grp).
+  if constexpr (SAFE) {
+    // the per-key form of key tiles 2 qt and 2 qt + 1 (the groups' diagonal tiles):
+    // 512 threads copy the 128 x 64 code bytes of a tile, 32 of them its 128 exponents
+    const uint8_t* hvk = a.vk + vrow0 * (int64_t)(np / 2);
+    const uint8_t* hvks = a.vks + (b * a.Hkv + hk) * (int64_t)np;
+    const int row = tid >> 2, part = tid & 3;
+#pragma unroll
+    for (int g = 0; g < 2; g++) {
+      const uint32_t ks0 = (uint32_t)vstart + 128u * (uint32_t)(2 * qt + g);
+      const uint32_t k1 = __builtin_elementwise_min(ks0 + 32u * part, np - 32);
+      const u4 c = *reinterpret_cast<const u4*>(hvk + ((uint32_t)row * (np / 2) + k1 / 2));
+      *reinterpret_cast<u4*>(smem + L::KEYR + g * L::KEYT + row * 80 + part * 16) = c;
+      if (tid < 32) {
+        const uint32_t s0 = __builtin_elementwise_min(ks0 + 4u * tid, np - 4);
+        *reinterpret_cast<uint32_t*>(smem + L::KEYR + g * L::KEYT + L::KEYX + 4 * tid) =
+            *reinterpret_cast<const uint32_t*>(hvks + s0);
+      }
+    }
+  }
   load_half(0);
   store_half(0);
   if (grp == 1) {
@@ -1203,12 +1364,15 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   if (grp == 1) __syncthreads();
   auto rot = [](uint32_t o) { return o == 2 * STAGE ? 0u : o + STAGE; };
   uint32_t sk = 0, sv = 2 * STAGE, ss = grp == 0 ? STAGE : 2 * STAGE;
-  for (int t = 0; t <= nkt; t++) {
-    phase_m(t, sk, sv);
+  // one M phase and one V phase; can_fold (a constant at each call) compiles the
+  // per-key fold in, which only the group's diagonal tile 2 qt + grp needs
+  auto step = [&](int t, bool can_fold) __attribute__((always_inline)) {
+    phase_m(t, sk, sv, can_fold);
     __builtin_amdgcn_sched_barrier(0);  // keep the phase's MFMAs on this side of the barrier
     __syncthreads();
     if (t < nkt) {
-      phase_v(t);
+      if (SAFE && can_fold && t == tdiag) phase_v_fold(t);
+      else phase_v(t);
       store_half(ss);
       const int nt = t + 2 + grp;
       load_half(nt < nkt ? nt : nkt - 1);
@@ -1218,12 +1382,18 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     sv = sk;
     sk = __builtin_amdgcn_readfirstlane(rot(sk));
     ss = __builtin_amdgcn_readfirstlane(rot(ss));
-  }
+  };
+  // tiles before 2 qt need no fold (the loop without it keeps its registers); the
+  // rest run with it
+  const int tsplit = SAFE ? (2 * (int)qt < nkt + 1 ? 2 * (int)qt : nkt + 1) : nkt + 1;
+  for (int t = 0; t < tsplit; t++) step(t, false);
+  if constexpr (SAFE)
+    for (int t = tsplit; t <= nkt; t++) step(t, true);
   if (grp == 0) __syncthreads();
 
   // ---------------- epilogue ----------------
   float l;
-  if constexpr (PMODE == PM_PNQ && PV == PV_FP4) l = Lacc[0];
+  if constexpr (PMODE == PM_PNQ && PV == PV_FP4) l = SAFE ? Lacc[0] + halves_sum(lfix) : Lacc[0];
   else l = halves_sum(lpart);
   float inv = l > 0.0f ? 1.0f / l : 0.0f;
   if constexpr (PMODE == PM_TWO_LEVEL) inv *= s1prev;
@@ -1280,12 +1450,25 @@ static hipError_t launch_one(const FwdArgs& a, hipStream_t st) {
   return launch_one_b<QK, PV, PMODE, PSC, VSC, false>(a, st);
 }
 
+template <int QK, int PV, int PMODE, int PSC, bool BIAS, bool SAFE>
+static hipError_t launch_pp_k(const FwdArgs& a, hipStream_t st) {
+  fwd_pp_kernel<QK, PV, PMODE, PSC, BIAS, SAFE><<<dim3((unsigned)a.grid), dim3(512), 0, st>>>(a);
+  return hipGetLastError();
+}
+
 template <int QK, int PV, int PMODE, int PSC>
 static hipError_t launch_pp(FwdArgs a, hipStream_t st) {
   if (a.plan == nullptr) a.grid = a.B * a.Hq * ((a.N + 255) / 256);
-  if (a.bias != nullptr) fwd_pp_kernel<QK, PV, PMODE, PSC, true><<<dim3((unsigned)a.grid), dim3(512), 0, st>>>(a);
-  else fwd_pp_kernel<QK, PV, PMODE, PSC, false><<<dim3((unsigned)a.grid), dim3(512), 0, st>>>(a);
-  return hipGetLastError();
+  const bool bias = a.bias != nullptr;
+  if constexpr (PV == PV_FP4 || PV == PV_BF16) {
+    if (a.vk != nullptr)
+      return bias ? launch_pp_k<QK, PV, PMODE, PSC, true, true>(a, st)
+                  : launch_pp_k<QK, PV, PMODE, PSC, false, true>(a, st);
+  } else if (a.vk != nullptr) {
+    return hipErrorNotSupported;
+  }
+  return bias ? launch_pp_k<QK, PV, PMODE, PSC, true, false>(a, st)
+              : launch_pp_k<QK, PV, PMODE, PSC, false, false>(a, st);
 }
 
 hipError_t launch_fwd(int qk, int pv, int pmode, int psc, int vsc, const FwdArgs& a, hipStream_t st) {
@@ -1302,6 +1485,8 @@ hipError_t launch_fwd(int qk, int pv, int pmode, int psc, int vsc, const FwdArgs
   MXP(QK_BF16, PV_FP8, PM_FP8_FIXED, SCALE_E8M0);
   MXP(QK_FP4, PV_FP8, PM_FP8_FIXED, SCALE_E8M0);
 #undef MXP
+  // the 4-wave kernel has no per-key V form: causally safe V scales are refused there
+  if (a.vk != nullptr) return hipErrorNotSupported;
 #define MXF(QK_, PV_, PM_, PS_, VS_) \
   if (qk == QK_ && pv == PV_ && pmode == PM_ && psc == PS_ && vsc == VS_) return launch_one<QK_, PV_, PM_, PS_, VS_>(a, st)
   // the rest (V with E4M3 scales per 16 keys; bf16 scores with FP4 PV): single-buffer kernel

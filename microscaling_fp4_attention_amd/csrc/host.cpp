@@ -32,7 +32,9 @@ int check_fmt(const mxattn_qfmt* f, int role) {
   if (f->elem != MXATTN_ELEM_E2M1 && f->elem != MXATTN_ELEM_E4M3) return MXATTN_E_INVALID;
   if (f->scale != MXATTN_SCALE_E8M0 && f->scale != MXATTN_SCALE_E4M3) return MXATTN_E_INVALID;
   if (f->block != 16 && f->block != 32) return MXATTN_E_UNSUPPORTED;
-  if (role != MXATTN_ROLE_QK && role != MXATTN_ROLE_V) return MXATTN_E_INVALID;
+  if (role != MXATTN_ROLE_QK && role != MXATTN_ROLE_V && role != MXATTN_ROLE_VKEY) return MXATTN_E_INVALID;
+  if (role == MXATTN_ROLE_VKEY && (f->elem != MXATTN_ELEM_E2M1 || f->scale != MXATTN_SCALE_E8M0))
+    return MXATTN_E_UNSUPPORTED;
   if (f->scale == MXATTN_SCALE_E8M0) {
     if (f->rule != MXATTN_RULE_OCP && f->rule != MXATTN_RULE_CEIL) return MXATTN_E_INVALID;
     if (f->rule == MXATTN_RULE_CEIL && !(f->qmax >= 1.0f && f->qmax <= 448.0f)) return MXATTN_E_INVALID;
@@ -122,10 +124,15 @@ int mxattn_qtensor_bytes(const mxattn_qfmt* fmt, int role, int64_t B, int64_t H,
     *code_bytes = (size_t)(B * H * N * d * bits / 8);
     *scale_bytes = (size_t)(B * H * N * (d / fmt->block));
     if (n_padded) *n_padded = N;
-  } else {
+  } else if (role == MXATTN_ROLE_V) {
     int64_t np = v_padded(N, ndocs, fmt->block);
     *code_bytes = (size_t)(B * H * d * np * bits / 8);
     *scale_bytes = (size_t)(B * H * d * (np / fmt->block));
+    if (n_padded) *n_padded = np;
+  } else {  // VKEY: role V's codes, one scale byte per key slot
+    int64_t np = v_padded(N, ndocs, fmt->block);
+    *code_bytes = (size_t)(B * H * d * np * bits / 8);
+    *scale_bytes = (size_t)(B * H * np);
     if (n_padded) *n_padded = np;
   }
   return MXATTN_OK;
@@ -139,7 +146,7 @@ int mxattn_quantize(const void* x_bf16, const int64_t x_strides[4], int64_t B, i
   int rc = mxattn_qtensor_bytes(fmt, role, B, H, N, d, ndocs, &cb, &sb, &np);
   if (rc != MXATTN_OK) return rc;
   if (out == nullptr || x_strides == nullptr) return MXATTN_E_INVALID;
-  if (ndocs > 1 && (cu_seqlens == nullptr || role != MXATTN_ROLE_V)) return MXATTN_E_INVALID;
+  if (ndocs > 1 && (cu_seqlens == nullptr || role == MXATTN_ROLE_QK)) return MXATTN_E_INVALID;
   if (x_strides[3] != 1 || x_strides[0] < 0 || x_strides[1] < 0 || x_strides[2] < 0) return MXATTN_E_INVALID;
   const int64_t nel = B * H * N;
   if (nel > 0) {
@@ -155,7 +162,7 @@ int mxattn_quantize(const void* x_bf16, const int64_t x_strides[4], int64_t B, i
   out->N = N;
   out->d = d;
   out->n_padded = np;
-  if (nel == 0 && !(role == MXATTN_ROLE_V && B * H > 0 && np > 0)) return MXATTN_OK;
+  if (nel == 0 && !(role != MXATTN_ROLE_QK && B * H > 0 && np > 0)) return MXATTN_OK;
 
   QuantArgs a;
   a.x = x_bf16;
@@ -175,7 +182,9 @@ int mxattn_quantize(const void* x_bf16, const int64_t x_strides[4], int64_t B, i
   a.codes = out->codes;
   a.scales = out->scales;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = role == MXATTN_ROLE_QK ? launch_quant_qk(a, st) : launch_quant_v(a, st);
+  hipError_t e = role == MXATTN_ROLE_QK ? launch_quant_qk(a, st)
+                 : role == MXATTN_ROLE_V  ? launch_quant_v(a, st)
+                                          : launch_quant_vkey(a, st);
   if (e != hipSuccess) return hip_fail(e, "mxattn_quantize launch");
   return MXATTN_OK;
 }
@@ -426,6 +435,20 @@ int mxattn_fwd(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn_qt
   a.plan = docs ? static_cast<const PlanHeader*>(workspace) : nullptr;
   a.bias = p->score_bias;
   if (a.bias != nullptr && !aligned16(a.bias)) return MXATTN_E_ALIGN;
+  a.vk = nullptr;
+  a.vks = nullptr;
+  if (p->vkey != nullptr) {  // causally safe V scales: the per-key form of the same V
+    const mxattn_qtensor* vk = p->vkey;
+    if (!p->causal || vk->role != MXATTN_ROLE_VKEY) return MXATTN_E_INVALID;
+    if (vk->B != v->B || vk->H != v->H || vk->N != v->N || vk->d != v->d || vk->n_padded != v->n_padded ||
+        vk->ndocs != v->ndocs || vk->fmt.block != v->fmt.block)
+      return MXATTN_E_INVALID;
+    if (pv == PV_FP8 || vsc != SCALE_E8M0) return MXATTN_E_UNSUPPORTED;  // 4-bit V with E8M0/32 only
+    if (!vk->codes || !vk->scales) return MXATTN_E_INVALID;
+    if (!aligned16(vk->codes) || !aligned16(vk->scales)) return MXATTN_E_ALIGN;
+    a.vk = static_cast<const uint8_t*>(vk->codes);
+    a.vks = static_cast<const uint8_t*>(vk->scales);
+  }
   const int64_t nqt = (N + 127) / 128;
   a.grid = docs ? Hq * (nqt + ndocs) : B * Hq * nqt;
   if (a.grid > 0x7FFFFFFF) return MXATTN_E_UNSUPPORTED;

@@ -27,6 +27,8 @@ struct QuantArgs {
 
 hipError_t launch_quant_qk(const QuantArgs& a, hipStream_t st);
 hipError_t launch_quant_v(const QuantArgs& a, hipStream_t st);
+// role VKEY: per-key E8M0 scale over the 128 channels, codes transposed as role V
+hipError_t launch_quant_vkey(const QuantArgs& a, hipStream_t st);
 
 // outlier pre-processing (preproc.hip)
 // mean: [B][H][nd][128] float, nd = max(ndocs, 1); a.cu/a.ndocs give the documents
@@ -96,6 +98,10 @@ struct FwdArgs {
   const PlanHeader* plan;  // packed documents, or null
   int64_t grid;            // workgroups launched
   const float* bias;       // per-key score bias [B][Hq][N] (centering compensation), or null
+  // per-key form of V for causally safe diagonal tiles (null: grouped V scales only):
+  // codes [B][Hkv][128][np / 2] (E2M1), one E8M0 byte per key slot [B][Hkv][np]
+  const uint8_t* vk;
+  const uint8_t* vks;
 };
 
 // psc: P block scale (SCALE_E8M0 -> blocks of 32, SCALE_E4M3 -> blocks of 16);

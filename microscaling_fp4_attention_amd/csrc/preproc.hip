@@ -37,26 +37,32 @@ __device__ __forceinline__ int doc_of_token(const int32_t* __restrict__ cu, int 
 }
 
 // ---------------------------------------------------------------------------
-// channel means: one workgroup of 512 threads per (b, h, document).  Thread i sums
-// channels 8 (i % 16) + [0, 8) over the tokens t0 + 32 k + i / 16 in double; the 32
-// partial sums of a channel are then added in a fixed order (deterministic).
-// mean: [B][H][nd][128]
+// channel means: 8 workgroups of 512 threads per (b, h, document) unit, one per group
+// of 16 channels.  The 8 workgroups of a unit get ids of one residue mod 8, which the
+// dispatcher deals to one XCD, so each 256-byte token row is fetched into one L2.
+// Thread i sums channels 16 g + 8 (i % 2) + [0, 8) over the tokens t0 + 256 k + i / 2
+// in double; the 256 partial sums of a channel are then added in a fixed order.
+// mean: [B][H][nd][128]; units = B H nd, the grid covers round_up(units, 8) * 8 ids.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(512) void channel_mean_kernel(const uint16_t* __restrict__ x, int64_t sB, int64_t sH,
                                                            int64_t sN, int64_t H, int64_t N,
-                                                           const int32_t* __restrict__ cu, int nd,
+                                                           const int32_t* __restrict__ cu, int nd, int64_t units,
                                                            float* __restrict__ mean) {
-  __shared__ double part[32][129];
-  const int tid = threadIdx.x, chunk = tid & 15, slot = tid >> 4;
-  const int64_t bhd = blockIdx.x, doc = bhd % nd, bh = bhd / nd, b = bh / H, h = bh % H;
+  __shared__ double part[256][17];
+  const int64_t id = blockIdx.x;
+  const int64_t unit = (id / 64) * 8 + id % 8;
+  const int cg = (int)((id / 8) % 8);
+  if (unit >= units) return;  // whole workgroup
+  const int tid = threadIdx.x, half = tid & 1, slot = tid >> 1;
+  const int64_t doc = unit % nd, bh = unit / nd, b = bh / H, h = bh % H;
   const int64_t t0 = cu ? cu[doc] : 0, t1 = cu ? cu[doc + 1] : N;
-  const uint16_t* base = x + b * sB + h * sH + chunk * 8;
+  const uint16_t* base = x + b * sB + h * sH + cg * 16 + half * 8;
   double s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   int64_t t = t0 + slot;
-  for (; t + 96 < t1; t += 128) {  // four tokens in flight per thread
+  for (; t + 768 < t1; t += 1024) {  // four tokens in flight per thread
     uint4 v[4];
 #pragma unroll
-    for (int u = 0; u < 4; u++) v[u] = *reinterpret_cast<const uint4*>(base + (t + 32 * u) * sN);
+    for (int u = 0; u < 4; u++) v[u] = *reinterpret_cast<const uint4*>(base + (t + 256 * u) * sN);
 #pragma unroll
     for (int u = 0; u < 4; u++) {
       s[0] += (double)bf16_lo_f(v[u].x); s[1] += (double)bf16_hi_f(v[u].x);
@@ -65,7 +71,7 @@ __global__ __launch_bounds__(512) void channel_mean_kernel(const uint16_t* __res
       s[6] += (double)bf16_lo_f(v[u].w); s[7] += (double)bf16_hi_f(v[u].w);
     }
   }
-  for (; t < t1; t += 32) {
+  for (; t < t1; t += 256) {
     uint4 v = *reinterpret_cast<const uint4*>(base + t * sN);
     s[0] += (double)bf16_lo_f(v.x); s[1] += (double)bf16_hi_f(v.x);
     s[2] += (double)bf16_lo_f(v.y); s[3] += (double)bf16_hi_f(v.y);
@@ -73,13 +79,13 @@ __global__ __launch_bounds__(512) void channel_mean_kernel(const uint16_t* __res
     s[6] += (double)bf16_lo_f(v.w); s[7] += (double)bf16_hi_f(v.w);
   }
 #pragma unroll
-  for (int j = 0; j < 8; j++) part[slot][chunk * 8 + j] = s[j];
+  for (int j = 0; j < 8; j++) part[slot][half * 8 + j] = s[j];
   __syncthreads();
-  if (tid < 128) {
+  if (tid < 16) {
     double acc = 0.0;
-    for (int k = 0; k < 32; k++) acc += part[k][tid];
+    for (int k = 0; k < 256; k++) acc += part[k][tid];
     const int64_t L = t1 - t0;
-    mean[bhd * 128 + tid] = L > 0 ? (float)(acc / (double)L) : 0.0f;
+    mean[unit * 128 + cg * 16 + tid] = L > 0 ? (float)(acc / (double)L) : 0.0f;
   }
 }
 
@@ -228,9 +234,10 @@ __global__ __launch_bounds__(256) void center_comp_kernel(const float* __restric
 
 hipError_t launch_channel_mean(const QuantArgs& a, float* mean, hipStream_t st) {
   const int nd = a.ndocs > 1 ? a.ndocs : 1;
-  const int64_t wgs = a.B * a.H * nd;
+  const int64_t units = a.B * a.H * nd;
+  const int64_t wgs = (units + 7) / 8 * 64;
   channel_mean_kernel<<<dim3((unsigned)wgs), 512, 0, st>>>(static_cast<const uint16_t*>(a.x), a.sB, a.sH, a.sN,
-                                                           a.H, a.N, a.ndocs > 1 ? a.cu : nullptr, nd, mean);
+                                                           a.H, a.N, a.ndocs > 1 ? a.cu : nullptr, nd, units, mean);
   return hipGetLastError();
 }
 

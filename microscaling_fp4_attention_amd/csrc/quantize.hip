@@ -185,6 +185,111 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// role VKEY: the per-key form of a 4-bit V for causally safe diagonal tiles ("FLAMIA",
+// section 3.2): per key slot one E8M0 scale over its 128 channels, E2M1 codes of
+// x / 2^e written transposed as for role V.  x [B][H][N][128] -> codes
+// [B][H][128][np / 2], scales [B][H][np].  The slot layout (documents starting at
+// BLOCK boundaries) is role V's, so a key has the same slot in both forms.
+// ---------------------------------------------------------------------------
+template <int BLOCK>
+__global__ __launch_bounds__(256) void quant_vkey_kernel(const uint16_t* __restrict__ x, int64_t sB, int64_t sH,
+                                                         int64_t sN, int64_t H, int64_t N, int64_t np,
+                                                         const int32_t* __restrict__ cu, int ndocs, E8m0Rule rule,
+                                                         uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  __shared__ int32_t tok[128];
+  __shared__ float inv_s[128];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[128 * VQ_ROW];
+  const int tid = threadIdx.x;
+  const int64_t ntiles = np / 128;
+  const int64_t bh = blockIdx.x / ntiles;
+  const int64_t t0 = (blockIdx.x % ntiles) * 128;
+  const int64_t b = bh / H, h = bh % H;
+  if (tid < 128) {
+    int64_t p = t0 + tid;
+    int32_t t = -1;
+    if (cu == nullptr) {
+      if (p < N) t = (int32_t)p;
+    } else {
+      int64_t voff = 0;
+      for (int k = 0; k < ndocs; k++) {
+        int64_t L = cu[k + 1] - cu[k];
+        int64_t span = (L + BLOCK - 1) / BLOCK * BLOCK;
+        if (p < voff + span) {
+          if (p - voff < L) t = (int32_t)(cu[k] + (p - voff));
+          break;
+        }
+        voff += span;
+      }
+    }
+    tok[tid] = t;
+  }
+  __syncthreads();
+  const uint16_t* xb = x + b * sB + h * sH;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    int c = tid + 256 * i;
+    int row = c >> 4, part = c & 15;
+    int32_t t = tok[row];
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (t >= 0) v = *reinterpret_cast<const uint4*>(xb + (int64_t)t * sN + part * 8);
+    *reinterpret_cast<uint4*>(tile + row * VQ_ROW + part * 16) = v;
+  }
+  __syncthreads();
+  // per slot: maximum over its 128 channels (two threads of 64 channels each)
+  {
+    const int slot = tid >> 1, half = tid & 1;
+    float M = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const uint4 v = *reinterpret_cast<const uint4*>(tile + slot * VQ_ROW + half * 128 + i * 16);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int u = 0; u < 4; u++)
+        M = __builtin_fmaxf(M, __builtin_fmaxf(__builtin_fabsf(u2f(w[u] << 16)), __builtin_fabsf(u2f(w[u] & 0xFFFF0000u))));
+    }
+    M = __builtin_fmaxf(M, __shfl_xor(M, 1));
+    const int e = e8m0_exp(M, rule);
+    if (half == 0) {
+      inv_s[slot] = exp2i_neg(e);
+      scales[bh * np + t0 + slot] = (uint8_t)(e + 127);
+    }
+  }
+  __syncthreads();
+  // lane -> (channel, 64 keys), codes stored contiguously per channel row
+  const int ch = tid & 127, sub = tid >> 7;
+  uint32_t out[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) out[i] = 0;
+#pragma unroll
+  for (int j = 0; j < 64; j++) {
+    const int key = sub * 64 + j;
+    const uint32_t hbits = *reinterpret_cast<const uint16_t*>(tile + key * VQ_ROW + ch * 2);
+    const float f = u2f(hbits << 16);
+    const uint32_t c = e2m1_mag(__builtin_fabsf(f) * inv_s[key]) | ((f2u(f) >> 31) << 3);
+    out[j >> 3] |= c << (4 * (j & 7));
+  }
+  uint8_t* cdst = codes + (bh * 128 + ch) * (np / 2) + (t0 + sub * 64) / 2;
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+    reinterpret_cast<uint4*>(cdst)[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+}
+
+hipError_t launch_quant_vkey(const QuantArgs& a, hipStream_t st) {
+  dim3 grid((unsigned)(a.B * a.H * (a.np / 128)));
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  uint8_t* c = static_cast<uint8_t*>(a.codes);
+  uint8_t* s = static_cast<uint8_t*>(a.scales);
+  if (a.elem != ELEM_E2M1 || a.scale != SCALE_E8M0) return hipErrorInvalidValue;
+  if (a.block == 32)
+    quant_vkey_kernel<32><<<grid, 256, 0, st>>>(x, a.sB, a.sH, a.sN, a.H, a.N, a.np, a.cu, a.ndocs, a.rule, c, s);
+  else if (a.block == 16)
+    quant_vkey_kernel<16><<<grid, 256, 0, st>>>(x, a.sB, a.sH, a.sN, a.H, a.N, a.np, a.cu, a.ndocs, a.rule, c, s);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_quant_qk(const QuantArgs& a, hipStream_t st) {

@@ -120,8 +120,28 @@ def ulp_diff(a: np.ndarray, b: np.ndarray) -> int:
     return int(np.abs(ia - ib).max()) if ia.size else 0
 
 
+def gpu_codes_vkey(qt, N, doc_off):
+    """GPU per-key V form in the oracle's layout: codes [B, H, N, d] (by token), exponents [B, H, N]."""
+    c = unpack_nibbles(qt.codes_view().cpu().numpy())  # [B, H, d, np]
+    slots = v_slots(N, doc_off, qt.desc.fmt.block)
+    codes = np.ascontiguousarray(np.swapaxes(c[..., slots], -1, -2))
+    ek = qt.scales_view().cpu().numpy()[..., slots].astype(np.int32) - 127
+    return codes, ek
+
+
+def oracle_vkey(vf, vfmt):
+    """oracle per-key form of V [B, H, N, d]: (codes [B,H,N,d], values [B,H,N,d], exponents [B,H,N])"""
+    B, H, N, d = vf.shape
+    codes = np.zeros((B, H, N, d), np.uint8)
+    ek = np.zeros((B, H, N), np.int32)
+    for b in range(B):
+        for h in range(H):
+            codes[b, h], ek[b, h] = oracle.quantize_keys(vf[b, h], vfmt)
+    return codes, oracle.e2m1_values(codes), ek
+
+
 def run_case(qfmt, vfmt, pmode, pfmt, B, Hq, Hkv, N, causal=False, kind="kmean", seed=0, doc_off=None,
-             rows=None, check_bytes=True, inputs=None, pre=None):
+             rows=None, check_bytes=True, inputs=None, pre=None, safe=False):
     """Run one forward on the GPU and on the oracle; returns a dict of results.
 
     pre: None, or a dict of outlier pre-processing for Q and K: {"center": both means
@@ -151,7 +171,8 @@ def run_case(qfmt, vfmt, pmode, pfmt, B, Hq, Hkv, N, causal=False, kind="kmean",
         Kq = mx.quantize(kg, mx.ROLE_QK, qfmt)
     Vq = mx.quantize(vg, mx.ROLE_V, vfmt, cu_seqlens=cu)
     delta_g = mx.center_comp(qmean_g, kg, kmean_g, cu) if center else None
-    params = mx.fwd_params(pmode, pfmt, causal=causal, score_bias=delta_g)
+    Vk = mx.quantize(vg, mx.ROLE_VKEY, vfmt, cu_seqlens=cu) if safe else None
+    params = mx.fwd_params(pmode, pfmt, causal=causal, score_bias=delta_g, vkey=Vk)
     ws, nd = None, 0
     if doc_off is not None:
         ws = mx.fwd_plan(doc_off, N, causal)
@@ -190,13 +211,21 @@ def run_case(qfmt, vfmt, pmode, pfmt, B, Hq, Hkv, N, causal=False, kind="kmean",
         gc, gs = gpu_codes_v(Vq, N, doc_off)
         assert np.array_equal(gc, vc), "V codes differ"
         assert np.array_equal(gs, vs), "V scales differ"
+    vk_vals = vk_exp = None
+    if safe:
+        vk_codes, vk_vals, vk_exp = oracle_vkey(vf, vfmt)
+        if check_bytes:
+            gkc, gke = gpu_codes_vkey(Vk, N, doc_off)
+            assert np.array_equal(gkc, vk_codes), "per-key V codes differ"
+            assert np.array_equal(gke, vk_exp), "per-key V exponents differ"
     O_ref, lse_ref, fb = oracle.attention(qd, kd, vd, PM_ORACLE[pmode], pfmt, causal=causal, doc_off=doc_off,
-                                          rows=rows, bias=bias)
+                                          rows=rows, bias=bias, vkey=vk_vals, vkey_exp=vk_exp)
     sel = np.arange(B * Hq * N) if rows is None else np.asarray(rows)
     Og = O_gpu[sel]
     err = np.abs(Og - O_ref)
     amax = np.abs(O_ref).max()
     bound = TOL * amax + fb[:, None]
     res.update(err=err, bound=bound, amax=amax, fb=fb, O_ref=O_ref, O_gpu=Og, lse_ref=lse_ref, lse_gpu=lse_gpu[sel],
+               O_gpu_all=O_gpu,
                ratio=float((err / bound).max()) if err.size else 0.0, n_fragile=int((fb > 0).sum()))
     return res
