@@ -89,6 +89,9 @@ def lib():
         L.orc_attention_ex.argtypes = [f32p, f32p, f32p, f32p, f32p, i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_int, i32p, ctypes.c_int, P(AttnParams), i64p,
                                        ctypes.c_int64, f32p, f32p, f64p]
+        L.orc_decode.restype = ctypes.c_int
+        L.orc_decode.argtypes = [f32p, f32p, f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_int, ctypes.c_int, i32p, ctypes.c_int, P(AttnParams), f32p, f32p, f64p]
         L.orc_quantize_keys.argtypes = [f32p, ctypes.c_int, ctypes.c_int, P(Fmt), u8p, i32p]
         L.orc_channel_mean.argtypes = [f32p, ctypes.c_int, ctypes.c_int, i32p, ctypes.c_int, f32p]
         L.orc_preprocess_rows.argtypes = [f32p, ctypes.c_int, ctypes.c_int, f32p, i32p, ctypes.c_int,
@@ -296,3 +299,28 @@ def e2m1_values(codes):
     """E2M1 codes -> their values (unit scale), float32"""
     table = np.array([e2m1_value(c) for c in range(16)], np.float32)
     return table[np.asarray(codes) & 15]
+
+
+# ---- decode with split keys ----
+def decode(Q, K, V, kv_len, pmode, pfmt=None, split=256, sm_scale=None, kv_tile=128):
+    """Q [B,Hq,R,d] (the R newest tokens), K/V [B,Hkv,N,d] dequantized float32, kv_len [B]:
+    split-key decode merged by log-sum-exp.  Returns (O [B,Hq,R,d], lse [B,Hq,R], fb [B,Hq,R])."""
+    Q = np.ascontiguousarray(Q, dtype=np.float32)
+    K = np.ascontiguousarray(K, dtype=np.float32)
+    V = np.ascontiguousarray(V, dtype=np.float32)
+    B, Hq, R, d = Q.shape
+    Hkv, N = K.shape[1], K.shape[2]
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    pf = fmt(pfmt) if pfmt is not None else Fmt(0, 0, 32, 0, 0.0)
+    p = AttnParams(pmode, pf, 1, float(sm_scale), kv_tile)
+    kl = np.ascontiguousarray(kv_len, dtype=np.int32)
+    O = np.zeros((B, Hq, R, d), np.float32)
+    lse = np.zeros((B, Hq, R), np.float32)
+    fb = np.zeros((B, Hq, R), np.float64)
+    rc = lib().orc_decode(_ptr(Q, ctypes.c_float), _ptr(K, ctypes.c_float), _ptr(V, ctypes.c_float), B, Hq, Hkv, R,
+                          N, d, _ptr(kl, ctypes.c_int32), split, ctypes.byref(p), _ptr(O, ctypes.c_float),
+                          _ptr(lse, ctypes.c_float), _ptr(fb, ctypes.c_double))
+    if rc != 0:
+        raise ValueError(f"orc_decode failed with {rc}")
+    return O, lse, fb

@@ -587,3 +587,63 @@ void orc_quantize_keys(const float* x, int N, int d, const orc_fmt* f, uint8_t* 
     ek[j] = (int)sb - 127;
   }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Decode with split keys and a log-sum-exp merge ([MPFA] section 5.3).      */
+/* ------------------------------------------------------------------------ */
+int orc_decode(const float* Q, const float* K, const float* V, int B, int Hq, int Hkv, int R, int N,
+               int d, const int* kv_len, int split, const orc_attn_params* p, float* O, float* lse,
+               double* fb) {
+  if (split <= 0 || split % p->kv_tile != 0 || !p->causal) return -1;
+  float* os = (float*)malloc(sizeof(float) * (size_t)d);
+  double* acc = (double*)malloc(sizeof(double) * (size_t)d);
+  for (int b = 0; b < B; b++) {
+    const int L = kv_len[b];
+    if (L < R || L > N) {
+      free(os);
+      free(acc);
+      return -2;
+    }
+    const int nsplit = (L + split - 1) / split;
+    for (int h = 0; h < Hq; h++) {
+      const int hk = h * Hkv / Hq;
+      const float* kb = K + ((int64_t)(b * Hkv + hk) * N) * d;
+      const float* vb = V + ((int64_t)(b * Hkv + hk) * N) * d;
+      for (int r = 0; r < R; r++) {
+        const int pos = L - R + r; /* keys 0..pos are visible */
+        const float* q = Q + ((int64_t)((b * Hq + h) * R + r)) * d;
+        double M = -INFINITY, wsum = 0.0, fbs = 0.0;
+        float ls;
+        double f1;
+        /* first pass: the maximum lse of the splits */
+        double* lses = (double*)malloc(sizeof(double) * (size_t)(nsplit > 0 ? nsplit : 1));
+        for (int s = 0; s < nsplit; s++) {
+          const int k0 = s * split, nk = (L - k0 < split) ? L - k0 : split;
+          const int vis = pos - k0 + 1 < 0 ? 0 : (pos - k0 + 1 < nk ? pos - k0 + 1 : nk);
+          orc_attn_row(q, kb + (int64_t)k0 * d, vb + (int64_t)k0 * d, nk, vis, d, p, os, &ls, &f1);
+          lses[s] = (vis > 0) ? (double)ls : -INFINITY;
+          if (lses[s] > M) M = lses[s];
+        }
+        for (int c = 0; c < d; c++) acc[c] = 0.0;
+        for (int s = 0; s < nsplit; s++) {
+          const int k0 = s * split, nk = (L - k0 < split) ? L - k0 : split;
+          const int vis = pos - k0 + 1 < 0 ? 0 : (pos - k0 + 1 < nk ? pos - k0 + 1 : nk);
+          if (vis <= 0 || lses[s] == -INFINITY) continue;
+          orc_attn_row(q, kb + (int64_t)k0 * d, vb + (int64_t)k0 * d, nk, vis, d, p, os, &ls, &f1);
+          const double w = exp(lses[s] - M);
+          wsum += w;
+          fbs += w * f1;
+          for (int c = 0; c < d; c++) acc[c] += w * (double)os[c];
+        }
+        float* o = O + ((int64_t)((b * Hq + h) * R + r)) * d;
+        for (int c = 0; c < d; c++) o[c] = wsum > 0.0 ? (float)(acc[c] / wsum) : 0.0f;
+        if (lse) lse[(b * Hq + h) * R + r] = wsum > 0.0 ? (float)(M + log(wsum)) : -INFINITY;
+        if (fb) fb[(b * Hq + h) * R + r] = wsum > 0.0 ? fbs / wsum : 0.0;
+        free(lses);
+      }
+    }
+  }
+  free(os);
+  free(acc);
+  return 0;
+}

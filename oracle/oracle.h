@@ -136,6 +136,21 @@ int orc_attention_ex(const float* Q, const float* K, const float* V, const float
  * rule and the element codes of V[j][c] / 2^ek[j].  x, codes: [N][d]; ek: [N]. */
 void orc_quantize_keys(const float* x, int N, int d, const orc_fmt* f, uint8_t* codes, int* ek);
 
+/* Decode with a split key range ([MPFA] section 5.3: the history is cut into fixed
+ * partitions, each keeps its own (m, l, O) state, and the states are merged by their
+ * log-sum-exp).  Q: [B][Hq][R][d] -- the R newest tokens of each request, row r at
+ * position kv_len[b] - R + r, attending causally to the kv_len[b] keys of K, V:
+ * [B][Hkv][N][d] (dequantized; N >= every kv_len).  The keys are cut into splits of
+ * `split` keys from key 0; each split runs orc_attn_row over its own keys (tiles of
+ * kv_tile from the split start, P quantized per tile against the split's running
+ * maximum), giving o_s and lse_s (a split that sees no key has lse_s = -inf).  The
+ * merge, in double: M = max lse_s, w_s = exp(lse_s - M), O = sum w_s o_s / sum w_s,
+ * lse = M + log(sum w_s).  fb: the merged flip budget sum w_s fb_s / sum w_s.
+ * O: [B][Hq][R][d]; lse, fb: [B][Hq][R] (may be NULL). */
+int orc_decode(const float* Q, const float* K, const float* V, int B, int Hq, int Hkv, int R, int N,
+               int d, const int* kv_len, int split, const orc_attn_params* p, float* O, float* lse,
+               double* fb);
+
 /* ---- outlier pre-processing of Q and K (before quantization) ---- */
 
 /* Per-channel mean over the tokens of each document of one head ([MPFA] section
