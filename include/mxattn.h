@@ -307,6 +307,34 @@ int mxattn_fwd(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn_qt
                const mxattn_fwd_params* params, int ndocs, void* out, const int64_t out_strides[4],
                float* lse, const void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Decode ("MpFA" section 5.3): the R newest tokens of each request attend to its
+ * key/value history.  The history of each (request, KV head) is cut into splits of
+ * 256 keys from key 0; each split runs the online softmax on its own (tiles of 128
+ * from the split start, P quantized per tile against the split's running maximum)
+ * and the splits of each query row are merged by their log-sum-exp.  The query
+ * heads of a KV head's group and the R rows share one matrix tile: (Hq/Hkv)*R <= 32.
+ *   q: role QK [B][Hq][R][d]; row r sits at position kv_len[b] - R + r and sees
+ *      keys 0..that position (params->causal must be 1).
+ *   k: role QK [B][Hkv][N][d]; v: role V [B][Hkv][d][n_padded] without documents.
+ *   Formats: MXFP4 Q/K/V (E2M1 with E8M0 per 32, any E8M0 rule); P modes DIRECT,
+ *   PNQ and TWO_LEVEL with P in E2M1 with E8M0 per 32.  score_bias and vkey must be
+ *   NULL.
+ *   kv_len: DEVICE int32 [B] with R <= kv_len[b] <= N, or NULL (every history has N
+ *   keys); the host does not read it.
+ *   out: [B][Hq][R][d] with element strides out_strides (out_strides[3] == 1),
+ *   float32 or bfloat16 per params->out_fp32; lse: optional float32 [B][Hq][R].
+ *   workspace: DEVICE, at least mxattn_decode_workspace_bytes(B, Hq, R, N) bytes,
+ *   16-byte aligned (split outputs and log-sum-exps; contents need no clearing).
+ * Errors: MXATTN_E_INVALID, MXATTN_E_UNSUPPORTED, MXATTN_E_ALIGN,
+ *   MXATTN_E_WORKSPACE, MXATTN_E_HIP.
+ */
+size_t mxattn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t R, int64_t N);
+int mxattn_decode(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn_qtensor* v,
+                  const mxattn_fwd_params* params, const int32_t* kv_len, void* out,
+                  const int64_t out_strides[4], float* lse, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -104,6 +104,11 @@ def _lib():
                                           P(QTensorC), vp]
         L.mxattn_center_comp.restype = i32
         L.mxattn_center_comp.argtypes = [vp, vp, P(i64), vp, i64, i64, i64, i64, i64, vp, i32, vp, vp]
+        L.mxattn_decode_workspace_bytes.restype = ctypes.c_size_t
+        L.mxattn_decode_workspace_bytes.argtypes = [i64, i64, i64, i64]
+        L.mxattn_decode.restype = i32
+        L.mxattn_decode.argtypes = [P(QTensorC), P(QTensorC), P(QTensorC), P(FwdParams), vp, vp, P(i64), vp, vp,
+                                    ctypes.c_size_t, vp]
         L.mxattn_fwd_workspace_bytes.restype = ctypes.c_size_t
         L.mxattn_fwd_workspace_bytes.argtypes = [i64, i32]
         L.mxattn_fwd_plan.restype = i32
@@ -308,4 +313,30 @@ def fwd(q: QTensor, k: QTensor, v: QTensor, params: FwdParams, out: torch.Tensor
     _check(_lib().mxattn_fwd(ctypes.byref(q.desc), ctypes.byref(k.desc), ctypes.byref(v.desc), ctypes.byref(params),
                              ndocs, ctypes.c_void_p(out.data_ptr()), _i64(out.stride()), lse_ptr, ws_ptr, ws_bytes,
                              _stream(stream)), "mxattn_fwd")
+    return out
+
+
+def decode_workspace_bytes(B: int, Hq: int, R: int, N: int) -> int:
+    return int(_lib().mxattn_decode_workspace_bytes(B, Hq, R, N))
+
+
+def decode(q: QTensor, k: QTensor, v: QTensor, params: FwdParams, kv_len: torch.Tensor | None = None,
+           out: torch.Tensor | None = None, lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+           stream=None) -> torch.Tensor:
+    """Split-key decode (mxattn_decode): q [B, Hq, R, 128] quantized (the R newest tokens),
+    k / v over the [B, Hkv, N] history; kv_len: int32 device tensor [B] or None.
+    Returns out [B, Hq, R, 128] (float32 or bfloat16 per params.out_fp32)."""
+    B, Hq, R, d = q.desc.B, q.desc.H, q.desc.N, q.desc.d
+    N = k.desc.N
+    if out is None:
+        dt = torch.float32 if params.out_fp32 else torch.bfloat16
+        out = torch.empty((B, Hq, R, d), dtype=dt, device=q.codes.device)
+    nbytes = decode_workspace_bytes(B, Hq, R, N)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.codes.device)
+    if kv_len is not None and (kv_len.dtype != torch.int32 or not kv_len.is_cuda):
+        raise ValueError("kv_len must be an int32 device tensor")
+    _check(_lib().mxattn_decode(ctypes.byref(q.desc), ctypes.byref(k.desc), ctypes.byref(v.desc), ctypes.byref(params),
+                                _ptr(kv_len), _ptr(out), _i64(out.stride()), _ptr(lse), _ptr(workspace),
+                                workspace.numel(), _stream(stream)), "mxattn_decode")
     return out

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxattn.so")
 OBJDIR = os.path.join(ROOT, "_build")
-SOURCES = ["quantize.hip", "preproc.hip", "fwd.hip", "host.cpp"]
+SOURCES = ["quantize.hip", "preproc.hip", "fwd.hip", "decode.hip", "host.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-variable",

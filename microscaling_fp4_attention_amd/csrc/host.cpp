@@ -298,6 +298,71 @@ int mxattn_center_comp(const float* qmean, const void* k_bf16, const int64_t k_s
 
 size_t mxattn_fwd_workspace_bytes(int64_t N, int ndocs) { return plan_bytes(N, ndocs); }
 
+size_t mxattn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t R, int64_t N) {
+  if (B <= 0 || Hq <= 0 || R <= 0 || N <= 0) return 0;
+  const int64_t rows = B * Hq * R * ((N + 255) / 256);
+  return (size_t)(rows * 128 * 4 + (rows * 4 + 15) / 16 * 16);
+}
+
+int mxattn_decode(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn_qtensor* v,
+                  const mxattn_fwd_params* p, const int32_t* kv_len, void* out, const int64_t os[4], float* lse,
+                  void* workspace, size_t ws_bytes, void* stream) {
+  if (!q || !k || !v || !p || !os) return MXATTN_E_INVALID;
+  if (q->role != MXATTN_ROLE_QK || k->role != MXATTN_ROLE_QK || v->role != MXATTN_ROLE_V) return MXATTN_E_INVALID;
+  if (q->d != 128 || k->d != 128 || v->d != 128) return MXATTN_E_UNSUPPORTED;
+  if (q->B != k->B || q->B != v->B || k->N != v->N || k->H != v->H || v->ndocs != 1) return MXATTN_E_INVALID;
+  if (q->H <= 0 || k->H <= 0 || q->H % k->H != 0) return MXATTN_E_INVALID;
+  if (!p->causal || p->kv_tile != 128 || p->score_bias != nullptr || p->vkey != nullptr) return MXATTN_E_INVALID;
+  if (!(p->sm_scale > 0.0f) || !isfinite(p->sm_scale)) return MXATTN_E_INVALID;
+  const int64_t B = q->B, Hq = q->H, Hkv = k->H, R = q->N, N = k->N;
+  if (R <= 0 || R > N || (Hq / Hkv) * R > 32) return MXATTN_E_UNSUPPORTED;
+  if (!same_fmt(q->fmt, k->fmt) || !is_mxfp4(q->fmt) || !is_mxfp4(v->fmt)) return MXATTN_E_UNSUPPORTED;
+  if (p->pmode != MXATTN_P_DIRECT && p->pmode != MXATTN_P_PNQ && p->pmode != MXATTN_P_TWO_LEVEL)
+    return MXATTN_E_UNSUPPORTED;
+  int prc = check_fmt(&p->pfmt, MXATTN_ROLE_V);
+  if (prc != MXATTN_OK) return prc;
+  if (!is_mxfp4(p->pfmt)) return MXATTN_E_UNSUPPORTED;
+  if (N > (int64_t(1) << 24)) return MXATTN_E_UNSUPPORTED;
+  if (B == 0) return MXATTN_OK;
+  if (!q->codes || !q->scales || !k->codes || !k->scales || !v->codes || !v->scales || !out) return MXATTN_E_INVALID;
+  if (!aligned16(q->codes) || !aligned16(k->codes) || !aligned16(v->codes) || !aligned16(q->scales) ||
+      !aligned16(k->scales) || !aligned16(v->scales) || !aligned16(out))
+    return MXATTN_E_ALIGN;
+  if (os[3] != 1 || os[0] < 0 || os[1] < 0 || os[2] < 0) return MXATTN_E_INVALID;
+  if (workspace == nullptr || ws_bytes < mxattn_decode_workspace_bytes(B, Hq, R, N)) return MXATTN_E_WORKSPACE;
+  if (!aligned16(workspace)) return MXATTN_E_ALIGN;
+  DecArgs a{};
+  a.q = static_cast<const uint8_t*>(q->codes);
+  a.qs = static_cast<const uint8_t*>(q->scales);
+  a.k = static_cast<const uint8_t*>(k->codes);
+  a.ks = static_cast<const uint8_t*>(k->scales);
+  a.v = static_cast<const uint8_t*>(v->codes);
+  a.vs = static_cast<const uint8_t*>(v->scales);
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.R = R;
+  a.N = N;
+  a.np = v->n_padded;
+  a.kv_len = kv_len;
+  a.lambda = (float)((double)p->sm_scale * 1.4426950408889634);
+  a.sm_scale = p->sm_scale;
+  a.prule = make_rule(&p->pfmt);
+  a.nsplit = (N + 255) / 256;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_lse = a.ws_o + B * Hq * R * a.nsplit * 128;
+  a.out = out;
+  a.oB = os[0];
+  a.oH = os[1];
+  a.oN = os[2];
+  a.out_fp32 = p->out_fp32 ? 1 : 0;
+  a.lse = lse;
+  hipError_t e = launch_decode(p->pmode, a, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return MXATTN_E_UNSUPPORTED;
+  if (e != hipSuccess) return hip_fail(e, "mxattn_decode launch");
+  return MXATTN_OK;
+}
+
 int mxattn_fwd_plan(const int32_t* cu_host, int ndocs, int64_t N, int causal, void* workspace, size_t ws_bytes,
                     void* stream) {
   if (cu_host == nullptr || ndocs <= 0 || N < 0) return MXATTN_E_INVALID;

@@ -104,6 +104,28 @@ struct FwdArgs {
   const uint8_t* vks;
 };
 
+// split-key decode (decode.hip)
+struct DecArgs {
+  const uint8_t* q;   // Q codes [B][Hq][R][64 B], scales [B][Hq][R][4]
+  const uint8_t* qs;
+  const uint8_t* k;   // K codes [B][Hkv][N][64 B], scales [B][Hkv][N][4]
+  const uint8_t* ks;
+  const uint8_t* v;   // V^T codes [B][Hkv][128][np / 2], scales [B][Hkv][128][np / 32]
+  const uint8_t* vs;
+  int64_t B, Hq, Hkv, R, N, np;
+  const int32_t* kv_len;  // device [B] keys of each request, or null (N each)
+  float lambda, sm_scale;
+  E8m0Rule prule;
+  int64_t nsplit;  // splits of 256 keys of the longest history: ceil(N / 256)
+  float* ws_o;     // [B][Hq][R][nsplit][128] normalized split outputs
+  float* ws_lse;   // [B][Hq][R][nsplit]
+  void* out;       // [B][Hq][R][128] with element strides oB, oH, oN
+  int64_t oB, oH, oN;
+  int out_fp32;
+  float* lse;      // [B][Hq][R] or null
+};
+hipError_t launch_decode(int pmode, const DecArgs& a, hipStream_t st);
+
 // psc: P block scale (SCALE_E8M0 -> blocks of 32, SCALE_E4M3 -> blocks of 16);
 // vsc: V block scale (same meaning).
 hipError_t launch_fwd(int qk, int pv, int pmode, int psc, int vsc, const FwdArgs& a, hipStream_t st);

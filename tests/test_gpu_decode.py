@@ -1,0 +1,88 @@
+"""GPU split-key decode (mxattn_decode) against the oracle's split decode ("MpFA ...",
+section 5.3): the same quantized bytes, splits of 256 keys merged by log-sum-exp,
+|dO| <= 2e-3 max|O| + the merged flip budget; ragged histories, several newest rows,
+packed GQA groups, and a 32:8 GQA decode over 32K keys."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import (PM_ORACLE, TOL, gpu_available, gpu_codes_qk, gpu_codes_v, oracle_quant_qk, oracle_quant_v)
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+FMT = {"direct": ("mxfp4", "mxfp4"), "pnq": ("mxfp4_uos", "mxfp4_uos"), "two_level": ("mxfp4", "mxfp4")}
+
+
+def _bf16(shape, seed, stream, shift=0.0):
+    x = synth.gaussian(seed, stream, shape) + np.float32(shift)
+    return synth.f32_to_bf16(x.astype(np.float32))
+
+
+def run_decode(pm, B, Hq, Hkv, R, N, kv_len, seed):
+    import torch
+    import microscaling_fp4_attention_amd as mx
+    qf_, vf_ = FMT[pm]
+    q, k, v = _bf16((B, Hq, R, 128), seed, 1), _bf16((B, Hkv, N, 128), seed, 2, 0.3), _bf16((B, Hkv, N, 128), seed, 3)
+    dev = "cuda:0"
+    t = {n: torch.from_numpy(a.astype(np.int16)).view(torch.bfloat16).to(dev) for n, a in (("q", q), ("k", k), ("v", v))}
+    Q = mx.quantize(t["q"], mx.ROLE_QK, qf_)
+    K = mx.quantize(t["k"], mx.ROLE_QK, qf_)
+    V = mx.quantize(t["v"], mx.ROLE_V, vf_)
+    kl = None if kv_len is None else torch.tensor(kv_len, dtype=torch.int32, device=dev)
+    lse = torch.empty((B, Hq, R), dtype=torch.float32, device=dev)
+    out = mx.decode(Q, K, V, mx.fwd_params(pm, qf_, causal=True, out_fp32=True), kv_len=kl, lse=lse)
+    torch.cuda.synchronize()
+    qc, qs, qd = oracle_quant_qk(synth.bf16_to_f32(q), qf_)
+    kc, ks, kd = oracle_quant_qk(synth.bf16_to_f32(k), qf_)
+    vc, vs, vd = oracle_quant_v(synth.bf16_to_f32(v), vf_)
+    assert np.array_equal(gpu_codes_qk(Q), qc) and np.array_equal(gpu_codes_qk(K), kc)
+    gc, gs = gpu_codes_v(V, N, None)
+    assert np.array_equal(gc, vc) and np.array_equal(gs, vs)
+    kvl = np.full(B, N, np.int32) if kv_len is None else np.asarray(kv_len, np.int32)
+    O_ref, lse_ref, fb = oracle.decode(qd, kd, vd, kvl, PM_ORACLE[pm], qf_, split=256)
+    O_gpu = out.cpu().numpy()
+    bound = TOL * np.abs(O_ref).max() + fb[..., None]
+    ratio = float((np.abs(O_gpu - O_ref) / bound).max())
+    lse_err = float(np.abs(lse.cpu().numpy() - lse_ref).max())
+    print(f"decode {pm} B{B} Hq{Hq} Hkv{Hkv} R{R} N{N}: max |dO|/bound {ratio:.3f}, |dlse| {lse_err:.2e}")
+    assert np.all(np.isfinite(O_gpu))
+    assert ratio <= 1.0
+    assert lse_err <= 1e-3 * max(1.0, float(np.abs(lse_ref).max()))
+
+
+@pytest.mark.parametrize("pm", ["direct", "pnq", "two_level"])
+def test_decode_ragged(pm):
+    run_decode(pm, B=2, Hq=8, Hkv=2, R=1, N=700, kv_len=[700, 333], seed=61)
+
+
+@pytest.mark.parametrize("R", [4, 8])
+def test_decode_several_rows(R):
+    """R newest rows per request with a causal mask among them; 4 x 8 fills all 32 columns"""
+    run_decode("pnq", B=1, Hq=4, Hkv=1, R=R, N=1300, kv_len=None, seed=62)
+
+
+def test_decode_minimal_history():
+    run_decode("direct", B=3, Hq=2, Hkv=2, R=2, N=260, kv_len=[2, 130, 257], seed=63)
+
+
+def test_decode_gqa_32_8_long():
+    run_decode("two_level", B=1, Hq=32, Hkv=8, R=1, N=32768, kv_len=None, seed=64)
+
+
+def test_decode_refused():
+    import torch
+    import microscaling_fp4_attention_amd as mx
+    dev = "cuda:0"
+    q = torch.from_numpy(_bf16((1, 8, 5, 128), 65, 1).astype(np.int16)).view(torch.bfloat16).to(dev)
+    k = torch.from_numpy(_bf16((1, 1, 300, 128), 65, 2).astype(np.int16)).view(torch.bfloat16).to(dev)
+    Q = mx.quantize(q, mx.ROLE_QK, "mxfp4")
+    K = mx.quantize(k, mx.ROLE_QK, "mxfp4")
+    V = mx.quantize(k, mx.ROLE_V, "mxfp4")
+    with pytest.raises(mx.MxattnError) as e:  # 8 heads x 5 rows > 32 columns
+        mx.decode(Q, K, V, mx.fwd_params("direct", "mxfp4", causal=True))
+    assert e.value.status == -2
+    Q1 = mx.quantize(q[:, :1], mx.ROLE_QK, "mxfp4")
+    with pytest.raises(mx.MxattnError):  # decode rows are the newest tokens: causal only
+        mx.decode(Q1, K, V, mx.fwd_params("direct", "mxfp4", causal=False))
+    torch.cuda.synchronize()
