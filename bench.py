@@ -127,6 +127,61 @@ def cpu_baseline(wl, x, qf, vf, pm, pf, causal, doc_off, budget_s=12.0):
                       f"Q, K and V ({t_quant:.1f} s); value = counted FLOP of those rows / attention time"}
 
 
+def bench_decode(args, torch, mx):
+    """Split-key decode step: quantize the new tokens' Q, then mxattn_decode over the cached,
+    already quantized history.  Inputs are seeded normal bf16 drawn on the device."""
+    B, Hq, Hkv, R, N = 4, 32, 8, 1, args.decode
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    q = torch.randn((B, Hq, R, 128), generator=g, device=dev).to(torch.bfloat16)
+    k = torch.randn((B, Hkv, N, 128), generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, N, 128), generator=g, device=dev).to(torch.bfloat16)
+    K = mx.quantize(k, mx.ROLE_QK, "mxfp4")
+    V = mx.quantize(v, mx.ROLE_V, "mxfp4")
+    del k, v
+    params = mx.fwd_params("two_level", "mxfp4", causal=True, out_fp32=False)
+    out = torch.empty((B, Hq, R, 128), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(mx.decode_workspace_bytes(B, Hq, R, N), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = []
+
+    def step(record):
+        Q = mx.quantize(q, mx.ROLE_QK, "mxfp4")
+        if record:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        mx.decode(Q, K, V, params, out=out, workspace=ws)
+        if record:
+            e1.record(stream)
+            ev.append((e0, e1))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(args.steps):
+        step(True)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    t_step = g0.elapsed_time(g1) / 1e3 / args.steps
+    t_dec = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    hist = K.codes.numel() + K.scales.numel() + V.codes.numel() + V.scales.numel()  # history bytes read once
+    gbs = hist / t_dec / 1e9
+    res = {"metric": "decode: quantized KV history read per second (GB/s), split-key MXFP4 decode",
+           "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(t_step * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "mxfp4", "data": "synthetic (seeded normal bf16 drawn on the device)",
+           "config": {"workload": f"decode: B{B} Hq{Hq} Hkv{Hkv} R{R} history {N} keys, MXFP4 K/V/Q, two-level P, "
+                                  "splits of 256 keys", "history_bytes": hist},
+           "t_decode_ms": round(t_dec * 1e3, 4),
+           "tokens_per_s": round(B * R / t_step, 1),
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                        "frac": round(gbs / 8000.0, 4), "traffic": None, "kernel": "split-key decode (mxattn_decode)"}}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -135,6 +190,15 @@ def main():
     ap.add_argument("--config", default="c3", choices=sorted(CONFIGS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--preproc", default="none", choices=["none", "smoothk", "center", "hadamard", "center+hadamard"],
+                    help="outlier pre-processing of Q and K inside the step: smooth-K (K mean), sequence centering "
+                         "with the compensation bias, and/or the normalized Hadamard rotation")
+    ap.add_argument("--causal-safe", action="store_true",
+                    help="causally safe V scales: quantize the per-key form of V in the step and use it on each "
+                         "row's diagonal tile (causal workloads with a 4-bit V)")
+    ap.add_argument("--decode", type=int, default=0, metavar="N",
+                    help="time the split-key decode instead: 4 requests, GQA 32:8, one new token each over an "
+                         "N-key MXFP4 history (HBM-bound; reports the history bytes read per second)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -157,7 +221,15 @@ def main():
         print(json.dumps({"copy_bytes": n, "launches": 3}))
         return
 
+    if args.decode:
+        bench_decode(args, torch, mx)
+        return
+
     name, qf, vf, pm, pf, desc = CONFIGS[args.config]
+    if args.causal_safe and (vf == "fp8v" or args.config in ("c1", "c2", "c3")):
+        print("--causal-safe applies to the causal workloads with a 4-bit V (c5); an FP8 V is made safe by its "
+              "round-up exponents", file=sys.stderr)
+        sys.exit(2)
     log = (lambda *a: None) if args.quiet else (lambda *a: print(*a, file=sys.stderr, flush=True))
     t0 = time.time()
     x = synth.workload(name)
@@ -172,6 +244,9 @@ def main():
     q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
     cu = None if doc_off is None else torch.from_numpy(doc_off.astype(np.int32)).to(dev)
     params = mx.fwd_params(pm, pf, causal=causal, out_fp32=False)
+    center = args.preproc.startswith("center")
+    smoothk = args.preproc == "smoothk"
+    had = args.preproc.endswith("hadamard")
     ws, nd = None, 0
     if doc_off is not None:
         ws = mx.fwd_plan(doc_off, N, causal)
@@ -182,14 +257,27 @@ def main():
     ev = []
 
     def step(record):
-        Q = mx.quantize(q, mx.ROLE_QK, qf)
-        K = mx.quantize(k, mx.ROLE_QK, qf)
+        p = params
+        if args.preproc == "none":
+            Q = mx.quantize(q, mx.ROLE_QK, qf)
+            K = mx.quantize(k, mx.ROLE_QK, qf)
+        else:
+            qm = mx.channel_mean(q, cu) if center else None
+            km = mx.channel_mean(k, cu) if (center or smoothk) else None
+            Q = mx.quantize(q, mx.ROLE_QK, qf, cu_seqlens=cu, mean=qm, hadamard=had)
+            K = mx.quantize(k, mx.ROLE_QK, qf, cu_seqlens=cu, mean=km, hadamard=had)
+            if center:
+                p = mx.fwd_params(pm, pf, causal=causal, out_fp32=False, score_bias=mx.center_comp(qm, k, km, cu))
         V = mx.quantize(v, mx.ROLE_V, vf, cu_seqlens=cu)
+        if args.causal_safe:
+            Vk = mx.quantize(v, mx.ROLE_VKEY, vf, cu_seqlens=cu)
+            p = mx.fwd_params(pm, pf, causal=causal, out_fp32=False, score_bias=getattr(p, "_score_bias_ref", None),
+                              vkey=Vk)
         if record:
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-        mx.fwd(Q, K, V, params, out=out, workspace=ws, ndocs=nd)
+        mx.fwd(Q, K, V, p, out=out, workspace=ws, ndocs=nd)
         if record:
             e1.record(stream)
             ev.append((e0, e1))
@@ -228,12 +316,13 @@ def main():
         "dtype": "mxfp4" if qf.startswith("mxfp4") else "nvfp4+fp8" if pm == "fp8" else "nvfp4",
         "data": "synthetic (seeded SplitMix64/Box-Muller bf16 tensors of the workload's shape and structure)",
         "config": {"workload": f"{name}: {desc}", "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": 128,
-                   "causal": bool(causal), "ndocs": nd, "counted_flop": flop},
+                   "causal": bool(causal), "ndocs": nd, "preproc": args.preproc,
+                   "causal_safe_v": bool(args.causal_safe), "counted_flop": flop},
         "pct_fp4_peak": round(100.0 * tops / FP4_PEAK_TFLOPS, 2),
         "t_fwd_ms": round(t_fwd * 1e3, 4),
-        "t_quant_ms": round((t_step - t_fwd) * 1e3, 4),
+        "t_quant_ms": round((t_step - t_fwd) * 1e3, 4),  # quantization and any pre-processing
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(fwd_tflops / peak, 4), "traffic": profiled_traffic(args.config),
+                     "frac": round(fwd_tflops / peak, 4), "traffic": profiled_traffic(args.config) if args.preproc == "none" and not args.causal_safe else None,
                      "kernel": "attention forward (mxattn_fwd)"},
     }
     if not args.no_cpu:

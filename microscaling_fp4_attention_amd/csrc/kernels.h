@@ -116,8 +116,8 @@ struct DecArgs {
   const int32_t* kv_len;  // device [B] keys of each request, or null (N each)
   float lambda, sm_scale;
   E8m0Rule prule;
-  int64_t nsplit;  // splits of 256 keys of the longest history: ceil(N / 256)
-  float* ws_o;     // [B][Hq][R][nsplit][128] normalized split outputs
+  int64_t nsplit;  // 1024-key chunks of the longest history: ceil(N / 1024)
+  float* ws_o;     // [B][Hq][R][nsplit][128] normalized chunk outputs (4 splits merged)
   float* ws_lse;   // [B][Hq][R][nsplit]
   void* out;       // [B][Hq][R][128] with element strides oB, oH, oN
   int64_t oB, oH, oN;
