@@ -20,6 +20,8 @@ ELEM_E2M1, ELEM_E4M3 = 0, 1
 SCALE_E8M0, SCALE_E4M3 = 0, 1
 RULE_OCP, RULE_CEIL = 0, 1
 P_NONE, P_DIRECT, P_TWO_LEVEL, P_PNQ, P_FP8_FIXED = 0, 1, 2, 3, 4
+EXP_EXACT, EXP_MITCHELL, EXP_SCHRAUDOLPH = 0, 1, 2
+EXP_MODES = {"exact": EXP_EXACT, "mitchell": EXP_MITCHELL, "schraudolph": EXP_SCHRAUDOLPH}
 
 
 class Fmt(ctypes.Structure):
@@ -29,7 +31,7 @@ class Fmt(ctypes.Structure):
 
 class AttnParams(ctypes.Structure):
     _fields_ = [("pmode", ctypes.c_int), ("pfmt", Fmt), ("causal", ctypes.c_int),
-                ("sm_scale", ctypes.c_float), ("kv_tile", ctypes.c_int)]
+                ("sm_scale", ctypes.c_float), ("kv_tile", ctypes.c_int), ("exp_mode", ctypes.c_int)]
 
 
 # named formats (the presets of the pages)
@@ -205,10 +207,11 @@ def dequant_cols(codes, scales, f, doc_off=None):
 
 
 def attention(Q, K, V, pmode, pfmt=None, causal=False, sm_scale=None, kv_tile=128, doc_off=None,
-              rows=None, bias=None, vkey=None, vkey_exp=None):
+              rows=None, bias=None, vkey=None, vkey_exp=None, exp_mode="exact"):
     """Q [B,Hq,N,d], K/V [B,Hkv,N,d] float32 (dequantized); bias: None or float32 [B,Hq,N]
     added to each key's scores; vkey [B,Hkv,N,d] / vkey_exp [B,Hkv,N]: the per-key form
-    of V used on each row's diagonal tile (causal only).  Returns (O [nrows,d], lse, fb)."""
+    of V used on each row's diagonal tile (causal only); exp_mode: "exact", "mitchell"
+    or "schraudolph" (the exponential of P~).  Returns (O [nrows,d], lse, fb)."""
     Q = np.ascontiguousarray(Q, dtype=np.float32)
     K = np.ascontiguousarray(K, dtype=np.float32)
     V = np.ascontiguousarray(V, dtype=np.float32)
@@ -217,7 +220,7 @@ def attention(Q, K, V, pmode, pfmt=None, causal=False, sm_scale=None, kv_tile=12
     if sm_scale is None:
         sm_scale = 1.0 / np.sqrt(d)
     pf = fmt(pfmt) if pfmt is not None else Fmt(0, 0, 32, 0, 0.0)
-    p = AttnParams(pmode, pf, int(bool(causal)), float(sm_scale), kv_tile)
+    p = AttnParams(pmode, pf, int(bool(causal)), float(sm_scale), kv_tile, EXP_MODES[exp_mode])
     r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
     nrows = B * Hq * N if r is None else len(r)
     O = np.zeros((nrows, d), dtype=np.float32)
@@ -302,7 +305,7 @@ def e2m1_values(codes):
 
 
 # ---- decode with split keys ----
-def decode(Q, K, V, kv_len, pmode, pfmt=None, split=256, sm_scale=None, kv_tile=128):
+def decode(Q, K, V, kv_len, pmode, pfmt=None, split=256, sm_scale=None, kv_tile=128, exp_mode="exact"):
     """Q [B,Hq,R,d] (the R newest tokens), K/V [B,Hkv,N,d] dequantized float32, kv_len [B]:
     split-key decode merged by log-sum-exp.  Returns (O [B,Hq,R,d], lse [B,Hq,R], fb [B,Hq,R])."""
     Q = np.ascontiguousarray(Q, dtype=np.float32)
@@ -313,7 +316,7 @@ def decode(Q, K, V, kv_len, pmode, pfmt=None, split=256, sm_scale=None, kv_tile=
     if sm_scale is None:
         sm_scale = 1.0 / np.sqrt(d)
     pf = fmt(pfmt) if pfmt is not None else Fmt(0, 0, 32, 0, 0.0)
-    p = AttnParams(pmode, pf, 1, float(sm_scale), kv_tile)
+    p = AttnParams(pmode, pf, 1, float(sm_scale), kv_tile, EXP_MODES[exp_mode])
     kl = np.ascontiguousarray(kv_len, dtype=np.int32)
     O = np.zeros((B, Hq, R, d), np.float32)
     lse = np.zeros((B, Hq, R), np.float32)
@@ -324,3 +327,18 @@ def decode(Q, K, V, kv_len, pmode, pfmt=None, split=256, sm_scale=None, kv_tile=
     if rc != 0:
         raise ValueError(f"orc_decode failed with {rc}")
     return O, lse, fb
+
+
+# ---- bit-level exponentials ----
+def exp2_bits(t):
+    """Mitchell's piecewise-linear 2^t read from a float's bits, with the clamp (orc_exp2_bits)."""
+    f = lib().orc_exp2_bits
+    f.restype, f.argtypes = ctypes.c_double, [ctypes.c_double]
+    return np.array([f(float(v)) for v in np.ravel(t)], np.float64).reshape(np.shape(t))
+
+
+def exp_offset(mode):
+    """the offset delta of a bit-level mode ("mitchell", "schraudolph"; 0 for "exact")"""
+    f = lib().orc_exp_offset
+    f.restype, f.argtypes = ctypes.c_double, [ctypes.c_int]
+    return f(EXP_MODES[mode])

@@ -296,6 +296,43 @@ static void p_block(const float* x, int n, const orc_fmt* f, double* deq, double
 }
 
 /* ------------------------------------------------------------------------ */
+/* Bit-level exponentials ([FLAMIA] section 3.7 and appendix C, after       */
+/* Mitchell 1962 and Schraudolph 1999).  A positive float read as an        */
+/* integer is 2^23 (e + 127) + mantissa, so the integer 2^23 (t + 127)      */
+/* puts floor(t) in the exponent field and the fraction of t in the         */
+/* mantissa: the float it spells is 2^floor(t) (1 + frac t).  With the      */
+/* exponent field at zero (t < -126) the same bits spell the subnormal      */
+/* (t + 127) 2^-126; a negative pattern is clamped to +0.                   */
+/* ------------------------------------------------------------------------ */
+double orc_exp2_bits(double t) {
+  double n;
+  if (!(t >= -127.0)) return 0.0; /* the clamp; NaN and -inf too */
+  if (t < -126.0) return ldexp(t + 127.0, -126);
+  n = floor(t);
+  return ldexp(1.0 + (t - n), (int)n);
+}
+
+/* Over one octave the line's ratio to 2^t is r(f) = (1 + f) 2^-f, f = frac t.
+ * log2 r(f) = log2(1 + f) - f is 0 at both ends and largest at f = 1/ln2 - 1,
+ * where it is E = log2(1/ln2) - 1/ln2 + 1 (about 0.0861).
+ *   Mitchell-P: the offset centres the error, delta = E/2, so log2 of the ratio
+ *   lies in [-E/2, E/2].
+ *   Schraudolph: the offset makes the ratio average one over f in [0, 1); the
+ *   integral of (1 + f) 2^-f over [0, 1] is 1/(2 ln^2 2), so delta = log2 of it. */
+double orc_exp_offset(int exp_mode) {
+  const double ln2 = log(2.0);
+  if (exp_mode == ORC_EXP_MITCHELL) return 0.5 * (log2(1.0 / ln2) - 1.0 / ln2 + 1.0);
+  if (exp_mode == ORC_EXP_SCHRAUDOLPH) return log2(1.0 / (2.0 * ln2 * ln2));
+  return 0.0;
+}
+
+/* P~ of a score at x = sm_scale (s - m) nats below the running maximum */
+static float p_exp(const orc_attn_params* p, double x) {
+  if (p->exp_mode == ORC_EXP_EXACT) return (float)exp(x);
+  return (float)orc_exp2_bits(x / log(2.0) - orc_exp_offset(p->exp_mode));
+}
+
+/* ------------------------------------------------------------------------ */
 /* Attention for one query row: FlashAttention-2 form of the online softmax */
 /* ([MXA] section 2 and Algorithm 1; [MPFA] Eqs. 3-6), with the P          */
 /* quantization of the chosen mode applied to each tile's unnormalised     */
@@ -359,7 +396,7 @@ static int attn_row_bias(const float* q, const float* K, const float* V, const f
     mnew = m > mt ? m : mt;
     alpha = (m == -INFINITY) ? 0.0f : (float)exp((double)p->sm_scale * ((double)m - (double)mnew));
     for (int j = 0; j < tl; j++)
-      pt[j] = (s[j] == -INFINITY) ? 0.0f : (float)exp((double)p->sm_scale * ((double)s[j] - (double)mnew));
+      pt[j] = (s[j] == -INFINITY) ? 0.0f : p_exp(p, (double)p->sm_scale * ((double)s[j] - (double)mnew));
     /* per-key fold of the diagonal tile: the quantizer sees P' = P~ 2^ek */
     const int fold = Vk != NULL && t0 == diag_t0;
     float* pq = pt;
@@ -481,6 +518,7 @@ int orc_attention_ex(const float* Q, const float* K, const float* V, const float
                      double* fb) {
   int64_t total = (int64_t)B * Hq * N;
   if (Vk && !p->causal) return -3; /* the per-key form serves causal diagonal tiles */
+  if (p->exp_mode < ORC_EXP_EXACT || p->exp_mode > ORC_EXP_SCHRAUDOLPH) return -4;
   if (!rows) nrows = total;
   if (doc_off && ndocs > 0 && B != 1) return -1;
   for (int64_t idx = 0; idx < nrows; idx++) {
@@ -595,6 +633,7 @@ int orc_decode(const float* Q, const float* K, const float* V, int B, int Hq, in
                int d, const int* kv_len, int split, const orc_attn_params* p, float* O, float* lse,
                double* fb) {
   if (split <= 0 || split % p->kv_tile != 0 || !p->causal) return -1;
+  if (p->exp_mode < ORC_EXP_EXACT || p->exp_mode > ORC_EXP_SCHRAUDOLPH) return -4;
   float* os = (float*)malloc(sizeof(float) * (size_t)d);
   double* acc = (double*)malloc(sizeof(double) * (size_t)d);
   for (int b = 0; b < B; b++) {

@@ -21,7 +21,8 @@
  *   - dot products: exact products of dequantized values summed in double, then
  *     rounded once to float;
  *   - exponentials: exp() in double of sm_scale*(s - m) formed in double from
- *     float operands, rounded once to float;
+ *     float operands, rounded once to float (the bit-level modes take the exact
+ *     piecewise-linear value of the same argument instead);
  *   - divisions x/scale, M/6, P/s1, 448*P: single float operations.
  *
  * Parity status of every function is recorded next to it ("pinned by ..." names
@@ -59,13 +60,33 @@ typedef struct {
   float qmax;  /* CEIL rule boundary: 6, 7.25, 448, ...       */
 } orc_fmt;
 
+/* the exponential that turns scores into P~ ([FLAMIA] section 3.7, appendix C) */
+enum {
+  ORC_EXP_EXACT = 0,      /* exp() in double, rounded to float                 */
+  ORC_EXP_MITCHELL = 1,   /* Mitchell's line, error centred (Mitchell-P)       */
+  ORC_EXP_SCHRAUDOLPH = 2 /* the same line, ratio to exp averaging one         */
+};
+
 typedef struct {
   int pmode;      /* ORC_P_*                                       */
   orc_fmt pfmt;   /* block format of P (DIRECT, TWO_LEVEL, PNQ)     */
   int causal;     /* key j visible to query i iff j <= i            */
   float sm_scale; /* 1/sqrt(d)                                      */
   int kv_tile;    /* keys per online-softmax step                   */
+  int exp_mode;   /* ORC_EXP_*: the exponential of P~ (the rescale  */
+                  /* factor between tiles stays exact)              */
 } orc_attn_params;
+
+/* ---- bit-level exponentials ([FLAMIA] section 3.7, appendix C) ----
+ * orc_exp2_bits(t): the value whose float bits are 2^23 (t + 127) read as an
+ * integer -- Mitchell's piecewise-linear 2^t = 2^floor(t) (1 + t - floor(t)) for
+ * t >= -126, continued by the subnormal line (t + 127) 2^-126 down to 0 at t = -127,
+ * and 0 below (the clamp) and for NaN.  Exact real arithmetic in double.
+ * orc_exp_offset(mode): delta subtracted from t before the line (0 for EXACT):
+ * Mitchell-P centres log2 of the line's ratio to 2^t, Schraudolph's form makes
+ * that ratio average one over an octave.  Pinned by tests/test_oracle_bitexp.py. */
+double orc_exp2_bits(double t);
+double orc_exp_offset(int exp_mode);
 
 /* ---- formats ---- */
 double orc_e2m1_value(int code);            /* code: sign<<3 | magnitude index     */
