@@ -34,13 +34,19 @@ FP4_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 MFMA
 # SHA-256 of the kernel source they were taken on (None when absent or stale)
 TRAFFIC_FILES = {"c3": "profiles/fwd_pp_kernel_c3_video_dit_32k_traffic.txt",
                  "c4": "profiles/fwd_pp_kernel_c4_gqa_causal_32k_traffic.txt"}
-KERNEL_SOURCE = "microscaling_fp4_attention_amd/csrc/fwd.hip"
+# the forward kernel's source: the kernel file and the headers it includes
+KERNEL_SOURCES = ["microscaling_fp4_attention_amd/csrc/fwd.hip", "microscaling_fp4_attention_amd/csrc/device_util.h",
+                  "microscaling_fp4_attention_amd/csrc/formats.h", "microscaling_fp4_attention_amd/csrc/kernels.h"]
 
 
 def kernel_source_sha256():
+    """SHA-256 over the forward kernel's source files, in KERNEL_SOURCES order"""
     import hashlib
-    with open(os.path.join(ROOT, KERNEL_SOURCE), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def profiled_traffic(cfg):
@@ -87,7 +93,7 @@ def counted_flop(B, H, N, d, causal, doc_off):
     return 4.0 * B * H * N * N * d
 
 
-def cpu_baseline(wl, x, qf, vf, pm, pf, causal, doc_off, budget_s=12.0):
+def cpu_baseline(wl, x, qf, vf, pm, pf, causal, doc_off, budget_s=12.0, exp_mode="exact"):
     """The oracle (single-threaded C) on a bounded sample: quantize one KV head
     and run the attention of sampled query rows of one query head."""
     import oracle
@@ -110,7 +116,7 @@ def cpu_baseline(wl, x, qf, vf, pm, pf, causal, doc_off, budget_s=12.0):
     while done < len(rows_all) and t_att < budget_s:
         r = rows_all[done:done + per]
         t0 = time.perf_counter()
-        oracle.attention(qd, kd, vd, PM_ORACLE[pm], pf, causal=causal, doc_off=doc_off, rows=r)
+        oracle.attention(qd, kd, vd, PM_ORACLE[pm], pf, causal=causal, doc_off=doc_off, rows=r, exp_mode=exp_mode)
         t_att += time.perf_counter() - t0
         for i in r:
             if doc_off is not None:
@@ -196,6 +202,9 @@ def main():
     ap.add_argument("--causal-safe", action="store_true",
                     help="causally safe V scales: quantize the per-key form of V in the step and use it on each "
                          "row's diagonal tile (causal workloads with a 4-bit V)")
+    ap.add_argument("--exp", default="exact", choices=["exact", "mitchell", "schraudolph"],
+                    help="exponential of P~: exact (hardware exp), or the bit-level Mitchell-P / Schraudolph "
+                         "approximations for inference (ping-pong kernel routes)")
     ap.add_argument("--decode", type=int, default=0, metavar="N",
                     help="time the split-key decode instead: 4 requests, GQA 32:8, one new token each over an "
                          "N-key MXFP4 history (HBM-bound; reports the history bytes read per second)")
@@ -243,7 +252,7 @@ def main():
 
     q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
     cu = None if doc_off is None else torch.from_numpy(doc_off.astype(np.int32)).to(dev)
-    params = mx.fwd_params(pm, pf, causal=causal, out_fp32=False)
+    params = mx.fwd_params(pm, pf, causal=causal, out_fp32=False, exp_mode=args.exp)
     center = args.preproc.startswith("center")
     smoothk = args.preproc == "smoothk"
     had = args.preproc.endswith("hadamard")
@@ -267,12 +276,13 @@ def main():
             Q = mx.quantize(q, mx.ROLE_QK, qf, cu_seqlens=cu, mean=qm, hadamard=had)
             K = mx.quantize(k, mx.ROLE_QK, qf, cu_seqlens=cu, mean=km, hadamard=had)
             if center:
-                p = mx.fwd_params(pm, pf, causal=causal, out_fp32=False, score_bias=mx.center_comp(qm, k, km, cu))
+                p = mx.fwd_params(pm, pf, causal=causal, out_fp32=False, score_bias=mx.center_comp(qm, k, km, cu),
+                                  exp_mode=args.exp)
         V = mx.quantize(v, mx.ROLE_V, vf, cu_seqlens=cu)
         if args.causal_safe:
             Vk = mx.quantize(v, mx.ROLE_VKEY, vf, cu_seqlens=cu)
             p = mx.fwd_params(pm, pf, causal=causal, out_fp32=False, score_bias=getattr(p, "_score_bias_ref", None),
-                              vkey=Vk)
+                              vkey=Vk, exp_mode=args.exp)
         if record:
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
@@ -317,17 +327,19 @@ def main():
         "data": "synthetic (seeded SplitMix64/Box-Muller bf16 tensors of the workload's shape and structure)",
         "config": {"workload": f"{name}: {desc}", "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": 128,
                    "causal": bool(causal), "ndocs": nd, "preproc": args.preproc,
-                   "causal_safe_v": bool(args.causal_safe), "counted_flop": flop},
+                   "causal_safe_v": bool(args.causal_safe), "exp": args.exp, "counted_flop": flop},
         "pct_fp4_peak": round(100.0 * tops / FP4_PEAK_TFLOPS, 2),
         "t_fwd_ms": round(t_fwd * 1e3, 4),
         "t_quant_ms": round((t_step - t_fwd) * 1e3, 4),  # quantization and any pre-processing
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(fwd_tflops / peak, 4), "traffic": profiled_traffic(args.config) if args.preproc == "none" and not args.causal_safe else None,
+                     "frac": round(fwd_tflops / peak, 4),
+                     "traffic": profiled_traffic(args.config)
+                     if args.preproc == "none" and not args.causal_safe and args.exp == "exact" else None,
                      "kernel": "attention forward (mxattn_fwd)"},
     }
     if not args.no_cpu:
         log("[bench] timing the CPU oracle on a bounded sample")
-        res["cpu_baseline"] = cpu_baseline(x, x, qf, vf, pm, pf, causal, doc_off)
+        res["cpu_baseline"] = cpu_baseline(x, x, qf, vf, pm, pf, causal, doc_off, exp_mode=args.exp)
     print(json.dumps(res), flush=True)
 
 

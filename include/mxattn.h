@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MXATTN_ABI_VERSION 3
+#define MXATTN_ABI_VERSION 4
 
 typedef enum {
   MXATTN_OK = 0,
@@ -91,6 +91,22 @@ typedef enum {
   MXATTN_P_PNQ = 3,       /* P^ = phi(P~) feeds both l and O                         */
   MXATTN_P_FP8_FIXED = 4  /* c = E4M3(448 P~), O += c V / 448; l from P~             */
 } mxattn_pmode;
+
+/* the exponential that turns scores into P~ ("FLAMIA" section 3.7 and appendix C).
+ * The bit-level modes write t = sm_scale (s - m) / ln 2 - delta in fixed point into
+ * the exponent and mantissa fields of a float, which is Mitchell's piecewise-linear
+ * 2^floor(t) (1 + frac t); below t = -127 the result is 0.  The rescale of the
+ * running sums when the row maximum moves stays exact.  They serve inference: the
+ * result is an approximation of softmax by a few per cent per weight. */
+typedef enum {
+  MXATTN_EXP_EXACT = 0,      /* hardware exponential (v_exp_f32)                       */
+  MXATTN_EXP_MITCHELL = 1,   /* Mitchell-P: delta = E/2 centres log2 of the line's ratio
+                                to 2^t, E = log2(1/ln 2) - 1/ln 2 + 1 (ratio within
+                                about +-3 %); meant for 4-bit P                          */
+  MXATTN_EXP_SCHRAUDOLPH = 2 /* Schraudolph's form: delta = log2(1 / (2 ln^2 2)) makes the
+                                ratio average one over an octave (no mean bias in the
+                                row sum); meant for FP8 P                                */
+} mxattn_exp_mode;
 
 /* a block format */
 typedef struct {
@@ -145,6 +161,8 @@ typedef struct {
                         tile uses v.  Needs a causal mask and a V in E2M1 with E8M0
                         scales per 32 keys (an FP8 V with round-up exponents needs no
                         per-key form).                                                 */
+  int32_t exp_mode; /* mxattn_exp_mode.  The bit-level modes need a V with E8M0 scales
+                       per 32 keys (E2M1 or E4M3) and are refused by mxattn_decode() */
 } mxattn_fwd_params;
 
 /* ABI version (MXATTN_ABI_VERSION of the built library). */

@@ -24,9 +24,10 @@ SCALE_E8M0, SCALE_E4M3 = 0, 1
 RULE_OCP, RULE_CEIL = 0, 1
 ROLE_QK, ROLE_V, ROLE_VKEY = 0, 1, 2
 P_DIRECT, P_TWO_LEVEL, P_PNQ, P_FP8_FIXED = 1, 2, 3, 4
+EXP_EXACT, EXP_MITCHELL, EXP_SCHRAUDOLPH = 0, 1, 2
 
 
-ABI_VERSION = 3  # MXATTN_ABI_VERSION of include/mxattn.h
+ABI_VERSION = 4  # MXATTN_ABI_VERSION of include/mxattn.h
 
 
 class QFmt(ctypes.Structure):
@@ -43,7 +44,7 @@ class QTensorC(ctypes.Structure):
 class FwdParams(ctypes.Structure):
     _fields_ = [("pmode", ctypes.c_int32), ("pfmt", QFmt), ("causal", ctypes.c_int32), ("sm_scale", ctypes.c_float),
                 ("kv_tile", ctypes.c_int32), ("out_fp32", ctypes.c_int32), ("score_bias", ctypes.c_void_p),
-                ("vkey", ctypes.c_void_p)]
+                ("vkey", ctypes.c_void_p), ("exp_mode", ctypes.c_int32)]
 
 
 class PreProc(ctypes.Structure):
@@ -59,6 +60,7 @@ FORMATS = {
     "fp8v": (ELEM_E4M3, SCALE_E8M0, 32, RULE_CEIL, 448.0),      # E4M3 values, E8M0 per 32, round up
 }
 PMODES = {"direct": P_DIRECT, "two_level": P_TWO_LEVEL, "pnq": P_PNQ, "fp8": P_FP8_FIXED}
+EXP_MODES = {"exact": EXP_EXACT, "mitchell": EXP_MITCHELL, "schraudolph": EXP_SCHRAUDOLPH}
 
 
 def qfmt(f) -> QFmt:
@@ -279,11 +281,13 @@ def fwd_plan(cu_seqlens_host, N: int, causal: bool, device="cuda", stream=None) 
 
 
 def fwd_params(pmode, pfmt="mxfp4", causal=False, sm_scale=None, d=128, out_fp32=True, kv_tile=128,
-               score_bias: torch.Tensor | None = None, vkey: "QTensor | None" = None) -> FwdParams:
+               score_bias: torch.Tensor | None = None, vkey: "QTensor | None" = None,
+               exp_mode="exact") -> FwdParams:
     """score_bias: float32 device tensor [B, Hq, N] added to each key's scores (the
     centering compensation from center_comp), or None.  vkey: the role-VKEY quantization
     of the same V (causally safe V scales on the diagonal tiles), or None.  The params
-    keep references to both."""
+    keep references to both.  exp_mode: "exact", "mitchell" or "schraudolph" (the
+    exponential of P~; the bit-level ones are approximations for inference)."""
     pm = PMODES[pmode] if isinstance(pmode, str) else int(pmode)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
@@ -292,7 +296,8 @@ def fwd_params(pmode, pfmt="mxfp4", causal=False, sm_scale=None, d=128, out_fp32
         raise ValueError("score_bias must be a contiguous float32 tensor [B, Hq, N]")
     p = FwdParams(pm, pf, int(bool(causal)), float(sm_scale), kv_tile, int(bool(out_fp32)),
                   None if score_bias is None else score_bias.data_ptr(),
-                  None if vkey is None else ctypes.addressof(vkey.desc))
+                  None if vkey is None else ctypes.addressof(vkey.desc),
+                  EXP_MODES[exp_mode] if isinstance(exp_mode, str) else int(exp_mode))
     p._score_bias_ref = score_bias
     p._vkey_ref = vkey
     return p

@@ -61,6 +61,17 @@ __device__ __forceinline__ v16f mfma_bf16(v8bf a, v8bf b, v16f c) {
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Bit-level exponential ("FLAMIA" section 3.7 and appendix C): y = 2^23 (t + 127) in a
+// float; the float whose bits are the integer part of y is Mitchell's line
+// 2^floor(t) (1 + frac t) (a subnormal below t = -126).  The max clamps negative y,
+// -inf and NaN to 0 (a float-to-unsigned conversion of those is undefined); y stays
+// below 2^31 for the t < 129 this serves.  v_max_f32 + v_cvt_u32_f32.  (The convert
+// alone saturates the same way, but written as inline assembly it split the
+// scheduling regions of the exponential loop and made the kernel spill.)
+__device__ __forceinline__ float exp2_bits(float y) {
+  return __builtin_bit_cast(float, (uint32_t)__builtin_fmaxf(y, 0.0f));
+}
+
 // the other lane half's value (lanes q and q+32 hold the two halves of a row)
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
 

@@ -636,7 +636,7 @@ struct PpLds {
   static constexpr int BYTES = KEYR + (SAFE ? 2 * KEYT : 0);
 };
 
-template <int QK, int PV, int PMODE, int PSC, bool BIAS, bool SAFE>
+template <int QK, int PV, int PMODE, int PSC, bool BIAS, bool SAFE, bool EXPB>
 __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   static_assert(!SAFE || PV == PV_FP4 || PV == PV_BF16, "the per-key form serves a 4-bit V");
   using L = PpLds<QK, PV, BIAS, SAFE>;
@@ -699,6 +699,19 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   int nkt = (klen + 127) / 128;
   if (a.causal && nkt > 2 * (int)qt + 2) nkt = 2 * (int)qt + 2;
   const float lam = a.lambda;
+  // P~ of a score s given the row's exponent offset ms = m lambda and, for the bit-level
+  // exponential, cm = exp_bias - ms 2^23: one FMA and the hardware exponential, or one
+  // FMA (2^23 (s lambda - ms - delta + 127), its rounding keeps 16 fraction bits of t),
+  // a clamp and a convert.  Both are monotone in s, so the value at a block's largest
+  // score is the block's largest P~.
+  const float lamb = lam * 0x1p23f;
+  auto pexp = [&](float sc, float ms, float cm) __attribute__((always_inline)) -> float {
+    if constexpr (EXPB) return exp2_bits(__builtin_fmaf(sc, lamb, cm));
+    else return exp2_hw(__builtin_fmaf(sc, lam, -ms));
+  };
+  auto pexp_c = [&](float ms) __attribute__((always_inline)) -> float {
+    return EXPB ? __builtin_fmaf(-ms, 0x1p23f, a.exp_bias) : 0.0f;
+  };
 
   // ---------------- Q operand ----------------
   v8i qop[2];
@@ -971,7 +984,9 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   auto phase_v = [&](int t) __attribute__((always_inline)) {
     const float mnew = fmaxn(m, tmax);
     const float ms = mnew == NEG_INF ? 0.0f : mnew * lam;
-    // exactly 1 when the max did not move (keeps the rescale skip exact), 0 while m = -inf
+    const float cm = pexp_c(ms);
+    // exactly 1 when the max did not move (keeps the rescale skip exact), 0 while m = -inf;
+    // the rescale is exact in both exponential modes
     const float alpha = m == mnew ? 1.0f : exp2_hw(__builtin_fmaf(m, lam, -ms));
     m = mnew;
 
@@ -980,7 +995,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     // the running maximum adds nothing and keeps s1)
     float k1 = 1.0f, scale_o = alpha;
     if constexpr (PMODE == PM_TWO_LEVEL) {
-      float r = exp2_hw(__builtin_fmaf(tmax, lam, -ms));
+      float r = pexp(tmax, ms, cm);
       if (r >= 0x1p-64f) {
         float s1 = r / 2688.0f;
         k1 = 1.0f / s1;
@@ -1001,15 +1016,13 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     }
 
     // block scales of P from the block maxima of P~ (exponentials of the score maxima)
-    // (exp2_hw is monotone, so the exponential of a block's largest score is the
-    // block's largest P~)
     float sc16[4], sv16[4], ki16[4];  // per 16 keys: convert scale, dequant factor, multiplier
     int e[2] = {0, 0};
     if constexpr (PV == PV_FP4 || (PV == PV_BF16 && PSC == SCALE_E8M0)) {
 #pragma unroll
       for (int p = 0; p < 2; p++) {
         const float bm = fmaxn(bm16[2 * p], bm16[2 * p + 1]);
-        int x = e8m0_exp(exp2_hw(__builtin_fmaf(bm, lam, -ms)) * k1, a.prule);
+        int x = e8m0_exp(pexp(bm, ms, cm) * k1, a.prule);
         e[p] = x < -126 ? -126 : x;
         const float sc = u2f((uint32_t)(e[p] + 127) << 23);
         sc16[2 * p] = sc16[2 * p + 1] = sv16[2 * p] = sv16[2 * p + 1] = sc;
@@ -1019,7 +1032,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     } else if constexpr (PV == PV_BF16) {  // E4M3 scale per 16 keys
 #pragma unroll
       for (int bb = 0; bb < 4; bb++) {
-        const float pm = exp2_hw(__builtin_fmaf(bm16[bb], lam, -ms)) * k1;
+        const float pm = pexp(bm16[bb], ms, cm) * k1;
         const float sv = e4m3_value(e4m3_mag(pm / 6.0f));
         sc16[bb] = 1.0f;
         sv16[bb] = sv;
@@ -1034,7 +1047,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       float y[16];
 #pragma unroll
       for (int j = 0; j < 16; j++) {
-        float pt = exp2_hw(__builtin_fmaf(S[bb][j], lam, -ms));
+        float pt = pexp(S[bb][j], ms, cm);
         if constexpr (PMODE != PM_PNQ) lsum += pt;
         if constexpr (PMODE == PM_TWO_LEVEL) pt *= k1;
         y[j] = pt;
@@ -1081,6 +1094,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   auto phase_v_fold = [&](int t) __attribute__((always_inline)) {
     const float mnew = fmaxn(m, tmax);
     const float ms = mnew == NEG_INF ? 0.0f : mnew * lam;
+    const float cm = pexp_c(ms);
     const float alpha = m == mnew ? 1.0f : exp2_hw(__builtin_fmaf(m, lam, -ms));
     m = mnew;
     const uint8_t* kx = smem + L::KEYR + grp * L::KEYT + L::KEYX;  // per-key bytes, key order
@@ -1096,7 +1110,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       float mx = 0.0f;
 #pragma unroll
       for (int j = 0; j < 16; j++) {
-        const float pt = exp2_hw(__builtin_fmaf(S[bb][j], lam, -ms));
+        const float pt = pexp(S[bb][j], ms, cm);
         if constexpr (PMODE != PM_PNQ) lsum += pt;
         const float pp = __builtin_ldexpf(pt, (int)((ew[j >> 2] >> (8 * (j & 3))) & 0xFFu) - 127);
         S[bb][j] = pp;
@@ -1312,7 +1326,10 @@ static hipError_t launch_one(const FwdArgs& a, hipStream_t st) {
 
 template <int QK, int PV, int PMODE, int PSC, bool BIAS, bool SAFE>
 static hipError_t launch_pp_k(const FwdArgs& a, hipStream_t st) {
-  fwd_pp_kernel<QK, PV, PMODE, PSC, BIAS, SAFE><<<dim3((unsigned)a.grid), dim3(512), 0, st>>>(a);
+  if (a.exp_bits)
+    fwd_pp_kernel<QK, PV, PMODE, PSC, BIAS, SAFE, true><<<dim3((unsigned)a.grid), dim3(512), 0, st>>>(a);
+  else
+    fwd_pp_kernel<QK, PV, PMODE, PSC, BIAS, SAFE, false><<<dim3((unsigned)a.grid), dim3(512), 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -1345,8 +1362,9 @@ hipError_t launch_fwd(int qk, int pv, int pmode, int psc, int vsc, const FwdArgs
   MXP(QK_BF16, PV_FP8, PM_FP8_FIXED, SCALE_E8M0);
   MXP(QK_FP4, PV_FP8, PM_FP8_FIXED, SCALE_E8M0);
 #undef MXP
-  // the 4-wave kernel has no per-key V form: causally safe V scales are refused there
-  if (a.vk != nullptr) return hipErrorNotSupported;
+  // the 4-wave kernel has no per-key V form and only the exact exponential: causally
+  // safe V scales and bit-level exponentials are refused there
+  if (a.vk != nullptr || a.exp_bits) return hipErrorNotSupported;
 #define MXF(QK_, PV_, PM_, PS_, VS_) \
   if (qk == QK_ && pv == PV_ && pmode == PM_ && psc == PS_ && vsc == VS_) return launch_one<QK_, PV_, PM_, PS_, VS_>(a, st)
   // the rest (V with E4M3 scales per 16 keys; bf16 scores with FP4 PV): single-buffer kernel

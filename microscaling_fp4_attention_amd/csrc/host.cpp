@@ -314,6 +314,8 @@ int mxattn_decode(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn
   if (q->H <= 0 || k->H <= 0 || q->H % k->H != 0) return MXATTN_E_INVALID;
   if (!p->causal || p->kv_tile != 128 || p->score_bias != nullptr || p->vkey != nullptr) return MXATTN_E_INVALID;
   if (!(p->sm_scale > 0.0f) || !isfinite(p->sm_scale)) return MXATTN_E_INVALID;
+  if (p->exp_mode != MXATTN_EXP_EXACT) return p->exp_mode == MXATTN_EXP_MITCHELL || p->exp_mode == MXATTN_EXP_SCHRAUDOLPH
+                                                 ? MXATTN_E_UNSUPPORTED : MXATTN_E_INVALID;
   const int64_t B = q->B, Hq = q->H, Hkv = k->H, R = q->N, N = k->N;
   if (R <= 0 || R > N || (Hq / Hkv) * R > 32) return MXATTN_E_UNSUPPORTED;
   if (!same_fmt(q->fmt, k->fmt) || !is_mxfp4(q->fmt) || !is_mxfp4(v->fmt)) return MXATTN_E_UNSUPPORTED;
@@ -459,6 +461,17 @@ int mxattn_fwd(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn_qt
   } else {
     return MXATTN_E_INVALID;
   }
+  // bit-level exponentials: the ping-pong kernel's routes (MXFP4 Q/K with an E8M0 V, or FP8 P)
+  float exp_bias = 0.0f;
+  if (p->exp_mode != MXATTN_EXP_EXACT) {
+    const double ln2 = 0.69314718055994531;
+    double delta;
+    if (p->exp_mode == MXATTN_EXP_MITCHELL) delta = 0.5 * (log2(1.0 / ln2) - 1.0 / ln2 + 1.0);
+    else if (p->exp_mode == MXATTN_EXP_SCHRAUDOLPH) delta = log2(1.0 / (2.0 * ln2 * ln2));
+    else return MXATTN_E_INVALID;
+    if (vsc != SCALE_E8M0 || (qk != QK_FP4 && pv != PV_FP8)) return MXATTN_E_UNSUPPORTED;
+    exp_bias = (float)ldexp(127.0 - delta, 23);
+  }
 
   const int64_t B = q->B, Hq = q->H, Hkv = k->H, N = q->N;
   if (B == 0 || N == 0) return MXATTN_OK;
@@ -514,6 +527,8 @@ int mxattn_fwd(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn_qt
     a.vk = static_cast<const uint8_t*>(vk->codes);
     a.vks = static_cast<const uint8_t*>(vk->scales);
   }
+  a.exp_bits = p->exp_mode != MXATTN_EXP_EXACT ? 1 : 0;
+  a.exp_bias = exp_bias;
   const int64_t nqt = (N + 127) / 128;
   a.grid = docs ? Hq * (nqt + ndocs) : B * Hq * nqt;
   if (a.grid > 0x7FFFFFFF) return MXATTN_E_UNSUPPORTED;

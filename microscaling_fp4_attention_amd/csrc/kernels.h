@@ -102,6 +102,10 @@ struct FwdArgs {
   // codes [B][Hkv][128][np / 2] (E2M1), one E8M0 byte per key slot [B][Hkv][np]
   const uint8_t* vk;
   const uint8_t* vks;
+  // exponential of P~: 0 exact (v_exp_f32); 1 bit-level, P~ = exp2_bits(s lambda 2^23 +
+  // exp_bias - m lambda 2^23) with exp_bias = 2^23 (127 - delta) of the chosen offset
+  int exp_bits;
+  float exp_bias;
 };
 
 // split-key decode (decode.hip)

@@ -141,12 +141,13 @@ def oracle_vkey(vf, vfmt):
 
 
 def run_case(qfmt, vfmt, pmode, pfmt, B, Hq, Hkv, N, causal=False, kind="kmean", seed=0, doc_off=None,
-             rows=None, check_bytes=True, inputs=None, pre=None, safe=False):
+             rows=None, check_bytes=True, inputs=None, pre=None, safe=False, exp_mode="exact"):
     """Run one forward on the GPU and on the oracle; returns a dict of results.
 
     pre: None, or a dict of outlier pre-processing for Q and K: {"center": both means
     subtracted and the compensation passed as score bias, "smoothk": K's mean only,
-    "hadamard": normalized rotation} (keys absent = off)."""
+    "hadamard": normalized rotation} (keys absent = off).  exp_mode: the exponential of
+    P~ ("exact", "mitchell", "schraudolph") on both sides."""
     import torch
     import microscaling_fp4_attention_amd as mx
 
@@ -172,7 +173,7 @@ def run_case(qfmt, vfmt, pmode, pfmt, B, Hq, Hkv, N, causal=False, kind="kmean",
     Vq = mx.quantize(vg, mx.ROLE_V, vfmt, cu_seqlens=cu)
     delta_g = mx.center_comp(qmean_g, kg, kmean_g, cu) if center else None
     Vk = mx.quantize(vg, mx.ROLE_VKEY, vfmt, cu_seqlens=cu) if safe else None
-    params = mx.fwd_params(pmode, pfmt, causal=causal, score_bias=delta_g, vkey=Vk)
+    params = mx.fwd_params(pmode, pfmt, causal=causal, score_bias=delta_g, vkey=Vk, exp_mode=exp_mode)
     ws, nd = None, 0
     if doc_off is not None:
         ws = mx.fwd_plan(doc_off, N, causal)
@@ -219,7 +220,7 @@ def run_case(qfmt, vfmt, pmode, pfmt, B, Hq, Hkv, N, causal=False, kind="kmean",
             assert np.array_equal(gkc, vk_codes), "per-key V codes differ"
             assert np.array_equal(gke, vk_exp), "per-key V exponents differ"
     O_ref, lse_ref, fb = oracle.attention(qd, kd, vd, PM_ORACLE[pmode], pfmt, causal=causal, doc_off=doc_off,
-                                          rows=rows, bias=bias, vkey=vk_vals, vkey_exp=vk_exp)
+                                          rows=rows, bias=bias, vkey=vk_vals, vkey_exp=vk_exp, exp_mode=exp_mode)
     sel = np.arange(B * Hq * N) if rows is None else np.asarray(rows)
     Og = O_gpu[sel]
     err = np.abs(Og - O_ref)

@@ -74,3 +74,37 @@ def test_host_validation(mx):
     assert L.mxattn_center_comp(None, None, mx._i64([0, 0, 128, 1]), None, 1, 3, 2, 5, 128, None, 0, None,
                                 None) == -1  # Hq not a multiple of Hkv
     assert mx.fwd_workspace_bytes(1000, 0) == 0 and mx.fwd_workspace_bytes(1000, 4) > 0
+
+
+def test_struct_layouts_match_the_header(mx, tmp_path):
+    """The binding's ctypes structures have the C structures' sizes and field offsets
+    (a C program built from include/mxattn.h with gcc prints them)."""
+    import subprocess
+    src = tmp_path / "layout.c"
+    src.write_text("""#include <stddef.h>
+#include <stdio.h>
+#include "mxattn.h"
+#define F(T, f) printf(#T " " #f " %zu\\n", offsetof(T, f))
+int main(void) {
+  printf("mxattn_fwd_params size %zu\\n", sizeof(mxattn_fwd_params));
+  printf("mxattn_qtensor size %zu\\n", sizeof(mxattn_qtensor));
+  printf("mxattn_preproc size %zu\\n", sizeof(mxattn_preproc));
+  F(mxattn_fwd_params, pmode); F(mxattn_fwd_params, pfmt); F(mxattn_fwd_params, causal);
+  F(mxattn_fwd_params, sm_scale); F(mxattn_fwd_params, kv_tile); F(mxattn_fwd_params, out_fp32);
+  F(mxattn_fwd_params, score_bias); F(mxattn_fwd_params, vkey); F(mxattn_fwd_params, exp_mode);
+  F(mxattn_qtensor, codes); F(mxattn_qtensor, scales); F(mxattn_qtensor, fmt); F(mxattn_qtensor, role);
+  F(mxattn_qtensor, ndocs); F(mxattn_qtensor, B); F(mxattn_qtensor, n_padded);
+  F(mxattn_preproc, mean); F(mxattn_preproc, hadamard);
+  return 0;
+}
+""")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    lines = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    py = {"mxattn_fwd_params": mx.FwdParams, "mxattn_qtensor": mx.QTensorC, "mxattn_preproc": mx.PreProc}
+    for line in filter(None, lines):
+        t, f, v = line.split()
+        if f == "size":
+            assert ctypes.sizeof(py[t]) == int(v), t
+        else:
+            assert getattr(py[t], f).offset == int(v), (t, f)
