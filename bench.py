@@ -83,6 +83,20 @@ CONFIGS = {
 }
 
 
+def route_peak(qf, vf, pm, pf):
+    """MFMA types of the forward's two products and their combined dense peak (TFLOP/s):
+    MXFP4 Q/K run on the FP4 MFMA, NVFP4 Q/K on bf16 after exact dequantization; PV runs
+    on FP8 for FP8 P, on FP4 for E8M0-scaled P with an MXFP4 V, on bf16 otherwise"""
+    qk = ("fp4", FP4_PEAK_TFLOPS) if qf.startswith("mxfp4") else ("bf16", BF16_PEAK_TFLOPS)
+    if pm == "fp8":
+        pv = ("fp8", FP8_PEAK_TFLOPS)
+    elif pf is not None and pf.startswith("mxfp4") and vf.startswith("mxfp4"):
+        pv = ("fp4", FP4_PEAK_TFLOPS)
+    else:
+        pv = ("bf16", BF16_PEAK_TFLOPS)
+    return f"QK {qk[0]}, PV {pv[0]}", 1.0 / (0.5 / qk[1] + 0.5 / pv[1])
+
+
 def counted_flop(B, H, N, d, causal, doc_off):
     if doc_off is not None:
         L = np.diff(np.asarray(doc_off, np.int64))
@@ -267,6 +281,9 @@ def main():
 
     def step(record):
         p = params
+        if record:
+            es = torch.cuda.Event(enable_timing=True)
+            es.record(stream)
         if args.preproc == "none":
             Q = mx.quantize(q, mx.ROLE_QK, qf)
             K = mx.quantize(k, mx.ROLE_QK, qf)
@@ -290,7 +307,7 @@ def main():
         mx.fwd(Q, K, V, p, out=out, workspace=ws, ndocs=nd)
         if record:
             e1.record(stream)
-            ev.append((e0, e1))
+            ev.append((es, e0, e1))
 
     for _ in range(args.warmup):
         step(False)
@@ -305,10 +322,16 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     t_step = g0.elapsed_time(g1) / 1e3 / args.steps
-    t_fwd = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    Qx, Kx, Vx = mx.quantize(q, mx.ROLE_QK, qf), mx.quantize(k, mx.ROLE_QK, qf), mx.quantize(v, mx.ROLE_V, vf, cu_seqlens=cu)
+    quant_bytes = 2 * (q.numel() + k.numel() + v.numel()) + sum(t.codes.numel() + t.scales.numel() for t in (Qx, Kx, Vx))
+    del Qx, Kx, Vx
+    fwd_ms = np.array([a.elapsed_time(b) for _, a, b in ev])
+    quant_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
+    t_fwd = float(np.mean(fwd_ms)) / 1e3
     log(f"[bench] step {t_step * 1e3:.3f} ms (wall {wall / args.steps * 1e3:.3f} ms), fwd {t_fwd * 1e3:.3f} ms")
 
     flop = counted_flop(B, Hq, N, 128, causal, doc_off)
+    route, rpeak = route_peak(qf, vf, pm, pf)
     tops = flop / t_step / 1e12
     fwd_tflops = flop / t_fwd / 1e12
     peak = FP4_PEAK_TFLOPS
@@ -331,11 +354,19 @@ def main():
         "pct_fp4_peak": round(100.0 * tops / FP4_PEAK_TFLOPS, 2),
         "t_fwd_ms": round(t_fwd * 1e3, 4),
         "t_quant_ms": round((t_step - t_fwd) * 1e3, 4),  # quantization and any pre-processing
+        "t_fwd_median_ms": round(float(np.median(fwd_ms)), 4),
+        "t_fwd_min_ms": round(float(np.min(fwd_ms)), 4),
+        "t_quant_median_ms": round(float(np.median(quant_ms)), 4),
+        # the quantize pass reads bf16 Q, K, V and writes their codes and scales
+        "quant_gbs": round(quant_bytes / (float(np.median(quant_ms)) * 1e-3) / 1e9, 1) if args.preproc == "none" else None,
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(fwd_tflops / peak, 4),
                      "traffic": profiled_traffic(args.config)
                      if args.preproc == "none" and not args.causal_safe and args.exp == "exact" else None,
-                     "kernel": "attention forward (mxattn_fwd)"},
+                     "kernel": "attention forward (mxattn_fwd)",
+                     # the operand route's own dense MFMA peak: QK and PV are half the FLOP each
+                     "route_peak": round(rpeak, 1), "route_frac": round(fwd_tflops / rpeak, 4),
+                     "route": route},
     }
     if not args.no_cpu:
         log("[bench] timing the CPU oracle on a bounded sample")

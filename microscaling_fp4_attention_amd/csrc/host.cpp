@@ -300,7 +300,7 @@ size_t mxattn_fwd_workspace_bytes(int64_t N, int ndocs) { return plan_bytes(N, n
 
 size_t mxattn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t R, int64_t N) {
   if (B <= 0 || Hq <= 0 || R <= 0 || N <= 0) return 0;
-  const int64_t rows = B * Hq * R * ((N + 1023) / 1024);  // one state per 1024-key chunk
+  const int64_t rows = B * Hq * R * ((N + 511) / 512);  // one state per 512-key chunk
   return (size_t)(rows * 128 * 4 + (rows * 4 + 15) / 16 * 16);
 }
 
@@ -333,6 +333,8 @@ int mxattn_decode(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn
   if (os[3] != 1 || os[0] < 0 || os[1] < 0 || os[2] < 0) return MXATTN_E_INVALID;
   if (workspace == nullptr || ws_bytes < mxattn_decode_workspace_bytes(B, Hq, R, N)) return MXATTN_E_WORKSPACE;
   if (!aligned16(workspace)) return MXATTN_E_ALIGN;
+  // grids: one workgroup per (request, KV head, 512-key chunk); four per merged row
+  if (B * Hkv * ((N + 511) / 512) > 0x7FFFFFFF || B * Hq * R * 4 > 0x7FFFFFFF) return MXATTN_E_UNSUPPORTED;
   DecArgs a{};
   a.q = static_cast<const uint8_t*>(q->codes);
   a.qs = static_cast<const uint8_t*>(q->scales);
@@ -350,7 +352,7 @@ int mxattn_decode(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn
   a.lambda = (float)((double)p->sm_scale * 1.4426950408889634);
   a.sm_scale = p->sm_scale;
   a.prule = make_rule(&p->pfmt);
-  a.nsplit = (N + 1023) / 1024;
+  a.nsplit = (N + 511) / 512;
   a.ws_o = static_cast<float*>(workspace);
   a.ws_lse = a.ws_o + B * Hq * R * a.nsplit * 128;
   a.out = out;

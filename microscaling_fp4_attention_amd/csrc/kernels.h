@@ -120,8 +120,8 @@ struct DecArgs {
   const int32_t* kv_len;  // device [B] keys of each request, or null (N each)
   float lambda, sm_scale;
   E8m0Rule prule;
-  int64_t nsplit;  // 1024-key chunks of the longest history: ceil(N / 1024)
-  float* ws_o;     // [B][Hq][R][nsplit][128] normalized chunk outputs (4 splits merged)
+  int64_t nsplit;  // 512-key chunks of the longest history: ceil(N / 512)
+  float* ws_o;     // [B][Hq][R][nsplit][128] normalized chunk outputs (4 tiles merged)
   float* ws_lse;   // [B][Hq][R][nsplit]
   void* out;       // [B][Hq][R][128] with element strides oB, oH, oN
   int64_t oB, oH, oN;
