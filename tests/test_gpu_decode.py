@@ -66,6 +66,13 @@ def test_decode_minimal_history():
     run_decode("direct", B=3, Hq=2, Hkv=2, R=2, N=260, kv_len=[2, 130, 257], seed=63)
 
 
+@pytest.mark.parametrize("N,kv_len", [(40, [40, 3]), (97, [97, 64]), (129, [129, 128])])
+def test_decode_short_histories(N, kv_len):
+    """histories shorter than a tile or a split: padded V^T rows of 64 to 160 keys, the
+    operand reads clamped inside their rows"""
+    run_decode("two_level", B=2, Hq=4, Hkv=2, R=1, N=N, kv_len=kv_len, seed=65)
+
+
 def test_decode_gqa_32_8_long():
     run_decode("two_level", B=1, Hq=32, Hkv=8, R=1, N=32768, kv_len=None, seed=64)
 
