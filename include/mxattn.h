@@ -125,8 +125,9 @@ typedef struct {
  *   role V : codes  [B][H][d][n_padded * bits / 8] scales [B][H][d][n_padded / block]
  * bits = 4 (E2M1) or 8 (E4M3).  For role V the key axis is padded: each document
  * (the whole sequence when there are no documents) occupies ceil(L / block) whole
- * blocks starting at a block boundary, in document order, and n_padded rounds
- * is the size given by mxattn_qtensor_bytes().  Slots after the last document
+ * blocks starting at a block boundary, in document order; n_padded is
+ * N + ndocs * (block - 1) for more than one document, else N, rounded up to a multiple
+ * of 128, as mxattn_qtensor_bytes() reports it.  Slots after the last document
  * and inside a document's last block hold code 0; blocks made only of padding
  * hold the scale of an all-zero block (E8M0 byte 127, E4M3 byte 0).
  */

@@ -69,11 +69,10 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecArgs a) {
 
   // ---- operands of the tile, all requested before any is used (the kernel is bound by
   // these reads, so none of them waits on the history length): MFMA row ql of sub-tile
-  // bb reads key kt0 + key_of(bb, (ql>>2)&1, 4(ql>>3) + (ql&3)); V^T rows are channels
-  // 32 db + ql.  Reads stay inside their row: keys past N take row N - 1, V chunks past
-  // the padded row end take its last chunk, and V scale bytes come from two aligned
-  // dwords (rows of np/32 bytes need not be dword-aligned).  What such reads return
-  // belongs to masked keys only.
+  // bb reads key kt0 + key_of(bb, (ql>>2)&1, 4(ql>>3) + (ql&3)), keys past N reading row
+  // N - 1 (masked); V^T rows are channels 32 db + ql.  The padded key axis of V is a
+  // multiple of 128, so a tile's codes and its 4 scale bytes lie inside the row and the
+  // scale dword is aligned.
   u4 k0[4], k1[4], v0[4], v1[4];
   uint32_t ks[4], vs[4];
   v16f S[4];
@@ -88,22 +87,13 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecArgs a) {
       k1[bb] = *reinterpret_cast<const u4*>(kp + 32 + 16 * hh);
       ks[bb] = *reinterpret_cast<const uint32_t*>(kscl + (int64_t)key * 4);
     }
-    const uint32_t rowb = np / 2, last = rowb - 16;   // code bytes per V^T row; last chunk
-    const uint32_t c0 = (uint32_t)kt0 / 2 + 16 * hh, c1 = c0 + 32;
-    const uint32_t srow = np / 32;                     // scale bytes per row
-    const int64_t stotal = (a.B * a.Hkv * 128) * (int64_t)srow;  // a multiple of 4
 #pragma unroll
     for (int db = 0; db < 4; db++) {
       const int64_t vrow = vrow0 + 32 * db + ql;
-      const uint8_t* vp = a.v + vrow * rowb;
-      v0[db] = *reinterpret_cast<const u4*>(vp + (c0 < last ? c0 : last));
-      v1[db] = *reinterpret_cast<const u4*>(vp + (c1 < last ? c1 : last));
-      const int64_t sb = vrow * srow + kt0 / 32;  // first scale byte of the tile
-      const int64_t a0 = sb & ~(int64_t)3;
-      const int64_t a1 = a0 + 4 < stotal ? a0 + 4 : stotal - 4;
-      const uint32_t d0 = *reinterpret_cast<const uint32_t*>(a.vs + a0);
-      const uint32_t d1 = *reinterpret_cast<const uint32_t*>(a.vs + a1);
-      vs[db] = __builtin_amdgcn_alignbyte(d1, d0, (uint32_t)(sb & 3));
+      const uint8_t* vp = a.v + vrow * (np / 2) + kt0 / 2;
+      v0[db] = *reinterpret_cast<const u4*>(vp + 16 * hh);
+      v1[db] = *reinterpret_cast<const u4*>(vp + 32 + 16 * hh);
+      vs[db] = *reinterpret_cast<const uint32_t*>(a.vs + vrow * (np / 32) + kt0 / 32);
     }
   }
   __builtin_amdgcn_sched_barrier(0);  // every read is in flight before the MFMAs

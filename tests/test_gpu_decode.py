@@ -68,8 +68,8 @@ def test_decode_minimal_history():
 
 @pytest.mark.parametrize("N,kv_len", [(40, [40, 3]), (97, [97, 64]), (129, [129, 128])])
 def test_decode_short_histories(N, kv_len):
-    """histories shorter than a tile or a split: padded V^T rows of 64 to 160 keys, the
-    operand reads clamped inside their rows"""
+    """histories shorter than a tile or a split (the last tile partly past N: its K rows
+    repeat row N - 1 and its keys are masked)"""
     run_decode("two_level", B=2, Hq=4, Hkv=2, R=1, N=N, kv_len=kv_len, seed=65)
 
 
