@@ -118,3 +118,14 @@ def test_fwd_bf16_output_matches_fp32():
     o32 = mx.fwd(Q, K, V, mx.fwd_params("direct", "mxfp4", out_fp32=True))
     o16 = mx.fwd(Q, K, V, mx.fwd_params("direct", "mxfp4", out_fp32=False))
     assert torch.equal(o32.to(torch.bfloat16), o16)
+
+
+@pytest.mark.parametrize("route", ["mxfp4_uos_pnq", "qk4pv8", "nvfp4_two_level"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_empty_documents(route, causal):
+    """packed documents with empty ones in the middle and at the end (repeated offsets):
+    the empty documents own no rows, no work items and no V blocks"""
+    q, v, pm, pf = ROUTES[route]
+    doc_off = np.array([0, 100, 100, 357, 357, 700, 700], np.int32)
+    res = run_case(q, v, pm, pf, B=1, Hq=2, Hkv=1, N=700, causal=causal, kind="outlier", seed=9, doc_off=doc_off)
+    _check(res, route + f" empty docs causal={causal}")
