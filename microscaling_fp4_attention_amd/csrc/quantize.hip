@@ -17,6 +17,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_util.h"
 #include "formats.h"
 #include "kernels.h"
 
@@ -63,32 +64,54 @@ __device__ __forceinline__ uint32_t block_scale(float M, E8m0Rule rule, float* i
 template <int SCALE, int BLOCK>
 __global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restrict__ x, int64_t sB, int64_t sH,
                                                        int64_t sN, int64_t H, int64_t N, int64_t rows,
-                                                       E8m0Rule rule, uint32_t* __restrict__ codes,
+                                                       int64_t nslot, E8m0Rule rule, uint32_t* __restrict__ codes,
                                                        uint8_t* __restrict__ scales) {
-  int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  int64_t row = gid >> 4;
-  int chunk = (int)(gid & 15);
-  bool live = row < rows;
-  int64_t r = live ? row : rows - 1;
-  int64_t n = r % N, bh = r / N;
-  int64_t h = bh % H, b = bh / H;
-  const uint4 v = *reinterpret_cast<const uint4*>(x + b * sB + h * sH + n * sN + chunk * 8);
-  float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-  float M = 0.0f;
+  // 16 lanes per token row (8 elements each); a thread quantizes the rows slot + u nslot,
+  // u < QK_ROWS, with all their loads issued first (a wave's load of one u covers 4
+  // consecutive rows); rows past the end load the last row and store nothing
+  constexpr int QK_ROWS = 4;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t slot = gid >> 4;
+  const int chunk = (int)(gid & 15);
+  uint4 v[QK_ROWS];
 #pragma unroll
-  for (int j = 0; j < 8; j++) M = __builtin_fmaxf(M, __builtin_fabsf(f[j]));
-  // lanes of one block are adjacent: 2 (BLOCK 16) or 4 (BLOCK 32)
-  M = __builtin_fmaxf(M, __shfl_xor(M, 1));
-  if constexpr (BLOCK == 32) M = __builtin_fmaxf(M, __shfl_xor(M, 2));
-  float inv, s;
-  uint32_t sb = block_scale<SCALE>(M, rule, &inv, &s);
-  uint32_t w = 0;
+  for (int u = 0; u < QK_ROWS; u++) {
+    const int64_t row = slot + u * nslot;
+    // row = (b H + h) N + n; 32-bit division (the host keeps rows below 2^31)
+    const uint32_t r = (uint32_t)(row < rows ? row : rows - 1);
+    const uint32_t n = r % (uint32_t)N, bh = r / (uint32_t)N;
+    const uint32_t h = bh % (uint32_t)H, b = bh / (uint32_t)H;
+    v[u] = *reinterpret_cast<const uint4*>(x + (int64_t)b * sB + (int64_t)h * sH + (int64_t)n * sN + chunk * 8);
+  }
 #pragma unroll
-  for (int j = 0; j < 8; j++) w |= encode_elem<ELEM_E2M1, SCALE>(f[j], inv, s) << (4 * j);
-  if (live) {
-    codes[row * 16 + chunk] = w;
-    if ((chunk & (BLOCK / 8 - 1)) == 0) scales[row * (128 / BLOCK) + chunk / (BLOCK / 8)] = (uint8_t)sb;
+  for (int u = 0; u < QK_ROWS; u++) {
+    const int64_t row = slot + u * nslot;
+    float f[8] = {bf16_lo(v[u].x), bf16_hi(v[u].x), bf16_lo(v[u].y), bf16_hi(v[u].y),
+                  bf16_lo(v[u].z), bf16_hi(v[u].z), bf16_lo(v[u].w), bf16_hi(v[u].w)};
+    float M = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; j++) M = __builtin_fmaxf(M, __builtin_fabsf(f[j]));
+    // lanes of one block are adjacent: 2 (BLOCK 16) or 4 (BLOCK 32)
+    M = __builtin_fmaxf(M, __shfl_xor(M, 1));
+    if constexpr (BLOCK == 32) M = __builtin_fmaxf(M, __shfl_xor(M, 2));
+    float inv, s;
+    uint32_t sb = block_scale<SCALE>(M, rule, &inv, &s);
+    uint32_t w = 0;
+    // power-of-two scales: the scaled FP4 convert rounds to nearest even with
+    // saturation and keeps the sign, as the element encoder does; blocks whose scale
+    // lies near the ends of the E8M0 range (where subnormal or non-finite inputs can
+    // occur) take the integer encoder
+    const int e = (int)sb - 127;
+    if (SCALE == SCALE_E8M0 && e >= -124 && e < 127) {
+      w = pack8_fp4(f, u2f((uint32_t)(e + 127) << 23));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; j++) w |= encode_elem<ELEM_E2M1, SCALE>(f[j], inv, s) << (4 * j);
+    }
+    if (row < rows) {
+      codes[row * 16 + chunk] = w;
+      if ((chunk & (BLOCK / 8 - 1)) == 0) scales[row * (128 / BLOCK) + chunk / (BLOCK / 8)] = (uint8_t)sb;
+    }
   }
 }
 
@@ -145,6 +168,44 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
     *reinterpret_cast<uint4*>(tile + row * VQ_ROW + part * 16) = v;
   }
   __syncthreads();
+  if constexpr (ELEM == ELEM_E2M1 && SCALE == SCALE_E8M0 && BLOCK == 32) {
+    // MXFP4: lane -> (channels 2 cp and 2 cp + 1, the 32 keys 32 kq + [0, 32)), one
+    // block per channel; dword reads of the staged rows (64 lanes cover a row)
+    const int cp = tid & 63, kq = tid >> 6;
+    float f[2][32];
+    float M[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 32; j++) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(tile + (32 * kq + j) * VQ_ROW + cp * 4);
+      f[0][j] = bf16_lo(w);
+      f[1][j] = bf16_hi(w);
+      M[0] = __builtin_fmaxf(M[0], __builtin_fabsf(f[0][j]));
+      M[1] = __builtin_fmaxf(M[1], __builtin_fabsf(f[1][j]));
+    }
+#pragma unroll
+    for (int c = 0; c < 2; c++) {
+      float inv, sdum;
+      const uint32_t sb = block_scale<SCALE_E8M0>(M[c], rule, &inv, &sdum);
+      const int e = (int)sb - 127;
+      uint32_t w[4];
+      if (e >= -124 && e < 127) {  // the scaled FP4 convert, as in the Q/K quantizer
+        const float sc = u2f((uint32_t)(e + 127) << 23);
+#pragma unroll
+        for (int i = 0; i < 4; i++) w[i] = pack8_fp4(&f[c][8 * i], sc);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          w[i] = 0;
+#pragma unroll
+          for (int j = 0; j < 8; j++) w[i] |= encode_elem<ELEM_E2M1, SCALE_E8M0>(f[c][8 * i + j], inv, 0.0f) << (4 * j);
+        }
+      }
+      const int64_t crow = bh * 128 + 2 * cp + c;
+      *reinterpret_cast<uint4*>(codes + crow * (np / 2) + (t0 + 32 * kq) / 2) = make_uint4(w[0], w[1], w[2], w[3]);
+      scales[crow * (np / 32) + (t0 + 32 * kq) / 32] = (uint8_t)sb;
+    }
+    return;
+  }
   // lane -> (channel, 64 keys)
   const int ch = tid & 127, sub = tid >> 7;
   const int64_t crow = bh * 128 + ch;
@@ -293,20 +354,22 @@ hipError_t launch_quant_vkey(const QuantArgs& a, hipStream_t st) {
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_quant_qk(const QuantArgs& a, hipStream_t st) {
-  int64_t threads = a.B * a.H * a.N * 16;
+  const int64_t rows = a.B * a.H * a.N;
+  if (rows >= (int64_t(1) << 31)) return hipErrorInvalidValue;  // 32-bit row indices
+  const int64_t nslot = (rows + 3) / 4;  // each thread quantizes 4 rows, nslot apart
+  const int64_t threads = nslot * 16;
   dim3 grid((unsigned)((threads + 255) / 256));
-  int64_t rows = a.B * a.H * a.N;
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   uint32_t* c = static_cast<uint32_t*>(a.codes);
   uint8_t* s = static_cast<uint8_t*>(a.scales);
   if (a.scale == SCALE_E8M0 && a.block == 32)
-    quant_qk_kernel<SCALE_E8M0, 32><<<grid, 256, 0, st>>>(x, a.sB, a.sH, a.sN, a.H, a.N, rows, a.rule, c, s);
+    quant_qk_kernel<SCALE_E8M0, 32><<<grid, 256, 0, st>>>(x, a.sB, a.sH, a.sN, a.H, a.N, rows, nslot, a.rule, c, s);
   else if (a.scale == SCALE_E8M0 && a.block == 16)
-    quant_qk_kernel<SCALE_E8M0, 16><<<grid, 256, 0, st>>>(x, a.sB, a.sH, a.sN, a.H, a.N, rows, a.rule, c, s);
+    quant_qk_kernel<SCALE_E8M0, 16><<<grid, 256, 0, st>>>(x, a.sB, a.sH, a.sN, a.H, a.N, rows, nslot, a.rule, c, s);
   else if (a.scale == SCALE_E4M3 && a.block == 16)
-    quant_qk_kernel<SCALE_E4M3, 16><<<grid, 256, 0, st>>>(x, a.sB, a.sH, a.sN, a.H, a.N, rows, a.rule, c, s);
+    quant_qk_kernel<SCALE_E4M3, 16><<<grid, 256, 0, st>>>(x, a.sB, a.sH, a.sN, a.H, a.N, rows, nslot, a.rule, c, s);
   else if (a.scale == SCALE_E4M3 && a.block == 32)
-    quant_qk_kernel<SCALE_E4M3, 32><<<grid, 256, 0, st>>>(x, a.sB, a.sH, a.sN, a.H, a.N, rows, a.rule, c, s);
+    quant_qk_kernel<SCALE_E4M3, 32><<<grid, 256, 0, st>>>(x, a.sB, a.sH, a.sN, a.H, a.N, rows, nslot, a.rule, c, s);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
