@@ -246,6 +246,8 @@ def quantize(x: torch.Tensor, role: int, fmt, cu_seqlens: torch.Tensor | None = 
                                           ctypes.byref(pre), cu, ndocs, ctypes.byref(desc), _stream(stream)),
                "mxattn_quantize_pre")
         return QTensor(codes, scales, desc)
+    if role == ROLE_QK:
+        cu_seqlens = None  # documents do not change a plain Q/K quantization
     ndocs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
     cb, sb, _ = qtensor_bytes(fmt, role, B, H, N, d, ndocs)
     codes = torch.empty(max(cb, 16), dtype=torch.uint8, device=x.device)[:cb]

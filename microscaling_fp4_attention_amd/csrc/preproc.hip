@@ -25,7 +25,8 @@ namespace mxattn {
 __device__ __forceinline__ float bf16_lo_f(uint32_t w) { return u2f(w << 16); }
 __device__ __forceinline__ float bf16_hi_f(uint32_t w) { return u2f(w & 0xFFFF0000u); }
 
-// document of token t: the last k with cu[k] <= t (cu: ndocs + 1 device offsets)
+// document of token t: the last k with cu[k] <= t (cu: ndocs + 1 offsets, in device
+// memory or staged in LDS)
 __device__ __forceinline__ int doc_of_token(const int32_t* __restrict__ cu, int ndocs, int64_t t) {
   if (cu == nullptr || ndocs <= 1) return 0;
   int lo = 0, hi = ndocs - 1;
@@ -34,6 +35,16 @@ __device__ __forceinline__ int doc_of_token(const int32_t* __restrict__ cu, int 
     if (cu[mid] <= t) lo = mid; else hi = mid - 1;
   }
   return lo;
+}
+
+// the document offsets a workgroup searches: copied to LDS when they fit (the whole
+// workgroup must call this), else the device array
+constexpr int DOCS_LDS = 1024;
+__device__ __forceinline__ const int32_t* stage_docs(const int32_t* __restrict__ cu, int ndocs, int32_t* scu) {
+  if (cu == nullptr || ndocs <= 1 || ndocs >= DOCS_LDS) return cu;
+  for (int i = threadIdx.x; i <= ndocs; i += blockDim.x) scu[i] = cu[i];
+  __syncthreads();
+  return scu;
 }
 
 // ---------------------------------------------------------------------------
@@ -81,9 +92,21 @@ __global__ __launch_bounds__(512) void channel_mean_kernel(const uint16_t* __res
 #pragma unroll
   for (int j = 0; j < 8; j++) part[slot][half * 8 + j] = s[j];
   __syncthreads();
+  // the 256 partial sums of a channel: 16 threads per channel add 16 each, then one
+  // thread adds those 16 (a fixed order; the sums are exact in double anyway)
+  __shared__ double part2[16][17];
+  if (tid < 256) {
+    const int c = tid & 15, g = tid >> 4;
+    double acc = 0.0;
+#pragma unroll
+    for (int k = 0; k < 16; k++) acc += part[16 * g + k][c];
+    part2[g][c] = acc;
+  }
+  __syncthreads();
   if (tid < 16) {
     double acc = 0.0;
-    for (int k = 0; k < 256; k++) acc += part[k][tid];
+#pragma unroll
+    for (int g = 0; g < 16; g++) acc += part2[g][tid];
     const int64_t L = t1 - t0;
     mean[unit * 128 + cg * 16 + tid] = L > 0 ? (float)(acc / (double)L) : 0.0f;
   }
@@ -117,6 +140,7 @@ __global__ __launch_bounds__(256) void quant_qk_pre_kernel(const uint16_t* __res
                                                            E8m0Rule rule, const float* __restrict__ mean,
                                                            const int32_t* __restrict__ cu, int ndocs, int hadamard,
                                                            uint32_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  __shared__ int32_t scu[DOCS_LDS];
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = gid >> 4;
   const int chunk = (int)(gid & 15);
@@ -127,19 +151,20 @@ __global__ __launch_bounds__(256) void quant_qk_pre_kernel(const uint16_t* __res
   const uint4 v = *reinterpret_cast<const uint4*>(x + b * sB + h * sH + n * sN + chunk * 8);
   const float f[8] = {bf16_lo_f(v.x), bf16_hi_f(v.x), bf16_lo_f(v.y), bf16_hi_f(v.y),
                       bf16_lo_f(v.z), bf16_hi_f(v.z), bf16_lo_f(v.w), bf16_hi_f(v.w)};
-  double y[8];
-#pragma unroll
-  for (int j = 0; j < 8; j++) y[j] = (double)f[j];
+  if (mean != nullptr) cu = stage_docs(cu, ndocs, scu);  // uniform condition
+  float mm[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (mean != nullptr) {
     const int nd = ndocs > 1 ? ndocs : 1;
     const float* mu = mean + ((bh * nd) + doc_of_token(cu, ndocs, n)) * 128 + chunk * 8;
     const float4 m0 = *reinterpret_cast<const float4*>(mu), m1 = *reinterpret_cast<const float4*>(mu + 4);
-    const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-#pragma unroll
-    for (int j = 0; j < 8; j++) y[j] -= (double)mm[j];
+    mm[0] = m0.x; mm[1] = m0.y; mm[2] = m0.z; mm[3] = m0.w;
+    mm[4] = m1.x; mm[5] = m1.y; mm[6] = m1.z; mm[7] = m1.w;
   }
   float z[8];
   if (hadamard) {
+    double y[8];  // x - mu and the butterflies in double (exact for bf16 x, float mu)
+#pragma unroll
+    for (int j = 0; j < 8; j++) y[j] = (double)f[j] - (double)mm[j];
     // channel c = 8 chunk + j; a butterfly of stride s maps (y[c], y[c+s]) to
     // (y[c] + y[c+s], y[c] - y[c+s]) for c with bit s clear
 #pragma unroll
@@ -163,8 +188,9 @@ __global__ __launch_bounds__(256) void quant_qk_pre_kernel(const uint16_t* __res
 #pragma unroll
     for (int j = 0; j < 8; j++) z[j] = (float)(y[j] * HADAMARD_C128);
   } else {
+    // fl32(x - mu): one correctly rounded float subtraction
 #pragma unroll
-    for (int j = 0; j < 8; j++) z[j] = (float)y[j];
+    for (int j = 0; j < 8; j++) z[j] = f[j] - mm[j];
   }
   float M = 0.0f;
 #pragma unroll
@@ -200,6 +226,7 @@ __global__ __launch_bounds__(256) void center_comp_kernel(const float* __restric
                                                           int64_t Hkv, int64_t N, int64_t rows,
                                                           const int32_t* __restrict__ cu, int ndocs,
                                                           float* __restrict__ delta) {
+  __shared__ int32_t scu[DOCS_LDS];
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = gid >> 4;  // (b, hk, token); the 16 lanes of a row are all live or all not
   const int chunk = (int)(gid & 15);
@@ -207,7 +234,7 @@ __global__ __launch_bounds__(256) void center_comp_kernel(const float* __restric
   const int64_t r = live ? row : rows - 1;
   const int64_t n = r % N, bhk = r / N, hk = bhk % Hkv, b = bhk / Hkv;
   const int nd = ndocs > 1 ? ndocs : 1;
-  const int doc = doc_of_token(cu, ndocs, n);
+  const int doc = doc_of_token(stage_docs(cu, ndocs, scu), ndocs, n);
   const uint4 v = *reinterpret_cast<const uint4*>(k + b * sB + hk * sH + n * sN + chunk * 8);
   const float f[8] = {bf16_lo_f(v.x), bf16_hi_f(v.x), bf16_lo_f(v.y), bf16_hi_f(v.y),
                       bf16_lo_f(v.z), bf16_hi_f(v.z), bf16_lo_f(v.w), bf16_hi_f(v.w)};
