@@ -626,7 +626,13 @@ struct PpLds {
   static constexpr int VROW = PV == PV_FP4 ? 80 : PV == PV_FP8 ? 144 : 256;
   static constexpr int KV = 128 * KROW;             // V^T rows follow the 128 key rows of a stage
   static constexpr int BOFF = 128 * (KROW + VROW);  // then the score bias of the 128 keys
-  static constexpr int STAGE = BOFF + (BIAS ? 512 : 0);
+  // then the E8M0 scale dwords of the K rows and of the V^T rows, each as two arrays of
+  // 128 dwords [lane half][row]: half h holds the row's dword shifted right by 8 h, so
+  // its low bytes are the scales of the blocks that half's operand elements cover, and
+  // the 32 lanes of a half read 32 consecutive dwords (no bank conflict)
+  static constexpr int KSC = BOFF + (BIAS ? 512 : 0);
+  static constexpr int VSC = KSC + (QK == QK_FP4 ? 1024 : 0);
+  static constexpr int STAGE = VSC + (PV == PV_BF16 ? 0 : 1024);
   // after the 3 stages, with causally safe V scales: the per-key form of the two
   // diagonal tiles of the workgroup (128 channel rows of 80 bytes, E2M1 codes, then
   // the 128 per-key E8M0 bytes in key order)
@@ -803,7 +809,10 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     }
     if constexpr (QK == QK_FP4) {
       *reinterpret_cast<u4*>(base + kpos_r * 80 + part * 16) = rk;
-      if (gt < 64) *reinterpret_cast<u2*>(base + kpos_s * 80 + 64) = mk2(rks, rks >> 8);
+      if (gt < 64) {
+        *reinterpret_cast<uint32_t*>(base + L::KSC + 4 * kpos_s) = rks;
+        *reinterpret_cast<uint32_t*>(base + L::KSC + 512 + 4 * kpos_s) = rks >> 8;
+      }
     } else {  // channels 32 part + [0, 32), E4M3 blocks 2 part and 2 part + 1
       const float s0 = e4m3_value(rks & 0xFF), s1 = e4m3_value((rks >> 8) & 0xFF);
       const uint32_t w4[4] = {rk.x, rk.y, rk.z, rk.w};
@@ -817,14 +826,16 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       *reinterpret_cast<u4*>(vb + kr * 80 + part * 16) = rv0;
       if (gt >= 64 && gt < 128) {
         const uint32_t w = __builtin_amdgcn_alignbyte(rvs_hi, rvs, vsh);
-        *reinterpret_cast<u2*>(vb + sr * 80 + 64) = mk2(w, w >> 8);
+        *reinterpret_cast<uint32_t*>(base + L::VSC + 4 * sr) = w;
+        *reinterpret_cast<uint32_t*>(base + L::VSC + 512 + 4 * sr) = w >> 8;
       }
     } else if constexpr (PV == PV_FP8) {
       *reinterpret_cast<u4*>(vb + kr * 144 + part * 16) = rv0;
       *reinterpret_cast<u4*>(vb + kr * 144 + (part + 4) * 16) = rv1;
       if (gt >= 64 && gt < 128) {
         const uint32_t w = __builtin_amdgcn_alignbyte(rvs_hi, rvs, vsh);
-        *reinterpret_cast<u2*>(vb + sr * 144 + 128) = mk2(w, w >> 8);
+        *reinterpret_cast<uint32_t*>(base + L::VSC + 4 * sr) = w;
+        *reinterpret_cast<uint32_t*>(base + L::VSC + 512 + 4 * sr) = w >> 8;
       }
     } else {  // bf16 row of 128 keys, chunk = key / 8, swizzled by the channel
       const float sv = scale_value(rvs, SCALE_E8M0);
@@ -851,7 +862,8 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   float pdq[4];                 // ... and the dequantization factor of each 16-key group
   // a staged scale dword is followed by a copy shifted right by 8 bits: lane half hh
   // reads the copy whose low bytes are its blocks' scales
-  const uint32_t koffk = (uint32_t)(ql * L::KROW + 16 * hh), ksok = (uint32_t)(ql * L::KROW + 64 + 4 * hh);
+  const uint32_t koffk = (uint32_t)(ql * L::KROW + 16 * hh);
+  const uint32_t soff = (uint32_t)(512 * hh + 4 * ql);  // this lane's scale dword of a 32-row group
 
   // M(t): PV of tile t-1 (stage offset sv), then S^T of tile t (stage offset sk) with
   // its mask and maxima
@@ -865,7 +877,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
 #pragma unroll
         for (int db = 0; db < 4; db++) {
           const uint8_t* rp = Vr + (32 * db + ql) * 80;
-          uint32_t vs4 = *reinterpret_cast<const uint32_t*>(rp + 64 + 4 * hh);
+          uint32_t vs4 = *reinterpret_cast<const uint32_t*>(smem + sv + L::VSC + 128 * db + soff);
           if constexpr (SAFE) vs4 = fold ? 0x7F7F7F7Fu : vs4;
           v8i a0 = v8_from4(*reinterpret_cast<const u4*>(rp + 16 * hh));
           v8i a1 = v8_from4(*reinterpret_cast<const u4*>(rp + 32 + 16 * hh));
@@ -883,7 +895,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
 #pragma unroll
         for (int db = 0; db < 4; db++) {
           const uint8_t* rp = Vs + (32 * db + ql) * 144;
-          const uint32_t vs4 = *reinterpret_cast<const uint32_t*>(rp + 128 + 4 * hh);
+          const uint32_t vs4 = *reinterpret_cast<const uint32_t*>(smem + sv + L::VSC + 128 * db + soff);
 #pragma unroll
           for (int kc = 0; kc < 2; kc++) {
             // operand element n holds key 64kc + 32(n/16) + 16h + n%16 (see key_of)
@@ -935,7 +947,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       for (int bb = 0; bb < 4; bb++) {
         if constexpr (QK == QK_FP4) {
           const uint8_t* rp = Ks + bb * 32 * 80;
-          const uint32_t ks4 = *reinterpret_cast<const uint32_t*>(rp + ksok);
+          const uint32_t ks4 = *reinterpret_cast<const uint32_t*>(Ks + L::KSC + 128 * bb + soff);
           v8i a0 = v8_from4(*reinterpret_cast<const u4*>(rp + koffk));
           v8i a1 = v8_from4(*reinterpret_cast<const u4*>(rp + koffk + 32));
           v16f acc = BIAS ? bias16(Ks + L::BOFF + 4 * key_of<SPLIT16>(bb, hh, 0)) : zero16();
