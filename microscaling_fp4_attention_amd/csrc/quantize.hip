@@ -117,27 +117,39 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restric
 
 // ---------------------------------------------------------------------------
 // role V: x [B][H][N][128] (strided) -> codes [B][H][128][np * bits/8],
-// scales [B][H][128][np / BLOCK].  One workgroup per (b, h, 128 key slots).
+// scales [B][H][128][np / BLOCK].  One workgroup per (b, h) and run of kt <= VQ_KT
+// tiles of 128 key slots, walked in order with the next tile's loads in flight while
+// the current one is encoded.  A tile gives each channel row only 128 / BLOCK scale
+// bytes; they are collected in LDS and each row's bytes of the whole run are written
+// at the end as one contiguous piece (per-tile byte writes to 128 rows cost a full
+// write granule for every 4 useful bytes).
 // cu: device document offsets (ndocs + 1) or null for one document [0, N).
 // ---------------------------------------------------------------------------
 constexpr int VQ_ROW = 128 * 2 + 16;  // bytes per staged token row (bf16, padded)
+constexpr int VQ_KT = 8;              // most key tiles of 128 slots per workgroup
 
 template <int ELEM, int SCALE, int BLOCK>
 __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict__ x, int64_t sB, int64_t sH,
                                                       int64_t sN, int64_t H, int64_t N, int64_t np,
                                                       const int32_t* __restrict__ cu, int ndocs, E8m0Rule rule,
-                                                      uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-  __shared__ int32_t tok[128];
+                                                      uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                      int kt) {
+  constexpr int SPT = 128 / BLOCK;      // scale bytes per channel row and tile
+  constexpr int SCW = VQ_KT * SPT;      // ... and per run
+  __shared__ int32_t tok[2][128];
   __shared__ __attribute__((aligned(16))) uint8_t tile[128 * VQ_ROW];
+  __shared__ __attribute__((aligned(16))) uint8_t sc[128 * SCW];
   const int tid = threadIdx.x;
-  const int64_t ntiles = np / 128;
-  const int64_t bh = blockIdx.x / ntiles;
-  const int64_t t0 = (blockIdx.x % ntiles) * 128;
+  const int64_t ntiles = np / 128, nruns = (ntiles + kt - 1) / kt;
+  const int64_t bh = blockIdx.x / nruns;
+  const int64_t tile0 = (blockIdx.x % nruns) * kt;
+  const int nt = (int)(ntiles - tile0 < kt ? ntiles - tile0 : kt);
   const int64_t b = bh / H, h = bh % H;
+  const uint16_t* xb = x + b * sB + h * sH;
 
-  // padded key slot -> token (or -1 for padding)
-  if (tid < 128) {
-    int64_t p = t0 + tid;
+  // padded key slot -> token (or -1 for padding) of tile tt, by threads < 128
+  auto slot_tokens = [&](int tt) __attribute__((always_inline)) {
+    const int64_t p = (tile0 + tt) * 128 + tid;
     int32_t t = -1;
     if (cu == nullptr) {
       if (p < N) t = (int32_t)p;
@@ -153,96 +165,118 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
         voff += span;
       }
     }
-    tok[tid] = t;
-  }
-  __syncthreads();
-  // stage 128 token rows x 256 bytes: 2048 chunks of 16 bytes
-  const uint16_t* xb = x + b * sB + h * sH;
+    tok[tt & 1][tid] = t;
+  };
+  // 128 token rows x 256 bytes: 2048 chunks of 16 bytes, 8 per thread
+  uint4 ld[8];
+  auto load_rows = [&](int tt) __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
-    int c = tid + 256 * i;
-    int row = c >> 4, part = c & 15;
-    int32_t t = tok[row];
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (t >= 0) v = *reinterpret_cast<const uint4*>(xb + (int64_t)t * sN + part * 8);
-    *reinterpret_cast<uint4*>(tile + row * VQ_ROW + part * 16) = v;
-  }
-  __syncthreads();
-  if constexpr (ELEM == ELEM_E2M1 && SCALE == SCALE_E8M0 && BLOCK == 32) {
-    // MXFP4: lane -> (channels 2 cp and 2 cp + 1, the 32 keys 32 kq + [0, 32)), one
-    // block per channel; dword reads of the staged rows (64 lanes cover a row)
-    const int cp = tid & 63, kq = tid >> 6;
-    float f[2][32];
-    float M[2] = {0.0f, 0.0f};
-#pragma unroll
-    for (int j = 0; j < 32; j++) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(tile + (32 * kq + j) * VQ_ROW + cp * 4);
-      f[0][j] = bf16_lo(w);
-      f[1][j] = bf16_hi(w);
-      M[0] = __builtin_fmaxf(M[0], __builtin_fabsf(f[0][j]));
-      M[1] = __builtin_fmaxf(M[1], __builtin_fabsf(f[1][j]));
+    for (int i = 0; i < 8; i++) {
+      const int c = tid + 256 * i, row = c >> 4, part = c & 15;
+      const int32_t t = tok[tt & 1][row];
+      ld[i] = make_uint4(0, 0, 0, 0);
+      if (t >= 0) ld[i] = *reinterpret_cast<const uint4*>(xb + (int64_t)t * sN + part * 8);
     }
+  };
+
+  if (tid < 128) slot_tokens(0);
+  __syncthreads();
+  load_rows(0);
+  for (int tt = 0; tt < nt; tt++) {
+    __syncthreads();  // the previous tile's encoding is done with the staged rows
 #pragma unroll
-    for (int c = 0; c < 2; c++) {
-      float inv, sdum;
-      const uint32_t sb = block_scale<SCALE_E8M0>(M[c], rule, &inv, &sdum);
-      const int e = (int)sb - 127;
-      uint32_t w[4];
-      if (e >= -124 && e < 127) {  // the scaled FP4 convert, as in the Q/K quantizer
-        const float sc = u2f((uint32_t)(e + 127) << 23);
+    for (int i = 0; i < 8; i++) {
+      const int c = tid + 256 * i, row = c >> 4, part = c & 15;
+      *reinterpret_cast<uint4*>(tile + row * VQ_ROW + part * 16) = ld[i];
+    }
+    if (tt + 1 < nt && tid < 128) slot_tokens(tt + 1);
+    __syncthreads();
+    if (tt + 1 < nt) load_rows(tt + 1);  // in flight during this tile's encoding
+    const int64_t t0 = (tile0 + tt) * 128;
+    if constexpr (ELEM == ELEM_E2M1 && SCALE == SCALE_E8M0 && BLOCK == 32) {
+      // MXFP4: lane -> (channels 2 cp and 2 cp + 1, the 32 keys 32 kq + [0, 32)), one
+      // block per channel; dword reads of the staged rows (64 lanes cover a row)
+      const int cp = tid & 63, kq = tid >> 6;
+      float f[2][32];
+      float M[2] = {0.0f, 0.0f};
 #pragma unroll
-        for (int i = 0; i < 4; i++) w[i] = pack8_fp4(&f[c][8 * i], sc);
-      } else {
+      for (int j = 0; j < 32; j++) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(tile + (32 * kq + j) * VQ_ROW + cp * 4);
+        f[0][j] = bf16_lo(w);
+        f[1][j] = bf16_hi(w);
+        M[0] = __builtin_fmaxf(M[0], __builtin_fabsf(f[0][j]));
+        M[1] = __builtin_fmaxf(M[1], __builtin_fabsf(f[1][j]));
+      }
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          w[i] = 0;
+      for (int c = 0; c < 2; c++) {
+        float inv, sdum;
+        const uint32_t sb = block_scale<SCALE_E8M0>(M[c], rule, &inv, &sdum);
+        const int e = (int)sb - 127;
+        uint32_t w[4];
+        if (e >= -124 && e < 127) {  // the scaled FP4 convert, as in the Q/K quantizer
+          const float scv = u2f((uint32_t)(e + 127) << 23);
 #pragma unroll
-          for (int j = 0; j < 8; j++) w[i] |= encode_elem<ELEM_E2M1, SCALE_E8M0>(f[c][8 * i + j], inv, 0.0f) << (4 * j);
+          for (int i = 0; i < 4; i++) w[i] = pack8_fp4(&f[c][8 * i], scv);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            w[i] = 0;
+#pragma unroll
+            for (int j = 0; j < 8; j++) w[i] |= encode_elem<ELEM_E2M1, SCALE_E8M0>(f[c][8 * i + j], inv, 0.0f) << (4 * j);
+          }
+        }
+        const int64_t crow = bh * 128 + 2 * cp + c;
+        *reinterpret_cast<uint4*>(codes + crow * (np / 2) + (t0 + 32 * kq) / 2) = make_uint4(w[0], w[1], w[2], w[3]);
+        sc[(2 * cp + c) * SCW + tt * SPT + kq] = (uint8_t)sb;
+      }
+    } else {
+      // lane -> (channel, 64 keys)
+      const int ch = tid & 127, sub = tid >> 7;
+      const int64_t crow = bh * 128 + ch;
+      constexpr int NB = 64 / BLOCK;
+      constexpr int BPE = ELEM == ELEM_E2M1 ? 4 : 8;  // bits per element
+      uint32_t out[64 * BPE / 32];
+#pragma unroll
+      for (int i = 0; i < 64 * BPE / 32; i++) out[i] = 0;
+      uint32_t sbytes = 0;
+#pragma unroll
+      for (int blk = 0; blk < NB; blk++) {
+        float f[BLOCK];
+        float M = 0.0f;
+#pragma unroll
+        for (int j = 0; j < BLOCK; j++) {
+          int key = sub * 64 + blk * BLOCK + j;
+          uint32_t hbits = *reinterpret_cast<const uint16_t*>(tile + key * VQ_ROW + ch * 2);
+          f[j] = u2f(hbits << 16);
+          M = __builtin_fmaxf(M, __builtin_fabsf(f[j]));
+        }
+        float inv, sv;
+        uint32_t sb = block_scale<SCALE>(M, rule, &inv, &sv);
+        sbytes |= sb << (8 * blk);
+#pragma unroll
+        for (int j = 0; j < BLOCK; j++) {
+          int e = blk * BLOCK + j;  // element index within this lane's 64 keys
+          uint32_t c = encode_elem<ELEM, SCALE>(f[j], inv, sv);
+          out[(e * BPE) / 32] |= c << ((e * BPE) % 32);
         }
       }
-      const int64_t crow = bh * 128 + 2 * cp + c;
-      *reinterpret_cast<uint4*>(codes + crow * (np / 2) + (t0 + 32 * kq) / 2) = make_uint4(w[0], w[1], w[2], w[3]);
-      scales[crow * (np / 32) + (t0 + 32 * kq) / 32] = (uint8_t)sb;
-    }
-    return;
-  }
-  // lane -> (channel, 64 keys)
-  const int ch = tid & 127, sub = tid >> 7;
-  const int64_t crow = bh * 128 + ch;
-  constexpr int NB = 64 / BLOCK;
-  constexpr int BPE = ELEM == ELEM_E2M1 ? 4 : 8;  // bits per element
-  uint32_t out[64 * BPE / 32];
+      uint8_t* cdst = codes + crow * (np * BPE / 8) + (t0 + sub * 64) * BPE / 8;
 #pragma unroll
-  for (int i = 0; i < 64 * BPE / 32; i++) out[i] = 0;
-  uint32_t sbytes = 0;
-#pragma unroll
-  for (int blk = 0; blk < NB; blk++) {
-    float f[BLOCK];
-    float M = 0.0f;
-#pragma unroll
-    for (int j = 0; j < BLOCK; j++) {
-      int key = sub * 64 + blk * BLOCK + j;
-      uint32_t hbits = *reinterpret_cast<const uint16_t*>(tile + key * VQ_ROW + ch * 2);
-      f[j] = u2f(hbits << 16);
-      M = __builtin_fmaxf(M, __builtin_fabsf(f[j]));
-    }
-    float inv, s;
-    uint32_t sb = block_scale<SCALE>(M, rule, &inv, &s);
-    sbytes |= sb << (8 * blk);
-#pragma unroll
-    for (int j = 0; j < BLOCK; j++) {
-      int e = blk * BLOCK + j;  // element index within this lane's 64 keys
-      uint32_t c = encode_elem<ELEM, SCALE>(f[j], inv, s);
-      out[(e * BPE) / 32] |= c << ((e * BPE) % 32);
+      for (int i = 0; i < 64 * BPE / 128; i++)
+        reinterpret_cast<uint4*>(cdst)[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+      uint8_t* sdst = sc + ch * SCW + tt * SPT + sub * NB;
+      if constexpr (NB == 2) *reinterpret_cast<uint16_t*>(sdst) = (uint16_t)sbytes;
+      else *reinterpret_cast<uint32_t*>(sdst) = sbytes;
     }
   }
-  uint8_t* cdst = codes + crow * (np * BPE / 8) + (t0 + sub * 64) * BPE / 8;
-#pragma unroll
-  for (int i = 0; i < 64 * BPE / 128; i++)
-    reinterpret_cast<uint4*>(cdst)[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
-  uint8_t* sdst = scales + crow * (np / BLOCK) + (t0 + sub * 64) / BLOCK;
-  if constexpr (NB == 2) *reinterpret_cast<uint16_t*>(sdst) = (uint16_t)sbytes;
-  else *reinterpret_cast<uint32_t*>(sdst) = sbytes;
+  __syncthreads();
+  // each channel row's nt * SPT scale bytes (a multiple of 4), one dword per thread step
+  const int dpr = nt * SPT / 4;
+  for (int i = tid; i < 128 * dpr; i += 256) {
+    const int r = i / dpr, w = i - r * dpr;
+    *reinterpret_cast<uint32_t*>(scales + (bh * 128 + r) * (np / BLOCK) + tile0 * SPT + 4 * w) =
+        *reinterpret_cast<const uint32_t*>(sc + r * SCW + 4 * w);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -376,13 +410,18 @@ hipError_t launch_quant_qk(const QuantArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_quant_v(const QuantArgs& a, hipStream_t st) {
-  dim3 grid((unsigned)(a.B * a.H * (a.np / 128)));
+  // runs of up to 8 tiles, shortened while that would leave fewer than 768 workgroups
+  // (3 per CU) for the whole tensor
+  const int64_t ntiles = a.np / 128;
+  int kt = VQ_KT;
+  while (kt > 1 && a.B * a.H * ((ntiles + kt - 1) / kt) < 768) kt /= 2;
+  dim3 grid((unsigned)(a.B * a.H * ((ntiles + kt - 1) / kt)));
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   uint8_t* c = static_cast<uint8_t*>(a.codes);
   uint8_t* s = static_cast<uint8_t*>(a.scales);
 #define MXQV(E, S, BL)                                                                                   \
   quant_v_kernel<E, S, BL><<<grid, 256, 0, st>>>(x, a.sB, a.sH, a.sN, a.H, a.N, a.np, a.cu, a.ndocs, a.rule, \
-                                                 c, s)
+                                                 c, s, kt)
   if (a.elem == ELEM_E2M1 && a.scale == SCALE_E8M0 && a.block == 32) MXQV(ELEM_E2M1, SCALE_E8M0, 32);
   else if (a.elem == ELEM_E2M1 && a.scale == SCALE_E8M0 && a.block == 16) MXQV(ELEM_E2M1, SCALE_E8M0, 16);
   else if (a.elem == ELEM_E2M1 && a.scale == SCALE_E4M3 && a.block == 16) MXQV(ELEM_E2M1, SCALE_E4M3, 16);

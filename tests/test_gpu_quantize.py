@@ -106,6 +106,27 @@ def test_quantize_v_bytes(fmt, docs):
     assert full.shape[-1] * (2 if qt.desc.fmt.elem == 0 else 1) == nb
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4_uos", "fp8v"])
+@pytest.mark.parametrize("docs", [None, [0, 9000, 9001, 30517, 48852]])
+def test_quantize_v_bytes_several_runs(fmt, docs):
+    # B=1, H=16, 48852 tokens: 382+ tiles of 128 key slots per head, enough for the
+    # quantizer to give each workgroup runs of 8 tiles with a ragged last run (its scale
+    # bytes are collected per run); codes and scales byte-exact
+    import torch
+    import microscaling_fp4_attention_amd as mx
+    N = 48852
+    x = synth.f32_to_bf16(synth.gaussian(4, 7, (1, 16, N, 128)))
+    doc_off = None if docs is None else np.array(docs, np.int32)
+    cu = None if docs is None else torch.tensor(docs, dtype=torch.int32, device="cuda:0")
+    qt = mx.quantize(_dev(x), mx.ROLE_V, fmt, cu_seqlens=cu)
+    ntiles = qt.n_padded // 128
+    assert ntiles % 8 != 0 and 16 * ((ntiles + 7) // 8) >= 768
+    c, s, _ = oracle_quant_v(synth.bf16_to_f32(x), fmt, doc_off)
+    gc, gs = gpu_codes_v(qt, N, doc_off)
+    assert np.array_equal(gc, c)
+    assert np.array_equal(gs, s)
+
+
 @pytest.mark.parametrize("fmt", V_FMTS)
 def test_quantize_v_edge_cases(fmt):
     import microscaling_fp4_attention_amd as mx
