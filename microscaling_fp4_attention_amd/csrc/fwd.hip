@@ -864,6 +864,53 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   // reads the copy whose low bytes are its blocks' scales
   const uint32_t koffk = (uint32_t)(ql * L::KROW + 16 * hh);
   const uint32_t soff = (uint32_t)(512 * hh + 4 * ql);  // this lane's scale dword of a 32-row group
+  bp[0] = bp[1] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+
+  // P of sub-tile bb (16 keys per lane) from its scores in S[bb]: the exponentials, this
+  // lane's share of the row sum (returned), and the quantized operand written in place
+  // (ms, cm: the row's exponent offset; k1: two-level pre-scale; sc, sv, ki: the 16-key
+  // group's convert scale, dequantization factor and multiplier)
+  auto p_sub = [&](int bb, float ms, float cm, float k1, float sc, float sv, float ki)
+      __attribute__((always_inline)) -> float {
+    float lsum = 0.0f;
+    float y[16];
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      float pt = pexp(S[bb][j], ms, cm);
+      if constexpr (PMODE != PM_PNQ) lsum += pt;
+      if constexpr (PMODE == PM_TWO_LEVEL) pt *= k1;
+      y[j] = pt;
+    }
+    if constexpr (PV == PV_FP4) {  // into the registers of the previous tile's P
+      const int e0 = 2 * (bb & 1);
+      bp[bb >> 1][e0] = (int)pack8_fp4(y, sc, (uint32_t)bp[bb >> 1][e0]);
+      bp[bb >> 1][e0 + 1] = (int)pack8_fp4(y + 8, sc, (uint32_t)bp[bb >> 1][e0 + 1]);
+    } else if constexpr (PV == PV_FP8) {  // c = E4M3(448 P~): 4 dwords per sub-tile
+#pragma unroll
+      for (int dw = 0; dw < 4; dw++) {
+        int x = __builtin_amdgcn_cvt_pk_fp8_f32(448.0f * y[4 * dw], 448.0f * y[4 * dw + 1], 0, false);
+        x = __builtin_amdgcn_cvt_pk_fp8_f32(448.0f * y[4 * dw + 2], 448.0f * y[4 * dw + 3], x, true);
+        bp[bb >> 1][4 * (bb & 1) + dw] = x;
+      }
+    } else {
+      float z[16];
+#pragma unroll
+      for (int j = 0; j < 16; j++) z[j] = PSC == SCALE_E8M0 ? y[j] : y[j] * ki;
+      pc[2 * bb] = pack8_fp4(z, sc);
+      pc[2 * bb + 1] = pack8_fp4(z + 8, sc);
+      pdq[bb] = sv;
+      if constexpr (PMODE == PM_PNQ) {  // row sum of the dequantized P
+#pragma unroll
+        for (int u = 0; u < 2; u++)
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            v2f pr = fp4_pair(pc[2 * bb + u], q);
+            lsum += (pr[0] + pr[1]) * sv;
+          }
+      }
+    }
+    return lsum;
+  };
 
   // M(t): PV of tile t-1 (stage offset sv), then S^T of tile t (stage offset sk) with
   // its mask and maxima
@@ -1028,7 +1075,8 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     }
 
     // block scales of P from the block maxima of P~ (exponentials of the score maxima)
-    float sc16[4], sv16[4], ki16[4];  // per 16 keys: convert scale, dequant factor, multiplier
+    float sc16[4] = {1.0f, 1.0f, 1.0f, 1.0f}, sv16[4] = {1.0f, 1.0f, 1.0f, 1.0f},
+          ki16[4] = {1.0f, 1.0f, 1.0f, 1.0f};  // per 16 keys: convert scale, dequant factor, multiplier
     int e[2] = {0, 0};
     if constexpr (PV == PV_FP4 || (PV == PV_BF16 && PSC == SCALE_E8M0)) {
 #pragma unroll
@@ -1053,50 +1101,9 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     }
 
     float lsum = 0.0f;
-    uint32_t w[8];
 #pragma unroll
-    for (int bb = 0; bb < 4; bb++) {
-      float y[16];
-#pragma unroll
-      for (int j = 0; j < 16; j++) {
-        float pt = pexp(S[bb][j], ms, cm);
-        if constexpr (PMODE != PM_PNQ) lsum += pt;
-        if constexpr (PMODE == PM_TWO_LEVEL) pt *= k1;
-        y[j] = pt;
-      }
-      if constexpr (PV == PV_FP4) {  // into the registers of the previous tile's P
-        w[2 * bb] = pack8_fp4(y, sc16[bb], (uint32_t)bp[bb >> 1][2 * (bb & 1)]);
-        w[2 * bb + 1] = pack8_fp4(y + 8, sc16[bb], (uint32_t)bp[bb >> 1][2 * (bb & 1) + 1]);
-      } else if constexpr (PV == PV_FP8) {  // c = E4M3(448 P~): 4 dwords per sub-tile
-#pragma unroll
-        for (int dw = 0; dw < 4; dw++) {
-          int x = __builtin_amdgcn_cvt_pk_fp8_f32(448.0f * y[4 * dw], 448.0f * y[4 * dw + 1], 0, false);
-          x = __builtin_amdgcn_cvt_pk_fp8_f32(448.0f * y[4 * dw + 2], 448.0f * y[4 * dw + 3], x, true);
-          bp[bb >> 1][4 * (bb & 1) + dw] = x;
-        }
-      } else {
-        float z[16];
-#pragma unroll
-        for (int j = 0; j < 16; j++) z[j] = PSC == SCALE_E8M0 ? y[j] : y[j] * ki16[bb];
-        pc[2 * bb] = pack8_fp4(z, sc16[bb]);
-        pc[2 * bb + 1] = pack8_fp4(z + 8, sc16[bb]);
-        pdq[bb] = sv16[bb];
-        if constexpr (PMODE == PM_PNQ) {  // row sum of the dequantized P
-#pragma unroll
-          for (int u = 0; u < 2; u++)
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-              v2f pr = fp4_pair(pc[2 * bb + u], q);
-              lsum += (pr[0] + pr[1]) * sv16[bb];
-            }
-        }
-      }
-    }
+    for (int bb = 0; bb < 4; bb++) lsum += p_sub(bb, ms, cm, k1, sc16[bb], sv16[bb], ki16[bb]);
     if constexpr (PMODE != PM_PNQ || PV != PV_FP4) lpart = alpha * lpart + lsum;
-    if constexpr (PV == PV_FP4) {
-      bp[0] = v8_from4(mk4(w[0], w[1], w[2], w[3]));
-      bp[1] = v8_from4(mk4(w[4], w[5], w[6], w[7]));
-    }
   };
 
   // V phase of the group's diagonal tile with causally safe V scales ("FLAMIA" section
