@@ -190,11 +190,28 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None, numel=None, contiguous=False):
+    """Check a caller tensor before its address reaches the library: the kernels take
+    raw device pointers and write through the sizes the descriptors give, so a host
+    tensor, a wrong element type or a short buffer must be refused here."""
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor, got one on {t.device}")
+
+
 def channel_mean(x: torch.Tensor, cu_seqlens: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Per-channel means of a bf16 tensor x [B, H, N, d] over each document's tokens:
     float32 [B, H, max(ndocs, 1), d] (mxattn_channel_mean)."""
     if x.dtype != torch.bfloat16 or x.dim() != 4:
         raise ValueError("x must be a 4-D bfloat16 tensor [B, H, N, d]")
+    _need(x, "x")
     B, H, N, d = x.shape
     cu, ndocs = _cu(cu_seqlens)
     mean = torch.empty((B, H, max(ndocs, 1), d), dtype=torch.float32, device=x.device)
@@ -207,9 +224,15 @@ def center_comp(qmean: torch.Tensor, k: torch.Tensor, kmean: torch.Tensor, cu_se
                 stream=None) -> torch.Tensor:
     """Centering compensation delta [B, Hq, N] (float32) for the forward's score_bias
     (mxattn_center_comp): qmean [B, Hq, nd, d], k bf16 [B, Hkv, N, d], kmean [B, Hkv, nd, d]."""
+    _need(k, "k", dtype=torch.bfloat16)
+    if k.dim() != 4 or qmean.dim() != 4:
+        raise ValueError("k must be [B, Hkv, N, d] and qmean [B, Hq, nd, d]")
     B, Hkv, N, d = k.shape
     Hq = qmean.shape[1]
     cu, ndocs = _cu(cu_seqlens)
+    nd = max(ndocs, 1)
+    _need(qmean, "qmean", dtype=torch.float32, shape=(B, Hq, nd, d))
+    _need(kmean, "kmean", dtype=torch.float32, shape=(B, Hkv, nd, d))
     delta = torch.empty((B, Hq, N), dtype=torch.float32, device=k.device)
     _check(_lib().mxattn_center_comp(_ptr(qmean.contiguous()), _ptr(k), _i64(k.stride()), _ptr(kmean.contiguous()),
                                      B, Hq, Hkv, N, d, cu, ndocs, _ptr(delta), _stream(stream)), "mxattn_center_comp")
@@ -228,10 +251,14 @@ def quantize(x: torch.Tensor, role: int, fmt, cu_seqlens: torch.Tensor | None = 
     """
     if x.dtype != torch.bfloat16 or x.dim() != 4:
         raise ValueError("x must be a 4-D bfloat16 tensor [B, H, N, d]")
+    _need(x, "x")
     B, H, N, d = x.shape
     if mean is not None or hadamard:
         if role != ROLE_QK:
             raise ValueError("pre-processing applies to role QK only")
+        if mean is not None:
+            nd = 1 if cu_seqlens is None else max(cu_seqlens.numel() - 1, 1)
+            _need(mean, "mean", dtype=torch.float32, shape=(B, H, nd, d))
         cb, sb, _ = qtensor_bytes(fmt, role, B, H, N, d, 0)
         codes = torch.empty(max(cb, 16), dtype=torch.uint8, device=x.device)[:cb]
         scales = torch.empty(max(sb, 16), dtype=torch.uint8, device=x.device)[:sb]
@@ -310,11 +337,18 @@ def fwd(q: QTensor, k: QTensor, v: QTensor, params: FwdParams, out: torch.Tensor
         stream=None) -> torch.Tensor:
     """Attention forward; returns out [B, Hq, N, 128] (float32 or bfloat16 per params.out_fp32)."""
     B, Hq, N, d = q.desc.B, q.desc.H, q.desc.N, q.desc.d
+    dt = torch.float32 if params.out_fp32 else torch.bfloat16
     if out is None:
-        dt = torch.float32 if params.out_fp32 else torch.bfloat16
         out = torch.empty((B, Hq, N, d), dtype=dt, device=q.codes.device)
+    _need(out, "out", dtype=dt, shape=(B, Hq, N, d))
+    if lse is not None:
+        _need(lse, "lse", dtype=torch.float32, numel=B * Hq * N, contiguous=True)
+    bias = getattr(params, "_score_bias_ref", None)
+    if bias is not None:
+        _need(bias, "score_bias", dtype=torch.float32, numel=B * Hq * N, contiguous=True)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
+        _need(workspace, "workspace", dtype=torch.uint8)
         ws_ptr, ws_bytes = ctypes.c_void_p(workspace.data_ptr()), workspace.numel()
     lse_ptr = None if lse is None else ctypes.c_void_p(lse.data_ptr())
     _check(_lib().mxattn_fwd(ctypes.byref(q.desc), ctypes.byref(k.desc), ctypes.byref(v.desc), ctypes.byref(params),
@@ -335,14 +369,18 @@ def decode(q: QTensor, k: QTensor, v: QTensor, params: FwdParams, kv_len: torch.
     Returns out [B, Hq, R, 128] (float32 or bfloat16 per params.out_fp32)."""
     B, Hq, R, d = q.desc.B, q.desc.H, q.desc.N, q.desc.d
     N = k.desc.N
+    dt = torch.float32 if params.out_fp32 else torch.bfloat16
     if out is None:
-        dt = torch.float32 if params.out_fp32 else torch.bfloat16
         out = torch.empty((B, Hq, R, d), dtype=dt, device=q.codes.device)
+    _need(out, "out", dtype=dt, shape=(B, Hq, R, d))
+    if lse is not None:
+        _need(lse, "lse", dtype=torch.float32, numel=B * Hq * R, contiguous=True)
     nbytes = decode_workspace_bytes(B, Hq, R, N)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.codes.device)
-    if kv_len is not None and (kv_len.dtype != torch.int32 or not kv_len.is_cuda):
-        raise ValueError("kv_len must be an int32 device tensor")
+    _need(workspace, "workspace", dtype=torch.uint8)
+    if kv_len is not None:
+        _need(kv_len, "kv_len", dtype=torch.int32, numel=B, contiguous=True)
     _check(_lib().mxattn_decode(ctypes.byref(q.desc), ctypes.byref(k.desc), ctypes.byref(v.desc), ctypes.byref(params),
                                 _ptr(kv_len), _ptr(out), _i64(out.stride()), _ptr(lse), _ptr(workspace),
                                 workspace.numel(), _stream(stream)), "mxattn_decode")
