@@ -41,10 +41,9 @@ struct Lds {
   static constexpr int VROW = PV == PV_FP4 ? 80 : PV == PV_BF16 ? 256 : 144;  // per V^T row
   static constexpr int BOFF = 128 * (KROW + VROW);       // then the score bias of the 128 keys
   static constexpr int STAGE = BOFF + (BIAS ? 512 : 0);  // one key tile
-  // Buffers of key tiles: 3 lets the next tile's scores and this tile's PV read
-  // different buffers while a third is refilled (one barrier per tile); 2 needs a
-  // second barrier; 1 (large bf16 tiles) falls back to compute-after-store.  Two
-  // workgroups share a CU's 160 KB.
+  // Buffers of key tiles: 3 let tile kt be read while tile kt+2 is stored into a third
+  // (one barrier per tile); 2 need a second barrier; 1 (large bf16 tiles) falls back
+  // to compute-after-store.  Two workgroups share a CU's 160 KB.
   static constexpr int NB = 3 * STAGE <= 80 * 1024 ? 3 : 2 * STAGE <= 80 * 1024 ? 2 : 1;
   static constexpr int BYTES = NB * STAGE;
 };
@@ -270,12 +269,11 @@ __global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(Fw
   };
 
   // ---------------- S^T = K Q^T of the tile in buffer `buf`, sub-tile bb (32 keys) ----------------
-  auto scores_sub = [&](int buf, int bb, uint32_t after = 0) __attribute__((always_inline)) -> v16f {
-    // `after`: a value this sub-tile's work must wait for.  Routing the LDS offset through
-    // an empty asm that reads it keeps the compiler from hoisting these loads and MFMAs
-    // (pure operations) above the work that produced it.
+  auto scores_sub = [&](int buf, int bb) __attribute__((always_inline)) -> v16f {
+    // the LDS offset passes through an empty asm, which keeps the compiler from hoisting
+    // these loads and MFMAs (pure operations) above the stores and barrier before them
     uint32_t boff = (uint32_t)(buf * L::STAGE);
-    asm volatile("" : "+v"(boff) : "v"(after));
+    asm volatile("" : "+v"(boff));
     const uint8_t* Ks = smem + boff;
     v16f acc = BIAS ? bias16(Ks + L::BOFF + 4 * key_of<SPLIT16>(bb, hh, 0)) : zero16();
     if constexpr (QK == QK_FP4) {
@@ -304,12 +302,8 @@ __global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(Fw
   };
 
   // ---------------- softmax, P quantization and PV of one tile ----------------
-  // ---------------- softmax, P quantization and PV of one tile ----------------
-  // S: this tile's scores (consumed).  When NEXT, the scores of the next tile (buffer
-  // nbuf) are computed into S on the matrix cores, one 32-key sub-tile at a time, as
-  // soon as this tile's sub-tile has been exponentiated and quantized, so that only
-  // one tile of scores is live and the MFMAs run between the exponentials.
-  auto softmax_pv = [&](int kt, int buf, v16f* S, bool next, int nbuf) __attribute__((always_inline)) {
+  // S: this tile's scores (consumed)
+  auto softmax_pv = [&](int kt, int buf, v16f* S) __attribute__((always_inline)) {
     const uint8_t* Vs = smem + buf * L::STAGE + 128 * L::KROW;
     // mask (tail keys, causal diagonal): wave-uniform test, per-element select
     const int k0 = kt * 128;
@@ -382,8 +376,7 @@ __global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(Fw
       }
     }
 
-    // per sub-tile: P~ = 2^(lambda (S - m)), row sum, quantized operand; then the next
-    // tile's scores of that sub-tile
+    // per sub-tile: P~ = 2^(lambda (S - m)), row sum, quantized operand
     float lsum = 0.0f;       // row sum of P~ (or of the dequantized P for PNQ on bf16)
     uint32_t pc[4][4];       // FP4 codes [sub-tile][dword 0..1] / FP8 codes [sub-tile][dword 0..3]
     uint32_t pw[4][8];       // bf16 P [sub-tile][dword]
@@ -420,15 +413,6 @@ __global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(Fw
           int x = __builtin_amdgcn_cvt_pk_fp8_f32(448.0f * y[4 * dw], 448.0f * y[4 * dw + 1], 0, false);
           pc[bb][dw] = __builtin_amdgcn_cvt_pk_fp8_f32(448.0f * y[4 * dw + 2], 448.0f * y[4 * dw + 3], x, true);
         }
-      }
-      // the next tile's scores of this sub-tile, into the registers just consumed (issued
-      // only after this sub-tile's operand is complete, so that one tile of scores is live)
-      if (next) {
-        uint32_t dep;
-        if constexpr (PV == PV_BF16) dep = pw[bb][7];
-        else if constexpr (PV == PV_FP8) dep = pc[bb][3];
-        else dep = pc[bb][1];
-        S[bb] = scores_sub(nbuf, bb, dep);
       }
     }
     if constexpr (PMODE != PM_PNQ || PV != PV_FP4) lpart = alpha * lpart + lsum;
@@ -542,26 +526,19 @@ __global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(Fw
         // tile: an unconditional load keeps the staging registers out of scratch memory)
         load_tile(kt + 1 < nkt ? kt + 1 : kt);
         scores(0, S);
-        softmax_pv(kt, 0, S, false, 0);
+        softmax_pv(kt, 0, S);
       }
     } else {
-      // software pipeline: the scores of tile kt+1 are computed on the matrix cores
-      // while the softmax of tile kt runs; tile kt+2 is staged behind them
+      // tiles kt+1 and kt+2 are staged while tile kt is computed
       load_tile(0);
       store_tile(0);
       load_tile(nkt > 1 ? 1 : 0);
       store_tile(1 % NB);
       __syncthreads();
       load_tile(nkt > 2 ? 2 : nkt - 1);
-#ifndef MXATTN_SCORE_PIPELINE
-#define MXATTN_SCORE_PIPELINE 0
-#endif
-      constexpr bool PIPE = MXATTN_SCORE_PIPELINE != 0;
-      if (PIPE) scores(0, S);
       for (int kt = 0; kt < nkt; kt++) {
-        // the next tile's scores land in S (stale data past the end is never used)
-        if (!PIPE) scores(kt % NB, S);
-        softmax_pv(kt, kt % NB, S, PIPE, (kt + 1) % NB);
+        scores(kt % NB, S);
+        softmax_pv(kt, kt % NB, S);
         if constexpr (NB == 2) __syncthreads();  // buffer kt % 2 is free once every PV read it
         store_tile((kt + 2) % NB);               // tile kt+2 (a repeat of the last tile past the end)
         load_tile(kt + 3 < nkt ? kt + 3 : nkt - 1);
