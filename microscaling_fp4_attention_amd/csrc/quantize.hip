@@ -104,6 +104,21 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restric
     const int e = (int)sb - 127;
     if (SCALE == SCALE_E8M0 && e >= -124 && e < 127) {
       w = pack8_fp4(f, u2f((uint32_t)(e + 127) << 23));
+    } else if (SCALE == SCALE_E4M3 && M < __builtin_inff()) {
+      // E4M3 scale: the quotient x / s correctly rounded from the block's correctly
+      // rounded reciprocal r by one residual step (q = x r, e = x - s q exactly by
+      // FMA, q + e r rounded once: Markstein's division), then the scaled FP4 convert
+      // at scale 1.  The quotient takes x's sign (a zero one included, as the element
+      // encoder keeps it); a zero scale gives zero quotients.
+      const float r = s > 0.0f ? 1.0f / s : 0.0f;
+      float y[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const float q = f[j] * r;
+        const float t = __builtin_fmaf(__builtin_fmaf(-q, s, f[j]), r, q);
+        y[j] = __builtin_copysignf(s > 0.0f ? t : 0.0f, f[j]);
+      }
+      w = pack8_fp4(y, 1.0f);
     } else {
 #pragma unroll
       for (int j = 0; j < 8; j++) w |= encode_elem<ELEM_E2M1, SCALE>(f[j], inv, s) << (4 * j);

@@ -87,6 +87,38 @@ def test_quantize_qk_strided_input():
     assert np.array_equal(qt.scales_view().cpu().numpy(), s)
 
 
+def _e4m3_value(c):
+    e, m = (c >> 3) & 15, c & 7
+    return m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+
+
+def test_quantize_nvfp4_every_element_under_every_scale():
+    """Every nonzero E4M3 block scale s (codes 1..126), each with blocks whose maximum is
+    6 s exactly (so the scale is s), and every positive bf16 magnitude up to that
+    maximum in both signs as the other 15 elements: the codes of x / s, including every
+    value on or next to an E2M1 rounding midpoint, byte-exact against the oracle."""
+    import microscaling_fp4_attention_amd as mx
+    mags = np.arange(0, 0x7F80, dtype=np.uint32)  # every finite non-negative bf16
+    vals = (mags << 16).view(np.float32)
+    blocks = []
+    for c in range(1, 127):
+        M = np.float32(6.0 * _e4m3_value(c))
+        assert synth.bf16_to_f32(synth.f32_to_bf16(np.array([M])))[0] == M
+        m = vals[vals <= M]
+        el = np.empty(2 * m.size, np.float32)
+        el[0::2], el[1::2] = m, -m
+        el = np.concatenate([el, np.zeros((-el.size) % 15, np.float32)]).reshape(-1, 15)
+        blocks.append(np.concatenate([np.full((el.shape[0], 1), M, np.float32), el], axis=1))
+    b = np.concatenate(blocks)
+    b = np.concatenate([b, np.zeros(((-b.shape[0]) % 8, 16), np.float32)])
+    x = synth.f32_to_bf16(b.reshape(1, 1, -1, 128))
+    assert x.shape[2] > 30000
+    qt = mx.quantize(_dev(x), mx.ROLE_QK, "nvfp4")
+    c, sc, _ = oracle_quant_qk(synth.bf16_to_f32(x), "nvfp4")
+    assert np.array_equal(qt.scales_view().cpu().numpy(), sc)
+    assert np.array_equal(gpu_codes_qk(qt), c)
+
+
 @pytest.mark.parametrize("fmt", V_FMTS)
 @pytest.mark.parametrize("docs", [None, [0, 37, 100, 229, 300], [0, 300]])
 def test_quantize_v_bytes(fmt, docs):
