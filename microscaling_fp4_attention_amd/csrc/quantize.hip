@@ -141,6 +141,31 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restric
 // cu: device document offsets (ndocs + 1) or null for one document [0, N).
 // ---------------------------------------------------------------------------
 constexpr int VQ_ROW = 128 * 2 + 16;  // bytes per staged token row (bf16, padded)
+constexpr int VQ_MAXDOC = 1024;       // document offsets staged in LDS (more: read from memory)
+
+// Token of padded V slot p, or -1 for padding.  Without documents slot p is token p
+// (p < N).  With documents each one's slots start at a multiple of BLOCK after the
+// previous document's (its blocks are document-local) and its last block is padded.
+template <int BLOCK>
+__device__ __forceinline__ int32_t slot_token(int64_t p, int64_t N, const int32_t* cu, int ndocs) {
+  if (cu == nullptr) return p < N ? (int32_t)p : -1;
+  int64_t voff = 0;
+  for (int k = 0; k < ndocs; k++) {
+    const int64_t L = cu[k + 1] - cu[k];
+    const int64_t span = (L + BLOCK - 1) / BLOCK * BLOCK;
+    if (p < voff + span) return p - voff < L ? (int32_t)(cu[k] + (p - voff)) : -1;
+    voff += span;
+  }
+  return -1;
+}
+
+// the document offsets a V quantizer reads: staged in LDS (cu_s, VQ_MAXDOC + 1 entries)
+// when they fit, else the device array
+__device__ __forceinline__ const int32_t* stage_offsets(const int32_t* cu, int ndocs, int32_t* cu_s) {
+  if (cu == nullptr || ndocs > VQ_MAXDOC) return cu;
+  for (int i = threadIdx.x; i <= ndocs; i += blockDim.x) cu_s[i] = cu[i];
+  return cu_s;  // visible after the caller's next barrier
+}
 constexpr int VQ_KT = 8;              // most key tiles of 128 slots per workgroup
 
 template <int ELEM, int SCALE, int BLOCK>
@@ -152,6 +177,7 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
   constexpr int SPT = 128 / BLOCK;      // scale bytes per channel row and tile
   constexpr int SCW = VQ_KT * SPT;      // ... and per run
   __shared__ int32_t tok[2][128];
+  __shared__ int32_t cu_s[VQ_MAXDOC + 1];
   __shared__ __attribute__((aligned(16))) uint8_t tile[128 * VQ_ROW];
   __shared__ __attribute__((aligned(16))) uint8_t sc[128 * SCW];
   const int tid = threadIdx.x;
@@ -163,24 +189,9 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
   const uint16_t* xb = x + b * sB + h * sH;
 
   // padded key slot -> token (or -1 for padding) of tile tt, by threads < 128
+  const int32_t* offs = stage_offsets(cu, ndocs, cu_s);
   auto slot_tokens = [&](int tt) __attribute__((always_inline)) {
-    const int64_t p = (tile0 + tt) * 128 + tid;
-    int32_t t = -1;
-    if (cu == nullptr) {
-      if (p < N) t = (int32_t)p;
-    } else {
-      int64_t voff = 0;
-      for (int k = 0; k < ndocs; k++) {
-        int64_t L = cu[k + 1] - cu[k];
-        int64_t span = (L + BLOCK - 1) / BLOCK * BLOCK;
-        if (p < voff + span) {
-          if (p - voff < L) t = (int32_t)(cu[k] + (p - voff));
-          break;
-        }
-        voff += span;
-      }
-    }
-    tok[tt & 1][tid] = t;
+    tok[tt & 1][tid] = slot_token<BLOCK>((tile0 + tt) * 128 + tid, N, offs, ndocs);
   };
   // 128 token rows x 256 bytes: 2048 chunks of 16 bytes, 8 per thread
   uint4 ld[8];
@@ -194,6 +205,7 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
     }
   };
 
+  __syncthreads();  // the staged document offsets
   if (tid < 128) slot_tokens(0);
   __syncthreads();
   load_rows(0);
@@ -307,6 +319,7 @@ __global__ __launch_bounds__(256) void quant_vkey_kernel(const uint16_t* __restr
                                                          const int32_t* __restrict__ cu, int ndocs, E8m0Rule rule,
                                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
   __shared__ int32_t tok[128];
+  __shared__ int32_t cu_s[VQ_MAXDOC + 1];
   __shared__ float inv_s[128];
   __shared__ __attribute__((aligned(16))) uint8_t tile[128 * VQ_ROW];
   const int tid = threadIdx.x;
@@ -314,25 +327,9 @@ __global__ __launch_bounds__(256) void quant_vkey_kernel(const uint16_t* __restr
   const int64_t bh = blockIdx.x / ntiles;
   const int64_t t0 = (blockIdx.x % ntiles) * 128;
   const int64_t b = bh / H, h = bh % H;
-  if (tid < 128) {
-    int64_t p = t0 + tid;
-    int32_t t = -1;
-    if (cu == nullptr) {
-      if (p < N) t = (int32_t)p;
-    } else {
-      int64_t voff = 0;
-      for (int k = 0; k < ndocs; k++) {
-        int64_t L = cu[k + 1] - cu[k];
-        int64_t span = (L + BLOCK - 1) / BLOCK * BLOCK;
-        if (p < voff + span) {
-          if (p - voff < L) t = (int32_t)(cu[k] + (p - voff));
-          break;
-        }
-        voff += span;
-      }
-    }
-    tok[tid] = t;
-  }
+  const int32_t* offs = stage_offsets(cu, ndocs, cu_s);
+  __syncthreads();
+  if (tid < 128) tok[tid] = slot_token<BLOCK>(t0 + tid, N, offs, ndocs);
   __syncthreads();
   const uint16_t* xb = x + b * sB + h * sH;
 #pragma unroll
@@ -425,11 +422,15 @@ hipError_t launch_quant_qk(const QuantArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_quant_v(const QuantArgs& a, hipStream_t st) {
-  // runs of up to 8 tiles, shortened while that would leave fewer than 768 workgroups
-  // (3 per CU) for the whole tensor
+  // the longest run (8, 4, 2 or 1 tiles) whose grid fills the CUs' 768 resident
+  // workgroups (3 per CU) to at least 85% over its rounds: longer runs write longer
+  // scale pieces, but a last round left mostly empty idles the CUs
   const int64_t ntiles = a.np / 128;
   int kt = VQ_KT;
-  while (kt > 1 && a.B * a.H * ((ntiles + kt - 1) / kt) < 768) kt /= 2;
+  for (; kt > 1; kt /= 2) {
+    const int64_t nwg = a.B * a.H * ((ntiles + kt - 1) / kt), rounds = (nwg + 767) / 768;
+    if (nwg * 100 >= rounds * 768 * 85) break;
+  }
   dim3 grid((unsigned)(a.B * a.H * ((ntiles + kt - 1) / kt)));
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   uint8_t* c = static_cast<uint8_t*>(a.codes);
