@@ -367,6 +367,11 @@ def main():
                      # the operand route's own dense MFMA peak: QK and PV are half the FLOP each
                      "route_peak": round(rpeak, 1), "route_frac": round(fwd_tflops / rpeak, 4),
                      "route": route},
+        # the second ceiling: one exponential per visible score element (4 d = 512 counted
+        # FLOP each), per nominal clock (2.4 GHz) per CU (256); 100% of the FP4 MFMA peak
+        # would need 10.1e15 / 512 / (2.4e9 * 256) = 32.1 per clock per CU
+        "softmax": {"exps_per_clk_per_cu": round(flop / 512.0 / t_fwd / (2.4e9 * 256), 2),
+                    "at_fp4_peak": round(FP4_PEAK_TFLOPS * 1e12 / 512.0 / (2.4e9 * 256), 2)},
     }
     if not args.no_cpu:
         log("[bench] timing the CPU oracle on a bounded sample")
