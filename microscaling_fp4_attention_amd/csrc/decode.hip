@@ -254,57 +254,68 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecArgs a) {
 
 // merge of the chunk states of one (request, query head, row) by their log-sum-exp.
 // Workgroup = (row, quarter of the 128 channels); its 8 groups of 32 threads (thread =
-// channel) take every 8th chunk, and the groups' partial sums are added in LDS.
+// channel) take every 8th chunk in one pass, 8 chunk states in flight, keeping a running
+// maximum (the weights of earlier chunks rescaled when it grows); the groups' states
+// are then combined in a fixed order in LDS (deterministic).
 constexpr int MERGE_GROUPS = 8;
+constexpr int MERGE_BATCH = 8;  // chunk states in flight per thread
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecArgs a) {
   const int64_t row = blockIdx.x >> 2;  // (b, hq, r)
   const int cq = blockIdx.x & 3;
   const int64_t r = row % a.R, bh = row / a.R, hq = bh % a.Hq, b = bh / a.Hq;
   const int c = 32 * cq + (threadIdx.x & 31), grp = threadIdx.x >> 5;
   const int L = a.kv_len != nullptr ? a.kv_len[b] : (int)a.N;
-  const int64_t ns = ((int64_t)L + DEC_CHUNK - 1) / DEC_CHUNK;  // chunks holding keys of this request
+  // chunks holding keys of this request (a length beyond N reads no state past the N keys)
+  int64_t ns = ((int64_t)L + DEC_CHUNK - 1) / DEC_CHUNK;
+  ns = ns < a.nsplit ? ns : a.nsplit;
   const float* lses = a.ws_lse + row * a.nsplit;
+  const float* outs = a.ws_o + row * a.nsplit * 128 + c;
   __shared__ float red[MERGE_GROUPS][32];
-  __shared__ float rmax[MERGE_GROUPS], wsums[MERGE_GROUPS];
-  float M = NEG_INF;
-  for (int64_t s = grp; s < ns; s += MERGE_GROUPS) M = fmaxn(M, lses[s]);
-  if ((threadIdx.x & 31) == 0) rmax[grp] = M;
-  __syncthreads();
+  __shared__ float gmax[MERGE_GROUPS], gsum[MERGE_GROUPS];
+  float M = NEG_INF, acc = 0.0f, wsum = 0.0f;
+  for (int64_t s0 = grp; s0 < ns; s0 += MERGE_GROUPS * MERGE_BATCH) {
+    float ls[MERGE_BATCH], ov[MERGE_BATCH];
 #pragma unroll
-  for (int g = 0; g < MERGE_GROUPS; g++) M = fmaxn(M, rmax[g]);
-  float acc = 0.0f, wsum = 0.0f;
-  if (M != NEG_INF) {
-    int64_t s = grp;
-    for (; s + 3 * MERGE_GROUPS < ns; s += 4 * MERGE_GROUPS) {  // four chunks in flight
-      float ls[4], ov[4];
-#pragma unroll
-      for (int u = 0; u < 4; u++) {
-        ls[u] = lses[s + MERGE_GROUPS * u];
-        ov[u] = a.ws_o[(row * a.nsplit + s + MERGE_GROUPS * u) * 128 + c];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; u++) {
-        const float wgt = ls[u] == NEG_INF ? 0.0f : __expf(ls[u] - M);
-        wsum += wgt;
-        acc += wgt * ov[u];
-      }
+    for (int u = 0; u < MERGE_BATCH; u++) {  // every read issued before any is used
+      const int64_t s = s0 + MERGE_GROUPS * u;
+      const bool in = s < ns;
+      ls[u] = in ? lses[s] : NEG_INF;
+      ov[u] = in ? outs[s * 128] : 0.0f;
     }
-    for (; s < ns; s += MERGE_GROUPS) {
-      const float ls = lses[s];
-      const float wgt = ls == NEG_INF ? 0.0f : __expf(ls - M);
-      wsum += wgt;
-      acc += wgt * a.ws_o[(row * a.nsplit + s) * 128 + c];
+    float Mn = M;
+#pragma unroll
+    for (int u = 0; u < MERGE_BATCH; u++) Mn = fmaxn(Mn, ls[u]);
+    if (Mn != NEG_INF) {
+      const float k = M == NEG_INF ? 0.0f : __expf(M - Mn);
+      acc *= k;
+      wsum *= k;
+#pragma unroll
+      for (int u = 0; u < MERGE_BATCH; u++) {
+        const float w = ls[u] == NEG_INF ? 0.0f : __expf(ls[u] - Mn);
+        wsum += w;
+        acc += w * ov[u];
+      }
+      M = Mn;
     }
   }
   red[grp][threadIdx.x & 31] = acc;
-  if ((threadIdx.x & 31) == 0) wsums[grp] = wsum;
+  if ((threadIdx.x & 31) == 0) {
+    gmax[grp] = M;
+    gsum[grp] = wsum;
+  }
   __syncthreads();
   if (grp != 0) return;
-  float ws_all = 0.0f, o = 0.0f;
+  float Mall = NEG_INF;
 #pragma unroll
-  for (int g = 0; g < MERGE_GROUPS; g++) {  // fixed order: deterministic
-    ws_all += wsums[g];
-    o += red[g][threadIdx.x & 31];
+  for (int g = 0; g < MERGE_GROUPS; g++) Mall = fmaxn(Mall, gmax[g]);
+  float ws_all = 0.0f, o = 0.0f;
+  if (Mall != NEG_INF) {
+#pragma unroll
+    for (int g = 0; g < MERGE_GROUPS; g++) {  // fixed order: deterministic
+      const float k = gmax[g] == NEG_INF ? 0.0f : __expf(gmax[g] - Mall);
+      ws_all += k * gsum[g];
+      o += k * red[g][threadIdx.x & 31];
+    }
   }
   o = ws_all > 0.0f ? o / ws_all : 0.0f;
   if (a.out_fp32) {
@@ -312,7 +323,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecArgs a) {
   } else {
     static_cast<uint16_t*>(a.out)[b * a.oB + hq * a.oH + r * a.oN + c] = (uint16_t)bf16_rne(o);
   }
-  if (a.lse != nullptr && cq == 0 && threadIdx.x == 0) a.lse[row] = ws_all > 0.0f ? M + __logf(ws_all) : NEG_INF;
+  if (a.lse != nullptr && cq == 0 && threadIdx.x == 0) a.lse[row] = ws_all > 0.0f ? Mall + __logf(ws_all) : NEG_INF;
 }
 
 hipError_t launch_decode(int pmode, const DecArgs& a, hipStream_t st) {
