@@ -158,7 +158,7 @@ def bench_decode(args, torch, mx):
     k = torch.randn((B, Hkv, N, 128), generator=g, device=dev).to(torch.bfloat16)
     v = torch.randn((B, Hkv, N, 128), generator=g, device=dev).to(torch.bfloat16)
     K = mx.quantize(k, mx.ROLE_QK, "mxfp4")
-    V = mx.quantize(v, mx.ROLE_V, "mxfp4")
+    V = mx.quantize(v, mx.ROLE_VT if args.decode_layout == "vt" else mx.ROLE_V, "mxfp4")
     del k, v
     params = mx.fwd_params("two_level", "mxfp4", causal=True, out_fp32=False)
     out = torch.empty((B, Hq, R, 128), dtype=torch.bfloat16, device=dev)
@@ -194,7 +194,8 @@ def bench_decode(args, torch, mx):
            "ms_per_step": round(t_step * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "mxfp4", "data": "synthetic (seeded normal bf16 drawn on the device)",
            "config": {"workload": f"decode: B{B} Hq{Hq} Hkv{Hkv} R{R} history {N} keys, MXFP4 K/V/Q, two-level P, "
-                                  "splits of 256 keys", "history_bytes": hist},
+                                  f"splits of 256 keys, V {'tile-major (role VT)' if args.decode_layout == 'vt' else 'role V'}",
+                      "history_bytes": hist},
            "t_decode_ms": round(t_dec * 1e3, 4),
            "tokens_per_s": round(B * R / t_step, 1),
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
@@ -222,6 +223,9 @@ def main():
     ap.add_argument("--decode", type=int, default=0, metavar="N",
                     help="time the split-key decode instead: 4 requests, GQA 32:8, one new token each over an "
                          "N-key MXFP4 history (HBM-bound; reports the history bytes read per second)")
+    ap.add_argument("--decode-layout", default="vt", choices=["vt", "v"],
+                    help="layout of the decode's quantized V history: tile-major (role VT, the decode's own) or "
+                         "role V (the prefill's)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (for scaling HBM byte counters)")
     args = ap.parse_args()

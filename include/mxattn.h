@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MXATTN_ABI_VERSION 4
+#define MXATTN_ABI_VERSION 5
 
 typedef enum {
   MXATTN_OK = 0,
@@ -76,11 +76,16 @@ typedef enum {
   MXATTN_ROLE_QK = 0, /* blocks along the head dimension d, one row per token     */
   MXATTN_ROLE_V = 1,  /* blocks along the tokens (the PV contraction axis), stored
                          transposed: one row per channel                           */
-  MXATTN_ROLE_VKEY = 2 /* the per-key form of a 4-bit V for causally safe diagonal
+  MXATTN_ROLE_VKEY = 2, /* the per-key form of a 4-bit V for causally safe diagonal
                           tiles ("FLAMIA" section 3.2): one E8M0 scale per key over
                           its d channels (fmt's rule), E2M1 codes stored transposed
                           in role V's slot layout (fmt->block fixes that layout);
                           scales are [B][H][n_padded], one byte per key slot      */
+  MXATTN_ROLE_VT = 3   /* role V's blocks and codes stored tile-major for the split-
+                          key decode (mxattn_decode): each 128-key tile of V^T is
+                          one contiguous run, so the decode reads the history tile
+                          by tile instead of 128 pieces one channel row apart.  No
+                          documents; E2M1 with E8M0 scales per 32 keys only        */
 } mxattn_role;
 
 /* how the softmax operand P is quantized inside the attention loop */
@@ -123,6 +128,8 @@ typedef struct {
  * dense and row-major:
  *   role QK: codes  [B][H][N][d * bits / 8]        scales [B][H][N][d / block]
  *   role V : codes  [B][H][d][n_padded * bits / 8] scales [B][H][d][n_padded / block]
+ *   role VT: codes  [B][H][n_padded / 128][d][64]    scales [B][H][n_padded / 128][d][4]
+ *            (role V's bytes of key tile t and channel c moved to [t][c])
  * bits = 4 (E2M1) or 8 (E4M3).  For role V the key axis is padded: each document
  * (the whole sequence when there are no documents) occupies ceil(L / block) whole
  * blocks starting at a block boundary, in document order; n_padded is
@@ -182,7 +189,8 @@ const char* mxattn_last_error(void);
  *   ndocs      : number of packed documents (0 or 1: one sequence)
  * Writes *code_bytes, *scale_bytes and, if not NULL, *n_padded: role V pads the
  * key axis to n_padded = round_up(N + ndocs * (block - 1), 128) slots (with
- * ndocs <= 1: round_up(N, 128)), role QK has n_padded = N.
+ * ndocs <= 1: round_up(N, 128)), role VT to round_up(N, 128) (it takes no
+ * documents: ndocs > 1 is MXATTN_E_INVALID), role QK has n_padded = N.
  * Errors: MXATTN_E_INVALID, MXATTN_E_UNSUPPORTED.
  */
 int mxattn_qtensor_bytes(const mxattn_qfmt* fmt, int role, int64_t B, int64_t H, int64_t N, int64_t d,
@@ -194,6 +202,8 @@ int mxattn_qtensor_bytes(const mxattn_qfmt* fmt, int role, int64_t B, int64_t H,
  *   role QK: per token, blocks of fmt->block consecutive channels.
  *   role V : per channel, blocks of fmt->block consecutive tokens inside one
  *            document, written transposed (see mxattn_qtensor).
+ *   role VT: as role V without documents, written tile-major (see mxattn_qtensor);
+ *            E2M1 with E8M0 scales per 32 keys only.
  * Per block with maximum magnitude M ("MXAttention" section 2; blog "NVFP4, not
  * MXFP4"):
  *   E8M0 scale: exponent by fmt->rule, clamped to [-127, 127]; M = 0 gives 2^0.
@@ -335,7 +345,8 @@ int mxattn_fwd(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn_qt
  * heads of a KV head's group and the R rows share one matrix tile: (Hq/Hkv)*R <= 32.
  *   q: role QK [B][Hq][R][d]; row r sits at position kv_len[b] - R + r and sees
  *      keys 0..that position (params->causal must be 1).
- *   k: role QK [B][Hkv][N][d]; v: role V [B][Hkv][d][n_padded] without documents.
+ *   k: role QK [B][Hkv][N][d]; v: role V [B][Hkv][d][n_padded] without documents,
+ *      or role VT (the same values tile-major: the faster layout for decode).
  *   Formats: MXFP4 Q/K/V (E2M1 with E8M0 per 32, any E8M0 rule); P modes DIRECT,
  *   PNQ and TWO_LEVEL with P in E2M1 with E8M0 per 32.  score_bias and vkey must be
  *   NULL.

@@ -22,12 +22,12 @@ OK, E_INVALID, E_UNSUPPORTED, E_ALIGN, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4, -
 ELEM_E2M1, ELEM_E4M3 = 0, 1
 SCALE_E8M0, SCALE_E4M3 = 0, 1
 RULE_OCP, RULE_CEIL = 0, 1
-ROLE_QK, ROLE_V, ROLE_VKEY = 0, 1, 2
+ROLE_QK, ROLE_V, ROLE_VKEY, ROLE_VT = 0, 1, 2, 3
 P_DIRECT, P_TWO_LEVEL, P_PNQ, P_FP8_FIXED = 1, 2, 3, 4
 EXP_EXACT, EXP_MITCHELL, EXP_SCHRAUDOLPH = 0, 1, 2
 
 
-ABI_VERSION = 4  # MXATTN_ABI_VERSION of include/mxattn.h
+ABI_VERSION = 5  # MXATTN_ABI_VERSION of include/mxattn.h
 
 
 class QFmt(ctypes.Structure):
@@ -153,20 +153,26 @@ class QTensor:
         return int(self.desc.n_padded)
 
     def codes_view(self) -> torch.Tensor:
-        """role QK: [B, H, N, d*bits/8]; role V: [B, H, d, n_padded*bits/8]."""
+        """role QK: [B, H, N, d*bits/8]; role V: [B, H, d, n_padded*bits/8];
+        role VT: [B, H, n_padded/128, d, 64]."""
         d = self.desc
         bits = 4 if d.fmt.elem == ELEM_E2M1 else 8
         if d.role == ROLE_QK:
             return self.codes.view(d.B, d.H, d.N, d.d * bits // 8)
+        if d.role == ROLE_VT:
+            return self.codes.view(d.B, d.H, d.n_padded // 128, d.d, 64)
         return self.codes.view(d.B, d.H, d.d, d.n_padded * bits // 8)
 
     def scales_view(self) -> torch.Tensor:
-        """role QK: [B, H, N, d/block]; role V: [B, H, d, n_padded/block]; role VKEY: [B, H, n_padded]."""
+        """role QK: [B, H, N, d/block]; role V: [B, H, d, n_padded/block]; role VKEY:
+        [B, H, n_padded]; role VT: [B, H, n_padded/128, d, 4]."""
         d = self.desc
         if d.role == ROLE_QK:
             return self.scales.view(d.B, d.H, d.N, d.d // d.fmt.block)
         if d.role == ROLE_VKEY:
             return self.scales.view(d.B, d.H, d.n_padded)
+        if d.role == ROLE_VT:
+            return self.scales.view(d.B, d.H, d.n_padded // 128, d.d, 4)
         return self.scales.view(d.B, d.H, d.d, d.n_padded // d.fmt.block)
 
 

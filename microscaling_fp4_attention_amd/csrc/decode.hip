@@ -34,7 +34,9 @@ namespace mxattn {
 constexpr int DEC_SPLIT = 256;  // keys per split (the partition of the merge)
 constexpr int DEC_CHUNK = 512;  // keys per workgroup: two splits, one tile per wave
 
-template <int PMODE>
+// VT: V is role VT (tile-major: key tile t of channel c at [t][c], 64 code bytes and 4
+// scale bytes), so a tile's V^T is one contiguous run
+template <int PMODE, bool VT>
 __global__ __launch_bounds__(256, 2) void decode_kernel(DecArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, ql = lane & 31, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -90,10 +92,14 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecArgs a) {
 #pragma unroll
     for (int db = 0; db < 4; db++) {
       const int64_t vrow = vrow0 + 32 * db + ql;
-      const uint8_t* vp = a.v + vrow * (np / 2) + kt0 / 2;
+      // slot of (tile, channel) in the tile-major form; kt0 < N <= np keeps both forms
+      // inside the head's V
+      const int64_t tslot = (int64_t)(kt0 / 128) * 128 + 32 * db + ql;
+      const uint8_t* vp = VT ? a.v + vrow0 * (np / 2) + tslot * 64 : a.v + vrow * (np / 2) + kt0 / 2;
       v0[db] = *reinterpret_cast<const u4*>(vp + 16 * hh);
       v1[db] = *reinterpret_cast<const u4*>(vp + 32 + 16 * hh);
-      vs[db] = *reinterpret_cast<const uint32_t*>(a.vs + vrow * (np / 32) + kt0 / 32);
+      vs[db] = *reinterpret_cast<const uint32_t*>(VT ? a.vs + vrow0 * (np / 32) + tslot * 4
+                                                     : a.vs + vrow * (np / 32) + kt0 / 32);
     }
   }
   __builtin_amdgcn_sched_barrier(0);  // every read is in flight before the MFMAs
@@ -341,9 +347,11 @@ hipError_t launch_decode(int pmode, const DecArgs& a, hipStream_t st) {
     return hipSuccess;
   };
   hipError_t e0;
-  if (pmode == PM_DIRECT) e0 = run(decode_kernel<PM_DIRECT>);
-  else if (pmode == PM_PNQ) e0 = run(decode_kernel<PM_PNQ>);
-  else if (pmode == PM_TWO_LEVEL) e0 = run(decode_kernel<PM_TWO_LEVEL>);
+  const bool vt = a.vtiled != 0;
+  if (pmode == PM_DIRECT) e0 = vt ? run(decode_kernel<PM_DIRECT, true>) : run(decode_kernel<PM_DIRECT, false>);
+  else if (pmode == PM_PNQ) e0 = vt ? run(decode_kernel<PM_PNQ, true>) : run(decode_kernel<PM_PNQ, false>);
+  else if (pmode == PM_TWO_LEVEL)
+    e0 = vt ? run(decode_kernel<PM_TWO_LEVEL, true>) : run(decode_kernel<PM_TWO_LEVEL, false>);
   else return hipErrorNotSupported;
   if (e0 != hipSuccess) return e0;
   hipError_t e = hipGetLastError();

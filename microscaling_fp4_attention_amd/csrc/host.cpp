@@ -32,8 +32,11 @@ int check_fmt(const mxattn_qfmt* f, int role) {
   if (f->elem != MXATTN_ELEM_E2M1 && f->elem != MXATTN_ELEM_E4M3) return MXATTN_E_INVALID;
   if (f->scale != MXATTN_SCALE_E8M0 && f->scale != MXATTN_SCALE_E4M3) return MXATTN_E_INVALID;
   if (f->block != 16 && f->block != 32) return MXATTN_E_UNSUPPORTED;
-  if (role != MXATTN_ROLE_QK && role != MXATTN_ROLE_V && role != MXATTN_ROLE_VKEY) return MXATTN_E_INVALID;
+  if (role != MXATTN_ROLE_QK && role != MXATTN_ROLE_V && role != MXATTN_ROLE_VKEY && role != MXATTN_ROLE_VT)
+    return MXATTN_E_INVALID;
   if (role == MXATTN_ROLE_VKEY && (f->elem != MXATTN_ELEM_E2M1 || f->scale != MXATTN_SCALE_E8M0))
+    return MXATTN_E_UNSUPPORTED;
+  if (role == MXATTN_ROLE_VT && (f->elem != MXATTN_ELEM_E2M1 || f->scale != MXATTN_SCALE_E8M0 || f->block != 32))
     return MXATTN_E_UNSUPPORTED;
   if (f->scale == MXATTN_SCALE_E8M0) {
     if (f->rule != MXATTN_RULE_OCP && f->rule != MXATTN_RULE_CEIL) return MXATTN_E_INVALID;
@@ -124,7 +127,8 @@ int mxattn_qtensor_bytes(const mxattn_qfmt* fmt, int role, int64_t B, int64_t H,
     *code_bytes = (size_t)(B * H * N * d * bits / 8);
     *scale_bytes = (size_t)(B * H * N * (d / fmt->block));
     if (n_padded) *n_padded = N;
-  } else if (role == MXATTN_ROLE_V) {
+  } else if (role == MXATTN_ROLE_V || role == MXATTN_ROLE_VT) {
+    if (role == MXATTN_ROLE_VT && ndocs > 1) return MXATTN_E_INVALID;  // tile-major V takes no documents
     int64_t np = v_padded(N, ndocs, fmt->block);
     *code_bytes = (size_t)(B * H * d * np * bits / 8);
     *scale_bytes = (size_t)(B * H * d * (np / fmt->block));
@@ -181,10 +185,11 @@ int mxattn_quantize(const void* x_bf16, const int64_t x_strides[4], int64_t B, i
   a.ndocs = ndocs > 1 ? ndocs : 1;
   a.codes = out->codes;
   a.scales = out->scales;
+  a.tiled = role == MXATTN_ROLE_VT ? 1 : 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = role == MXATTN_ROLE_QK ? launch_quant_qk(a, st)
-                 : role == MXATTN_ROLE_V  ? launch_quant_v(a, st)
-                                          : launch_quant_vkey(a, st);
+  hipError_t e = role == MXATTN_ROLE_QK                               ? launch_quant_qk(a, st)
+                 : role == MXATTN_ROLE_V || role == MXATTN_ROLE_VT ? launch_quant_v(a, st)
+                                                                   : launch_quant_vkey(a, st);
   if (e != hipSuccess) return hip_fail(e, "mxattn_quantize launch");
   return MXATTN_OK;
 }
@@ -308,7 +313,9 @@ int mxattn_decode(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn
                   const mxattn_fwd_params* p, const int32_t* kv_len, void* out, const int64_t os[4], float* lse,
                   void* workspace, size_t ws_bytes, void* stream) {
   if (!q || !k || !v || !p || !os) return MXATTN_E_INVALID;
-  if (q->role != MXATTN_ROLE_QK || k->role != MXATTN_ROLE_QK || v->role != MXATTN_ROLE_V) return MXATTN_E_INVALID;
+  if (q->role != MXATTN_ROLE_QK || k->role != MXATTN_ROLE_QK ||
+      (v->role != MXATTN_ROLE_V && v->role != MXATTN_ROLE_VT))
+    return MXATTN_E_INVALID;
   if (q->d != 128 || k->d != 128 || v->d != 128) return MXATTN_E_UNSUPPORTED;
   if (q->B != k->B || q->B != v->B || k->N != v->N || k->H != v->H || v->ndocs != 1) return MXATTN_E_INVALID;
   if (q->H <= 0 || k->H <= 0 || q->H % k->H != 0) return MXATTN_E_INVALID;
@@ -349,6 +356,7 @@ int mxattn_decode(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn
   a.N = N;
   a.np = v->n_padded;
   a.kv_len = kv_len;
+  a.vtiled = v->role == MXATTN_ROLE_VT ? 1 : 0;
   a.lambda = (float)((double)p->sm_scale * 1.4426950408889634);
   a.sm_scale = p->sm_scale;
   a.prule = make_rule(&p->pfmt);

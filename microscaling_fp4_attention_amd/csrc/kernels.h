@@ -23,6 +23,7 @@ struct QuantArgs {
   int ndocs;
   void* codes;
   void* scales;
+  int tiled;  // role VT: V written tile-major ([tile][channel][64 B] codes, [tile][channel][4 B] scales)
 };
 
 hipError_t launch_quant_qk(const QuantArgs& a, hipStream_t st);
@@ -114,10 +115,12 @@ struct DecArgs {
   const uint8_t* qs;
   const uint8_t* k;   // K codes [B][Hkv][N][64 B], scales [B][Hkv][N][4]
   const uint8_t* ks;
-  const uint8_t* v;   // V^T codes [B][Hkv][128][np / 2], scales [B][Hkv][128][np / 32]
+  const uint8_t* v;   // V^T codes [B][Hkv][128][np / 2], scales [B][Hkv][128][np / 32] (vtiled: tile-major,
+                      // [B][Hkv][np / 128][128][64 B] and [B][Hkv][np / 128][128][4 B])
   const uint8_t* vs;
   int64_t B, Hq, Hkv, R, N, np;
   const int32_t* kv_len;  // device [B] keys of each request, or null (N each)
+  int vtiled;             // V is role VT (tile-major)
   float lambda, sm_scale;
   E8m0Rule prule;
   int64_t nsplit;  // 512-key chunks of the longest history: ceil(N / 512)

@@ -168,7 +168,9 @@ __device__ __forceinline__ const int32_t* stage_offsets(const int32_t* cu, int n
 }
 constexpr int VQ_KT = 8;              // most key tiles of 128 slots per workgroup
 
-template <int ELEM, int SCALE, int BLOCK>
+// TILED (role VT, MXFP4 only): the same bytes tile-major, key tile t of channel c at
+// [t][c] (64 code bytes, 4 scale bytes).
+template <int ELEM, int SCALE, int BLOCK, bool TILED = false>
 __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict__ x, int64_t sB, int64_t sH,
                                                       int64_t sN, int64_t H, int64_t N, int64_t np,
                                                       const int32_t* __restrict__ cu, int ndocs, E8m0Rule rule,
@@ -253,7 +255,9 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
           }
         }
         const int64_t crow = bh * 128 + 2 * cp + c;
-        *reinterpret_cast<uint4*>(codes + crow * (np / 2) + (t0 + 32 * kq) / 2) = make_uint4(w[0], w[1], w[2], w[3]);
+        uint8_t* cdst = TILED ? codes + ((bh * ntiles + t0 / 128) * 128 + 2 * cp + c) * 64 + 16 * kq
+                              : codes + crow * (np / 2) + (t0 + 32 * kq) / 2;
+        *reinterpret_cast<uint4*>(cdst) = make_uint4(w[0], w[1], w[2], w[3]);
         sc[(2 * cp + c) * SCW + tt * SPT + kq] = (uint8_t)sb;
       }
     } else {
@@ -301,8 +305,9 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
   const int dpr = nt * SPT / 4;
   for (int i = tid; i < 128 * dpr; i += 256) {
     const int r = i / dpr, w = i - r * dpr;
-    *reinterpret_cast<uint32_t*>(scales + (bh * 128 + r) * (np / BLOCK) + tile0 * SPT + 4 * w) =
-        *reinterpret_cast<const uint32_t*>(sc + r * SCW + 4 * w);
+    uint8_t* sdst = TILED ? scales + ((bh * ntiles + tile0 + w) * 128 + r) * 4  // SPT = 4: one dword per tile
+                          : scales + (bh * 128 + r) * (np / BLOCK) + tile0 * SPT + 4 * w;
+    *reinterpret_cast<uint32_t*>(sdst) = *reinterpret_cast<const uint32_t*>(sc + r * SCW + 4 * w);
   }
 }
 
@@ -438,6 +443,12 @@ hipError_t launch_quant_v(const QuantArgs& a, hipStream_t st) {
 #define MXQV(E, S, BL)                                                                                   \
   quant_v_kernel<E, S, BL><<<grid, 256, 0, st>>>(x, a.sB, a.sH, a.sN, a.H, a.N, a.np, a.cu, a.ndocs, a.rule, \
                                                  c, s, kt)
+  if (a.tiled) {  // role VT: MXFP4 only (checked by the host)
+    if (a.elem != ELEM_E2M1 || a.scale != SCALE_E8M0 || a.block != 32) return hipErrorInvalidValue;
+    quant_v_kernel<ELEM_E2M1, SCALE_E8M0, 32, true><<<grid, 256, 0, st>>>(x, a.sB, a.sH, a.sN, a.H, a.N, a.np, a.cu,
+                                                                         a.ndocs, a.rule, c, s, kt);
+    return hipGetLastError();
+  }
   if (a.elem == ELEM_E2M1 && a.scale == SCALE_E8M0 && a.block == 32) MXQV(ELEM_E2M1, SCALE_E8M0, 32);
   else if (a.elem == ELEM_E2M1 && a.scale == SCALE_E8M0 && a.block == 16) MXQV(ELEM_E2M1, SCALE_E8M0, 16);
   else if (a.elem == ELEM_E2M1 && a.scale == SCALE_E4M3 && a.block == 16) MXQV(ELEM_E2M1, SCALE_E4M3, 16);

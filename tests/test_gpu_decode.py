@@ -77,6 +77,30 @@ def test_decode_gqa_32_8_long():
     run_decode("two_level", B=1, Hq=32, Hkv=8, R=1, N=32768, kv_len=None, seed=64)
 
 
+@pytest.mark.parametrize("pm,B,Hq,Hkv,R,N,kv_len", [("direct", 2, 8, 2, 1, 700, [700, 333]),
+                                                      ("pnq", 1, 4, 1, 8, 1300, None),
+                                                      ("two_level", 2, 4, 2, 1, 129, [129, 128]),
+                                                      ("two_level", 1, 32, 8, 1, 32768, None)])
+def test_decode_vt_equals_v(pm, B, Hq, Hkv, R, N, kv_len):
+    """The decode over role VT (V tile-major) gives exactly the decode over role V."""
+    import torch
+    import microscaling_fp4_attention_amd as mx
+    qf_, vf_ = FMT[pm]
+    q, k, v = _bf16((B, Hq, R, 128), 71, 1), _bf16((B, Hkv, N, 128), 71, 2, 0.3), _bf16((B, Hkv, N, 128), 71, 3)
+    dev = "cuda:0"
+    t = {n: torch.from_numpy(a.astype(np.int16)).view(torch.bfloat16).to(dev) for n, a in (("q", q), ("k", k), ("v", v))}
+    Q, K = mx.quantize(t["q"], mx.ROLE_QK, qf_), mx.quantize(t["k"], mx.ROLE_QK, qf_)
+    kl = None if kv_len is None else torch.tensor(kv_len, dtype=torch.int32, device=dev)
+    p = mx.fwd_params(pm, qf_, causal=True, out_fp32=True)
+    res = []
+    for role in (mx.ROLE_V, mx.ROLE_VT):
+        lse = torch.empty((B, Hq, R), dtype=torch.float32, device=dev)
+        out = mx.decode(Q, K, mx.quantize(t["v"], role, vf_), p, kv_len=kl, lse=lse)
+        res.append((out, lse))
+    torch.cuda.synchronize()
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
 def test_decode_refused():
     import torch
     import microscaling_fp4_attention_amd as mx

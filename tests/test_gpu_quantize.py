@@ -87,6 +87,25 @@ def test_quantize_qk_strided_input():
     assert np.array_equal(qt.scales_view().cpu().numpy(), s)
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp4_uos"])
+@pytest.mark.parametrize("N", [1000, 4500])
+def test_quantize_vt_is_v_tile_major(fmt, N):
+    """Role VT holds role V's bytes with key tile t of channel c moved to [t][c]."""
+    import microscaling_fp4_attention_amd as mx
+    x = _dev(synth.make_inputs("plain", 2, 3, 3, N, 128, seed=5)["v"])
+    v, vt = mx.quantize(x, mx.ROLE_V, fmt), mx.quantize(x, mx.ROLE_VT, fmt)
+    assert vt.n_padded == v.n_padded
+    nt = v.n_padded // 128
+    cv = v.codes_view().reshape(2, 3, 128, nt, 64).permute(0, 1, 3, 2, 4)
+    sv = v.scales_view().reshape(2, 3, 128, nt, 4).permute(0, 1, 3, 2, 4)
+    assert torch_equal(vt.codes_view(), cv) and torch_equal(vt.scales_view(), sv)
+
+
+def torch_equal(a, b):
+    import torch
+    return bool(torch.equal(a.contiguous(), b.contiguous()))
+
+
 def _e4m3_value(c):
     e, m = (c >> 3) & 15, c & 7
     return m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)

@@ -154,3 +154,18 @@ def test_decode_checks(mx):
     assert dec(mx, q, k, v, p, ws_bytes=need - 1) == WORKSPACE
     assert dec(mx, q, k, v, p, ws=FAKE + 4, ws_bytes=need) == ALIGN
     assert dec(mx, q, k, v, p, out=FAKE + 2) == ALIGN
+
+
+def test_role_vt_checks(mx):
+    # the tile-major V of the decode: role V's sizes, no documents, MXFP4 (E8M0 per 32) only
+    assert mx.qtensor_bytes("mxfp4_uos", mx.ROLE_VT, 2, 3, 1000) == mx.qtensor_bytes("mxfp4_uos", mx.ROLE_V, 2, 3, 1000)
+    with pytest.raises(mx.MxattnError) as e:
+        mx.qtensor_bytes("mxfp4", mx.ROLE_VT, 1, 2, 1000, ndocs=3)
+    assert e.value.status == INVALID
+    for fmt in ("nvfp4", "fp8v"):
+        with pytest.raises(mx.MxattnError) as e:
+            mx.qtensor_bytes(fmt, mx.ROLE_VT, 1, 2, 1000)
+        assert e.value.status == UNSUPPORTED
+    # the prefill takes role V only
+    q, k, v, p, _ = base(mx)
+    assert fwd(mx, q, k, qt(mx, mx.ROLE_VT, H=2), p) == INVALID
