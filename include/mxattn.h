@@ -216,8 +216,9 @@ int mxattn_qtensor_bytes(const mxattn_qfmt* fmt, int role, int64_t B, int64_t H,
  *   decrease; the kernel reads them, the host does not check them.
  * out: caller-owned descriptor whose codes/scales point to buffers of at least
  *   the sizes from mxattn_qtensor_bytes(); the library fills the other fields.
- * Errors: MXATTN_E_INVALID, MXATTN_E_UNSUPPORTED (d != 128, block not 16/32,
- *   E4M3 elements with an E4M3 scale), MXATTN_E_ALIGN, MXATTN_E_HIP.
+ * Errors: MXATTN_E_INVALID (also role VT with documents), MXATTN_E_UNSUPPORTED
+ *   (d != 128, block not 16/32, E4M3 elements with an E4M3 scale, role VT in any
+ *   format but E2M1 with E8M0 per 32), MXATTN_E_ALIGN, MXATTN_E_HIP.
  */
 int mxattn_quantize(const void* x_bf16, const int64_t x_strides[4], int64_t B, int64_t H, int64_t N,
                     int64_t d, int role, const mxattn_qfmt* fmt, const int32_t* cu_seqlens, int ndocs,
