@@ -851,11 +851,15 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       __attribute__((always_inline)) -> float {
     float lsum = 0.0f;
     float y[16];
+    // an E4M3 group scale's multiplier is applied with the two-level pre-scale in one
+    // product (k1 ki rounded once per group instead of each element rounded twice)
+    constexpr bool FOLD = PV == PV_BF16 && PSC != SCALE_E8M0;
+    const float kel = FOLD ? (PMODE == PM_TWO_LEVEL ? k1 * ki : ki) : k1;
 #pragma unroll
     for (int j = 0; j < 16; j++) {
       float pt = pexp(S[bb][j], ms, cm);
       if constexpr (PMODE != PM_PNQ) lsum += pt;
-      if constexpr (PMODE == PM_TWO_LEVEL) pt *= k1;
+      if constexpr (PMODE == PM_TWO_LEVEL || FOLD) pt *= kel;
       y[j] = pt;
     }
     if constexpr (PV == PV_FP4) {  // into the registers of the previous tile's P
@@ -870,11 +874,8 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
         bp[bb >> 1][4 * (bb & 1) + dw] = x;
       }
     } else {
-      float z[16];
-#pragma unroll
-      for (int j = 0; j < 16; j++) z[j] = PSC == SCALE_E8M0 ? y[j] : y[j] * ki;
-      pc[2 * bb] = pack8_fp4(z, sc);
-      pc[2 * bb + 1] = pack8_fp4(z + 8, sc);
+      pc[2 * bb] = pack8_fp4(y, sc);  // y already carries the group's multiplier
+      pc[2 * bb + 1] = pack8_fp4(y + 8, sc);
       pdq[bb] = sv;
       if constexpr (PMODE == PM_PNQ) {  // row sum of the dequantized P
 #pragma unroll
