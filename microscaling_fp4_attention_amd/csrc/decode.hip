@@ -14,8 +14,9 @@
 //     their log-sum-exp (the same arithmetic as the sequential rescale, up to FP32
 //     rounding).  One tile per wave keeps a wave's live registers low, so two
 //     workgroups share a CU and more of the history is in flight;
-//   * the query heads of the KV head's group and the R newest tokens share the 32
-//     query columns of the MFMA (column c = head (c / R), row (c % R));
+//   * the query heads of the KV head's group and the R newest tokens share the query
+//     columns of the MFMA (column c = head (c / R), row (c % R)): up to 16 columns on
+//     the 16x16x128 MFMA (whole-row operand reads, below), up to 32 on the 32x32x64;
 //   * each wave reads its K and V operands straight from HBM in the MFMA operand
 //     layout (no LDS: the waves share no tile); K rows are read in the key order that
 //     makes each lane's 16 scores 16 consecutive keys (key_of), so the P codes built in
@@ -33,6 +34,45 @@ namespace mxattn {
 
 constexpr int DEC_SPLIT = 256;  // keys per split (the partition of the merge)
 constexpr int DEC_CHUNK = 512;  // keys per workgroup: two splits, one tile per wave
+
+// the 4 tile states of a chunk (normalized outputs in `so` as [tile][column][channel],
+// rows padded to 129, and log-sum-exps in `slse`), merged by their log-sum-exp into the
+// chunk's state in the workspace; thread -> (column tid / 8, 16 channels from 16 (tid % 8))
+__device__ __forceinline__ void merge_chunk(const DecArgs& a, const float* so, const float (*slse)[32], int ncol,
+                                            int64_t b, int64_t hk, int gsz, int64_t chunk) {
+  const int tid = threadIdx.x;
+  auto sidx = [&](int w, int c, int ch) { return (w * ncol + c) * 129 + ch; };
+  const int cc = tid >> 3, c0 = 16 * (tid & 7);
+  if (cc >= ncol) return;
+  const int gg = cc / (int)a.R, rr = cc % (int)a.R;
+  const int64_t orow = ((b * a.Hq + hk * gsz + gg) * a.R + rr) * a.nsplit + chunk;
+  float M = NEG_INF;
+#pragma unroll
+  for (int w = 0; w < 4; w++) M = fmaxn(M, slse[w][cc]);
+  float wt[4], wsum = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 4; w++) {
+    wt[w] = (M == NEG_INF || slse[w][cc] == NEG_INF) ? 0.0f : __expf(slse[w][cc] - M);
+    wsum += wt[w];
+  }
+  const float winv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  float* op = a.ws_o + orow * 128 + c0;
+#pragma unroll
+  for (int c = 0; c < 16; c += 4) {
+    float4 t;
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++)
+      v[u] = (wt[0] * so[sidx(0, cc, c0 + c + u)] + wt[1] * so[sidx(1, cc, c0 + c + u)] +
+              wt[2] * so[sidx(2, cc, c0 + c + u)] + wt[3] * so[sidx(3, cc, c0 + c + u)]) * winv;
+    t.x = v[0];
+    t.y = v[1];
+    t.z = v[2];
+    t.w = v[3];
+    *reinterpret_cast<float4*>(op + c) = t;
+  }
+  if ((tid & 7) == 0) a.ws_lse[orow] = wsum > 0.0f ? M + __logf(wsum) : NEG_INF;
+}
 
 // VT: V is role VT (tile-major: key tile t of channel c at [t][c], 64 code bytes and 4
 // scale bytes), so a tile's V^T is one contiguous run
@@ -216,46 +256,181 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecArgs a) {
   // so: [tile][column < ncol][channel] (rows padded to 129), sized by the launch
   extern __shared__ float so[];
   __shared__ float slse[4][32];
-  auto sidx = [&](int w, int c, int ch) { return (w * ncol + c) * 129 + ch; };
   if (cvalid)
 #pragma unroll
     for (int db = 0; db < 4; db++)
 #pragma unroll
-      for (int j = 0; j < 16; j++) so[sidx(wave, ql, 32 * db + 8 * (j >> 2) + 4 * hh + (j & 3))] = O[db][j] * inv;
+      for (int j = 0; j < 16; j++)
+        so[(wave * ncol + ql) * 129 + 32 * db + 8 * (j >> 2) + 4 * hh + (j & 3)] = O[db][j] * inv;
   if (hh == 0) slse[wave][ql] = l > 0.0f ? __logf(l) + m * a.sm_scale : NEG_INF;
   __syncthreads();
-  // thread -> (column cc = tid / 8, 16 channels from 16 (tid % 8))
-  const int cc = tid >> 3, c0 = 16 * (tid & 7);
-  if (cc < ncol) {
-    const int gg = cc / (int)a.R, rr = cc % (int)a.R;
-    const int64_t orow = ((b * a.Hq + hk * gsz + gg) * a.R + rr) * a.nsplit + chunk;
-    float M = NEG_INF;
-#pragma unroll
-    for (int w = 0; w < 4; w++) M = fmaxn(M, slse[w][cc]);
-    float wt[4], wsum = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; w++) {
-      wt[w] = (M == NEG_INF || slse[w][cc] == NEG_INF) ? 0.0f : __expf(slse[w][cc] - M);
-      wsum += wt[w];
-    }
-    const float winv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-    float* op = a.ws_o + orow * 128 + c0;
-#pragma unroll
-    for (int c = 0; c < 16; c += 4) {
-      float4 t;
-      float v[4];
-#pragma unroll
-      for (int u = 0; u < 4; u++)
-        v[u] = (wt[0] * so[sidx(0, cc, c0 + c + u)] + wt[1] * so[sidx(1, cc, c0 + c + u)] +
-                wt[2] * so[sidx(2, cc, c0 + c + u)] + wt[3] * so[sidx(3, cc, c0 + c + u)]) * winv;
-      t.x = v[0];
-      t.y = v[1];
-      t.z = v[2];
-      t.w = v[3];
-      *reinterpret_cast<float4*>(op + c) = t;
-    }
-    if ((tid & 7) == 0) a.ws_lse[orow] = wsum > 0.0f ? M + __logf(wsum) : NEG_INF;
+  merge_chunk(a, so, slse, ncol, b, hk, gsz, chunk);
+}
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// The same decode for up to 16 query columns on the 16x16x128 block-scaled MFMA.  A
+// 16-row operand holds each row's 128 contraction elements in four 16-byte blocks, one
+// per quarter of the wave (lane l: row l % 16, block l / 16), so one 16-byte load per
+// lane covers 16 whole 64-byte rows: the K rows of a sub-tile and the V^T channel rows
+// are read as whole rows, where the 32-column form reads half of each of 32 rows.
+//   * S^T = K Q^T per 16-key sub-tile st (8 per tile): MFMA row r reads key
+//     32 (r / 4) + 4 st + r % 4 of the tile, so the lane of (column c, row group g)
+//     holds the scores of the 32 consecutive keys [32 g, 32 g + 32) over the 8
+//     sub-tiles (element 4 st + i is key 32 g + 4 st + i): one 32-key P block per lane,
+//     whose maximum needs no other lane, and whose codes are the lane's B operand of
+//     O^T = V^T P^T (block g of column c);
+//   * K rows of a sub-tile come in four runs of 4 consecutive keys (256 contiguous
+//     bytes each), V^T channel rows in one 1 KB run (tile-major) or 16 runs of 64 B.
+template <int PMODE, bool VT>
+__global__ __launch_bounds__(256, 2) void decode16_kernel(DecArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63, qc = lane & 15, kb = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t nchunk = (a.N + DEC_CHUNK - 1) / DEC_CHUNK;
+  const int64_t chunk = blockIdx.x % nchunk, bhk = blockIdx.x / nchunk;
+  const int64_t b = bhk / a.Hkv, hk = bhk % a.Hkv;
+  const int gsz = (int)(a.Hq / a.Hkv);
+  const int ncol = gsz * (int)a.R;  // <= 16
+  const bool cvalid = qc < ncol;
+  const int g = cvalid ? qc / (int)a.R : 0, r = cvalid ? qc % (int)a.R : 0;
+  const int64_t hq = hk * gsz + g;
+  const int kt0 = (int)chunk * DEC_CHUNK + 128 * wave;
+  const float lam = a.lambda;
+
+  // Q operand (B of S^T = K Q^T): column qc, channel block kb; an absent column reads
+  // column 0's row (its scores are masked)
+  v8i qop;
+  uint32_t qsc;
+  {
+    const int64_t qrow = (b * a.Hq + hq) * a.R + r;
+    qop = v8_from4(*reinterpret_cast<const u4*>(a.q + qrow * 64 + 16 * kb));
+    qsc = *reinterpret_cast<const uint32_t*>(a.qs + qrow * 4) >> (8 * kb);
   }
+  const uint8_t* kc = a.k + (b * a.Hkv + hk) * a.N * 64;
+  const uint8_t* kscl = a.ks + (b * a.Hkv + hk) * a.N * 4;
+  const int64_t vrow0 = (b * a.Hkv + hk) * 128;
+  const uint32_t np = (uint32_t)a.np;
+
+  // ---- every operand of the tile requested before any is used; keys past N read row
+  // N - 1 (masked).  The padded key axis of V is a multiple of 128, so a tile's V codes
+  // and its 4 scale bytes lie inside the row and the scale dword is aligned.
+  u4 kq[8], vq[8];
+  uint32_t ks[8], vs[8];
+  if (kt0 < (int)a.N) {
+#pragma unroll
+    for (int st = 0; st < 8; st++) {
+      int key = kt0 + 32 * (qc >> 2) + 4 * st + (qc & 3);
+      key = key < (int)a.N ? key : (int)a.N - 1;
+      kq[st] = *reinterpret_cast<const u4*>(kc + (int64_t)key * 64 + 16 * kb);
+      ks[st] = *reinterpret_cast<const uint32_t*>(kscl + (int64_t)key * 4);
+    }
+#pragma unroll
+    for (int db = 0; db < 8; db++) {
+      const int64_t vrow = vrow0 + 16 * db + qc;
+      // slot of (tile, channel) in the tile-major form; kt0 < N <= np keeps both forms
+      // inside the head's V
+      const int64_t tslot = (int64_t)(kt0 / 128) * 128 + 16 * db + qc;
+      const uint8_t* vp = VT ? a.v + vrow0 * (np / 2) + tslot * 64 : a.v + vrow * (np / 2) + kt0 / 2;
+      vq[db] = *reinterpret_cast<const u4*>(vp + 16 * kb);
+      vs[db] = *reinterpret_cast<const uint32_t*>(VT ? a.vs + vrow0 * (np / 32) + tslot * 4
+                                                     : a.vs + vrow * (np / 32) + kt0 / 32);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every read is in flight before the MFMAs
+  const int L = a.kv_len != nullptr ? a.kv_len[b] : (int)a.N;
+  const int pos = L - (int)a.R + r;  // keys <= pos are visible to this column's query
+  const bool live = kt0 < L;
+  float y[32];  // the lane's 32 scores, key kt0 + 32 kb + j
+  float bmax = NEG_INF, tmax = NEG_INF;
+  if (live) {
+#pragma unroll
+    for (int st = 0; st < 8; st++) {
+      v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(v8_from4(kq[st]), qop, acc, 4, 4, 0,
+                                                             (int)(ks[st] >> (8 * kb)), 0, (int)qsc);
+#pragma unroll
+      for (int i = 0; i < 4; i++) y[4 * st + i] = acc[i];
+    }
+#pragma unroll
+    for (int j = 0; j < 32; j++) {
+      const int key = kt0 + 32 * kb + j;
+      y[j] = (cvalid && key <= pos) ? y[j] : NEG_INF;  // pos < L
+      bmax = fmaxn(bmax, y[j]);
+    }
+    tmax = fmaxn(bmax, __shfl_xor(bmax, 16));
+    tmax = fmaxn(tmax, __shfl_xor(tmax, 32));
+  }
+
+  // ---- the running maximum before this tile: the split's first tile starts from
+  // -inf, its second from the first tile's maximum
+  __shared__ float smax[4][32];
+  if (kb == 0) smax[wave][qc] = tmax;
+  __syncthreads();
+  const float m0 = (wave & 1) ? smax[wave - 1][qc] : NEG_INF;
+
+  float m = m0, l = 0.0f, s1 = 1.0f;
+  v4f O[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) O[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  if (live) {
+    // ---- online softmax step and P quantization (E2M1, one E8M0 scale per lane's
+    // 32-key block); the tile's state starts empty, so nothing needs the rescale
+    const float mnew = fmaxn(m0, tmax);
+    const float ms = mnew == NEG_INF ? 0.0f : mnew * lam;
+    m = mnew;
+    float k1s = 1.0f;
+    if constexpr (PMODE == PM_TWO_LEVEL) {
+      const float rr = exp2_hw(__builtin_fmaf(tmax, lam, -ms));
+      if (rr >= 0x1p-64f) {
+        s1 = rr / 2688.0f;
+        k1s = 1.0f / s1;
+      } else {
+        k1s = 0.0f;  // a tile whose P~ stays below 2^-64 of the running maximum adds nothing
+      }
+    }
+    int e = e8m0_exp(exp2_hw(__builtin_fmaf(bmax, lam, -ms)) * k1s, a.prule);
+    e = e < -126 ? -126 : e;
+    const float sc = u2f((uint32_t)(e + 127) << 23);
+    float lsum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; j++) {
+      float pt = exp2_hw(__builtin_fmaf(y[j], lam, -ms));
+      if constexpr (PMODE != PM_PNQ) lsum += pt;
+      if constexpr (PMODE == PM_TWO_LEVEL) pt *= k1s;
+      y[j] = pt;
+    }
+    const v8i bp = v8_from4(mk4(pack8_fp4(y, sc), pack8_fp4(y + 8, sc), pack8_fp4(y + 16, sc), pack8_fp4(y + 24, sc)));
+    const int psc = e + 127;
+
+    // ---- O^T = V^T P^T: channel rows 16 db + qc, keys kt0 + [0, 128) in order
+#pragma unroll
+    for (int db = 0; db < 8; db++)
+      O[db] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(v8_from4(vq[db]), bp, O[db], 4, 4, 0,
+                                                               (int)(vs[db] >> (8 * kb)), 0, psc);
+    if constexpr (PMODE == PM_PNQ) {  // row sum of the dequantized P: a block of ones times P^T
+      const v8i ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};
+      v4f Lacc = {0.0f, 0.0f, 0.0f, 0.0f};
+      Lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, bp, Lacc, 4, 4, 0, 127, 0, psc);
+      l = Lacc[0];
+    } else {
+      lsum += __shfl_xor(lsum, 16);
+      l = lsum + __shfl_xor(lsum, 32);
+    }
+  }
+
+  // ---- the tile's normalized output and log-sum-exp, then the chunk merge
+  float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  if constexpr (PMODE == PM_TWO_LEVEL) inv *= s1;
+  extern __shared__ float so[];  // [tile][column < ncol][channel], rows padded to 129
+  __shared__ float slse[4][32];
+  if (cvalid)
+#pragma unroll
+    for (int db = 0; db < 8; db++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) so[(wave * ncol + qc) * 129 + 16 * db + 4 * kb + i] = O[db][i] * inv;
+  if (kb == 0) slse[wave][qc] = l > 0.0f ? __logf(l) + m * a.sm_scale : NEG_INF;
+  __syncthreads();
+  merge_chunk(a, so, slse, ncol, b, hk, gsz, chunk);
 }
 
 // merge of the chunk states of one (request, query head, row) by their log-sum-exp.
@@ -346,12 +521,19 @@ hipError_t launch_decode(int pmode, const DecArgs& a, hipStream_t st) {
     kern<<<grid, 256, shm, st>>>(a);
     return hipSuccess;
   };
+  // up to 16 query columns: the 16-column form, which reads whole K and V rows
+  auto pick = [&](auto k32, auto k16) { return (a.Hq / a.Hkv) * a.R <= 16 ? run(k16) : run(k32); };
   hipError_t e0;
   const bool vt = a.vtiled != 0;
-  if (pmode == PM_DIRECT) e0 = vt ? run(decode_kernel<PM_DIRECT, true>) : run(decode_kernel<PM_DIRECT, false>);
-  else if (pmode == PM_PNQ) e0 = vt ? run(decode_kernel<PM_PNQ, true>) : run(decode_kernel<PM_PNQ, false>);
+  if (pmode == PM_DIRECT)
+    e0 = vt ? pick(decode_kernel<PM_DIRECT, true>, decode16_kernel<PM_DIRECT, true>)
+            : pick(decode_kernel<PM_DIRECT, false>, decode16_kernel<PM_DIRECT, false>);
+  else if (pmode == PM_PNQ)
+    e0 = vt ? pick(decode_kernel<PM_PNQ, true>, decode16_kernel<PM_PNQ, true>)
+            : pick(decode_kernel<PM_PNQ, false>, decode16_kernel<PM_PNQ, false>);
   else if (pmode == PM_TWO_LEVEL)
-    e0 = vt ? run(decode_kernel<PM_TWO_LEVEL, true>) : run(decode_kernel<PM_TWO_LEVEL, false>);
+    e0 = vt ? pick(decode_kernel<PM_TWO_LEVEL, true>, decode16_kernel<PM_TWO_LEVEL, true>)
+            : pick(decode_kernel<PM_TWO_LEVEL, false>, decode16_kernel<PM_TWO_LEVEL, false>);
   else return hipErrorNotSupported;
   if (e0 != hipSuccess) return e0;
   hipError_t e = hipGetLastError();

@@ -1,7 +1,9 @@
 """GPU split-key decode (mxattn_decode) against the oracle's split decode ("MpFA ...",
 section 5.3): the same quantized bytes, splits of 256 keys merged by log-sum-exp,
 |dO| <= 2e-3 max|O| + the merged flip budget; ragged histories, several newest rows,
-packed GQA groups, and a 32:8 GQA decode over 32K keys."""
+packed GQA groups, and a 32:8 GQA decode over 32K keys.  Up to 16 packed query columns
+(query heads per KV head x newest rows) run on the 16-column kernel, 17 to 32 on the
+32-column one; both are covered for every P mode."""
 import numpy as np
 import pytest
 
@@ -62,6 +64,14 @@ def test_decode_several_rows(R):
     run_decode("pnq", B=1, Hq=4, Hkv=1, R=R, N=1300, kv_len=None, seed=62)
 
 
+@pytest.mark.parametrize("pm", ["direct", "pnq", "two_level"])
+@pytest.mark.parametrize("Hq,Hkv,R", [(8, 1, 3), (16, 2, 2), (4, 1, 4)])
+def test_decode_column_forms(pm, Hq, Hkv, R):
+    """24 and 16 packed columns: the 32-column kernel and the 16-column kernel at its
+    limit, over a ragged history"""
+    run_decode(pm, B=2, Hq=Hq, Hkv=Hkv, R=R, N=1100, kv_len=[1100, 517], seed=66)
+
+
 def test_decode_minimal_history():
     run_decode("direct", B=3, Hq=2, Hkv=2, R=2, N=260, kv_len=[2, 130, 257], seed=63)
 
@@ -80,7 +90,8 @@ def test_decode_gqa_32_8_long():
 @pytest.mark.parametrize("pm,B,Hq,Hkv,R,N,kv_len", [("direct", 2, 8, 2, 1, 700, [700, 333]),
                                                       ("pnq", 1, 4, 1, 8, 1300, None),
                                                       ("two_level", 2, 4, 2, 1, 129, [129, 128]),
-                                                      ("two_level", 1, 32, 8, 1, 32768, None)])
+                                                      ("two_level", 1, 32, 8, 1, 32768, None),
+                                                      ("two_level", 2, 8, 1, 3, 1100, [1100, 517])])
 def test_decode_vt_equals_v(pm, B, Hq, Hkv, R, N, kv_len):
     """The decode over role VT (V tile-major) gives exactly the decode over role V."""
     import torch
