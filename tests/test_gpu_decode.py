@@ -65,10 +65,10 @@ def test_decode_several_rows(R):
 
 
 @pytest.mark.parametrize("pm", ["direct", "pnq", "two_level"])
-@pytest.mark.parametrize("Hq,Hkv,R", [(8, 1, 3), (16, 2, 2), (4, 1, 4)])
+@pytest.mark.parametrize("Hq,Hkv,R", [(8, 1, 3), (17, 1, 1), (16, 2, 2), (4, 1, 4)])
 def test_decode_column_forms(pm, Hq, Hkv, R):
-    """24 and 16 packed columns: the 32-column kernel and the 16-column kernel at its
-    limit, over a ragged history"""
+    """24 and 17 packed columns (the 32-column kernel) and 16 (the 16-column kernel at
+    its limit), over a ragged history"""
     run_decode(pm, B=2, Hq=Hq, Hkv=Hkv, R=R, N=1100, kv_len=[1100, 517], seed=66)
 
 
