@@ -52,7 +52,8 @@ __device__ __forceinline__ const int32_t* stage_docs(const int32_t* __restrict__
 // of 16 channels.  The 8 workgroups of a unit get ids of one residue mod 8, which the
 // dispatcher deals to one XCD, so each 256-byte token row is fetched into one L2.
 // Thread i sums channels 16 g + 8 (i % 2) + [0, 8) over the tokens t0 + 256 k + i / 2
-// in double; the 256 partial sums of a channel are then added in a fixed order.
+// in double, 8 reads in flight; the 256 partial sums of a channel are then added in a
+// fixed order.
 // mean: [B][H][nd][128]; units = B H nd, the grid covers round_up(units, 8) * 8 ids.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(512) void channel_mean_kernel(const uint16_t* __restrict__ x, int64_t sB, int64_t sH,
@@ -65,29 +66,31 @@ __global__ __launch_bounds__(512) void channel_mean_kernel(const uint16_t* __res
   const int cg = (int)((id / 8) % 8);
   if (unit >= units) return;  // whole workgroup
   const int tid = threadIdx.x, half = tid & 1, slot = tid >> 1;
-  const int64_t doc = unit % nd, bh = unit / nd, b = bh / H, h = bh % H;
+  // units are numbered document-major, u = doc * (B H) + (b H + h): the heads of one
+  // document then have consecutive numbers and spread over the XCDs, where numbering
+  // by head first would send every head of a document to the XCD of its residue
+  const int64_t BH = units / nd;
+  const int64_t doc = unit / BH, bh = unit % BH, b = bh / H, h = bh % H;
   const int64_t t0 = cu ? cu[doc] : 0, t1 = cu ? cu[doc + 1] : N;
   const uint16_t* base = x + b * sB + h * sH + cg * 16 + half * 8;
   double s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  int64_t t = t0 + slot;
-  for (; t + 768 < t1; t += 1024) {  // four tokens in flight per thread
-    uint4 v[4];
+  // rounds of 8 tokens per thread, every read of a round issued before any is added;
+  // a token past the document adds nothing (not even +0, which would turn a -0 sum
+  // positive), so each thread adds its tokens t0 + slot + 256 k in increasing k
+  for (int64_t t = t0 + slot; t < t1; t += 8 * 256) {
+    uint4 v[8];
 #pragma unroll
-    for (int u = 0; u < 4; u++) v[u] = *reinterpret_cast<const uint4*>(base + (t + 256 * u) * sN);
+    for (int u = 0; u < 8; u++)
+      v[u] = t + 256 * u < t1 ? *reinterpret_cast<const uint4*>(base + (t + 256 * u) * sN) : uint4{0, 0, 0, 0};
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
-      s[0] += (double)bf16_lo_f(v[u].x); s[1] += (double)bf16_hi_f(v[u].x);
-      s[2] += (double)bf16_lo_f(v[u].y); s[3] += (double)bf16_hi_f(v[u].y);
-      s[4] += (double)bf16_lo_f(v[u].z); s[5] += (double)bf16_hi_f(v[u].z);
-      s[6] += (double)bf16_lo_f(v[u].w); s[7] += (double)bf16_hi_f(v[u].w);
+    for (int u = 0; u < 8; u++) {
+      if (t + 256 * u < t1) {
+        s[0] += (double)bf16_lo_f(v[u].x); s[1] += (double)bf16_hi_f(v[u].x);
+        s[2] += (double)bf16_lo_f(v[u].y); s[3] += (double)bf16_hi_f(v[u].y);
+        s[4] += (double)bf16_lo_f(v[u].z); s[5] += (double)bf16_hi_f(v[u].z);
+        s[6] += (double)bf16_lo_f(v[u].w); s[7] += (double)bf16_hi_f(v[u].w);
+      }
     }
-  }
-  for (; t < t1; t += 256) {
-    uint4 v = *reinterpret_cast<const uint4*>(base + t * sN);
-    s[0] += (double)bf16_lo_f(v.x); s[1] += (double)bf16_hi_f(v.x);
-    s[2] += (double)bf16_lo_f(v.y); s[3] += (double)bf16_hi_f(v.y);
-    s[4] += (double)bf16_lo_f(v.z); s[5] += (double)bf16_hi_f(v.z);
-    s[6] += (double)bf16_lo_f(v.w); s[7] += (double)bf16_hi_f(v.w);
   }
 #pragma unroll
   for (int j = 0; j < 8; j++) part[slot][half * 8 + j] = s[j];
@@ -108,7 +111,7 @@ __global__ __launch_bounds__(512) void channel_mean_kernel(const uint16_t* __res
 #pragma unroll
     for (int g = 0; g < 16; g++) acc += part2[g][tid];
     const int64_t L = t1 - t0;
-    mean[unit * 128 + cg * 16 + tid] = L > 0 ? (float)(acc / (double)L) : 0.0f;
+    mean[(bh * nd + doc) * 128 + cg * 16 + tid] = L > 0 ? (float)(acc / (double)L) : 0.0f;
   }
 }
 
