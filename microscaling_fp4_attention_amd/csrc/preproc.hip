@@ -17,6 +17,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_util.h"
 #include "formats.h"
 #include "kernels.h"
 
@@ -203,14 +204,22 @@ __global__ __launch_bounds__(256) void quant_qk_pre_kernel(const uint16_t* __res
   float inv, s;
   const uint32_t sb = pre_block_scale<SCALE>(M, rule, &inv, &s);
   uint32_t w = 0;
+  const int e = (int)sb - 127;
+  if (SCALE == SCALE_E8M0 && e >= -124 && e < 127) {
+    // power-of-two scale away from the ends of the E8M0 range: the scaled FP4 convert
+    // (z 2^-e is exact wherever it can round to a nonzero code; round to nearest even,
+    // saturation at 6, sign kept, as the encoder below)
+    w = pack8_fp4(z, u2f((uint32_t)(e + 127) << 23));
+  } else {
 #pragma unroll
-  for (int j = 0; j < 8; j++) {
-    const uint32_t sign = f2u(z[j]) >> 31;
-    const float a = __builtin_fabsf(z[j]);
-    float q;
-    if constexpr (SCALE == SCALE_E8M0) q = a * inv;
-    else q = (s == 0.0f) ? 0.0f : a / s;
-    w |= (e2m1_mag(q) | (sign << 3)) << (4 * j);
+    for (int j = 0; j < 8; j++) {
+      const uint32_t sign = f2u(z[j]) >> 31;
+      const float a = __builtin_fabsf(z[j]);
+      float q;
+      if constexpr (SCALE == SCALE_E8M0) q = a * inv;
+      else q = (s == 0.0f) ? 0.0f : a / s;
+      w |= (e2m1_mag(q) | (sign << 3)) << (4 * j);
+    }
   }
   if (live) {
     codes[row * 16 + chunk] = w;
