@@ -149,9 +149,10 @@ __global__ __launch_bounds__(256) void quant_qk_pre_kernel(const uint16_t* __res
   const int64_t row = gid >> 4;
   const int chunk = (int)(gid & 15);
   const bool live = row < rows;
-  const int64_t r = live ? row : rows - 1;
-  const int64_t n = r % N, bh = r / N;
-  const int64_t h = bh % H, b = bh / H;
+  // row = (b H + h) N + n; 32-bit division (the launcher keeps rows below 2^31)
+  const uint32_t r = (uint32_t)(live ? row : rows - 1);
+  const int64_t n = r % (uint32_t)N, bh = r / (uint32_t)N;
+  const int64_t h = (uint32_t)bh % (uint32_t)H, b = (uint32_t)bh / (uint32_t)H;
   const uint4 v = *reinterpret_cast<const uint4*>(x + b * sB + h * sH + n * sN + chunk * 8);
   const float f[8] = {bf16_lo_f(v.x), bf16_hi_f(v.x), bf16_lo_f(v.y), bf16_hi_f(v.y),
                       bf16_lo_f(v.z), bf16_hi_f(v.z), bf16_lo_f(v.w), bf16_hi_f(v.w)};
@@ -243,8 +244,10 @@ __global__ __launch_bounds__(256) void center_comp_kernel(const float* __restric
   const int64_t row = gid >> 4;  // (b, hk, token); the 16 lanes of a row are all live or all not
   const int chunk = (int)(gid & 15);
   const bool live = row < rows;
-  const int64_t r = live ? row : rows - 1;
-  const int64_t n = r % N, bhk = r / N, hk = bhk % Hkv, b = bhk / Hkv;
+  // row = (b Hkv + hk) N + n; 32-bit division (the launcher keeps rows below 2^31)
+  const uint32_t r = (uint32_t)(live ? row : rows - 1);
+  const int64_t n = r % (uint32_t)N, bhk = r / (uint32_t)N;
+  const int64_t hk = (uint32_t)bhk % (uint32_t)Hkv, b = (uint32_t)bhk / (uint32_t)Hkv;
   const int nd = ndocs > 1 ? ndocs : 1;
   const int doc = doc_of_token(stage_docs(cu, ndocs, scu), ndocs, n);
   const uint4 v = *reinterpret_cast<const uint4*>(k + b * sB + hk * sH + n * sN + chunk * 8);
@@ -282,6 +285,7 @@ hipError_t launch_channel_mean(const QuantArgs& a, float* mean, hipStream_t st) 
 
 hipError_t launch_quant_qk_pre(const QuantArgs& a, const float* mean, int hadamard, hipStream_t st) {
   const int64_t rows = a.B * a.H * a.N;
+  if (rows >= (int64_t(1) << 31)) return hipErrorInvalidValue;  // 32-bit row indices
   dim3 grid((unsigned)((rows * 16 + 255) / 256));
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   uint32_t* c = static_cast<uint32_t*>(a.codes);
@@ -301,6 +305,7 @@ hipError_t launch_quant_qk_pre(const QuantArgs& a, const float* mean, int hadama
 
 hipError_t launch_center_comp(const CompArgs& a, hipStream_t st) {
   const int64_t rows = a.B * a.Hkv * a.N;
+  if (rows >= (int64_t(1) << 31)) return hipErrorInvalidValue;  // 32-bit row indices
   center_comp_kernel<<<dim3((unsigned)((rows * 16 + 255) / 256)), 256, 0, st>>>(
       a.qmean, static_cast<const uint16_t*>(a.k), a.sB, a.sH, a.sN, a.kmean, a.Hq, a.Hkv, a.N, rows,
       a.ndocs > 1 ? a.cu : nullptr, a.ndocs, a.delta);
