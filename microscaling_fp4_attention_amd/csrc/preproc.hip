@@ -211,6 +211,21 @@ __global__ __launch_bounds__(256) void quant_qk_pre_kernel(const uint16_t* __res
     // (z 2^-e is exact wherever it can round to a nonzero code; round to nearest even,
     // saturation at 6, sign kept, as the encoder below)
     w = pack8_fp4(z, u2f((uint32_t)(e + 127) << 23));
+  } else if (SCALE == SCALE_E4M3 && M < __builtin_inff()) {
+    // E4M3 scale: fl32(z / s) from the block's correctly rounded reciprocal r by one
+    // residual step (q = z r, e = z - s q exactly by FMA, q + e r rounded once:
+    // Markstein's division, equal to the IEEE quotient for every float z of every
+    // binade whose quotients stay normal), then the scaled FP4 convert at scale 1,
+    // with z's sign; a zero scale gives zero quotients
+    const float r = s > 0.0f ? 1.0f / s : 0.0f;
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const float q = z[j] * r;
+      const float t = __builtin_fmaf(__builtin_fmaf(-q, s, z[j]), r, q);
+      y[j] = __builtin_copysignf(s > 0.0f ? t : 0.0f, z[j]);
+    }
+    w = pack8_fp4(y, 1.0f);
   } else {
 #pragma unroll
     for (int j = 0; j < 8; j++) {
