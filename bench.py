@@ -37,28 +37,35 @@ TRAFFIC_FILES = {"c3": "profiles/fwd_pp_kernel_c3_video_dit_32k_traffic.txt",
 # the forward kernel's source: the kernel file and the headers it includes
 KERNEL_SOURCES = ["microscaling_fp4_attention_amd/csrc/fwd.hip", "microscaling_fp4_attention_amd/csrc/device_util.h",
                   "microscaling_fp4_attention_amd/csrc/formats.h", "microscaling_fp4_attention_amd/csrc/kernels.h"]
+# the same for the split-key decode at 128K keys (V tile-major), its main kernel
+DECODE_TRAFFIC_FILE = "profiles/decode_kernel_gqa_128k_traffic.txt"
+DECODE_SOURCES = ["microscaling_fp4_attention_amd/csrc/decode.hip"] + KERNEL_SOURCES[1:]
 
 
-def kernel_source_sha256():
-    """SHA-256 over the forward kernel's source files, in KERNEL_SOURCES order"""
+def kernel_source_sha256(sources=None):
+    """SHA-256 over a kernel's source files (the forward's by default), in list order"""
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
 def profiled_traffic(cfg):
-    path = os.path.join(ROOT, TRAFFIC_FILES.get(cfg, ""))
-    if not os.path.isfile(path):
+    return read_traffic(TRAFFIC_FILES.get(cfg, ""), KERNEL_SOURCES)
+
+
+def read_traffic(rel, sources):
+    path = os.path.join(ROOT, rel)
+    if not rel or not os.path.isfile(path):
         return None
     fields = {}
     for line in open(path):
         if "=" in line:
             k, v = line.split("=", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256") != kernel_source_sha256():
+    if fields.get("kernel_source_sha256") != kernel_source_sha256(sources):
         return None  # the kernel changed since the counters were taken
     v = fields.get("traffic_bytes_per_launch")
     return int(v) if v is not None else None
@@ -199,7 +206,10 @@ def bench_decode(args, torch, mx):
            "t_decode_ms": round(t_dec * 1e3, 4),
            "tokens_per_s": round(B * R / t_step, 1),
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
-                        "frac": round(gbs / 8000.0, 4), "traffic": None, "kernel": "split-key decode (mxattn_decode)"}}
+                        "frac": round(gbs / 8000.0, 4),
+                        "traffic": read_traffic(DECODE_TRAFFIC_FILE, DECODE_SOURCES)
+                        if (N, args.decode_layout) == (131072, "vt") else None,
+                        "kernel": "split-key decode (mxattn_decode)"}}
     print(json.dumps(res), flush=True)
 
 
