@@ -25,8 +25,14 @@ def _inputs(B, H, N, seed, shift=1.5):
     return synth.f32_to_bf16(x.astype(np.float32))
 
 
-@pytest.mark.parametrize("B,H,N,docs", [(2, 3, 1000, None), (1, 2, 777, [0, 1, 300, 301, 777]), (1, 1, 1, None)])
+DOCS8 = [0, 1, 130, 131, 700, 1500, 2600, 2601, 3000]  # 8 documents, two of one token
+
+
+@pytest.mark.parametrize("B,H,N,docs", [(2, 3, 1000, None), (1, 2, 777, [0, 1, 300, 301, 777]), (1, 1, 1, None),
+                                        (1, 16, 3000, DOCS8), (1, 17, 3000, DOCS8), (4, 40, 300, None)])
 def test_channel_mean_bitexact(B, H, N, docs):
+    """including 128, 136 and 160 (batch, head, document) units: documents of one
+    token, units numbered document-major over several XCD rounds"""
     import torch
     import microscaling_fp4_attention_amd as mx
     h = _inputs(B, H, N, 11)
