@@ -8,11 +8,15 @@
  * Parity status: every function below is pinned by tests/test_oracle_pins.py
  * (formats, scale rules, quantizers, two-level stretch, PNQ normalisation) and
  * tests/test_oracle_attention.py (online softmax against brute force, masks,
- * GQA, packed documents).  The flip budget is a bound, not a result; it is
- * exercised by the GPU parity tests only.
+ * GQA, packed documents).  The flip budget is pinned by
+ * tests/test_oracle_flip_budget.py on constructed rows whose fragile decisions
+ * and their effect on O are known in closed form (an element on an E2M1
+ * midpoint, a block maximum on an E8M0 boundary, a row with none), and its
+ * two-level pre-scale by the per-tile invariance it implies.
  */
 #include "oracle.h"
 
+#include <limits.h>
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
@@ -230,15 +234,18 @@ void orc_dequant_cols(const uint8_t* codes, const uint8_t* scales, int N, int d,
 }
 
 /* ------------------------------------------------------------------------ */
-/* Flip budget: rounding decisions within a relative 2^-12 of a threshold   */
-/* may be taken the other way by an implementation whose exp and dot        */
-/* products differ from this one by a few ulps.  For every such decision    */
-/* the budget adds the largest change of the dequantized value it can make. */
+/* Flip budget.  An implementation under test computes every value that     */
+/* feeds a rounding decision (an element code, a block scale) with its own  */
+/* FP32 arithmetic, so its value differs from this one by a bounded         */
+/* relative amount w (the decision's window, see decision_window below).  A  */
+/* decision whose value lies within w of a threshold may be taken the other  */
+/* way; for each such decision the budget adds the largest change of the    */
+/* dequantized values it can make.                                          */
 /* ------------------------------------------------------------------------ */
-#define FRAG 0x1p-12
 
-/* alternative code of an element decision, or -1 */
-static int elem_alt(int elem, float y, int code) {
+/* alternative code of an element decision whose value y carries a relative
+ * window w, or -1 */
+static int elem_alt(int elem, float y, int code, double w) {
   double a = fabs((double)y);
   int mag = elem == ORC_ELEM_E2M1 ? (code & 7) : (code & 0x7f);
   int top = elem == ORC_ELEM_E2M1 ? 7 : 0x7e;
@@ -248,16 +255,18 @@ static int elem_alt(int elem, float y, int code) {
     double mid;
     if (other < 0 || other > top) continue;
     mid = 0.5 * (fabs(elem_value(elem, mag)) + fabs(elem_value(elem, other)));
-    if (fabs(a - mid) <= FRAG * mid) return sign | other;
+    if (fabs(a - mid) <= w * a) return sign | other;
   }
   return -1;
 }
 
-/* alternative scale byte of a block decision, or -1 */
-static int scale_alt(float amax, const orc_fmt* f, int sb) {
-  float lo = (float)((double)amax * (1.0 - FRAG)), hi = (float)((double)amax * (1.0 + FRAG));
-  int a = scale_byte_for(lo, f), b = scale_byte_for(hi, f);
-  if (amax == 0.0f) return -1;
+/* alternative scale byte of a block decision whose maximum lies in [lo, hi]
+ * on the implementation under test, or -1 */
+static int scale_alt(double lo, double hi, const orc_fmt* f, int sb) {
+  int a, b;
+  if (hi <= 0.0) return -1;
+  a = scale_byte_for((float)lo, f);
+  b = scale_byte_for((float)hi, f);
   if (a != sb) return a;
   if (b != sb) return b;
   return -1;
@@ -265,26 +274,31 @@ static int scale_alt(float amax, const orc_fmt* f, int sb) {
 
 /* Quantize-dequantize one P block of n values (n <= 64) and report, per
  * element, the largest change of its dequantized value that a fragile
- * decision could make (delta[]).  Returns nothing; deq[] receives code*scale. */
-static void p_block(const float* x, int n, const orc_fmt* f, double* deq, double* delta) {
+ * decision could make (delta[]).  w[j]: relative window of x[j] for its
+ * element decision; ws[j]: relative window of x[j] as an input of the
+ * block's scale decision (0 where the implementation reproduces x[j]
+ * exactly).  deq[] receives code*scale. */
+static void p_block(const float* x, const double* w, const double* ws, int n, const orc_fmt* f,
+                    double* deq, double* delta) {
   uint8_t codes[64], sb;
   float s = orc_quant_block(x, n, f, codes, &sb);
   int alt_sb;
+  double lo = 0.0, hi = 0.0;
   for (int j = 0; j < n; j++) {
     int alt;
     deq[j] = elem_value(f->elem, codes[j]) * (double)s;
     delta[j] = 0.0;
     if (s != 0.0f) {
-      alt = elem_alt(f->elem, x[j] / s, codes[j]);
+      alt = elem_alt(f->elem, x[j] / s, codes[j], w[j]);
       if (alt >= 0) delta[j] = fabs(elem_value(f->elem, alt) - elem_value(f->elem, codes[j])) * (double)s;
     }
+    {
+      double a = fabs((double)x[j]);
+      if (a * (1.0 - ws[j]) > lo) lo = a * (1.0 - ws[j]);
+      if (a * (1.0 + ws[j]) > hi) hi = a * (1.0 + ws[j]);
+    }
   }
-  {
-    float amax = 0.0f;
-    for (int j = 0; j < n; j++)
-      if (fabsf(x[j]) > amax) amax = fabsf(x[j]);
-    alt_sb = scale_alt(amax, f, sb);
-  }
+  alt_sb = scale_alt(lo, hi, f, sb);
   if (alt_sb >= 0) {
     float s2 = (float)orc_scale_value(f, alt_sb);
     for (int j = 0; j < n; j++) {
@@ -293,6 +307,48 @@ static void p_block(const float* x, int n, const orc_fmt* f, double* deq, double
       if (fabs(v2 - deq[j]) > delta[j]) delta[j] = fabs(v2 - deq[j]);
     }
   }
+}
+
+/* log2 of the largest power of two that divides a nonzero float (its last set
+ * bit): the grain of the value; a product of two floats has the sum of their
+ * grains as its grain */
+static int grain_exp(float v) {
+  uint32_t b;
+  int e;
+  memcpy(&b, &v, 4);
+  e = (int)((b >> 23) & 0xFF);
+  b &= 0x7FFFFFu;
+  if (e == 0) return -149 + __builtin_ctz(b); /* subnormal (v != 0) */
+  return e - 150 + __builtin_ctz(b | 0x800000u);
+}
+
+/* Relative window of an exponential P~_j = 2^(a_j), a_j = lambda (s_j - m) with
+ * lambda = sm_scale / ln 2, as an implementation in FP32 computes it.  The bound,
+ * term by term (u = 2^-24, the unit roundoff of FP32):
+ *   - scores: the implementation sums the exact products of the dequantized
+ *     operands in FP32 with score_rounds roundings, each of relative size u of a
+ *     partial sum no larger than A = sum_c |q_c k_c| (+ |bias|), so
+ *     |S - s| <= es = score_rounds u A (es = 0 when every partial sum is exact:
+ *     A below 2^24 times the smallest power of two dividing all the terms), and
+ *     the running maximum moves by at most es as well: the argument moves by at
+ *     most 2 lambda es;
+ *   - lambda rounded to FP32: u |a_j|;
+ *   - the row offset fl(lambda m): u lambda |m|;
+ *   - the rounding of the argument itself: u |a_j|;
+ *   - the exponential: 1 ulp of its result on the implementation, 0.5 ulp here
+ *     (3 u), plus the products of the P quantization (a reciprocal 1/s, its
+ *     product with the two-level pre-scale and the element's product with it,
+ *     against this oracle's single division: 4 u): 2^-20 covers both.
+ * A change d of the argument changes 2^a by a factor 2^d, |2^d - 1| <= ln2 |d|
+ * (1 + ln2 |d|).  The bit-level modes add 2^-15 (the line keeps 16 fraction bits
+ * of its argument in an FP32 FMA). */
+static double p_window(const orc_attn_params* p, double lam, double es, double a, double m) {
+  const double u = 0x1p-24;
+  double darg = 2.0 * lam * es + 2.0 * u * fabs(a) + u * lam * fabs(m);
+  const double ln2 = 0.69314718055994530942;
+  double w = ln2 * darg * (1.0 + ln2 * darg) + 0x1p-20;
+  if (p->exp_mode != ORC_EXP_EXACT) w += 0x1p-15;
+  return w;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -374,8 +430,17 @@ static int attn_row_bias(const float* q, const float* K, const float* V, const f
   double* ph = (double*)malloc(sizeof(double) * (size_t)T);
   double* dl = (double*)malloc(sizeof(double) * (size_t)T);
   double* col = (double*)malloc(sizeof(double) * (size_t)d);
+  double* we = (double*)malloc(sizeof(double) * (size_t)T); /* element windows   */
+  double* ws = (double*)malloc(sizeof(double) * (size_t)T); /* scale-input windows */
   double fb1 = 0.0, fb2 = 0.0; /* flip budget: O part, l part (PNQ) */
+  /* flip-budget bookkeeping: the largest error bound of a visible score so far,
+   * and the two largest visible scores (is the running maximum unique?) */
+  const double lam = (double)p->sm_scale / 0.69314718055994530942;
+  const int rounds = p->score_rounds > 0 ? p->score_rounds : 2;
+  double es_max = 0.0, m1 = -INFINITY, m2 = -INFINITY;
 
+  int* qg = (int*)malloc(sizeof(int) * (size_t)d); /* grains of the query's entries */
+  for (int c = 0; c < d; c++) qg[c] = q[c] != 0.0f ? grain_exp(q[c]) : 0;
   if (vis > nk) vis = nk;
   for (int t0 = 0; t0 < vis; t0 += T) {
     int tl = nk - t0 < T ? nk - t0 : T; /* keys in this tile */
@@ -384,11 +449,35 @@ static int attn_row_bias(const float* q, const float* K, const float* V, const f
     /* S = Q K^T: exact products of dequantized values summed in double */
     for (int j = 0; j < tl; j++) {
       if (t0 + j < vis) {
-        double acc_d = 0.0;
-        for (int c = 0; c < d; c++) acc_d += (double)q[c] * (double)K[(int64_t)(t0 + j) * d + c];
-        if (sbias) acc_d += (double)sbias[t0 + j];
+        double acc_d = 0.0, abs_d = 0.0;
+        int gmin = INT_MAX;
+        for (int c = 0; c < d; c++) {
+          const float kv = K[(int64_t)(t0 + j) * d + c];
+          double pr = (double)q[c] * (double)kv;
+          acc_d += pr;
+          abs_d += fabs(pr);
+          if (pr != 0.0 && qg[c] + grain_exp(kv) < gmin) gmin = qg[c] + grain_exp(kv);
+        }
+        if (sbias) {
+          acc_d += (double)sbias[t0 + j];
+          abs_d += fabs((double)sbias[t0 + j]);
+          if (sbias[t0 + j] != 0.0f && grain_exp(sbias[t0 + j]) < gmin) gmin = grain_exp(sbias[t0 + j]);
+        }
+        const double grain = gmin == INT_MAX ? INFINITY : ldexp(1.0, gmin);
         s[j] = (float)acc_d;
+        /* every partial sum of these terms, in any order, is a multiple of the grain
+         * no larger than abs_d: below 2^24 grains all of them are exact in FP32 and
+         * the implementation's score equals this one; otherwise each of its
+         * score_rounds roundings is at most 2^-24 abs_d */
+        if (!(abs_d < 0x1p24 * grain) && rounds * 0x1p-24 * abs_d > es_max) es_max = rounds * 0x1p-24 * abs_d;
         if (s[j] > mt) mt = s[j];
+        /* the two largest visible scores so far (a tie gives m1 == m2) */
+        if ((double)s[j] > m1) {
+          m2 = m1;
+          m1 = s[j];
+        } else if ((double)s[j] > m2) {
+          m2 = s[j];
+        }
       } else {
         s[j] = -INFINITY;
       }
@@ -397,6 +486,18 @@ static int attn_row_bias(const float* q, const float* K, const float* V, const f
     alpha = (m == -INFINITY) ? 0.0f : (float)exp((double)p->sm_scale * ((double)m - (double)mnew));
     for (int j = 0; j < tl; j++)
       pt[j] = (s[j] == -INFINITY) ? 0.0f : p_exp(p, (double)p->sm_scale * ((double)s[j] - (double)mnew));
+    /* windows of this tile's exponentials (p_window); the element at the maximum
+     * is exactly 1 on both sides when no other score lies within the score error
+     * of it (the implementation forms block maxima as 2^(lambda (max - m))) */
+    {
+      const double es = es_max;
+      const int unique = es == 0.0 || (double)mnew - m2 > 2.0 * es;
+      for (int j = 0; j < tl; j++) {
+        double a = s[j] == -INFINITY ? 0.0 : lam * ((double)s[j] - (double)mnew);
+        we[j] = p_window(p, lam, es, a, mnew);
+        ws[j] = (p->exp_mode == ORC_EXP_EXACT && s[j] == mnew && unique) ? 0.0 : we[j];
+      }
+    }
     /* per-key fold of the diagonal tile: the quantizer sees P' = P~ 2^ek */
     const int fold = Vk != NULL && t0 == diag_t0;
     float* pq = pt;
@@ -412,28 +513,39 @@ static int attn_row_bias(const float* q, const float* K, const float* V, const f
     }
     if (p->pmode == ORC_P_TWO_LEVEL) {
       float r = 0.0f, s1;
-      for (int j = 0; j < tl; j++)
+      double rlo = 0.0, rhi = 0.0, wr;
+      for (int j = 0; j < tl; j++) {
         if (pq[j] > r) r = pq[j];
+        if ((double)pq[j] * (1.0 - ws[j]) > rlo) rlo = (double)pq[j] * (1.0 - ws[j]);
+        if ((double)pq[j] * (1.0 + ws[j]) > rhi) rhi = (double)pq[j] * (1.0 + ws[j]);
+      }
       if (r == 0.0f) { /* nothing visible in this tile */
         m = mnew;
         continue;
       }
+      /* the pre-scale's window: where the implementation's tile maximum can lie */
+      wr = ((double)r - rlo) / (double)r;
+      if ((rhi - (double)r) / (double)r > wr) wr = (rhi - (double)r) / (double)r;
       s1 = r / (448.0f * 6.0f);
-      for (int j = 0; j < tl; j++) x2[j] = pq[j] / s1; /* in place when folded */
+      for (int j = 0; j < tl; j++) {
+        x2[j] = pq[j] / s1; /* in place when folded */
+        we[j] += wr;
+        ws[j] += wr;
+      }
       for (int b0 = 0; b0 < tl; b0 += p->pfmt.block) {
         int n = tl - b0 < p->pfmt.block ? tl - b0 : p->pfmt.block;
-        p_block(x2 + b0, n, &p->pfmt, ph + b0, dl + b0);
+        p_block(x2 + b0, we + b0, ws + b0, n, &p->pfmt, ph + b0, dl + b0);
       }
       mult = s1;
     } else if (p->pmode == ORC_P_DIRECT || p->pmode == ORC_P_PNQ) {
       for (int b0 = 0; b0 < tl; b0 += p->pfmt.block) {
         int n = tl - b0 < p->pfmt.block ? tl - b0 : p->pfmt.block;
-        p_block(pq + b0, n, &p->pfmt, ph + b0, dl + b0);
+        p_block(pq + b0, we + b0, ws + b0, n, &p->pfmt, ph + b0, dl + b0);
       }
     } else if (p->pmode == ORC_P_FP8_FIXED) {
       for (int j = 0; j < tl; j++) {
         float y = 448.0f * pt[j];
-        int c = orc_e4m3_encode(y), alt = elem_alt(ORC_ELEM_E4M3, y, c);
+        int c = orc_e4m3_encode(y), alt = elem_alt(ORC_ELEM_E4M3, y, c, we[j]);
         ph[j] = orc_e4m3_value(c);
         if (alt >= 0) dl[j] = fabs(orc_e4m3_value(alt) - ph[j]);
       }
@@ -495,6 +607,9 @@ static int attn_row_bias(const float* q, const float* K, const float* V, const f
   free(ph);
   free(dl);
   free(col);
+  free(we);
+  free(ws);
+  free(qg);
   return 0;
 }
 

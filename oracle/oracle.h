@@ -75,6 +75,8 @@ typedef struct {
   int kv_tile;    /* keys per online-softmax step                   */
   int exp_mode;   /* ORC_EXP_*: the exponential of P~ (the rescale  */
                   /* factor between tiles stays exact)              */
+  int score_rounds; /* flip budget only: FP32 roundings in the score   */
+                  /* sums of the implementation under test (0: 2)   */
 } orc_attn_params;
 
 /* ---- bit-level exponentials ([FLAMIA] section 3.7, appendix C) ----
@@ -120,8 +122,10 @@ void orc_dequant_cols(const uint8_t* codes, const uint8_t* scales, int N, int d,
 /* One query row.  K, V: [nk][d] dequantized keys/values of the row's key range
  * (a document, or the whole sequence); tiles are aligned to key 0 of that range.
  * vis: number of visible keys (keys 0..vis-1).  Outputs o[d], *lse and the row's
- * flip budget *fb (bound on |dO| from rounding decisions that lie within a
- * relative 2^-12 of a threshold).  Returns 0. */
+ * flip budget *fb: a bound on |dO| from the rounding decisions (element codes,
+ * block scales) whose input lies within its window of a threshold, the window
+ * being a bound on how far an FP32 implementation's value of that input can be
+ * from this oracle's (p_window in oracle.c states it term by term).  Returns 0. */
 int orc_attn_row(const float* q, const float* K, const float* V, int nk, int vis, int d,
                  const orc_attn_params* p, float* o, float* lse, double* fb);
 
