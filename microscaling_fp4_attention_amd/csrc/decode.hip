@@ -191,10 +191,11 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecArgs a) {
     // tile's state starts empty, so nothing carried needs the rescale
     const float mnew = fmaxn(m0, tmax);
     const float ms = mnew == NEG_INF ? 0.0f : mnew * lam;
+    const float msub = mnew == NEG_INF ? 0.0f : mnew;
     m = mnew;
     float k1s = 1.0f;
     if constexpr (PMODE == PM_TWO_LEVEL) {
-      const float rr = exp2_hw(__builtin_fmaf(tmax, lam, -ms));
+      const float rr = exp2_diff(tmax, msub, lam);
       if (rr >= 0x1p-64f) {
         s1 = rr / 2688.0f;
         k1s = 1.0f / s1;
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecArgs a) {
 #pragma unroll
     for (int p = 0; p < 2; p++) {
       const float bm = fmaxn(bm16[2 * p], bm16[2 * p + 1]);
-      const int x = e8m0_exp(exp2_hw(__builtin_fmaf(bm, lam, -ms)) * k1s, a.prule);
+      const int x = e8m0_exp(exp2_diff(bm, msub, lam) * k1s, a.prule);
       e[p] = x < -126 ? -126 : x;
     }
     const uint32_t pscw = (uint32_t)(e[0] + 127) | ((uint32_t)(e[1] + 127) << 8);
@@ -377,10 +378,11 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecArgs a) {
     // 32-key block); the tile's state starts empty, so nothing needs the rescale
     const float mnew = fmaxn(m0, tmax);
     const float ms = mnew == NEG_INF ? 0.0f : mnew * lam;
+    const float msub = mnew == NEG_INF ? 0.0f : mnew;
     m = mnew;
     float k1s = 1.0f;
     if constexpr (PMODE == PM_TWO_LEVEL) {
-      const float rr = exp2_hw(__builtin_fmaf(tmax, lam, -ms));
+      const float rr = exp2_diff(tmax, msub, lam);
       if (rr >= 0x1p-64f) {
         s1 = rr / 2688.0f;
         k1s = 1.0f / s1;
@@ -388,7 +390,7 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecArgs a) {
         k1s = 0.0f;  // a tile whose P~ stays below 2^-64 of the running maximum adds nothing
       }
     }
-    int e = e8m0_exp(exp2_hw(__builtin_fmaf(bmax, lam, -ms)) * k1s, a.prule);
+    int e = e8m0_exp(exp2_diff(bmax, msub, lam) * k1s, a.prule);
     e = e < -126 ? -126 : e;
     const float sc = u2f((uint32_t)(e + 127) << 23);
     float lsum = 0.0f;

@@ -61,6 +61,13 @@ __device__ __forceinline__ v16f mfma_bf16(v8bf a, v8bf b, v16f c) {
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 2^(lambda (x - msub)) formed from the difference x - msub, so that it is exactly 1
+// at x = msub: block scales and the two-level pre-scale are chosen from this value,
+// and at the row's maximum P~ must be the exactly represented 1 ("MXAttention",
+// section 4.2; for the OCP rule 1 sits on a scale boundary, Table 1).  msub is the
+// running maximum, or 0 while that is -inf (then every x is -inf and the result 0).
+__device__ __forceinline__ float exp2_diff(float x, float msub, float lam) { return exp2_hw((x - msub) * lam); }
+
 // Bit-level exponential ("FLAMIA" section 3.7 and appendix C): y = 2^23 (t + 127) in a
 // float; the float whose bits are the integer part of y is Mitchell's line
 // 2^floor(t) (1 + frac t) (a subnormal below t = -126).  The max clamps negative y,

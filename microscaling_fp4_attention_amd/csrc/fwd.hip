@@ -332,19 +332,21 @@ __global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(Fw
     tmax = __builtin_fmaxf(tmax, swap_halves(tmax));
     const float mnew = __builtin_fmaxf(m, tmax);
     const float ms = mnew == NEG_INF ? 0.0f : mnew * lam;  // exponent offset of this tile
+    const float msub = mnew == NEG_INF ? 0.0f : mnew;
     // exactly 1 when the max did not move (keeps the rescale skip exact), 0 while m = -inf
-    const float alpha = m == mnew ? 1.0f : exp2_hw(__builtin_fmaf(m, lam, -ms));
+    const float alpha = m == mnew ? 1.0f : exp2_diff(m, mnew, lam);
     m = mnew;
 
-    // the maxima of P~ are the exponentials of the maxima of S (same operations, monotone)
+    // the maxima of P~ are the exponentials of the maxima of S (monotone), formed from
+    // the difference to the running maximum so that the row's maximum gives exactly 1
     float pm16[4];
 #pragma unroll
-    for (int bb = 0; bb < 4; bb++) pm16[bb] = exp2_hw(__builtin_fmaf(bm16[bb], lam, -ms));
+    for (int bb = 0; bb < 4; bb++) pm16[bb] = exp2_diff(bm16[bb], msub, lam);
 
     // two-level pre-scale s1 = rowmax_tile(P~) / (448 * 6)
     float s1 = 1.0f, k1 = 1.0f;
     if constexpr (PMODE == PM_TWO_LEVEL) {
-      float r = exp2_hw(__builtin_fmaf(tmax, lam, -ms));
+      float r = exp2_diff(tmax, msub, lam);
       s1 = r / 2688.0f;
       k1 = r > 0.0f ? 1.0f / s1 : 0.0f;  // a row with nothing visible in this tile adds nothing
       if (r == 0.0f) s1 = 0.0f;
@@ -695,6 +697,14 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   auto pexp_c = [&](float ms) __attribute__((always_inline)) -> float {
     return EXPB ? __builtin_fmaf(-ms, 0x1p23f, a.exp_bias) : 0.0f;
   };
+  // P~ at a block's or a tile's largest score, the input of a block-scale or pre-scale
+  // decision: the exact exponential is formed from the difference to the running
+  // maximum (msub), which makes it exactly 1 at the row's maximum; the bit-level line
+  // uses its own form (monotone, so the block's largest P~ either way)
+  auto pmax = [&](float sc, float ms, float cm, float msub) __attribute__((always_inline)) -> float {
+    if constexpr (EXPB) return exp2_bits(__builtin_fmaf(sc, lamb, cm));
+    else return exp2_diff(sc, msub, lam);
+  };
 
   // ---------------- Q operand ----------------
   v8i qop[2];
@@ -1021,10 +1031,11 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   auto phase_v = [&](int t) __attribute__((always_inline)) {
     const float mnew = fmaxn(m, tmax);
     const float ms = mnew == NEG_INF ? 0.0f : mnew * lam;
+    const float msub = mnew == NEG_INF ? 0.0f : mnew;
     const float cm = pexp_c(ms);
     // exactly 1 when the max did not move (keeps the rescale skip exact), 0 while m = -inf;
     // the rescale is exact in both exponential modes
-    const float alpha = m == mnew ? 1.0f : exp2_hw(__builtin_fmaf(m, lam, -ms));
+    const float alpha = m == mnew ? 1.0f : exp2_diff(m, mnew, lam);
     m = mnew;
 
     // two-level: s1 = rowmax_tile(P~)/2688; the accumulator holds O / s1 and is carried
@@ -1032,7 +1043,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     // the running maximum adds nothing and keeps s1)
     float k1 = 1.0f, scale_o = alpha;
     if constexpr (PMODE == PM_TWO_LEVEL) {
-      float r = pexp(tmax, ms, cm);
+      float r = pmax(tmax, ms, cm, msub);
       if (r >= 0x1p-64f) {
         float s1 = r / 2688.0f;
         k1 = 1.0f / s1;
@@ -1060,7 +1071,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
 #pragma unroll
       for (int p = 0; p < 2; p++) {
         const float bm = fmaxn(bm16[2 * p], bm16[2 * p + 1]);
-        int x = e8m0_exp(pexp(bm, ms, cm) * k1, a.prule);
+        int x = e8m0_exp(pmax(bm, ms, cm, msub) * k1, a.prule);
         e[p] = x < -126 ? -126 : x;
         const float sc = u2f((uint32_t)(e[p] + 127) << 23);
         sc16[2 * p] = sc16[2 * p + 1] = sv16[2 * p] = sv16[2 * p + 1] = sc;
@@ -1070,7 +1081,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     } else if constexpr (PV == PV_BF16) {  // E4M3 scale per 16 keys
 #pragma unroll
       for (int bb = 0; bb < 4; bb++) {
-        const float pm = pexp(bm16[bb], ms, cm) * k1;
+        const float pm = pmax(bm16[bb], ms, cm, msub) * k1;
         const float sv = e4m3_value(e4m3_mag(pm / 6.0f));
         sc16[bb] = 1.0f;
         sv16[bb] = sv;
@@ -1091,8 +1102,9 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   auto phase_v_fold = [&](int t) __attribute__((always_inline)) {
     const float mnew = fmaxn(m, tmax);
     const float ms = mnew == NEG_INF ? 0.0f : mnew * lam;
+    const float msub = mnew == NEG_INF ? 0.0f : mnew;
     const float cm = pexp_c(ms);
-    const float alpha = m == mnew ? 1.0f : exp2_hw(__builtin_fmaf(m, lam, -ms));
+    const float alpha = m == mnew ? 1.0f : exp2_diff(m, mnew, lam);
     m = mnew;
     const uint8_t* kx = smem + L::KEYR + grp * L::KEYT + L::KEYX;  // per-key bytes, key order
     // exponent of the lane's key j of sub-tile bb (re-read where needed, not held)
@@ -1107,7 +1119,9 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       float mx = 0.0f;
 #pragma unroll
       for (int j = 0; j < 16; j++) {
-        const float pt = pexp(S[bb][j], ms, cm);
+        // on this one tile per row every P~ takes the difference form, so the one at
+        // the row's maximum is exactly 1 and the block maxima of P' are exact there
+        const float pt = pmax(S[bb][j], ms, cm, msub);
         if constexpr (PMODE != PM_PNQ) lsum += pt;
         const float pp = __builtin_ldexpf(pt, (int)((ew[j >> 2] >> (8 * (j & 3))) & 0xFFu) - 127);
         S[bb][j] = pp;

@@ -31,3 +31,20 @@ def golden(name):
             k, v = line.split("=", 1)
             out[k.strip()] = v.strip()
     return out
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """One line per parity comparison of the session: worst |dO| / bound and the
+    rows whose flip budget is nonzero (the evidence behind each passing case)."""
+    helpers = sys.modules.get("helpers")
+    rows = getattr(helpers, "PARITY", None)
+    if not rows:
+        return
+    tr = terminalreporter
+    tr.write_sep("-", f"parity against the oracle: {len(rows)} comparisons")
+    for name, ratio, nf, n, med in rows:
+        tr.write_line(f"parity {name}: max |dO|/bound {ratio:.3e}, flip budget on {nf}/{n} rows "
+                      f"(median budget/tolerance {med:.2e})")
+    worst = max(rows, key=lambda r: r[1])
+    tr.write_line(f"parity worst: {worst[0]} at {worst[1]:.3e}; "
+                  f"largest fragile share {max(r[2] / max(r[3], 1) for r in rows):.3f}")

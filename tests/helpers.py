@@ -4,8 +4,11 @@ same seeded inputs and compare them.
 The oracle side quantizes with its own C routines; the GPU side with
 mxattn_quantize.  Quantized bytes must agree exactly; the forward output (FP32)
 must satisfy |dO| <= 2e-3 * max|O_oracle| + flip budget of the row, where the
-flip budget bounds the effect of rounding decisions that lie within a relative
-2^-12 of a threshold (the oracle reports it per row).
+flip budget bounds the effect of the rounding decisions whose input lies within
+its window of a threshold (the oracle derives each window from a bound on how
+far FP32 arithmetic can move that input and reports the budget per row).
+Every comparison is recorded in PARITY, which tests/conftest.py prints at the end
+of the session (worst |dO|/bound and the share of rows with a nonzero budget).
 """
 from __future__ import annotations
 
@@ -15,6 +18,38 @@ import oracle
 import synth
 
 TOL = 2e-3
+# Rows whose flip budget is nonzero, as a share of the rows compared, must stay below
+# FRAGILE_CAP on the exact exponential over rows of at most a few thousand keys; and on
+# every comparison the median row's budget must stay below the plain tolerance, so the
+# bound is not mostly budget.  (The share grows with the keys per row: a row of 32K keys
+# makes 32 times the decisions of one of 1K; the bit-level exponentials keep 16 fraction
+# bits of their argument, so their window is 2^-15 instead of about 2^-20.)
+FRAGILE_CAP = 0.10
+
+# (case, worst |dO| / bound, rows with a nonzero flip budget, rows compared, median budget / tolerance)
+PARITY: list = []
+
+
+def record_parity(name, ratio, fb_over_tol, cap_share=FRAGILE_CAP):
+    """Keep one comparison for the session summary and check how much of its bound is
+    flip budget.  fb_over_tol: each compared row's budget over the plain tolerance
+    2e-3 max|O|; cap_share: the largest share of rows with a budget (None: not
+    checked, for long rows and the bit-level exponentials)."""
+    r = np.asarray(fb_over_tol, np.float64).ravel()
+    n_fragile, n_rows = int((r > 0).sum()), int(r.size)
+    med = float(np.median(r)) if r.size else 0.0
+    PARITY.append((name, float(ratio), n_fragile, n_rows, med))
+    assert med <= 1.0, f"{name}: the median row's flip budget is {med:.2f} times the tolerance"
+    if cap_share is not None:
+        cap = max(3, int(cap_share * n_rows))
+        assert n_fragile <= cap, f"{name}: {n_fragile} of {n_rows} rows have a flip budget (cap {cap})"
+
+
+def score_rounds(qfmt) -> int:
+    """FP32 roundings in the HIP path's score sums: two chained FP4 MFMAs (64 channels
+    each) for MXFP4 Q/K, eight bf16 MFMAs (16 channels each) for NVFP4 Q/K; the oracle
+    widens the window of every decision by what they can move a score."""
+    return 8 if str(qfmt).startswith("nvfp4") else 2
 
 
 def gpu_available() -> bool:
@@ -220,7 +255,8 @@ def run_case(qfmt, vfmt, pmode, pfmt, B, Hq, Hkv, N, causal=False, kind="kmean",
             assert np.array_equal(gkc, vk_codes), "per-key V codes differ"
             assert np.array_equal(gke, vk_exp), "per-key V exponents differ"
     O_ref, lse_ref, fb = oracle.attention(qd, kd, vd, PM_ORACLE[pmode], pfmt, causal=causal, doc_off=doc_off,
-                                          rows=rows, bias=bias, vkey=vk_vals, vkey_exp=vk_exp, exp_mode=exp_mode)
+                                          rows=rows, bias=bias, vkey=vk_vals, vkey_exp=vk_exp, exp_mode=exp_mode,
+                                          score_rounds=score_rounds(qfmt))
     sel = np.arange(B * Hq * N) if rows is None else np.asarray(rows)
     Og = O_gpu[sel]
     err = np.abs(Og - O_ref)

@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import PM_ORACLE, TOL, gpu_available, run_case
+from helpers import PM_ORACLE, TOL, gpu_available, record_parity, run_case, score_rounds
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
@@ -38,6 +38,7 @@ def lse_bound(res):
 
 def _check(res, name):
     print(f"{name}: max err/bound {res['ratio']:.3f}, fragile rows {res['n_fragile']}, amax {res['amax']:.3f}")
+    record_parity(name, res["ratio"], res["fb"] / (TOL * res["amax"]), None)
     assert np.all(np.isfinite(res["O_gpu"]))
     assert res["ratio"] <= 1.0, name
     lg, lr = res["lse_gpu"], res["lse_ref"]
@@ -156,17 +157,19 @@ def test_bits_fullsize_sampled_rows(name, exp_mode):
     rng = np.random.default_rng(2024)
     heads = sorted({0, Hq - 1, int(rng.integers(0, Hq))})
     rows = sorted({0, N - 1, *map(int, rng.integers(0, N, 10))})
-    worst = 0.0
+    worst, fbt = 0.0, []
     for h in heads:
         hk = h * Hkv // Hq
         _, _, qd = oracle_quant_qk(synth.bf16_to_f32(x["q"][:1, h:h + 1]), qf)
         _, _, kd = oracle_quant_qk(synth.bf16_to_f32(x["k"][:1, hk:hk + 1]), qf)
         _, _, vd = oracle_quant_v(synth.bf16_to_f32(x["v"][:1, hk:hk + 1]), vf)
         O_ref, _, fb = oracle.attention(qd, kd, vd, PM_ORACLE[pm], pf, causal=causal, rows=np.array(rows, np.int64),
-                                        exp_mode=exp_mode)
+                                        exp_mode=exp_mode, score_rounds=score_rounds(qf))
         O_gpu = out[0, h].cpu().numpy()[rows]
         assert np.all(np.isfinite(O_gpu))
         bound = TOL * np.abs(O_ref).max() + fb[:, None]
         worst = max(worst, float((np.abs(O_gpu - O_ref) / bound).max()))
+        fbt.append(fb / (TOL * np.abs(O_ref).max()))
     print(f"{name} {exp_mode}: heads {heads}, {len(rows)} rows, max |dO|/bound = {worst:.2e}")
+    record_parity(f"full size {name} {exp_mode}", worst, np.concatenate(fbt), None)
     assert worst <= 1.0

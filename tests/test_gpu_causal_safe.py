@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import synth
-from helpers import gpu_available, run_case
+from helpers import TOL, gpu_available, record_parity, run_case
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
@@ -23,6 +23,7 @@ SAFE_ROUTES = {
 
 def _check(res, name):
     print(f"{name}: max err/bound {res['ratio']:.3f}, fragile rows {res['n_fragile']}, amax {res['amax']:.3f}")
+    record_parity(name, res["ratio"], res["fb"] / (TOL * res["amax"]))
     assert np.all(np.isfinite(res["O_gpu"]))
     assert res["ratio"] <= 1.0, name
 

@@ -9,7 +9,8 @@ import pytest
 
 import oracle
 import synth
-from helpers import (PM_ORACLE, TOL, gpu_available, gpu_codes_qk, gpu_codes_v, oracle_quant_qk, oracle_quant_v)
+from helpers import (PM_ORACLE, TOL, gpu_available, gpu_codes_qk, gpu_codes_v, oracle_quant_qk, oracle_quant_v,
+                     FRAGILE_CAP, record_parity)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
@@ -48,6 +49,8 @@ def run_decode(pm, B, Hq, Hkv, R, N, kv_len, seed):
     ratio = float((np.abs(O_gpu - O_ref) / bound).max())
     lse_err = float(np.abs(lse.cpu().numpy() - lse_ref).max())
     print(f"decode {pm} B{B} Hq{Hq} Hkv{Hkv} R{R} N{N}: max |dO|/bound {ratio:.3f}, |dlse| {lse_err:.2e}")
+    record_parity(f"decode {pm} B{B} Hq{Hq} Hkv{Hkv} R{R} N{N}", ratio, fb / (TOL * np.abs(O_ref).max()),
+                  None if N > 4096 else FRAGILE_CAP)
     assert np.all(np.isfinite(O_gpu))
     assert ratio <= 1.0
     assert lse_err <= 1e-3 * max(1.0, float(np.abs(lse_ref).max()))

@@ -7,8 +7,8 @@ import pytest
 
 import oracle
 import synth
-from helpers import (gpu_available, gpu_codes_qk, oracle_comp, oracle_preproc, oracle_quant_qk, run_case,
-                     ulp_diff)
+from helpers import (TOL, gpu_available, gpu_codes_qk, oracle_comp, oracle_preproc, oracle_quant_qk, record_parity,
+                     run_case, score_rounds, ulp_diff)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
@@ -102,6 +102,7 @@ BIAS_ROUTES = {
 
 def _check(res, name):
     print(f"{name}: max err/bound {res['ratio']:.3f}, delta ulp {res.get('delta_ulp')}, amax {res['amax']:.3f}")
+    record_parity(name, res["ratio"], res["fb"] / (TOL * res["amax"]))
     assert np.all(np.isfinite(res["O_gpu"]))
     assert res["ratio"] <= 1.0, name
 
@@ -154,7 +155,7 @@ def test_fullsize_gqa_causal_centered():
     rows = sorted({0, N - 1, *map(int, rng.integers(0, N, 10))})
     qcodes, kcodes = gpu_codes_qk(Q), gpu_codes_qk(K)
     dg = delta.cpu().numpy()
-    worst = 0.0
+    worst, fbt = 0.0, []
     for h in heads:
         hk = h * Hkv // Hq
         qf = synth.bf16_to_f32(x["q"][:1, h:h + 1])
@@ -170,9 +171,11 @@ def test_fullsize_gqa_causal_centered():
         bias = oracle_comp(qmean, kf, kmean, 1, None)
         assert ulp_diff(dg[0, h], bias[0, 0]) <= 1
         O_ref, _, fb = oracle.attention(qd, kd, vd, PM_ORACLE["fp8"], None, causal=True,
-                                        rows=np.array(rows, np.int64), bias=bias)
+                                        rows=np.array(rows, np.int64), bias=bias, score_rounds=score_rounds("nvfp4"))
         O_gpu = out[0, h].cpu().numpy()[rows]
         bound = TOL * np.abs(O_ref).max() + fb[:, None]
         worst = max(worst, float((np.abs(O_gpu - O_ref) / bound).max()))
+        fbt.append(fb / (TOL * np.abs(O_ref).max()))
     print(f"c4 centered: heads {heads}, {len(rows)} rows, max |dO|/bound = {worst:.2e}")
+    record_parity("full size c4 centered", worst, np.concatenate(fbt), None)
     assert worst <= 1.0
