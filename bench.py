@@ -87,6 +87,15 @@ CONFIGS = {
     "c5": ("c5_varlen_causal_64k", "mxfp4", "mxfp4", "two_level", "nvfp4",
            "packed 65536 tokens (log-uniform 512..16384), H16 d128 block-diagonal causal, K outliers; "
            "MXFP4 Q/K/V, two-level P (E4M3/16)"),
+    # the two-level forward at N = 32K, d = 128 on the video-DiT inputs, in both readings
+    # of the level-2 block format: E4M3 per 16 keys (PV on the bf16 MFMA after exact
+    # dequantization) and E8M0 per 32 keys (PV on the FP4 MFMA)
+    "two_level_e4m3": ("c3_video_dit_32k", "mxfp4", "mxfp4", "two_level", "nvfp4",
+                       "B1 H24 N32768 d128 non-causal, rank-16 peaked Q/K; MXFP4 Q/K/V, two-level P "
+                       "(level-2 E4M3 per 16 keys)"),
+    "two_level_e8m0": ("c3_video_dit_32k", "mxfp4", "mxfp4", "two_level", "mxfp4",
+                       "B1 H24 N32768 d128 non-causal, rank-16 peaked Q/K; MXFP4 Q/K/V, two-level P "
+                       "(level-2 E8M0 per 32 keys, OCP rule)"),
 }
 
 
