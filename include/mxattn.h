@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MXATTN_ABI_VERSION 5
+#define MXATTN_ABI_VERSION 6
 
 typedef enum {
   MXATTN_OK = 0,
@@ -179,7 +179,8 @@ int mxattn_abi_version(void);
 /* Static text of a status code. */
 const char* mxattn_status_str(int status);
 
-/* Text of the last MXATTN_E_HIP failure on the calling thread ("" if none). */
+/* Text of the last MXATTN_E_HIP failure on the calling thread, or of the last
+ * MXATTN_E_WORKSPACE of mxattn_decode_noalloc() ("" if none). */
 const char* mxattn_last_error(void);
 
 /*
@@ -365,6 +366,26 @@ int mxattn_decode(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn
                   const mxattn_fwd_params* params, const int32_t* kv_len, void* out,
                   const int64_t out_strides[4], float* lse, void* workspace, size_t workspace_bytes,
                   void* stream);
+
+/*
+ * mxattn_decode() without a workspace and without any allocation, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The split states live in a static device array
+ * of the library, 32 MiB per GPU (MXATTN_DECODE_SCRATCH_BYTES), held from the first
+ * call on a GPU until the process ends.  Arguments, layouts and results are those of
+ * mxattn_decode(), bit for bit.
+ *   Limit: mxattn_decode_workspace_bytes(B, Hq, R, N) must not exceed
+ *   MXATTN_DECODE_SCRATCH_BYTES (B * Hq * R * ceil(N / 512) <= 65027 split rows, e.g. 4
+ *   requests x 32 query heads x 1 row over 254K keys); larger calls return
+ *   MXATTN_E_WORKSPACE with the sizes in mxattn_last_error().
+ *   Every call on one GPU uses the same array: calls that overlap on one GPU (other
+ *   streams or threads) race, so serialize them.  Nothing needs clearing between calls.
+ * Errors: as mxattn_decode().
+ */
+#define MXATTN_DECODE_SCRATCH_BYTES (32u << 20)
+int mxattn_decode_noalloc(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn_qtensor* v,
+                          const mxattn_fwd_params* params, const int32_t* kv_len, void* out,
+                          const int64_t out_strides[4], float* lse, void* stream);
 
 #ifdef __cplusplus
 }

@@ -27,7 +27,8 @@ P_DIRECT, P_TWO_LEVEL, P_PNQ, P_FP8_FIXED = 1, 2, 3, 4
 EXP_EXACT, EXP_MITCHELL, EXP_SCHRAUDOLPH = 0, 1, 2
 
 
-ABI_VERSION = 5  # MXATTN_ABI_VERSION of include/mxattn.h
+ABI_VERSION = 6  # MXATTN_ABI_VERSION of include/mxattn.h
+DECODE_SCRATCH_BYTES = 32 << 20  # MXATTN_DECODE_SCRATCH_BYTES
 
 
 class QFmt(ctypes.Structure):
@@ -72,7 +73,7 @@ def qfmt(f) -> QFmt:
 class MxattnError(RuntimeError):
     def __init__(self, status: int, what: str):
         msg = _lib().mxattn_status_str(status).decode()
-        extra = _lib().mxattn_last_error().decode() if status == E_HIP else ""
+        extra = _lib().mxattn_last_error().decode() if status in (E_HIP, E_WORKSPACE) else ""
         super().__init__(f"{what}: {msg} ({status}) {extra}".strip())
         self.status = status
 
@@ -111,6 +112,9 @@ def _lib():
         L.mxattn_decode.restype = i32
         L.mxattn_decode.argtypes = [P(QTensorC), P(QTensorC), P(QTensorC), P(FwdParams), vp, vp, P(i64), vp, vp,
                                     ctypes.c_size_t, vp]
+        L.mxattn_decode_noalloc.restype = i32
+        L.mxattn_decode_noalloc.argtypes = [P(QTensorC), P(QTensorC), P(QTensorC), P(FwdParams), vp, vp, P(i64), vp,
+                                            vp]
         L.mxattn_fwd_workspace_bytes.restype = ctypes.c_size_t
         L.mxattn_fwd_workspace_bytes.argtypes = [i64, i32]
         L.mxattn_fwd_plan.restype = i32
@@ -390,4 +394,24 @@ def decode(q: QTensor, k: QTensor, v: QTensor, params: FwdParams, kv_len: torch.
     _check(_lib().mxattn_decode(ctypes.byref(q.desc), ctypes.byref(k.desc), ctypes.byref(v.desc), ctypes.byref(params),
                                 _ptr(kv_len), _ptr(out), _i64(out.stride()), _ptr(lse), _ptr(workspace),
                                 workspace.numel(), _stream(stream)), "mxattn_decode")
+    return out
+
+
+def decode_noalloc(q: QTensor, k: QTensor, v: QTensor, params: FwdParams, kv_len: torch.Tensor | None = None,
+                   out: torch.Tensor | None = None, lse: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """mxattn_decode_noalloc: decode() with the split states in the library's static
+    scratch (no workspace, no allocation in the library; pass `out` to allocate nothing
+    here either).  Calls that overlap on one GPU race."""
+    B, Hq, R, d = q.desc.B, q.desc.H, q.desc.N, q.desc.d
+    dt = torch.float32 if params.out_fp32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((B, Hq, R, d), dtype=dt, device=q.codes.device)
+    _need(out, "out", dtype=dt, shape=(B, Hq, R, d))
+    if lse is not None:
+        _need(lse, "lse", dtype=torch.float32, numel=B * Hq * R, contiguous=True)
+    if kv_len is not None:
+        _need(kv_len, "kv_len", dtype=torch.int32, numel=B, contiguous=True)
+    _check(_lib().mxattn_decode_noalloc(ctypes.byref(q.desc), ctypes.byref(k.desc), ctypes.byref(v.desc),
+                                        ctypes.byref(params), _ptr(kv_len), _ptr(out), _i64(out.stride()), _ptr(lse),
+                                        _stream(stream)), "mxattn_decode_noalloc")
     return out

@@ -26,6 +26,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "device_util.h"
 #include "formats.h"
 #include "kernels.h"
@@ -542,6 +544,36 @@ hipError_t launch_decode(int pmode, const DecArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   decode_merge_kernel<<<dim3((unsigned)(a.B * a.Hq * a.R * 4)), 256, 0, st>>>(a);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free decode (mxattn_decode_noalloc): the split states of a
+// call live in this file-scope array instead of a caller workspace.  Each GPU holds
+// its own copy until the process ends, at its own address; on the host the array's
+// name is not a device address, so host code uses only what hipGetSymbolAddress
+// returns for the current device.  Every call on one GPU shares the array: calls that
+// overlap (other streams, other threads) race.  The decode writes every split state
+// before the merge reads it, so nothing needs clearing between calls.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[DECODE_SCRATCH_BYTES];
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace mxattn

@@ -309,9 +309,13 @@ size_t mxattn_decode_workspace_bytes(int64_t B, int64_t Hq, int64_t R, int64_t N
   return (size_t)(rows * 128 * 4 + (rows * 4 + 15) / 16 * 16);
 }
 
-int mxattn_decode(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn_qtensor* v,
-                  const mxattn_fwd_params* p, const int32_t* kv_len, void* out, const int64_t os[4], float* lse,
-                  void* workspace, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+// mxattn_decode and its allocation-free variant: workspace == nullptr with
+// use_scratch takes the split states from the library's static scratch
+static int decode_impl(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn_qtensor* v,
+                       const mxattn_fwd_params* p, const int32_t* kv_len, void* out, const int64_t os[4], float* lse,
+                       void* workspace, size_t ws_bytes, void* stream, bool use_scratch) {
   if (!q || !k || !v || !p || !os) return MXATTN_E_INVALID;
   if (q->role != MXATTN_ROLE_QK || k->role != MXATTN_ROLE_QK ||
       (v->role != MXATTN_ROLE_V && v->role != MXATTN_ROLE_VT))
@@ -338,7 +342,18 @@ int mxattn_decode(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn
       !aligned16(k->scales) || !aligned16(v->scales) || !aligned16(out))
     return MXATTN_E_ALIGN;
   if (os[3] != 1 || os[0] < 0 || os[1] < 0 || os[2] < 0) return MXATTN_E_INVALID;
-  if (workspace == nullptr || ws_bytes < mxattn_decode_workspace_bytes(B, Hq, R, N)) return MXATTN_E_WORKSPACE;
+  const size_t need = mxattn_decode_workspace_bytes(B, Hq, R, N);
+  if (use_scratch) {
+    if (need > DECODE_SCRATCH_BYTES) {
+      snprintf(g_err, sizeof g_err, "mxattn_decode_noalloc: the split states need %zu bytes, the static scratch "
+               "holds %zu", need, DECODE_SCRATCH_BYTES);
+      return MXATTN_E_WORKSPACE;
+    }
+    hipError_t es = decode_scratch(&workspace);
+    if (es != hipSuccess) return hip_fail(es, "mxattn_decode_noalloc scratch address");
+    ws_bytes = DECODE_SCRATCH_BYTES;
+  }
+  if (workspace == nullptr || ws_bytes < need) return MXATTN_E_WORKSPACE;
   if (!aligned16(workspace)) return MXATTN_E_ALIGN;
   // grids: one workgroup per (request, KV head, 512-key chunk); four per merged row
   if (B * Hkv * ((N + 511) / 512) > 0x7FFFFFFF || B * Hq * R * 4 > 0x7FFFFFFF) return MXATTN_E_UNSUPPORTED;
@@ -371,8 +386,22 @@ int mxattn_decode(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn
   a.lse = lse;
   hipError_t e = launch_decode(p->pmode, a, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return MXATTN_E_UNSUPPORTED;
-  if (e != hipSuccess) return hip_fail(e, "mxattn_decode launch");
+  if (e != hipSuccess) return hip_fail(e, use_scratch ? "mxattn_decode_noalloc launch" : "mxattn_decode launch");
   return MXATTN_OK;
+}
+
+extern "C" {
+
+int mxattn_decode(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn_qtensor* v,
+                  const mxattn_fwd_params* p, const int32_t* kv_len, void* out, const int64_t os[4], float* lse,
+                  void* workspace, size_t ws_bytes, void* stream) {
+  return decode_impl(q, k, v, p, kv_len, out, os, lse, workspace, ws_bytes, stream, false);
+}
+
+int mxattn_decode_noalloc(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn_qtensor* v,
+                          const mxattn_fwd_params* p, const int32_t* kv_len, void* out, const int64_t os[4],
+                          float* lse, void* stream) {
+  return decode_impl(q, k, v, p, kv_len, out, os, lse, nullptr, 0, stream, true);
 }
 
 int mxattn_fwd_plan(const int32_t* cu_host, int ndocs, int64_t N, int causal, void* workspace, size_t ws_bytes,

@@ -133,6 +133,12 @@ struct DecArgs {
 };
 hipError_t launch_decode(int pmode, const DecArgs& a, hipStream_t st);
 
+// Allocation-free decode: the split states live in a file-scope device array of
+// DECODE_SCRATCH_BYTES (decode.hip), one copy per GPU.  decode_scratch() returns its
+// address on the current device (looked up once per device with hipGetSymbolAddress).
+constexpr size_t DECODE_SCRATCH_BYTES = size_t(32) << 20;
+hipError_t decode_scratch(void** ptr);
+
 // psc: P block scale (SCALE_E8M0 -> blocks of 32, SCALE_E4M3 -> blocks of 16);
 // vsc: V block scale (same meaning).
 hipError_t launch_fwd(int qk, int pv, int pmode, int psc, int vsc, const FwdArgs& a, hipStream_t st);
