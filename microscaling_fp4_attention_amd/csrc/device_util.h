@@ -13,6 +13,8 @@ namespace mxattn {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
@@ -59,7 +61,22 @@ __device__ __forceinline__ v16f mfma_bf16(v8bf a, v8bf b, v16f c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ v16f mfma_f16(v8h a, v8h b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// A wave-uniform float held in a VGPR.  On gfx950 a VALU instruction with an SGPR
+// operand issues at about 4.5 cycles per wave64 instruction, one with VGPR operands
+// only at about 2.8 (an FMA; measured with independent chains), so a constant read
+// once per score element (the exponent scale lambda) is copied to a VGPR once.  The
+// copy is opaque to the compiler, which would otherwise keep the value in an SGPR.
+__device__ __forceinline__ float to_vgpr(float x) {
+  float y;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));
+  return y;
+}
 
 // 2^(lambda (x - msub)) formed from the difference x - msub, so that it is exactly 1
 // at x = msub: block scales and the two-level pre-scale are chosen from this value,
@@ -141,6 +158,36 @@ __device__ __forceinline__ u4 dq8_bf16(uint32_t w, float s) {
   v2f p0 = fp4_pair(w, 0), p1 = fp4_pair(w, 1), p2 = fp4_pair(w, 2), p3 = fp4_pair(w, 3);
   return mk4(pack_bf16_exact(p0[0] * s, p0[1] * s), pack_bf16_exact(p1[0] * s, p1[1] * s),
                     pack_bf16_exact(p2[0] * s, p2[1] * s), pack_bf16_exact(p3[0] * s, p3[1] * s));
+}
+
+// 8 E2M1 codes (one dword, low nibble first) times a power of two `sc` (the convert
+// uses the exponent of its scale operand) -> 8 f16 (4 dwords)
+__device__ __forceinline__ u4 dq8_f16_pow2(uint32_t w, float sc) {
+  return mk4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 0)),
+             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 1)),
+             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 2)),
+             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 3)));
+}
+
+// 8 E2M1 codes times an E4M3 value s2 (both halves) -> 8 f16, exact: an E2M1 value
+// times an E4M3 value has at most 6 significant bits and lies in [2^-10, 2688]
+__device__ __forceinline__ v8h dq8_f16(uint32_t w, v2h s2) {
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+  return v8h{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// fl32(x / 6), the input of an E4M3 block scale, by Markstein's division: the quotient
+// from the correctly rounded reciprocal of 6 by one residual step, equal to the IEEE
+// quotient for every float whose quotient is normal (6 is an E4M3 value; the host test
+// of the quantizer's division checks every float of one binade under each of them);
+// smaller quotients encode to the zero scale either way
+__device__ __forceinline__ float div6(float x) {
+  const float r = 0x1.555556p-3f;  // fl32(1/6)
+  const float q = x * r;
+  return __builtin_fmaf(__builtin_fmaf(-q, 6.0f, x), r, q);
 }
 
 __device__ __forceinline__ float scale_value(uint32_t byte, int kind) {

@@ -629,6 +629,8 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[L::BYTES];
   constexpr int STAGE = L::STAGE, KV = L::KV;
   constexpr bool SPLIT16 = PV == PV_FP8;
+  // E4M3-scaled P with MXFP4 V: the PV product in f16 (the per-key V form keeps bf16)
+  constexpr bool H16 = PV == PV_BF16 && !SAFE;
   const int tid = threadIdx.x, lane = tid & 63, ql = lane & 31, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int grp = wave >> 2;  // 0: group A, 1: group B
@@ -684,6 +686,9 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   int nkt = (klen + 127) / 128;
   if (a.causal && nkt > 2 * (int)qt + 2) nkt = 2 * (int)qt + 2;
   const float lam = a.lambda;
+  // two-level P: lambda in a VGPR for the per-element FMA (2.8% faster at N = 32K; the
+  // other modes measured 0.5-1.5% slower with it)
+  const float lamv = PMODE == PM_TWO_LEVEL ? to_vgpr(lam) : lam;
   // P~ of a score s given the row's exponent offset ms = m lambda and, for the bit-level
   // exponential, cm = exp_bias - ms 2^23: one FMA and the hardware exponential, or one
   // FMA (2^23 (s lambda - ms - delta + 127), its rounding keeps 16 fraction bits of t),
@@ -692,7 +697,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   const float lamb = lam * 0x1p23f;
   auto pexp = [&](float sc, float ms, float cm) __attribute__((always_inline)) -> float {
     if constexpr (EXPB) return exp2_bits(__builtin_fmaf(sc, lamb, cm));
-    else return exp2_hw(__builtin_fmaf(sc, lam, -ms));
+    else return exp2_hw(__builtin_fmaf(sc, lamv, -ms));
   };
   auto pexp_c = [&](float ms) __attribute__((always_inline)) -> float {
     return EXPB ? __builtin_fmaf(-ms, 0x1p23f, a.exp_bias) : 0.0f;
@@ -750,6 +755,68 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   u4 rk, rv0, rv1;
   uint32_t rks = 0, rvs = 0, rvs_hi = 0;
   float rb = 0.0f;
+  // f16 PV: each channel row c of V is staged as V 2^vshift_c, which places the largest
+  // E8M0 exponent among the row's blocks this workgroup reads at 13 (6 2^13 < 65504).
+  // Every block within 36 binades of it is then exact in f16 (its values are multiples
+  // of 2^-24).  Row c of O^T = V^T P^T is the same channel, so the epilogue scales each
+  // channel back by 2^-vshift_c.  The staging thread of channel row c (tid / 4) scans
+  // that row's scale bytes with the three other threads of its quad, over the blocks
+  // that hold keys of this workgroup's range; blocks staged past it (the tail tile's
+  // next document or padding) meet only masked keys and are clamped to 2^13.  An
+  // all-zero block carries the byte of 2^0: when that byte is the row's largest and a
+  // block lies more than 36 binades below it, the zero blocks are told apart by their
+  // codes and left out.
+  int vshift = 0;
+  __shared__ int vshift_lds[H16 ? 128 : 1];
+  if constexpr (H16) {
+    const uint32_t b0 = (uint32_t)(vstart >> 5);
+    const uint32_t bk = (uint32_t)((vstart + klen + 31) >> 5);       // past the range's keys
+    const uint32_t bt = b0 + 4u * (uint32_t)nkt;                      // past the tiles read
+    const uint32_t b1 = bk < bt ? bk : bt;                            // blocks [b0, b1)
+    const uint32_t row = (uint32_t)(tid >> 2);
+    const uint8_t* rp = hv_sbase + row * nvb;
+    uint32_t mx = 0, mn = 255;
+    auto bmax4 = [](uint32_t w) {
+      return __builtin_elementwise_max(__builtin_elementwise_max(w & 0xFFu, (w >> 8) & 0xFFu),
+                                       __builtin_elementwise_max((w >> 16) & 0xFFu, w >> 24));
+    };
+    auto bmin4 = [](uint32_t w) {
+      return __builtin_elementwise_min(__builtin_elementwise_min(w & 0xFFu, (w >> 8) & 0xFFu),
+                                       __builtin_elementwise_min((w >> 16) & 0xFFu, w >> 24));
+    };
+    // aligned dwords (nvb is a multiple of 4); bytes outside [b0, b1) are kept out
+    for (uint32_t i = (b0 & ~3u) + 4u * (uint32_t)(tid & 3); i < b1; i += 16u) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(rp + i);
+      uint32_t keep = 0xFFFFFFFFu;
+      if (i < b0) keep &= 0xFFFFFFFFu << (8u * (b0 - i));
+      if (i + 4u > b1) keep &= 0xFFFFFFFFu >> (8u * (i + 4u - b1));
+      mx = __builtin_elementwise_max(mx, bmax4(w & keep));
+      mn = __builtin_elementwise_min(mn, bmin4(w | ~keep));
+    }
+    mx = __builtin_elementwise_max(mx, (uint32_t)__shfl_xor((int)mx, 1));
+    mx = __builtin_elementwise_max(mx, (uint32_t)__shfl_xor((int)mx, 2));
+    mn = __builtin_elementwise_min(mn, (uint32_t)__shfl_xor((int)mn, 1));
+    mn = __builtin_elementwise_min(mn, (uint32_t)__shfl_xor((int)mn, 2));
+    if (mx == 127u && mn + 36u < 127u) {
+      // the largest byte is 2^0, possibly of all-zero blocks: take the largest over the
+      // blocks that are not 2^0 or have a nonzero code (codes: 16 bytes per block)
+      const uint8_t* cp = hv_codes + row * vrow_bytes;
+      uint32_t m2 = 0;
+      for (uint32_t bl = b0 + (uint32_t)(tid & 3); bl < b1; bl += 4u) {
+        const uint32_t byte = rp[bl];
+        bool real = byte != 127u;
+        if (!real) {
+          const u4 c = *reinterpret_cast<const u4*>(cp + 16u * bl);
+          real = (c.x | c.y | c.z | c.w) != 0u;
+        }
+        if (real) m2 = __builtin_elementwise_max(m2, byte);
+      }
+      m2 = __builtin_elementwise_max(m2, (uint32_t)__shfl_xor((int)m2, 1));
+      mx = __builtin_elementwise_max(m2, (uint32_t)__shfl_xor((int)m2, 2));
+    }
+    vshift = 140 - (int)mx;  // biased byte mx -> exponent 13
+    if ((tid & 3) == 0) vshift_lds[row] = vshift;
+  }
   auto load_half = [&](int t) __attribute__((always_inline)) {
     if constexpr (BIAS) {
       if (gt >= 128 && gt < 192) {  // wave-uniform
@@ -824,6 +891,16 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
         *reinterpret_cast<uint32_t*>(base + L::VSC + 4 * sr) = w;
         *reinterpret_cast<uint32_t*>(base + L::VSC + 512 + 4 * sr) = w >> 8;
       }
+    } else if constexpr (H16) {  // f16 row of 128 keys (V 2^vshift), chunk = key / 8, swizzled
+      // scale 2^(e + vshift) as the convert's operand: biased exponent byte + vshift
+      // (140 at most inside the scanned blocks, clamped there outside them); blocks more
+      // than 139 binades below the largest become 0
+      const int be = __builtin_elementwise_min((int)rvs + vshift, 140);
+      const float sc = u2f((uint32_t)(be > 1 ? be : 1) << 23);
+      const uint32_t w4[4] = {rv0.x, rv0.y, rv0.z, rv0.w};
+#pragma unroll
+      for (int u = 0; u < 4; u++)
+        *reinterpret_cast<u4*>(vb + kr * 256 + (((4 * part + u) ^ (kr & 15)) * 16)) = dq8_f16_pow2(w4[u], sc);
     } else {  // bf16 row of 128 keys, chunk = key / 8, swizzled by the channel
       const float sv = scale_value(rvs, SCALE_E8M0);
       const uint32_t w4[4] = {rv0.x, rv0.y, rv0.z, rv0.w};
@@ -941,6 +1018,26 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
             else O[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bp[1], O[db], 0, 0, 2, (int)vs4, 0, 127);
           }
         }
+      } else if constexpr (H16) {
+        // P^ of step s (keys 64(s/4) + 32h + 8(s%4) + [0, 8) = sub-tile 2(s/4) + (s%4)/2,
+        // entries 8((s%4)%2) + [0, 8)) dequantized exactly to f16 from its codes
+        v8h pb[8];
+#pragma unroll
+        for (int s = 0; s < 8; s++) {
+          const int bb = 2 * (s >> 2) + ((s & 3) >> 1);
+          const _Float16 sh = (_Float16)pdq[bb];  // an E4M3 value: exact in f16
+          pb[s] = dq8_f16(pc[2 * bb + ((s & 3) & 1)], v2h{sh, sh});
+        }
+#pragma unroll
+        for (int db = 0; db < 4; db++) {
+          const uint8_t* rp = Vs + (32 * db + ql) * 256;
+#pragma unroll
+          for (int s = 0; s < 8; s++) {
+            const int chunk = (8 * (s >> 2) + 4 * hh + (s & 3)) ^ (ql & 15);
+            v8h av = *reinterpret_cast<const v8h*>(rp + chunk * 16);
+            O[db] = mfma_f16(av, pb[s], O[db]);
+          }
+        }
       } else {
         // P^ of step s (keys 64(s/4) + 32h + 8(s%4) + [0, 8) = sub-tile 2(s/4) + (s%4)/2,
         // entries 8((s%4)%2) + [0, 8)) dequantized exactly to bf16 from its codes
@@ -1046,8 +1143,8 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       float r = pmax(tmax, ms, cm, msub);
       if (r >= 0x1p-64f) {
         float s1 = r / 2688.0f;
-        k1 = 1.0f / s1;
-        scale_o = alpha * (s1prev / s1);
+        k1 = __builtin_amdgcn_rcpf(s1);  // within an ulp: the P values' products carry it
+        scale_o = alpha * (s1prev * k1);
         s1prev = s1;
       } else {
         k1 = 0.0f;
@@ -1082,10 +1179,10 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
 #pragma unroll
       for (int bb = 0; bb < 4; bb++) {
         const float pm = pmax(bm16[bb], ms, cm, msub) * k1;
-        const float sv = e4m3_value(e4m3_mag(pm / 6.0f));
+        const float sv = e4m3_value(e4m3_mag(div6(pm)));
         sc16[bb] = 1.0f;
         sv16[bb] = sv;
-        ki16[bb] = sv > 0.0f ? 1.0f / sv : 0.0f;
+        ki16[bb] = sv > 0.0f ? __builtin_amdgcn_rcpf(sv) : 0.0f;
       }
     }
 
@@ -1185,8 +1282,8 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     } else {  // PV_BF16: E4M3 scale per 16 keys
 #pragma unroll
       for (int bb = 0; bb < 4; bb++) {
-        const float sv = e4m3_value(e4m3_mag(pm16[bb] * k1 / 6.0f));
-        const float ki = sv > 0.0f ? 1.0f / sv : 0.0f;
+        const float sv = e4m3_value(e4m3_mag(div6(pm16[bb] * k1)));
+        const float ki = sv > 0.0f ? __builtin_amdgcn_rcpf(sv) : 0.0f;
         float z[16];
 #pragma unroll
         for (int j = 0; j < 16; j++) z[j] = (PMODE == PM_TWO_LEVEL ? S[bb][j] * k1 : S[bb][j]) * ki;
@@ -1283,6 +1380,15 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   float inv = l > 0.0f ? 1.0f / l : 0.0f;
   if constexpr (PMODE == PM_TWO_LEVEL) inv *= s1prev;
   if constexpr (PV == PV_FP8) inv = inv / 448.0f;
+  if constexpr (H16) {  // undo each channel's 2^vshift (exact); register j of block db
+                         // holds channel 32 db + 8 (j / 4) + 4 hh + j % 4
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 16; j++)
+        O[i][j] = __builtin_ldexpf(O[i][j] * inv, -vshift_lds[32 * i + 8 * (j >> 2) + 4 * hh + (j & 3)]);
+    inv = 1.0f;
+  }
   if (qloc < klen) {
     const int64_t orow = qstart + qloc;
     if (a.out_fp32) {

@@ -130,3 +130,49 @@ def test_fwd_empty_documents(route, causal):
     doc_off = np.array([0, 100, 100, 357, 357, 700, 700], np.int32)
     res = run_case(q, v, pm, pf, B=1, Hq=2, Hkv=1, N=700, causal=causal, kind="outlier", seed=9, doc_off=doc_off)
     _check(res, route + f" empty docs causal={causal}")
+
+
+def _scaled_v(x, scale_of_channel):
+    """inputs x with V's channel c multiplied by scale_of_channel[c] (powers of two: exact)"""
+    v = synth.bf16_to_f32(x["v"]) * np.asarray(scale_of_channel, np.float32)
+    y = dict(x)
+    y["v"] = synth.f32_to_bf16(v)
+    return y
+
+
+@pytest.mark.parametrize("route", ["mxfp4_two_level_e4m3", "mxfp4_direct_e4m3p"])
+@pytest.mark.parametrize("case", ["huge", "tiny", "tiny_zero_blocks", "split_channels"])
+def test_fwd_f16_pv_v_range(route, case):
+    """E4M3-scaled P with MXFP4 V runs its PV product in f16 with each V channel shifted
+    by a power of two into f16's range.  V far above f16's largest value (x 2^40), far
+    below its smallest (x 2^-60; also with two all-zero 32-key blocks, whose scale byte is
+    that of 2^0), and channels 2^60 apart (half x 2^30, half x 2^-30): each channel group
+    is checked against its own scale."""
+    q, v, pm, pf = ROUTES[route]
+    x = synth.make_inputs("kmean", 1, 2, 2, 300, 128, 7)
+    ch = np.ones(128, np.float32)
+    if case == "huge":
+        ch[:] = 2.0 ** 40
+    elif case == "split_channels":
+        ch[:64], ch[64:] = 2.0 ** 30, 2.0 ** -30
+    if case.startswith("tiny"):
+        ch[:] = 2.0 ** -60
+    xs = _scaled_v(x, ch)
+    if case == "tiny_zero_blocks":
+        va = xs["v"].copy()
+        va[:, :, 64:128, :] = 0  # keys 64..127 of every channel: two zero blocks
+        xs["v"] = va
+    res = run_case(q, v, pm, pf, B=1, Hq=2, Hkv=2, N=300, inputs=xs)
+    assert np.all(np.isfinite(res["O_gpu"]))
+    groups = [np.arange(128)] if case != "split_channels" else [np.arange(64), np.arange(64, 128)]
+    vmax = float(np.abs(synth.bf16_to_f32(xs["v"])).max())
+    for g in groups:
+        Og, Or = res["O_gpu"][:, g], res["O_ref"][:, g]
+        # the flip budget bounds |dp^| max|v| / l over all channels; this group's share
+        # scales with its own largest |v|
+        vg = float(np.abs(synth.bf16_to_f32(xs["v"])[..., g]).max())
+        bound = TOL * np.abs(Or).max() + res["fb"][:, None] * (vg / vmax)
+        ratio = float((np.abs(Og - Or) / bound).max())
+        record_parity(f"{route} V range {case} channels {g[0]}..{g[-1]}", ratio,
+                      res["fb"] * (vg / vmax) / (TOL * np.abs(Or).max()))
+        assert ratio <= 1.0, (case, g[0], ratio)
