@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MXATTN_ABI_VERSION 6
+#define MXATTN_ABI_VERSION 7
 
 typedef enum {
   MXATTN_OK = 0,
@@ -184,6 +184,14 @@ const char* mxattn_status_str(int status);
 const char* mxattn_last_error(void);
 
 /*
+ * Test hook of the error path: the next `count` device submissions made by library
+ * calls on the calling thread are not made; each such call returns MXATTN_E_HIP with
+ * hipErrorLaunchFailure in mxattn_last_error(), after its host checks passed.
+ * count <= 0 turns the hook off.  Returns the count that was pending.
+ */
+int mxattn_debug_fail_launches(int count);
+
+/*
  * Bytes of the codes and scales buffers of a quantized tensor.
  *   fmt, role  : format and role as passed to mxattn_quantize()
  *   B, H, N, d : shape of the bf16 tensor ([B][H][N][d])
@@ -219,7 +227,8 @@ int mxattn_qtensor_bytes(const mxattn_qfmt* fmt, int role, int64_t B, int64_t H,
  *   the sizes from mxattn_qtensor_bytes(); the library fills the other fields.
  * Errors: MXATTN_E_INVALID (also role VT with documents), MXATTN_E_UNSUPPORTED
  *   (d != 128, block not 16/32, E4M3 elements with an E4M3 scale, role VT in any
- *   format but E2M1 with E8M0 per 32), MXATTN_E_ALIGN, MXATTN_E_HIP.
+ *   format but E2M1 with E8M0 per 32, role QK with B*H*N >= 2^30), MXATTN_E_ALIGN,
+ *   MXATTN_E_HIP.
  */
 int mxattn_quantize(const void* x_bf16, const int64_t x_strides[4], int64_t B, int64_t H, int64_t N,
                     int64_t d, int role, const mxattn_qfmt* fmt, const int32_t* cu_seqlens, int ndocs,
@@ -264,7 +273,8 @@ typedef struct {
  *   pre: NULL (plain quantization) or the pre-processing to apply.
  *   cu_seqlens/ndocs: DEVICE document offsets selecting each token's mean row
  *   (the qtensor is laid out as without documents: role QK has no padding).
- * Errors: as mxattn_quantize(), plus MXATTN_E_INVALID for role V.
+ * Errors: as mxattn_quantize(), plus MXATTN_E_INVALID for role V and
+ *   MXATTN_E_UNSUPPORTED for B*H*N >= 2^28.
  */
 int mxattn_quantize_pre(const void* x_bf16, const int64_t x_strides[4], int64_t B, int64_t H, int64_t N,
                         int64_t d, int role, const mxattn_qfmt* fmt, const mxattn_preproc* pre,
@@ -280,8 +290,8 @@ int mxattn_quantize_pre(const void* x_bf16, const int64_t x_strides[4], int64_t 
  *   qmean: DEVICE [B][Hq][max(ndocs,1)][d]; kmean: DEVICE [B][Hkv][max(ndocs,1)][d]
  *   k: bf16 [B][Hkv][N][d] with element strides k_strides (the unquantized K);
  *   delta: DEVICE float32 [B][Hq][N].
- * Errors: MXATTN_E_INVALID, MXATTN_E_UNSUPPORTED (d != 128), MXATTN_E_ALIGN,
- *   MXATTN_E_HIP.
+ * Errors: MXATTN_E_INVALID, MXATTN_E_UNSUPPORTED (d != 128, B*Hkv*N >= 2^28),
+ *   MXATTN_E_ALIGN, MXATTN_E_HIP.
  */
 int mxattn_center_comp(const float* qmean, const void* k_bf16, const int64_t k_strides[4], const float* kmean,
                        int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, const int32_t* cu_seqlens,
@@ -318,6 +328,11 @@ int mxattn_fwd_plan(const int32_t* cu_seqlens_host, int ndocs, int64_t N, int ca
  *     documents (B == 1), `v` must have been quantized with the same documents
  *     and `workspace` must hold a plan from mxattn_fwd_plan().  Attention never
  *     crosses a document, and key tiles start at each document's first token.
+ *     The kernels check the plan's header against the call (document count, N,
+ *     causal flag, list sizes): a workspace that holds no plan, or one built
+ *     for other arguments, makes every row of `out` and `lse` NaN; the entries
+ *     of a plan are bounds-checked, so none is read past N.  A plan for other
+ *     offsets with the same counts cannot be told apart.
  *   out: [B][Hq][N][d] with element strides out_strides (out_strides[3] == 1,
  *     16-byte aligned rows), float32 or bfloat16 per params->out_fp32.
  *   lse: optional float32 [B][Hq][N] log-sum-exp (natural log) of each row, or

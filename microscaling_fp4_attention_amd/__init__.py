@@ -27,7 +27,7 @@ P_DIRECT, P_TWO_LEVEL, P_PNQ, P_FP8_FIXED = 1, 2, 3, 4
 EXP_EXACT, EXP_MITCHELL, EXP_SCHRAUDOLPH = 0, 1, 2
 
 
-ABI_VERSION = 6  # MXATTN_ABI_VERSION of include/mxattn.h
+ABI_VERSION = 7  # MXATTN_ABI_VERSION of include/mxattn.h
 DECODE_SCRATCH_BYTES = 32 << 20  # MXATTN_DECODE_SCRATCH_BYTES
 
 
@@ -95,6 +95,8 @@ def _lib():
         L.mxattn_status_str.restype = ctypes.c_char_p
         L.mxattn_status_str.argtypes = [i32]
         L.mxattn_last_error.restype = ctypes.c_char_p
+        L.mxattn_debug_fail_launches.restype = i32
+        L.mxattn_debug_fail_launches.argtypes = [i32]
         L.mxattn_qtensor_bytes.restype = i32
         L.mxattn_qtensor_bytes.argtypes = [P(QFmt), i32, i64, i64, i64, i64, i32, P(ctypes.c_size_t),
                                            P(ctypes.c_size_t), P(i64)]

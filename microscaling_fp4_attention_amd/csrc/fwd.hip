@@ -52,6 +52,47 @@ struct Lds {
 template <int QK, int PV>
 constexpr int waves_per_simd() { return 2; }
 
+// ---------------------------------------------------------------------------
+// Plans of packed documents.  A plan is used only when its header matches the call:
+// magic, document count, token count, causal flag and list sizes.  Otherwise every
+// workgroup fills its rows of O and LSE with NaN, the mark of a mismatched workspace.
+// Each entry is bounds-checked before it steers a read: a damaged entry is skipped.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool plan_header_ok(const FwdArgs& a) {
+  const PlanHeader* ph = a.plan;
+  const int64_t cap128 = (a.N + 127) / 128 + a.ndocs, cap256 = (a.N + 255) / 256 + a.ndocs;
+  return ph->magic == PLAN_MAGIC && ph->ndocs == a.ndocs && (int64_t)ph->n_tokens == a.N &&
+         ph->causal == (a.causal ? 1 : 0) && (int64_t)ph->cap128 == cap128 && ph->n_items >= 0 &&
+         (int64_t)ph->n_items <= cap128 && ph->n_items256 >= 0 && (int64_t)ph->n_items256 <= cap256;
+}
+
+// a work item's document lies inside [0, N), its query tile inside the document and its
+// V segment (vblock-aligned start, length rounded up to vblock) inside the padded keys
+__device__ __forceinline__ bool plan_item_ok(const FwdArgs& a, const DocEntry& de, const WorkItem& wi, int rows,
+                                             int64_t voff, int vblock) {
+  return de.start >= 0 && de.len >= 0 && (int64_t)de.start <= a.N - de.len && wi.qtile >= 0 &&
+         (int64_t)wi.qtile * rows < de.len && voff >= 0 &&
+         voff + ((int64_t)de.len + vblock - 1) / vblock * vblock <= a.np;
+}
+
+// rows [r0, r0 + nrows) of query head hq (batch 0) of O and LSE set to NaN
+__device__ void fill_nan_rows(const FwdArgs& a, int64_t hq, int64_t r0, int nrows) {
+  for (int idx = threadIdx.x; idx < 2 * nrows; idx += blockDim.x) {
+    const int64_t row = r0 + idx / 2;
+    if (row >= a.N) continue;
+    const int c0 = 64 * (idx & 1);
+    if (a.out_fp32) {
+      float* op = static_cast<float*>(a.out) + hq * a.oH + row * a.oN + c0;
+      const float nan = __builtin_nanf("");
+      for (int c = 0; c < 64; c += 4) *reinterpret_cast<float4*>(op + c) = make_float4(nan, nan, nan, nan);
+    } else {
+      uint16_t* op = static_cast<uint16_t*>(a.out) + hq * a.oH + row * a.oN + c0;
+      for (int c = 0; c < 64; c += 8) *reinterpret_cast<u4*>(op + c) = mk4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+    }
+    if (a.lse != nullptr && (idx & 1) == 0) a.lse[hq * a.N + row] = __builtin_nanf("");
+  }
+}
+
 template <int QK, int PV, int PMODE, int PSC, int VSC, bool BIAS>
 __global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -67,13 +108,19 @@ __global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(Fw
   if (a.plan != nullptr) {
     const PlanHeader* ph = a.plan;
     const DocEntry* docs = reinterpret_cast<const DocEntry*>(ph + 1);
-    const WorkItem* items = reinterpret_cast<const WorkItem*>(docs + ph->ndocs);
+    const WorkItem* items = reinterpret_cast<const WorkItem*>(docs + a.ndocs);
     int64_t item = blockIdx.x / a.Hq;
     hq = blockIdx.x % a.Hq;
     b = 0;
+    if (!plan_header_ok(a)) {
+      fill_nan_rows(a, hq, item * 128, 128);
+      return;
+    }
     if (item >= ph->n_items) return;
     WorkItem wi = items[item];
+    if ((uint32_t)wi.doc >= (uint32_t)a.ndocs) return;
     DocEntry de = docs[wi.doc];
+    if (!plan_item_ok(a, de, wi, 128, VB == 32 ? de.voff32 : de.voff16, VB)) return;
     qt = wi.qtile;
     qstart = de.start;
     qlen = de.len;
@@ -642,13 +689,19 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   if (a.plan != nullptr) {
     const PlanHeader* ph = a.plan;
     const DocEntry* docs = reinterpret_cast<const DocEntry*>(ph + 1);
-    const WorkItem* items = reinterpret_cast<const WorkItem*>(docs + ph->ndocs) + ph->cap128;
+    const WorkItem* items = reinterpret_cast<const WorkItem*>(docs + a.ndocs) + ((a.N + 127) / 128 + a.ndocs);
     const int64_t item = blockIdx.x / a.Hq;
     hq = blockIdx.x % a.Hq;
     b = 0;
+    if (!plan_header_ok(a)) {
+      fill_nan_rows(a, hq, item * 256, 256);
+      return;
+    }
     if (item >= ph->n_items256) return;
     const WorkItem wi = items[item];
+    if ((uint32_t)wi.doc >= (uint32_t)a.ndocs) return;
     const DocEntry de = docs[wi.doc];
+    if (!plan_item_ok(a, de, wi, 256, de.voff32, 32)) return;
     qt = wi.qtile;
     qstart = de.start;
     klen = de.len;

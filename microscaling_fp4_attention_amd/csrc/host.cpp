@@ -19,6 +19,16 @@ namespace {
 
 thread_local char g_err[256] = "";
 
+// test hook: the next g_fail_launches device submissions on this thread are not made
+// and report hipErrorLaunchFailure (mxattn_debug_fail_launches)
+thread_local int g_fail_launches = 0;
+
+hipError_t forced_failure() {
+  if (g_fail_launches <= 0) return hipSuccess;
+  g_fail_launches--;
+  return hipErrorLaunchFailure;
+}
+
 int hip_fail(hipError_t e, const char* what) {
   snprintf(g_err, sizeof g_err, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
   return MXATTN_E_HIP;
@@ -114,6 +124,12 @@ const char* mxattn_status_str(int s) {
 
 const char* mxattn_last_error(void) { return g_err; }
 
+int mxattn_debug_fail_launches(int count) {
+  const int prev = g_fail_launches;
+  g_fail_launches = count > 0 ? count : 0;
+  return prev;
+}
+
 int mxattn_qtensor_bytes(const mxattn_qfmt* fmt, int role, int64_t B, int64_t H, int64_t N, int64_t d, int ndocs,
                          size_t* code_bytes, size_t* scale_bytes, int64_t* n_padded) {
   int rc = check_fmt(fmt, role);
@@ -167,6 +183,8 @@ int mxattn_quantize(const void* x_bf16, const int64_t x_strides[4], int64_t B, i
   out->d = d;
   out->n_padded = np;
   if (nel == 0 && !(role != MXATTN_ROLE_QK && B * H > 0 && np > 0)) return MXATTN_OK;
+  // role QK: 4 rows per thread and 16 threads per 4 rows, 32-bit row indices
+  if (role == MXATTN_ROLE_QK && nel >= (int64_t(1) << 30)) return MXATTN_E_UNSUPPORTED;
 
   QuantArgs a;
   a.x = x_bf16;
@@ -187,9 +205,11 @@ int mxattn_quantize(const void* x_bf16, const int64_t x_strides[4], int64_t B, i
   a.scales = out->scales;
   a.tiled = role == MXATTN_ROLE_VT ? 1 : 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = role == MXATTN_ROLE_QK                               ? launch_quant_qk(a, st)
-                 : role == MXATTN_ROLE_V || role == MXATTN_ROLE_VT ? launch_quant_v(a, st)
-                                                                   : launch_quant_vkey(a, st);
+  hipError_t e = forced_failure();
+  if (e == hipSuccess)
+    e = role == MXATTN_ROLE_QK                               ? launch_quant_qk(a, st)
+        : role == MXATTN_ROLE_V || role == MXATTN_ROLE_VT ? launch_quant_v(a, st)
+                                                          : launch_quant_vkey(a, st);
   if (e != hipSuccess) return hip_fail(e, "mxattn_quantize launch");
   return MXATTN_OK;
 }
@@ -214,7 +234,8 @@ int mxattn_channel_mean(const void* x_bf16, const int64_t x_strides[4], int64_t 
   a.N = N;
   a.cu = ndocs > 1 ? cu_seqlens : nullptr;
   a.ndocs = ndocs > 1 ? ndocs : 1;
-  hipError_t e = launch_channel_mean(a, mean, static_cast<hipStream_t>(stream));
+  hipError_t e = forced_failure();
+  if (e == hipSuccess) e = launch_channel_mean(a, mean, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mxattn_channel_mean launch");
   return MXATTN_OK;
 }
@@ -248,6 +269,7 @@ int mxattn_quantize_pre(const void* x_bf16, const int64_t x_strides[4], int64_t 
   out->d = d;
   out->n_padded = np;
   if (nel == 0) return MXATTN_OK;
+  if (nel >= (int64_t(1) << 28)) return MXATTN_E_UNSUPPORTED;  // 16 threads per row, 32-bit thread ids
   QuantArgs a{};
   a.x = x_bf16;
   a.sB = x_strides[0];
@@ -265,7 +287,8 @@ int mxattn_quantize_pre(const void* x_bf16, const int64_t x_strides[4], int64_t 
   a.ndocs = ndocs > 1 ? ndocs : 1;
   a.codes = out->codes;
   a.scales = out->scales;
-  hipError_t e = launch_quant_qk_pre(a, pre->mean, pre->hadamard, static_cast<hipStream_t>(stream));
+  hipError_t e = forced_failure();
+  if (e == hipSuccess) e = launch_quant_qk_pre(a, pre->mean, pre->hadamard, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mxattn_quantize_pre launch");
   return MXATTN_OK;
 }
@@ -279,6 +302,7 @@ int mxattn_center_comp(const float* qmean, const void* k_bf16, const int64_t k_s
   if (ndocs > 1 && cu_seqlens == nullptr) return MXATTN_E_INVALID;
   if (k_strides[3] != 1 || k_strides[0] < 0 || k_strides[1] < 0 || k_strides[2] < 0) return MXATTN_E_INVALID;
   if (B * N == 0) return MXATTN_OK;
+  if (B * Hkv * N >= (int64_t(1) << 28)) return MXATTN_E_UNSUPPORTED;  // 16 threads per key row
   if (qmean == nullptr || kmean == nullptr || k_bf16 == nullptr || delta == nullptr) return MXATTN_E_INVALID;
   if (!aligned16(qmean) || !aligned16(kmean) || !aligned16(k_bf16) || !aligned16(delta)) return MXATTN_E_ALIGN;
   if ((k_strides[0] % 8) || (k_strides[1] % 8) || (k_strides[2] % 8)) return MXATTN_E_ALIGN;
@@ -296,7 +320,8 @@ int mxattn_center_comp(const float* qmean, const void* k_bf16, const int64_t k_s
   a.cu = ndocs > 1 ? cu_seqlens : nullptr;
   a.ndocs = ndocs > 1 ? ndocs : 1;
   a.delta = delta;
-  hipError_t e = launch_center_comp(a, static_cast<hipStream_t>(stream));
+  hipError_t e = forced_failure();
+  if (e == hipSuccess) e = launch_center_comp(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mxattn_center_comp launch");
   return MXATTN_OK;
 }
@@ -384,7 +409,8 @@ static int decode_impl(const mxattn_qtensor* q, const mxattn_qtensor* k, const m
   a.oN = os[2];
   a.out_fp32 = p->out_fp32 ? 1 : 0;
   a.lse = lse;
-  hipError_t e = launch_decode(p->pmode, a, static_cast<hipStream_t>(stream));
+  hipError_t e = forced_failure();
+  if (e == hipSuccess) e = launch_decode(p->pmode, a, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return MXATTN_E_UNSUPPORTED;
   if (e != hipSuccess) return hip_fail(e, use_scratch ? "mxattn_decode_noalloc launch" : "mxattn_decode launch");
   return MXATTN_OK;
@@ -455,7 +481,10 @@ int mxattn_fwd_plan(const int32_t* cu_host, int ndocs, int64_t N, int causal, vo
   ph->magic = PLAN_MAGIC;
   ph->n_items256 = (int32_t)cand256.size();
   ph->cap128 = (int32_t)cap128;
-  hipError_t e = hipMemcpyAsync(workspace, buf.data(), need, hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
+  ph->n_tokens = (int32_t)N;
+  hipError_t e = forced_failure();
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(workspace, buf.data(), need, hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mxattn_fwd_plan copy");
   return MXATTN_OK;
 }
@@ -550,6 +579,7 @@ int mxattn_fwd(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn_qt
   a.out_fp32 = p->out_fp32 ? 1 : 0;
   a.lse = lse;
   a.plan = docs ? static_cast<const PlanHeader*>(workspace) : nullptr;
+  a.ndocs = docs ? ndocs : 0;
   a.bias = p->score_bias;
   if (a.bias != nullptr && !aligned16(a.bias)) return MXATTN_E_ALIGN;
   a.vk = nullptr;
@@ -571,7 +601,8 @@ int mxattn_fwd(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn_qt
   const int64_t nqt = (N + 127) / 128;
   a.grid = docs ? Hq * (nqt + ndocs) : B * Hq * nqt;
   if (a.grid > 0x7FFFFFFF) return MXATTN_E_UNSUPPORTED;
-  hipError_t e = launch_fwd(qk, pv, pm, psc, vsc, a, static_cast<hipStream_t>(stream));
+  hipError_t e = forced_failure();
+  if (e == hipSuccess) e = launch_fwd(qk, pv, pm, psc, vsc, a, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return MXATTN_E_UNSUPPORTED;
   if (e != hipSuccess) return hip_fail(e, "mxattn_fwd launch");
   return MXATTN_OK;

@@ -74,7 +74,7 @@ struct WorkItem {
 // query tiles (n_items256 used); each list longest first.
 struct PlanHeader {
   int32_t n_items, ndocs, causal, magic;
-  int32_t n_items256, cap128, pad0, pad1;
+  int32_t n_items256, cap128, n_tokens, pad1;  // n_tokens: N the plan was built for
 };
 constexpr int32_t PLAN_MAGIC = 0x4D585031;  // "MXP1"
 
@@ -97,6 +97,7 @@ struct FwdArgs {
   int out_fp32;
   float* lse;
   const PlanHeader* plan;  // packed documents, or null
+  int ndocs;               // documents of the plan (checked against its header)
   int64_t grid;            // workgroups launched
   const float* bias;       // per-key score bias [B][Hq][N] (centering compensation), or null
   // per-key form of V for causally safe diagonal tiles (null: grouped V scales only):

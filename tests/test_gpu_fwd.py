@@ -176,3 +176,82 @@ def test_fwd_f16_pv_v_range(route, case):
         record_parity(f"{route} V range {case} channels {g[0]}..{g[-1]}", ratio,
                       res["fb"] * (vg / vmax) / (TOL * np.abs(Or).max()))
         assert ratio <= 1.0, (case, g[0], ratio)
+
+
+@pytest.mark.parametrize("bad", ["unplanned", "causal_flag", "doc_count"])
+def test_fwd_mismatched_plan_gives_nan(bad):
+    """A workspace whose plan does not match the call (none written, another causal
+    flag, another document count over the same tokens) is detected by the kernel from
+    the plan's header: every output row and LSE is NaN, and nothing is read out of
+    bounds."""
+    import torch
+    import microscaling_fp4_attention_amd as mx
+    N = 700
+    doc_off = np.array([0, 100, 101, 357, 490, 700], np.int32)
+    x = synth.make_inputs("plain", 1, 2, 2, N, 128, 11)
+    dev = "cuda:0"
+    t = {n: torch.from_numpy(x[n].astype(np.int16)).view(torch.bfloat16).to(dev) for n in ("q", "k", "v")}
+    cu = torch.from_numpy(doc_off).to(dev)
+    Q = mx.quantize(t["q"], mx.ROLE_QK, "mxfp4_uos")
+    K = mx.quantize(t["k"], mx.ROLE_QK, "mxfp4_uos")
+    V = mx.quantize(t["v"], mx.ROLE_V, "mxfp4_uos", cu_seqlens=cu)
+    p = mx.fwd_params("pnq", "mxfp4_uos", causal=True, out_fp32=True)
+    nd = len(doc_off) - 1
+    if bad == "unplanned":
+        ws = torch.zeros(mx.fwd_workspace_bytes(N, nd), dtype=torch.uint8, device=dev)
+    elif bad == "causal_flag":
+        ws = mx.fwd_plan(doc_off, N, False)
+    else:  # a plan of 2 documents, padded to the byte size of the 5-document one
+        ws2 = mx.fwd_plan(np.array([0, 350, 700], np.int32), N, True)
+        ws = torch.zeros(mx.fwd_workspace_bytes(N, nd), dtype=torch.uint8, device=dev)
+        ws[:ws2.numel()] = ws2
+    lse = torch.empty((1, 2, N), dtype=torch.float32, device=dev)
+    out = mx.fwd(Q, K, V, p, lse=lse, workspace=ws, ndocs=nd)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(out).all()) and bool(torch.isnan(lse).all()), bad
+    # the matching plan gives finite rows
+    out = mx.fwd(Q, K, V, p, lse=lse, workspace=mx.fwd_plan(doc_off, N, True), ndocs=nd)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+
+
+@pytest.mark.parametrize("route", ["mxfp4_uos_pnq", "mxfp4_two_level_e4m3", "nvfp4_direct"])
+def test_fwd_work_order_independence(route):
+    """The plan's work lists (document, query tile) are ordered longest first only for
+    load balance: any order gives the same output bit for bit.  The lists are shuffled
+    in place in the workspace (header: int32 n_items, ndocs, causal, magic, n_items256,
+    cap128, n_tokens, pad; then 16-byte document entries; then cap128 entries of the
+    128-row list and the 256-row list, 8 bytes each) and the forward is run again."""
+    import torch
+    import microscaling_fp4_attention_amd as mx
+    q, v, pm, pf = ROUTES[route]
+    doc_off = np.array([0, 700, 701, 1500, 1800, 3000, 3333], np.int32)
+    N, nd = int(doc_off[-1]), len(doc_off) - 1
+    x = synth.make_inputs("outlier", 1, 2, 2, N, 128, 12)
+    dev = "cuda:0"
+    t = {n: torch.from_numpy(x[n].astype(np.int16)).view(torch.bfloat16).to(dev) for n in ("q", "k", "v")}
+    cu = torch.from_numpy(doc_off).to(dev)
+    Q = mx.quantize(t["q"], mx.ROLE_QK, q)
+    K = mx.quantize(t["k"], mx.ROLE_QK, q)
+    V = mx.quantize(t["v"], mx.ROLE_V, v, cu_seqlens=cu)
+    p = mx.fwd_params(pm, pf, causal=True, out_fp32=True)
+    ws = mx.fwd_plan(doc_off, N, True)
+    lse1 = torch.empty((1, 2, N), dtype=torch.float32, device=dev)
+    out1 = mx.fwd(Q, K, V, p, lse=lse1, workspace=ws, ndocs=nd)
+    torch.cuda.synchronize()
+    h = ws.cpu().numpy()
+    hdr = h[:32].view(np.int32)
+    n128, n256, cap128 = int(hdr[0]), int(hdr[4]), int(hdr[5])
+    off = 32 + 16 * nd
+    l128 = h[off:off + 8 * cap128].view(np.int32).reshape(-1, 2)
+    l256 = h[off + 8 * cap128:].view(np.int32)[:2 * n256].reshape(-1, 2)
+    rng = np.random.default_rng(5)
+    l128[:n128] = l128[:n128][rng.permutation(n128)]
+    l256[:n256] = l256[:n256][rng.permutation(n256)]
+    ws2 = torch.from_numpy(h).to(dev)
+    lse2 = torch.empty_like(lse1)
+    out2 = mx.fwd(Q, K, V, p, lse=lse2, workspace=ws2, ndocs=nd)
+    torch.cuda.synchronize()
+    assert not np.array_equal(ws.cpu().numpy(), h)  # the order did change
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+    assert bool(torch.isfinite(out1).all())

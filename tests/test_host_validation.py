@@ -169,3 +169,67 @@ def test_role_vt_checks(mx):
     # the prefill takes role V only
     q, k, v, p, _ = base(mx)
     assert fwd(mx, q, k, qt(mx, mx.ROLE_VT, H=2), p) == INVALID
+
+
+def test_grid_size_limits_are_unsupported(mx):
+    """Launch grids of 16 threads per row (pre-quantizer, compensation) or per 4 rows (Q/K
+    quantizer) use 32-bit thread ids: sizes past them are refused on the host as
+    unsupported, before any device work (not reported later as a HIP error)."""
+    by = ctypes.byref
+    L = mx.lib()
+    out = mx.QTensorC()
+    out.codes, out.scales = FAKE, FAKE + 0x100000
+    f = mx.qfmt("mxfp4")
+    big = (1 << 20, 8, 128)  # B*H*N = 2^30 rows
+    strides = mx._i64((8 * 128 * 128, 128 * 128, 128, 1))
+    assert L.mxattn_quantize(FAKE, strides, *big, 128, mx.ROLE_QK, by(f), None, 0, by(out), None) == UNSUPPORTED
+    pre = mx.PreProc()
+    pre.mean, pre.hadamard = None, 1
+    mid = (1 << 18, 8, 128)  # 2^28 rows
+    assert L.mxattn_quantize_pre(FAKE, strides, *mid, 128, mx.ROLE_QK, by(f), by(pre), None, 0, by(out),
+                                 None) == UNSUPPORTED
+    assert L.mxattn_center_comp(FAKE, FAKE, strides, FAKE, 1 << 18, 8, 8, 128, 128, None, 0, FAKE,
+                                None) == UNSUPPORTED
+
+
+def test_forced_launch_failure_reports_hip_error(mx):
+    """The test hook makes the next submission fail after the host checks: the call
+    returns MXATTN_E_HIP and mxattn_last_error() names the call and the HIP error; the
+    binding raises MxattnError with that text.  No device work is made.  The hook and
+    the error text are per thread: the case runs on a thread of its own and leaves this
+    one's state untouched."""
+    import threading
+    by = ctypes.byref
+    L = mx.lib()
+    q, k, v, p, _ = base(mx)
+    before = L.mxattn_last_error()
+    failures = []
+
+    def case():
+        try:
+            assert L.mxattn_debug_fail_launches(1) == 0
+            assert fwd(mx, q, k, v, p) == -5
+            err = L.mxattn_last_error().decode()
+            assert "mxattn_fwd launch" in err, err
+            assert L.mxattn_debug_fail_launches(0) == 0  # the one forced failure was used
+            # the plan builder's copy takes the same path
+            cu = (ctypes.c_int32 * 3)(0, 500, 1000)
+            L.mxattn_debug_fail_launches(1)
+            ws = mx.fwd_workspace_bytes(1000, 2)
+            assert L.mxattn_fwd_plan(cu, 2, 1000, 1, FAKE, ws, None) == -5
+            assert "mxattn_fwd_plan copy" in L.mxattn_last_error().decode()
+            with pytest.raises(mx.MxattnError) as ei:
+                L.mxattn_debug_fail_launches(1)
+                mx._check(fwd(mx, q, k, v, p), "mxattn_fwd")
+            assert ei.value.status == mx.E_HIP and "mxattn_fwd launch" in str(ei.value)
+            L.mxattn_debug_fail_launches(0)
+        except BaseException as e:  # reported on the test's own thread
+            failures.append(e)
+
+    t = threading.Thread(target=case)
+    t.start()
+    t.join()
+    if failures:
+        raise failures[0]
+    assert L.mxattn_last_error() == before
+    assert L.mxattn_debug_fail_launches(0) == 0
