@@ -54,13 +54,18 @@ typedef enum {
 typedef enum {
   MXATTN_ELEM_E2M1 = 0, /* FP4: magnitudes {0,.5,1,1.5,2,3,4,6}, sign bit 3, 2 codes per
                            byte with the even element in the low nibble            */
-  MXATTN_ELEM_E4M3 = 1  /* OCP FP8 E4M3: one code per byte, max 448, no infinity   */
+  MXATTN_ELEM_E4M3 = 1, /* OCP FP8 E4M3: one code per byte, max 448, no infinity   */
+  MXATTN_ELEM_BF16 = 2  /* unquantized: the bf16 values themselves, with scale NONE
+                           ("MXAttention" section 2, "MpFA" section 3 Eq. 2: the
+                           attention the quantized routes approximate); every role
+                           keeps the [B][H][N][d] layout (V is not transposed)     */
 } mxattn_elem;
 
 /* format of the shared block scale */
 typedef enum {
   MXATTN_SCALE_E8M0 = 0, /* power of two 2^e, byte e + 127 (0xFF never written)  */
-  MXATTN_SCALE_E4M3 = 1  /* OCP E4M3 value s = E4M3(amax / 6)                      */
+  MXATTN_SCALE_E4M3 = 1, /* OCP E4M3 value s = E4M3(amax / 6)                      */
+  MXATTN_SCALE_NONE = 2  /* no scale: bf16 elements only                             */
 } mxattn_scale;
 
 /* how an E8M0 exponent is chosen from the block maximum M ("MXAttention",
@@ -90,6 +95,9 @@ typedef enum {
 
 /* how the softmax operand P is quantized inside the attention loop */
 typedef enum {
+  MXATTN_P_NONE = 0,      /* unquantized route (Q, K, V in bf16): l = sum P~ in FP32;
+                             O += P V with P~ rounded to bf16 (nearest even) as the
+                             bf16 matrix-core operand                               */
   MXATTN_P_DIRECT = 1,    /* P^ = phi(P~); row sum l from the unquantized P~         */
   MXATTN_P_TWO_LEVEL = 2, /* s1 = rowmax_tile(P~)/(448*6) in FP32, P^ = phi(P~/s1),
                              O += s1 * P^ V; l from P~                              */
@@ -128,6 +136,7 @@ typedef struct {
  * dense and row-major:
  *   role QK: codes  [B][H][N][d * bits / 8]        scales [B][H][N][d / block]
  *   role V : codes  [B][H][d][n_padded * bits / 8] scales [B][H][d][n_padded / block]
+ *   BF16 (either role): codes [B][H][N][d] bf16, no scales, n_padded = N
  *   role VT: codes  [B][H][n_padded / 128][d][64]    scales [B][H][n_padded / 128][d][4]
  *            (role V's bytes of key tile t and channel c moved to [t][c])
  * bits = 4 (E2M1) or 8 (E4M3).  For role V the key axis is padded: each document
@@ -344,6 +353,10 @@ int mxattn_fwd_plan(const int32_t* cu_seqlens_host, int ndocs, int64_t N, int ca
  *   Q/K: MXFP4 (E2M1, E8M0/32) or NVFP4 (E2M1, E4M3/16), the same for both.
  *   P/V: DIRECT, PNQ or TWO_LEVEL with P in E2M1 (E8M0/32 or E4M3/16) and V in
  *        E2M1 (E8M0/32 or E4M3/16); FP8_FIXED with V in E4M3 with E8M0/32.
+ *   Unquantized: Q, K and V all BF16 with pmode NONE (softmax(Q K^T sm_scale) V:
+ *        scores from exact products summed in FP32, P~ in FP32, P rounded to bf16
+ *        for the PV product); score_bias allowed, no per-key V form, exact
+ *        exponential only.
  * Sizes: N and the padded key count of `v` at most 2^24 (MXATTN_E_UNSUPPORTED
  *   beyond).
  * Errors: MXATTN_E_INVALID, MXATTN_E_UNSUPPORTED, MXATTN_E_ALIGN,

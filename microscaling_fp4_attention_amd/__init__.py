@@ -19,11 +19,11 @@ LIB_PATH = os.path.join(_HERE, "libmxattn.so")
 
 # enums of mxattn.h
 OK, E_INVALID, E_UNSUPPORTED, E_ALIGN, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4, -5
-ELEM_E2M1, ELEM_E4M3 = 0, 1
-SCALE_E8M0, SCALE_E4M3 = 0, 1
+ELEM_E2M1, ELEM_E4M3, ELEM_BF16 = 0, 1, 2
+SCALE_E8M0, SCALE_E4M3, SCALE_NONE = 0, 1, 2
 RULE_OCP, RULE_CEIL = 0, 1
 ROLE_QK, ROLE_V, ROLE_VKEY, ROLE_VT = 0, 1, 2, 3
-P_DIRECT, P_TWO_LEVEL, P_PNQ, P_FP8_FIXED = 1, 2, 3, 4
+P_NONE, P_DIRECT, P_TWO_LEVEL, P_PNQ, P_FP8_FIXED = 0, 1, 2, 3, 4
 EXP_EXACT, EXP_MITCHELL, EXP_SCHRAUDOLPH = 0, 1, 2
 
 
@@ -59,8 +59,9 @@ FORMATS = {
     "mxfp4_tfs": (ELEM_E2M1, SCALE_E8M0, 32, RULE_CEIL, 6.0),   # truncation-free scaling
     "nvfp4": (ELEM_E2M1, SCALE_E4M3, 16, RULE_OCP, 0.0),        # 1x16 blocks, E4M3 scale amax/6
     "fp8v": (ELEM_E4M3, SCALE_E8M0, 32, RULE_CEIL, 448.0),      # E4M3 values, E8M0 per 32, round up
+    "bf16": (ELEM_BF16, SCALE_NONE, 0, RULE_OCP, 0.0),          # unquantized route
 }
-PMODES = {"direct": P_DIRECT, "two_level": P_TWO_LEVEL, "pnq": P_PNQ, "fp8": P_FP8_FIXED}
+PMODES = {"none": P_NONE, "direct": P_DIRECT, "two_level": P_TWO_LEVEL, "pnq": P_PNQ, "fp8": P_FP8_FIXED}
 EXP_MODES = {"exact": EXP_EXACT, "mitchell": EXP_MITCHELL, "schraudolph": EXP_SCHRAUDOLPH}
 
 
@@ -162,6 +163,8 @@ class QTensor:
         """role QK: [B, H, N, d*bits/8]; role V: [B, H, d, n_padded*bits/8];
         role VT: [B, H, n_padded/128, d, 64]."""
         d = self.desc
+        if d.fmt.elem == ELEM_BF16:  # the values, [B, H, N, d]
+            return self.codes.view(torch.bfloat16).view(d.B, d.H, d.N, d.d)
         bits = 4 if d.fmt.elem == ELEM_E2M1 else 8
         if d.role == ROLE_QK:
             return self.codes.view(d.B, d.H, d.N, d.d * bits // 8)

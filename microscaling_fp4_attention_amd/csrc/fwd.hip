@@ -38,7 +38,7 @@ namespace mxattn {
 template <int QK, int PV, bool BIAS = false>
 struct Lds {
   static constexpr int KROW = QK == QK_FP4 ? 80 : 256;  // bytes per staged key row
-  static constexpr int VROW = PV == PV_FP4 ? 80 : PV == PV_BF16 ? 256 : 144;  // per V^T row
+  static constexpr int VROW = PV == PV_FP4 ? 80 : (PV == PV_BF16 || PV == PV_RAW) ? 256 : 144;  // per V^T row
   static constexpr int BOFF = 128 * (KROW + VROW);       // then the score bias of the 128 keys
   static constexpr int STAGE = BOFF + (BIAS ? 512 : 0);  // one key tile
   // Buffers of key tiles: 3 let tile kt be read while tile kt+2 is stored into a third
@@ -120,12 +120,14 @@ __global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(Fw
     WorkItem wi = items[item];
     if ((uint32_t)wi.doc >= (uint32_t)a.ndocs) return;
     DocEntry de = docs[wi.doc];
-    if (!plan_item_ok(a, de, wi, 128, VB == 32 ? de.voff32 : de.voff16, VB)) return;
+    // a bf16 V keeps the token layout: its rows start at the document's first token
+    const int64_t voff = PV == PV_RAW ? de.start : VB == 32 ? de.voff32 : de.voff16;
+    if (!plan_item_ok(a, de, wi, 128, voff, PV == PV_RAW ? 1 : VB)) return;
     qt = wi.qtile;
     qstart = de.start;
     qlen = de.len;
     klen = de.len;
-    vstart = VB == 32 ? de.voff32 : de.voff16;
+    vstart = voff;
   } else {
     int64_t nqt = (a.N + 127) / 128, BH = a.B * a.Hq, G = a.grid;
     int64_t id = blockIdx.x, bh;
@@ -167,6 +169,10 @@ __global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(Fw
       qop[c] = v8_from4(*reinterpret_cast<const u4*>(qp + 32 * c + 16 * hh));
       qsc[c] = (int)((s4 >> (8 * (2 * c + hh))) & 0xFF);
     }
+  } else if constexpr (QK == QK_RAW) {  // bf16 row of 128 channels: step s takes 16 s + 8 h + [0, 8)
+    const uint8_t* qp = a.q + qrow * 256;
+#pragma unroll
+    for (int s = 0; s < 8; s++) qbf[s] = *reinterpret_cast<const v8bf*>(qp + 32 * s + 16 * hh);
   } else {
     const uint8_t* qp = a.q + qrow * 64;
     u2 s8 = *reinterpret_cast<const u2*>(a.qs + qrow * 8);
@@ -188,8 +194,10 @@ __global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(Fw
   Lacc = zero16();
 
   // ---------------- staging registers (a tile in flight) ----------------
-  constexpr int NKC = 2;                                   // K code chunks of 16 B per thread
-  constexpr int NVC = (PV == PV_FP8 || VB == 16) ? 4 : 2;  // V code chunks per thread
+  // K code chunks of 16 B per thread (a bf16 K row is 16 of them); V code chunks per
+  // thread (a bf16 V: 8 rows of an 8-key x 8-channel block, transposed when stored)
+  constexpr int NKC = QK == QK_RAW ? 8 : 2;
+  constexpr int NVC = PV == PV_RAW ? 8 : (PV == PV_FP8 || VB == 16) ? 4 : 2;
   u4 kreg[NKC];
   uint32_t kscr[NKC];  // QK_FP4: row scales in [0]; QK_BF16: 2 scale bytes per chunk
   u4 vreg[NVC];        // VB == 16 with E2M1: only .x, .y used (8-byte chunks)
@@ -209,12 +217,19 @@ __global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(Fw
     // K rows: 512 chunks of 16 bytes
 #pragma unroll
     for (int i = 0; i < NKC; i++) {
-      int c = tid + 256 * i, row = c >> 2, part = c & 3;
-      int key = kt * 128 + row;
-      if (key >= klen32) key = klen32 - 1;
-      kreg[i] = *reinterpret_cast<const u4*>(a.k + (kbase + key) * 64 + part * 16);
-      if constexpr (QK == QK_BF16)
-        kscr[i] = *reinterpret_cast<const uint16_t*>(a.ks + (kbase + key) * 8 + 2 * part);
+      if constexpr (QK == QK_RAW) {  // 16 chunks of 8 channels per key row
+        int c = tid + 256 * i, row = c >> 4, part = c & 15;
+        int key = kt * 128 + row;
+        if (key >= klen32) key = klen32 - 1;
+        kreg[i] = *reinterpret_cast<const u4*>(a.k + (kbase + key) * 256 + part * 16);
+      } else {
+        int c = tid + 256 * i, row = c >> 2, part = c & 3;
+        int key = kt * 128 + row;
+        if (key >= klen32) key = klen32 - 1;
+        kreg[i] = *reinterpret_cast<const u4*>(a.k + (kbase + key) * 64 + part * 16);
+        if constexpr (QK == QK_BF16)
+          kscr[i] = *reinterpret_cast<const uint16_t*>(a.ks + (kbase + key) * 8 + 2 * part);
+      }
     }
     if constexpr (QK == QK_FP4) {  // every thread loads (row tid % 128); threads < 128 store
       int key = kt * 128 + (tid & 127);
@@ -226,7 +241,11 @@ __global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(Fw
 #pragma unroll
     for (int i = 0; i < NVC; i++) {
       int c = tid + 256 * i;
-      if constexpr (PV == PV_FP8) {  // 8 chunks of 16 keys per channel
+      if constexpr (PV == PV_RAW) {  // keys 8 (tid / 16) + i, channels 8 (tid % 16) + [0, 8)
+        int key = kt * 128 + 8 * (tid >> 4) + i;
+        if (key >= klen32) key = klen32 - 1;
+        vreg[i] = *reinterpret_cast<const u4*>(a.v + ((b * a.Hkv + hk) * a.N + vstart + key) * 256 + 16 * (tid & 15));
+      } else if constexpr (PV == PV_FP8) {  // 8 chunks of 16 keys per channel
         int ch = c >> 3, part = c & 7;
         int64_t key = vstart + kt * 128 + 16 * part;
         if (key > a.np - 16) key = a.np - 16;
@@ -246,7 +265,7 @@ __global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(Fw
         if constexpr (PV == PV_BF16) vscr[i] = a.vs[(vrow0 + ch) * nvb + key / 32];
       }
     }
-    if constexpr (PV != PV_BF16) {  // every thread loads (channel tid % 128); threads >= 128 store
+    if constexpr (PV == PV_FP4 || PV == PV_FP8) {  // every thread loads (channel tid % 128); threads >= 128 store
       int ch = tid & 127;
       uint32_t w = 0;
 #pragma unroll
@@ -267,6 +286,12 @@ __global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(Fw
     }
 #pragma unroll
     for (int i = 0; i < NKC; i++) {
+      if constexpr (QK == QK_RAW) {  // chunk = 8 channels, swizzled by the row position
+        int c = tid + 256 * i, row = c >> 4, part = c & 15;
+        int pos = kpos<SPLIT16>(row);
+        *reinterpret_cast<u4*>(Ks + pos * 256 + ((part ^ (pos & 15)) * 16)) = kreg[i];
+        continue;
+      }
       int c = tid + 256 * i, row = c >> 2, part = c & 3;
       int pos = kpos<SPLIT16>(row);
       if constexpr (QK == QK_FP4) {
@@ -285,10 +310,29 @@ __global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(Fw
     if constexpr (QK == QK_FP4) {
       if (tid < 128) *reinterpret_cast<uint32_t*>(Ks + kpos<SPLIT16>(tid) * 80 + 64) = kscr[0];
     }
+    if constexpr (PV == PV_RAW) {
+      // the 8 x 8 block (rows: keys 8 kb + r, dword j: channels 2j, 2j + 1) transposed:
+      // channel 8 cb + c gets its 8 keys as one 16-byte chunk kb of its bf16 row
+      const int kb = tid >> 4, cb = tid & 15;
+      const uint32_t R[8][4] = {{vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w}, {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w},
+                                {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w}, {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w},
+                                {vreg[4].x, vreg[4].y, vreg[4].z, vreg[4].w}, {vreg[5].x, vreg[5].y, vreg[5].z, vreg[5].w},
+                                {vreg[6].x, vreg[6].y, vreg[6].z, vreg[6].w}, {vreg[7].x, vreg[7].y, vreg[7].z, vreg[7].w}};
 #pragma unroll
-    for (int i = 0; i < NVC; i++) {
+      for (int c = 0; c < 8; c++) {
+        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;  // high or low halves of keys 2m, 2m+1
+        uint32_t w[4];
+#pragma unroll
+        for (int m = 0; m < 4; m++) w[m] = __builtin_amdgcn_perm(R[2 * m + 1][c >> 1], R[2 * m][c >> 1], sel);
+        const int ch = 8 * cb + c;
+        *reinterpret_cast<u4*>(Vs + ch * 256 + ((kb ^ (ch & 15)) * 16)) = mk4(w[0], w[1], w[2], w[3]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < (PV == PV_RAW ? 0 : NVC); i++) {
       int c = tid + 256 * i;
-      if constexpr (PV == PV_FP8) {
+      if constexpr (PV == PV_RAW) {
+      } else if constexpr (PV == PV_FP8) {
         int ch = c >> 3, part = c & 7;
         *reinterpret_cast<u4*>(Vs + ch * 144 + part * 16) = vreg[i];
       } else if constexpr (PV == PV_FP4) {
@@ -442,6 +486,9 @@ __global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(Fw
       if constexpr (PV == PV_FP4) {
         pc[bb][0] = pack8_fp4(y, sc16[bb]);
         pc[bb][1] = pack8_fp4(y + 8, sc16[bb]);
+      } else if constexpr (PV == PV_RAW) {  // P~ rounded to bf16 (nearest even)
+#pragma unroll
+        for (int t = 0; t < 8; t++) pw[bb][t] = bf16_rne(y[2 * t]) | (bf16_rne(y[2 * t + 1]) << 16);
       } else if constexpr (PV == PV_BF16) {
         float z[16];
 #pragma unroll
@@ -507,7 +554,7 @@ __global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(Fw
         Lacc = mfma_fp4(ones, bp[0], Lacc, 127, psc[0]);
         Lacc = mfma_fp4(ones, bp[1], Lacc, 127, psc[1]);
       }
-    } else if constexpr (PV == PV_BF16) {
+    } else if constexpr (PV == PV_BF16 || PV == PV_RAW) {
 #pragma unroll
       for (int db = 0; db < 4; db++) {
         const uint8_t* rp = Vs + (32 * db + ql) * 256;
@@ -565,15 +612,18 @@ __global__ __launch_bounds__(256, (waves_per_simd<QK, PV>())) void fwd_kernel(Fw
   if (nkt > 0) {
     v16f S[4];
     if constexpr (NB == 1) {
-      // one buffer: store, then compute on it (two barriers per tile)
-      load_tile(0);
+      // one buffer: store, then compute on it (two barriers per tile).  The unquantized
+      // route's staging registers (a bf16 tile is 4 times the codes) are not held across
+      // the math: it loads each tile right before storing it.
+      if constexpr (QK != QK_RAW) load_tile(0);
       for (int kt = 0; kt < nkt; kt++) {
         __syncthreads();  // the previous tile's LDS reads are done
+        if constexpr (QK == QK_RAW) load_tile(kt);
         store_tile(0);
         __syncthreads();
         // next tile in flight during this tile's math (the last iteration reloads its own
         // tile: an unconditional load keeps the staging registers out of scratch memory)
-        load_tile(kt + 1 < nkt ? kt + 1 : kt);
+        if constexpr (QK != QK_RAW) load_tile(kt + 1 < nkt ? kt + 1 : kt);
         scores(0, S);
         softmax_pv(kt, 0, S);
       }
@@ -1549,6 +1599,7 @@ hipError_t launch_fwd(int qk, int pv, int pmode, int psc, int vsc, const FwdArgs
   MXF(QK_FP4, PV_BF16, PM_DIRECT, SCALE_E4M3, SCALE_E4M3);
   MXF(QK_FP4, PV_BF16, PM_TWO_LEVEL, SCALE_E4M3, SCALE_E4M3);
   MXF(QK_FP4, PV_BF16, PM_PNQ, SCALE_E4M3, SCALE_E4M3);
+  MXF(QK_RAW, PV_RAW, PM_NONE, SCALE_E8M0, SCALE_E8M0);  // unquantized route
 #undef MXF
   return hipErrorNotSupported;  // no kernel instantiated for this route
 }

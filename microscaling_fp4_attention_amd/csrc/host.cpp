@@ -39,6 +39,11 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // format checks shared by sizing and quantization
 int check_fmt(const mxattn_qfmt* f, int role) {
   if (f == nullptr) return MXATTN_E_INVALID;
+  if (f->elem == MXATTN_ELEM_BF16) {  // the unquantized route: plain bf16 values
+    if (f->scale != MXATTN_SCALE_NONE) return MXATTN_E_INVALID;
+    if (role != MXATTN_ROLE_QK && role != MXATTN_ROLE_V) return MXATTN_E_UNSUPPORTED;
+    return MXATTN_OK;
+  }
   if (f->elem != MXATTN_ELEM_E2M1 && f->elem != MXATTN_ELEM_E4M3) return MXATTN_E_INVALID;
   if (f->scale != MXATTN_SCALE_E8M0 && f->scale != MXATTN_SCALE_E4M3) return MXATTN_E_INVALID;
   if (f->block != 16 && f->block != 32) return MXATTN_E_UNSUPPORTED;
@@ -77,7 +82,9 @@ int64_t v_padded(int64_t N, int ndocs, int block) {
   return (n + 127) / 128 * 128;
 }
 
-int bits_of(int elem) { return elem == MXATTN_ELEM_E2M1 ? 4 : 8; }
+int bits_of(int elem) { return elem == MXATTN_ELEM_E2M1 ? 4 : elem == MXATTN_ELEM_BF16 ? 16 : 8; }
+
+bool is_bf16(const mxattn_qfmt& f) { return f.elem == MXATTN_ELEM_BF16 && f.scale == MXATTN_SCALE_NONE; }
 
 bool same_fmt(const mxattn_qfmt& a, const mxattn_qfmt& b) {
   if (a.elem != b.elem || a.scale != b.scale || a.block != b.block) return false;
@@ -139,7 +146,11 @@ int mxattn_qtensor_bytes(const mxattn_qfmt* fmt, int role, int64_t B, int64_t H,
   if (d != 128) return MXATTN_E_UNSUPPORTED;
   if (ndocs > 1 && B != 1) return MXATTN_E_INVALID;
   int bits = bits_of(fmt->elem);
-  if (role == MXATTN_ROLE_QK) {
+  if (fmt->elem == MXATTN_ELEM_BF16) {  // every role: the values as [B][H][N][d]
+    *code_bytes = (size_t)(B * H * N * d * 2);
+    *scale_bytes = 0;
+    if (n_padded) *n_padded = N;
+  } else if (role == MXATTN_ROLE_QK) {
     *code_bytes = (size_t)(B * H * N * d * bits / 8);
     *scale_bytes = (size_t)(B * H * N * (d / fmt->block));
     if (n_padded) *n_padded = N;
@@ -169,9 +180,10 @@ int mxattn_quantize(const void* x_bf16, const int64_t x_strides[4], int64_t B, i
   if (ndocs > 1 && (cu_seqlens == nullptr || role == MXATTN_ROLE_QK)) return MXATTN_E_INVALID;
   if (x_strides[3] != 1 || x_strides[0] < 0 || x_strides[1] < 0 || x_strides[2] < 0) return MXATTN_E_INVALID;
   const int64_t nel = B * H * N;
+  const bool raw = fmt->elem == MXATTN_ELEM_BF16;
   if (nel > 0) {
-    if (x_bf16 == nullptr || out->codes == nullptr || out->scales == nullptr) return MXATTN_E_INVALID;
-    if (!aligned16(x_bf16) || !aligned16(out->codes) || !aligned16(out->scales)) return MXATTN_E_ALIGN;
+    if (x_bf16 == nullptr || out->codes == nullptr || (!raw && out->scales == nullptr)) return MXATTN_E_INVALID;
+    if (!aligned16(x_bf16) || !aligned16(out->codes) || (!raw && !aligned16(out->scales))) return MXATTN_E_ALIGN;
     if ((x_strides[0] % 8) || (x_strides[1] % 8) || (x_strides[2] % 8)) return MXATTN_E_ALIGN;
   }
   out->fmt = *fmt;
@@ -182,6 +194,16 @@ int mxattn_quantize(const void* x_bf16, const int64_t x_strides[4], int64_t B, i
   out->N = N;
   out->d = d;
   out->n_padded = np;
+  if (raw) {  // the unquantized route: a dense copy, [B][H][N][d]
+    if (nel == 0) return MXATTN_OK;
+    if (nel >= (int64_t(1) << 27)) return MXATTN_E_UNSUPPORTED;  // 16 threads per row, 32-bit ids
+    hipError_t e = forced_failure();
+    if (e == hipSuccess)
+      e = launch_copy_bf16(x_bf16, x_strides[0], x_strides[1], x_strides[2], B, H, N, out->codes,
+                           static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "mxattn_quantize launch");
+    return MXATTN_OK;
+  }
   if (nel == 0 && !(role != MXATTN_ROLE_QK && B * H > 0 && np > 0)) return MXATTN_OK;
   // role QK: 4 rows per thread and 16 threads per 4 rows, 32-bit row indices
   if (role == MXATTN_ROLE_QK && nel >= (int64_t(1) << 30)) return MXATTN_E_UNSUPPORTED;
@@ -507,12 +529,22 @@ int mxattn_fwd(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn_qt
   if (os[3] != 1 || os[0] < 0 || os[1] < 0 || os[2] < 0) return MXATTN_E_INVALID;
 
   // operand routes
-  int qk, pv, psc = SCALE_E8M0, vsc;
-  if (is_mxfp4(q->fmt)) qk = QK_FP4;
+  int qk, pv, psc = SCALE_E8M0, vsc = SCALE_E8M0;
+  const int pm = p->pmode;
+  const bool raw = is_bf16(q->fmt);
+  if (raw != is_bf16(v->fmt) || raw != (pm == MXATTN_P_NONE)) {
+    // the unquantized route takes Q, K, V in bf16 with P unquantized, nothing else
+    if (pm != MXATTN_P_NONE && (pm < MXATTN_P_DIRECT || pm > MXATTN_P_FP8_FIXED)) return MXATTN_E_INVALID;
+    return MXATTN_E_UNSUPPORTED;
+  }
+  if (raw) qk = QK_RAW;
+  else if (is_mxfp4(q->fmt)) qk = QK_FP4;
   else if (is_nvfp4(q->fmt)) qk = QK_BF16;
   else return MXATTN_E_UNSUPPORTED;
-  const int pm = p->pmode;
-  if (pm == MXATTN_P_FP8_FIXED) {
+  if (raw) {
+    if (p->vkey != nullptr || p->exp_mode != MXATTN_EXP_EXACT) return MXATTN_E_UNSUPPORTED;
+    pv = PV_RAW;
+  } else if (pm == MXATTN_P_FP8_FIXED) {
     if (!is_fp8v(v->fmt)) return MXATTN_E_UNSUPPORTED;
     pv = PV_FP8;
     vsc = SCALE_E8M0;
@@ -545,10 +577,11 @@ int mxattn_fwd(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn_qt
   if (B == 0 || N == 0) return MXATTN_OK;
   // the kernels address one head's K and V with 32-bit offsets
   if (N > (int64_t(1) << 24) || v->n_padded > (int64_t(1) << 24)) return MXATTN_E_UNSUPPORTED;
-  if (!q->codes || !q->scales || !k->codes || !k->scales || !v->codes || !v->scales || !out) return MXATTN_E_INVALID;
-  if (!aligned16(q->codes) || !aligned16(k->codes) || !aligned16(v->codes) || !aligned16(q->scales) ||
-      !aligned16(k->scales) || !aligned16(v->scales) || !aligned16(out))
+  if (!q->codes || !k->codes || !v->codes || !out) return MXATTN_E_INVALID;
+  if (!raw && (!q->scales || !k->scales || !v->scales)) return MXATTN_E_INVALID;
+  if (!aligned16(q->codes) || !aligned16(k->codes) || !aligned16(v->codes) || !aligned16(out))
     return MXATTN_E_ALIGN;
+  if (!raw && (!aligned16(q->scales) || !aligned16(k->scales) || !aligned16(v->scales))) return MXATTN_E_ALIGN;
   const int esz = p->out_fp32 ? 4 : 2;
   if ((os[0] * esz) % 16 || (os[1] * esz) % 16 || (os[2] * esz) % 16) return MXATTN_E_ALIGN;
   if (docs) {

@@ -10,7 +10,7 @@ namespace mxattn {
 // element / scale / P-mode values (the mxattn.h enums)
 enum { ELEM_E2M1 = 0, ELEM_E4M3 = 1 };
 enum { SCALE_E8M0 = 0, SCALE_E4M3 = 1 };
-enum { PM_DIRECT = 1, PM_TWO_LEVEL = 2, PM_PNQ = 3, PM_FP8_FIXED = 4 };
+enum { PM_NONE = 0, PM_DIRECT = 1, PM_TWO_LEVEL = 2, PM_PNQ = 3, PM_FP8_FIXED = 4 };
 
 struct QuantArgs {
   const void* x;
@@ -30,6 +30,10 @@ hipError_t launch_quant_qk(const QuantArgs& a, hipStream_t st);
 hipError_t launch_quant_v(const QuantArgs& a, hipStream_t st);
 // role VKEY: per-key E8M0 scale over the 128 channels, codes transposed as role V
 hipError_t launch_quant_vkey(const QuantArgs& a, hipStream_t st);
+// unquantized (bf16) tensors: x with element strides (sB, sH, sN, 1) copied densely to
+// dst [B][H][N][128]
+hipError_t launch_copy_bf16(const void* x, int64_t sB, int64_t sH, int64_t sN, int64_t B, int64_t H, int64_t N,
+                            void* dst, hipStream_t st);
 
 // outlier pre-processing (preproc.hip)
 // mean: [B][H][nd][128] float, nd = max(ndocs, 1); a.cu/a.ndocs give the documents
@@ -56,8 +60,10 @@ hipError_t launch_center_comp(const CompArgs& a, hipStream_t st);
 //   PV_FP4 : P in E2M1 with E8M0/32 scales, V in E2M1 with E8M0/32, scaled FP4 MFMA.
 //   PV_BF16: P and V in E2M1 with E8M0/32 or E4M3/16 scales, dequantized to bf16.
 //   PV_FP8 : P as E4M3(448 P~) with unit scale, V in E4M3 with E8M0/32, scaled FP8 MFMA.
-enum { QK_FP4 = 0, QK_BF16 = 1 };
-enum { PV_FP4 = 0, PV_BF16 = 1, PV_FP8 = 2 };
+//   QK_RAW, PV_RAW: the unquantized route: Q, K, V in bf16 ([B][H][N][128], V not
+//            transposed; V^T tiles are formed while staging), P~ rounded to bf16.
+enum { QK_FP4 = 0, QK_BF16 = 1, QK_RAW = 2 };
+enum { PV_FP4 = 0, PV_BF16 = 1, PV_FP8 = 2, PV_RAW = 3 };
 
 // Document entry of a forward plan (workspace): first token, length, and the first
 // padded key slot of the document in a V layout with blocks of 32 and of 16.

@@ -402,6 +402,31 @@ hipError_t launch_quant_vkey(const QuantArgs& a, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
+// unquantized route: a dense copy of a strided bf16 tensor, 16 bytes per thread
+// (16 threads per 128-channel row)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void copy_bf16_kernel(const uint16_t* __restrict__ x, int64_t sB, int64_t sH,
+                                                        int64_t sN, int64_t H, int64_t N, int64_t rows,
+                                                        uint16_t* __restrict__ dst) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = t >> 4;
+  if (row >= rows) return;
+  const int part = (int)(t & 15);
+  const int64_t n = row % N, bh = row / N, h = bh % H, b = bh / H;
+  const u4 v = *reinterpret_cast<const u4*>(x + b * sB + h * sH + n * sN + 8 * part);
+  *reinterpret_cast<u4*>(dst + row * 128 + 8 * part) = v;
+}
+
+hipError_t launch_copy_bf16(const void* x, int64_t sB, int64_t sH, int64_t sN, int64_t B, int64_t H, int64_t N,
+                            void* dst, hipStream_t st) {
+  const int64_t rows = B * H * N;
+  if (rows >= (int64_t(1) << 27)) return hipErrorNotSupported;  // 32-bit thread ids
+  copy_bf16_kernel<<<dim3((unsigned)((rows * 16 + 255) / 256)), 256, 0, st>>>(
+      static_cast<const uint16_t*>(x), sB, sH, sN, H, N, rows, static_cast<uint16_t*>(dst));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_quant_qk(const QuantArgs& a, hipStream_t st) {

@@ -40,7 +40,8 @@ int main() {
   const mxattn_qfmt uos = fmt(MXATTN_ELEM_E2M1, MXATTN_SCALE_E8M0, 32, MXATTN_RULE_CEIL, 7.25f);
   const mxattn_qfmt nv = fmt(MXATTN_ELEM_E2M1, MXATTN_SCALE_E4M3, 16, MXATTN_RULE_OCP, 0.0f);
   const mxattn_qfmt f8 = fmt(MXATTN_ELEM_E4M3, MXATTN_SCALE_E8M0, 32, MXATTN_RULE_CEIL, 448.0f);
-  const mxattn_qfmt* fmts[] = {&mx, &uos, &nv, &f8};
+  const mxattn_qfmt bf = fmt(MXATTN_ELEM_BF16, MXATTN_SCALE_NONE, 0, MXATTN_RULE_OCP, 0.0f);
+  const mxattn_qfmt* fmts[] = {&mx, &uos, &nv, &f8, &bf};
   for (int s = -7; s <= 1; s++) CHECK(mxattn_status_str(s) != nullptr);
   CHECK(mxattn_abi_version() == MXATTN_ABI_VERSION);
 
@@ -145,7 +146,7 @@ int main() {
     CHECK(g_launches == before + 1);
     CHECK(mxattn_fwd(&q, &k, &v, &p, nd, fake(0x7000000), os, nullptr, w, wb - 1, nullptr) == MXATTN_E_WORKSPACE);
     // every P mode and format against every V format
-    for (int pm = 0; pm <= MXATTN_P_FP8_FIXED + 1; pm++)
+    for (int pm = MXATTN_P_NONE; pm <= MXATTN_P_FP8_FIXED + 1; pm++)
       for (const mxattn_qfmt* pf : fmts)
         for (const mxattn_qfmt* vf : fmts) {
           p.pmode = pm;

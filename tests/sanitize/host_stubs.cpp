@@ -23,6 +23,9 @@ static unsigned char g_scratch[64];
 hipError_t launch_quant_qk(const QuantArgs&, hipStream_t) { return g_launches++, hipSuccess; }
 hipError_t launch_quant_v(const QuantArgs&, hipStream_t) { return g_launches++, hipSuccess; }
 hipError_t launch_quant_vkey(const QuantArgs&, hipStream_t) { return g_launches++, hipSuccess; }
+hipError_t launch_copy_bf16(const void*, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, void*, hipStream_t) {
+  return g_launches++, hipSuccess;
+}
 hipError_t launch_channel_mean(const QuantArgs&, float*, hipStream_t) { return g_launches++, hipSuccess; }
 hipError_t launch_quant_qk_pre(const QuantArgs&, const float*, int, hipStream_t) { return g_launches++, hipSuccess; }
 hipError_t launch_center_comp(const CompArgs&, hipStream_t) { return g_launches++, hipSuccess; }

@@ -233,3 +233,44 @@ def test_forced_launch_failure_reports_hip_error(mx):
         raise failures[0]
     assert L.mxattn_last_error() == before
     assert L.mxattn_debug_fail_launches(0) == 0
+
+
+def test_unquantized_route_checks(mx):
+    """Q, K and V in bf16 (scale NONE) with pmode NONE is the unquantized route; any
+    mix with quantized operands or P modes is unsupported.  Acceptance is seen through
+    the launch hook: the call passes its host checks and stops at the forced failure."""
+    L = mx.lib()
+    qb, kb = qt(mx, mx.ROLE_QK, "bf16"), qt(mx, mx.ROLE_QK, "bf16", H=2)
+    vb = qt(mx, mx.ROLE_V, "bf16", H=2)
+    vb.n_padded = 1000
+    pn = params(mx, "none", "bf16")
+    os = (4 * 1000 * 128, 1000 * 128, 128, 1)
+    rcs = []
+
+    def accepted():  # on a thread of its own: the hook and the error text are per thread
+        L.mxattn_debug_fail_launches(1)
+        rcs.append(fwd(mx, qb, kb, vb, pn, os=os))
+        L.mxattn_debug_fail_launches(0)
+
+    import threading
+    t = threading.Thread(target=accepted)
+    t.start()
+    t.join()
+    assert rcs == [-5]                                                             # accepted
+    q, k, v, p, _ = base(mx)
+    assert fwd(mx, qb, kb, vb, params(mx, "pnq", "mxfp4")) == UNSUPPORTED          # quantized P on bf16
+    assert fwd(mx, q, k, v, pn) == UNSUPPORTED                                     # P NONE on quantized
+    assert fwd(mx, qb, kb, v, pn) == UNSUPPORTED                                   # mixed V
+    assert fwd(mx, qb, kb, vb, params(mx, "none", "bf16", exp_mode=mx.EXP_MITCHELL)) == UNSUPPORTED
+    bad = params(mx, "none", "bf16")
+    bad.pmode = 9
+    assert fwd(mx, qb, kb, vb, bad) == INVALID
+    cb, sb, npad = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_int64()
+    f = mx.qfmt("bf16")
+    by = ctypes.byref
+    assert L.mxattn_qtensor_bytes(by(f), mx.ROLE_VT, 1, 2, 100, 128, 0, by(cb), by(sb), by(npad)) == UNSUPPORTED
+    g = mx.qfmt("bf16")
+    g.scale = mx.SCALE_E8M0
+    assert L.mxattn_qtensor_bytes(by(g), mx.ROLE_QK, 1, 2, 100, 128, 0, by(cb), by(sb), by(npad)) == INVALID
+    assert L.mxattn_qtensor_bytes(by(f), mx.ROLE_V, 1, 2, 100, 128, 5, by(cb), by(sb), by(npad)) == 0
+    assert (cb.value, sb.value, npad.value) == (2 * 100 * 128 * 2, 0, 100)
