@@ -1080,6 +1080,88 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     return lsum;
   };
 
+  // V-phase state (phase_v_pre): the exponent offset, the rescale, the two-level
+  // pre-scale and the block scales of P.  With E8M0 P scales it is prepared at the end
+  // of the M phase, which waits at its barrier for the co-resident wave's V phase, so
+  // this short dependent chain runs in that slack instead of at the head of the V
+  // phase (video-DiT 32K PNQ 1%, two-level E8M0 5.5% faster); the E4M3 scales of the
+  // f16 route (a division, a rounding with branches and a reciprocal per 16 keys)
+  // measured 20% slower there and stay in the V phase.
+  constexpr bool PRE_IN_M = PV != PV_BF16;
+  float vp_ms = 0.0f, vp_cm = 0.0f, vp_k1 = 1.0f, vp_alpha = 1.0f;
+  float vp_sc[4] = {1.0f, 1.0f, 1.0f, 1.0f}, vp_sv[4] = {1.0f, 1.0f, 1.0f, 1.0f}, vp_ki[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+  auto phase_v_pre = [&]() __attribute__((always_inline)) {
+    const float mnew = fmaxn(m, tmax);
+    const float ms = mnew == NEG_INF ? 0.0f : mnew * lam;
+    const float msub = mnew == NEG_INF ? 0.0f : mnew;
+    const float cm = pexp_c(ms);
+    // exactly 1 when the max did not move (keeps the rescale skip exact), 0 while m = -inf;
+    // the rescale is exact in both exponential modes
+    const float alpha = m == mnew ? 1.0f : exp2_diff(m, mnew, lam);
+    m = mnew;
+
+    // two-level: s1 = rowmax_tile(P~)/2688; the accumulator holds O / s1 and is carried
+    // to the new s1 by beta = alpha s1_prev / s1 (a tile whose P~ stays below 2^-64 of
+    // the running maximum adds nothing and keeps s1)
+    float k1 = 1.0f, scale_o = alpha;
+    if constexpr (PMODE == PM_TWO_LEVEL) {
+      float r = pmax(tmax, ms, cm, msub);
+      if (r >= 0x1p-64f) {
+        float s1 = r / 2688.0f;
+        k1 = __builtin_amdgcn_rcpf(s1);  // within an ulp: the P values' products carry it
+        scale_o = alpha * (s1prev * k1);
+        s1prev = s1;
+      } else {
+        k1 = 0.0f;
+      }
+    }
+    const bool any_rescale = __builtin_amdgcn_ballot_w64(scale_o != 1.0f) != 0;
+    if (any_rescale) {
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 16; j++) O[i][j] *= scale_o;
+      Lacc[0] *= alpha;
+      if constexpr (SAFE) lfix *= alpha;
+    }
+
+    // block scales of P from the block maxima of P~ (exponentials of the score maxima)
+    float sc16[4] = {1.0f, 1.0f, 1.0f, 1.0f}, sv16[4] = {1.0f, 1.0f, 1.0f, 1.0f},
+          ki16[4] = {1.0f, 1.0f, 1.0f, 1.0f};  // per 16 keys: convert scale, dequant factor, multiplier
+    int e[2] = {0, 0};
+    if constexpr (PV == PV_FP4 || (PV == PV_BF16 && PSC == SCALE_E8M0)) {
+#pragma unroll
+      for (int p = 0; p < 2; p++) {
+        const float bm = fmaxn(bm16[2 * p], bm16[2 * p + 1]);
+        int x = e8m0_exp(pmax(bm, ms, cm, msub) * k1, a.prule);
+        e[p] = x < -126 ? -126 : x;
+        const float sc = u2f((uint32_t)(e[p] + 127) << 23);
+        sc16[2 * p] = sc16[2 * p + 1] = sv16[2 * p] = sv16[2 * p + 1] = sc;
+        ki16[2 * p] = ki16[2 * p + 1] = 1.0f;
+      }
+      pscw = (uint32_t)(e[0] + 127) | ((uint32_t)(e[1] + 127) << 8);
+    } else if constexpr (PV == PV_BF16) {  // E4M3 scale per 16 keys
+#pragma unroll
+      for (int bb = 0; bb < 4; bb++) {
+        const float pm = pmax(bm16[bb], ms, cm, msub) * k1;
+        const float sv = e4m3_value(e4m3_mag(div6(pm)));
+        sc16[bb] = 1.0f;
+        sv16[bb] = sv;
+        ki16[bb] = sv > 0.0f ? __builtin_amdgcn_rcpf(sv) : 0.0f;
+      }
+    }
+
+    vp_ms = ms;
+    vp_cm = cm;
+    vp_k1 = k1;
+    vp_alpha = alpha;
+#pragma unroll
+    for (int bb = 0; bb < 4; bb++) {
+      vp_sc[bb] = sc16[bb];
+      vp_sv[bb] = sv16[bb];
+      vp_ki[bb] = ki16[bb];
+    }
+  };
   // M(t): PV of tile t-1 (stage offset sv), then S^T of tile t (stage offset sk) with
   // its mask and maxima
   auto phase_m = [&](int t, uint32_t sk, uint32_t sv, bool can_fold) __attribute__((always_inline)) {
@@ -1224,75 +1306,18 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
         bm16[bb] = fmaxn(y0, y1);
       }
       tmax = halves_max(fmaxn(fmaxn(bm16[0], bm16[1]), fmaxn(bm16[2], bm16[3])));
+      if (PRE_IN_M && !(SAFE && can_fold && t == tdiag)) phase_v_pre();
     }
   };
 
   // V(t): exponentials and P quantization of tile t (its row max came with M(t))
+  // V(t): exponentials and P quantization of tile t with the state from phase_v_pre
   auto phase_v = [&](int t) __attribute__((always_inline)) {
-    const float mnew = fmaxn(m, tmax);
-    const float ms = mnew == NEG_INF ? 0.0f : mnew * lam;
-    const float msub = mnew == NEG_INF ? 0.0f : mnew;
-    const float cm = pexp_c(ms);
-    // exactly 1 when the max did not move (keeps the rescale skip exact), 0 while m = -inf;
-    // the rescale is exact in both exponential modes
-    const float alpha = m == mnew ? 1.0f : exp2_diff(m, mnew, lam);
-    m = mnew;
-
-    // two-level: s1 = rowmax_tile(P~)/2688; the accumulator holds O / s1 and is carried
-    // to the new s1 by beta = alpha s1_prev / s1 (a tile whose P~ stays below 2^-64 of
-    // the running maximum adds nothing and keeps s1)
-    float k1 = 1.0f, scale_o = alpha;
-    if constexpr (PMODE == PM_TWO_LEVEL) {
-      float r = pmax(tmax, ms, cm, msub);
-      if (r >= 0x1p-64f) {
-        float s1 = r / 2688.0f;
-        k1 = __builtin_amdgcn_rcpf(s1);  // within an ulp: the P values' products carry it
-        scale_o = alpha * (s1prev * k1);
-        s1prev = s1;
-      } else {
-        k1 = 0.0f;
-      }
-    }
-    const bool any_rescale = __builtin_amdgcn_ballot_w64(scale_o != 1.0f) != 0;
-    if (any_rescale) {
-#pragma unroll
-      for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 16; j++) O[i][j] *= scale_o;
-      Lacc[0] *= alpha;
-      if constexpr (SAFE) lfix *= alpha;
-    }
-
-    // block scales of P from the block maxima of P~ (exponentials of the score maxima)
-    float sc16[4] = {1.0f, 1.0f, 1.0f, 1.0f}, sv16[4] = {1.0f, 1.0f, 1.0f, 1.0f},
-          ki16[4] = {1.0f, 1.0f, 1.0f, 1.0f};  // per 16 keys: convert scale, dequant factor, multiplier
-    int e[2] = {0, 0};
-    if constexpr (PV == PV_FP4 || (PV == PV_BF16 && PSC == SCALE_E8M0)) {
-#pragma unroll
-      for (int p = 0; p < 2; p++) {
-        const float bm = fmaxn(bm16[2 * p], bm16[2 * p + 1]);
-        int x = e8m0_exp(pmax(bm, ms, cm, msub) * k1, a.prule);
-        e[p] = x < -126 ? -126 : x;
-        const float sc = u2f((uint32_t)(e[p] + 127) << 23);
-        sc16[2 * p] = sc16[2 * p + 1] = sv16[2 * p] = sv16[2 * p + 1] = sc;
-        ki16[2 * p] = ki16[2 * p + 1] = 1.0f;
-      }
-      pscw = (uint32_t)(e[0] + 127) | ((uint32_t)(e[1] + 127) << 8);
-    } else if constexpr (PV == PV_BF16) {  // E4M3 scale per 16 keys
-#pragma unroll
-      for (int bb = 0; bb < 4; bb++) {
-        const float pm = pmax(bm16[bb], ms, cm, msub) * k1;
-        const float sv = e4m3_value(e4m3_mag(div6(pm)));
-        sc16[bb] = 1.0f;
-        sv16[bb] = sv;
-        ki16[bb] = sv > 0.0f ? __builtin_amdgcn_rcpf(sv) : 0.0f;
-      }
-    }
-
+    if constexpr (!PRE_IN_M) phase_v_pre();
     float lsum = 0.0f;
 #pragma unroll
-    for (int bb = 0; bb < 4; bb++) lsum += p_sub(bb, ms, cm, k1, sc16[bb], sv16[bb], ki16[bb]);
-    if constexpr (PMODE != PM_PNQ || PV != PV_FP4) lpart = alpha * lpart + lsum;
+    for (int bb = 0; bb < 4; bb++) lsum += p_sub(bb, vp_ms, vp_cm, vp_k1, vp_sc[bb], vp_sv[bb], vp_ki[bb]);
+    if constexpr (PMODE != PM_PNQ || PV != PV_FP4) lpart = vp_alpha * lpart + lsum;
   };
 
   // V phase of the group's diagonal tile with causally safe V scales ("FLAMIA" section
