@@ -339,12 +339,20 @@ static int grain_exp(float v) {
  *     (3 u), plus the products of the P quantization (a reciprocal 1/s, its
  *     product with the two-level pre-scale and the element's product with it,
  *     against this oracle's single division: 4 u): 2^-20 covers both.
+ *   - fold: with the exact exponential an implementation may apply the multiplier
+ *     of the P quantization (the two-level 1/s1, an E4M3 block scale's 1/s) as an
+ *     offset of the argument instead of a product: P~/s1 = 2^(lambda (s - t) + L)
+ *     with t the tile's largest score and L = log2(448 * 6), and 1/s as -log2 s.
+ *     Its offsets are rounded to FP32 once or twice more and log2 s comes from a
+ *     hardware logarithm within 2^-20 for every E4M3 value (measured); attn_row_bias
+ *     passes these terms, an absolute change of the argument, as fold.
  * A change d of the argument changes 2^a by a factor 2^d, |2^d - 1| <= ln2 |d|
  * (1 + ln2 |d|).  The bit-level modes add 2^-15 (the line keeps 16 fraction bits
  * of its argument in an FP32 FMA). */
-static double p_window(const orc_attn_params* p, double lam, double es, double a, double m) {
+static double p_window(const orc_attn_params* p, double lam, double es, double a, double m,
+                       double fold) {
   const double u = 0x1p-24;
-  double darg = 2.0 * lam * es + 2.0 * u * fabs(a) + u * lam * fabs(m);
+  double darg = 2.0 * lam * es + 2.0 * u * fabs(a) + u * lam * fabs(m) + fold;
   const double ln2 = 0.69314718055994530942;
   double w = ln2 * darg * (1.0 + ln2 * darg) + 0x1p-20;
   if (p->exp_mode != ORC_EXP_EXACT) w += 0x1p-15;
@@ -492,9 +500,19 @@ static int attn_row_bias(const float* q, const float* K, const float* V, const f
     {
       const double es = es_max;
       const int unique = es == 0.0 || (double)mnew - m2 > 2.0 * es;
+      /* the multiplier applied as an offset of the argument (p_window): the two-level
+       * offset fl(lambda t - L) and L's own rounding, an E4M3 scale's offset added to it
+       * (or to fl(lambda m)) and its logarithm, and the larger argument */
+      double fold = 0.0;
+      if (p->exp_mode == ORC_EXP_EXACT && p->pmode != ORC_P_FP8_FIXED && mt != -INFINITY) {
+        const double u = 0x1p-24, L = log2(448.0 * 6.0);
+        const double c1 = p->pmode == ORC_P_TWO_LEVEL ? fabs(lam * (double)mt - L) : lam * fabs((double)mnew);
+        if (p->pmode == ORC_P_TWO_LEVEL) fold = u * (c1 + 1.5 * L);
+        if (p->pfmt.scale == ORC_SCALE_E4M3) fold += u * (c1 + 20.0) + 0x1p-20;
+      }
       for (int j = 0; j < tl; j++) {
         double a = s[j] == -INFINITY ? 0.0 : lam * ((double)s[j] - (double)mnew);
-        we[j] = p_window(p, lam, es, a, mnew);
+        we[j] = p_window(p, lam, es, a, mnew, fold);
         ws[j] = (p->exp_mode == ORC_EXP_EXACT && s[j] == mnew && unique) ? 0.0 : we[j];
       }
     }
