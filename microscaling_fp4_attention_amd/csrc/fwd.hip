@@ -1340,7 +1340,6 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     }
   };
 
-  // V(t): exponentials and P quantization of tile t (its row max came with M(t))
   // V(t): exponentials and P quantization of tile t with the state from phase_v_pre
   auto phase_v = [&](int t) __attribute__((always_inline)) {
     if constexpr (!PRE_IN_M) phase_v_pre();
@@ -1513,13 +1512,26 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   uint32_t sk = 0, sv = 2 * STAGE, ss = grp == 0 ? STAGE : 2 * STAGE;
   // one M phase and one V phase; can_fold (a constant at each call) compiles the
   // per-key fold in, which only the group's diagonal tile 2 qt + grp needs
+  // Issue priority: the SIMD issues the older wave first, so a phase of the younger
+  // group waits behind the co-resident wave's stream.  Where one phase's stream is the
+  // one that holds up the pair, it runs at raised priority (s_setprio): the M phase
+  // on the FP4 PV route (its MFMAs need an issue slot every 32 cycles, and its scale
+  // chain ends the phase: video-DiT 32K 5.88 -> 5.60 ms, two-level E8M0 1.3% faster),
+  // the V phase on the f16 PV route (two-level E4M3 32K 11.20 -> 10.90 ms, packed
+  // documents 2-3% faster); the FP8 PV route measured best without.
+  constexpr int MPRIO = QK == QK_FP4 && PV == PV_FP4 ? 1 : 0;
+  constexpr int VPRIO = QK == QK_FP4 && PV == PV_BF16 ? 1 : 0;
   auto step = [&](int t, bool can_fold) __attribute__((always_inline)) {
+    if constexpr (MPRIO) __builtin_amdgcn_s_setprio(MPRIO);
     phase_m(t, sk, sv, can_fold);
     __builtin_amdgcn_sched_barrier(0);  // keep the phase's MFMAs on this side of the barrier
+    if constexpr (MPRIO) __builtin_amdgcn_s_setprio(0);
     __syncthreads();
     if (t < nkt) {
+      if constexpr (VPRIO) __builtin_amdgcn_s_setprio(VPRIO);
       if (SAFE && can_fold && t == tdiag) phase_v_fold(t);
       else phase_v(t);
+      if constexpr (VPRIO) __builtin_amdgcn_s_setprio(0);
       store_half(ss);
       const int nt = t + 2 + grp;
       load_half(nt < nkt ? nt : nkt - 1);
