@@ -225,23 +225,27 @@ def bench_decode(args, torch, mx):
     """Split-key decode step: quantize the new tokens' Q, then mxattn_decode over the cached,
     already quantized history.  Inputs are seeded normal bf16 drawn on the device."""
     B, Hq, Hkv, R, N = 4, 32, 8, 1, args.decode
+    q4p8 = args.decode_route == "qk4pv8"  # NVFP4 Q/K, FP8 P and V (V in role V only)
+    qkf, vf = ("nvfp4", "fp8v") if q4p8 else ("mxfp4", "mxfp4")
+    layout = "v" if q4p8 else args.decode_layout
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev)
     g.manual_seed(0)
     q = torch.randn((B, Hq, R, 128), generator=g, device=dev).to(torch.bfloat16)
     k = torch.randn((B, Hkv, N, 128), generator=g, device=dev).to(torch.bfloat16)
     v = torch.randn((B, Hkv, N, 128), generator=g, device=dev).to(torch.bfloat16)
-    K = mx.quantize(k, mx.ROLE_QK, "mxfp4")
-    V = mx.quantize(v, mx.ROLE_VT if args.decode_layout == "vt" else mx.ROLE_V, "mxfp4")
+    K = mx.quantize(k, mx.ROLE_QK, qkf)
+    V = mx.quantize(v, mx.ROLE_VT if layout == "vt" else mx.ROLE_V, vf)
     del k, v
-    params = mx.fwd_params("two_level", "mxfp4", causal=True, out_fp32=False)
+    params = mx.fwd_params("fp8", None, causal=True, out_fp32=False) if q4p8 else \
+        mx.fwd_params("two_level", "mxfp4", causal=True, out_fp32=False)
     out = torch.empty((B, Hq, R, 128), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(mx.decode_workspace_bytes(B, Hq, R, N), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     ev = []
 
     def step(record):
-        Q = mx.quantize(q, mx.ROLE_QK, "mxfp4")
+        Q = mx.quantize(q, mx.ROLE_QK, qkf)
         if record:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -263,19 +267,21 @@ def bench_decode(args, torch, mx):
     t_dec = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
     hist = K.codes.numel() + K.scales.numel() + V.codes.numel() + V.scales.numel()  # history bytes read once
     gbs = hist / t_dec / 1e9
-    res = {"metric": "decode: quantized KV history read per second (GB/s), split-key MXFP4 decode",
+    route = "NVFP4 Q/K, FP8 P (E4M3 448 P~) and V" if q4p8 else "MXFP4 K/V/Q, two-level P"
+    res = {"metric": "decode: quantized KV history read per second (GB/s), split-key "
+                     + ("QK4PV8 decode" if q4p8 else "MXFP4 decode"),
            "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(t_step * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "mxfp4", "data": "synthetic (seeded normal bf16 drawn on the device)",
-           "config": {"workload": f"decode: B{B} Hq{Hq} Hkv{Hkv} R{R} history {N} keys, MXFP4 K/V/Q, two-level P, "
-                                  f"splits of 256 keys, V {'tile-major (role VT)' if args.decode_layout == 'vt' else 'role V'}",
+           "dtype": "nvfp4+fp8" if q4p8 else "mxfp4", "data": "synthetic (seeded normal bf16 drawn on the device)",
+           "config": {"workload": f"decode: B{B} Hq{Hq} Hkv{Hkv} R{R} history {N} keys, {route}, "
+                                  f"splits of 256 keys, V {'tile-major (role VT)' if layout == 'vt' else 'role V'}",
                       "history_bytes": hist},
            "t_decode_ms": round(t_dec * 1e3, 4),
            "tokens_per_s": round(B * R / t_step, 1),
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
                         "frac": round(gbs / 8000.0, 4),
                         "traffic": read_traffic(DECODE_TRAFFIC_FILE, DECODE_SOURCES)
-                        if (N, args.decode_layout) == (131072, "vt") else None,
+                        if (N, layout, q4p8) == (131072, "vt", False) else None,
                         "kernel": "split-key decode (mxattn_decode)"}}
     print(json.dumps(res), flush=True)
 
@@ -303,6 +309,9 @@ def main():
     ap.add_argument("--decode-layout", default="vt", choices=["vt", "v"],
                     help="layout of the decode's quantized V history: tile-major (role VT, the decode's own) or "
                          "role V (the prefill's)")
+    ap.add_argument("--decode-route", default="mxfp4", choices=["mxfp4", "qk4pv8"],
+                    help="operand route of the decode: MXFP4 Q/K/V with two-level P, or NVFP4 Q/K with FP8 P and V "
+                         "(role V)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (for scaling HBM byte counters)")
     args = ap.parse_args()

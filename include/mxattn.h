@@ -377,9 +377,12 @@ int mxattn_fwd(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn_qt
  *      keys 0..that position (params->causal must be 1).
  *   k: role QK [B][Hkv][N][d]; v: role V [B][Hkv][d][n_padded] without documents,
  *      or role VT (the same values tile-major: the faster layout for decode).
- *   Formats: MXFP4 Q/K/V (E2M1 with E8M0 per 32, any E8M0 rule); P modes DIRECT,
- *   PNQ and TWO_LEVEL with P in E2M1 with E8M0 per 32.  score_bias and vkey must be
- *   NULL.
+ *   Formats: MXFP4 Q/K/V (E2M1 with E8M0 per 32, any E8M0 rule) with P modes
+ *   DIRECT, PNQ and TWO_LEVEL and P in E2M1 with E8M0 per 32; or the QK4PV8 route
+ *   ("MpFA" sections 4.1 and 5.3): NVFP4 (or MXFP4) Q/K, V in E4M3 with E8M0 per 32
+ *   keys in role V (not VT), P mode FP8_FIXED (P = E4M3(448 P~), the row sum from
+ *   P~).  v->n_padded must be role V's padded length for N.  score_bias and vkey
+ *   must be NULL.
  *   kv_len: DEVICE int32 [B] with R <= kv_len[b] <= N, or NULL (every history has N
  *   keys); the host does not read it.
  *   out: [B][Hq][R][d] with element strides out_strides (out_strides[3] == 1),

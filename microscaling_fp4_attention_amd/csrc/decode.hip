@@ -270,6 +270,196 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecArgs a) {
   merge_chunk(a, so, slse, ncol, b, hk, gsz, chunk);
 }
 
+// The QK4PV8 route ("MpFA", sections 4.1 and 5.3: NVFP4 Q and K, FP8 P and V): the
+// same split-key decode, 32 query columns at most, with
+//   * S^T = K Q^T on the bf16 MFMA after exact dequantization (an E2M1 value times an
+//     E4M3 block scale has at most 6 significant bits); the contraction slot j of lane
+//     half h in step s holds channel 64 h + 8 s + j, so a lane reads one contiguous
+//     half of each K row (32 code bytes) and its 4 block scales (one dword), and Q the
+//     same half (MXFP4 Q and K take the scaled FP4 MFMA instead);
+//   * P = E4M3(448 P~) (the oracle's FP8_FIXED), O^T = V^T P^T on the scaled FP8 MFMA
+//     with V's E8M0 scale per 32 keys and P's unit scale, the row sum from P~, and O
+//     divided by 448 with it; K rows are read in the FP8 operand's key order
+//     (key_of<true>), so the P codes built in registers are the PV B operand.
+template <int QK>
+__global__ __launch_bounds__(256, 2) void decode_q4p8_kernel(DecArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63, ql = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t nchunk = (a.N + DEC_CHUNK - 1) / DEC_CHUNK;
+  const int64_t chunk = blockIdx.x % nchunk, bhk = blockIdx.x / nchunk;
+  const int64_t b = bhk / a.Hkv, hk = bhk % a.Hkv;
+  const int gsz = (int)(a.Hq / a.Hkv);
+  const int ncol = gsz * (int)a.R;
+  const bool cvalid = ql < ncol;
+  const int g = cvalid ? ql / (int)a.R : 0, r = cvalid ? ql % (int)a.R : 0;
+  const int64_t hq = hk * gsz + g;
+  const int kt0 = (int)chunk * DEC_CHUNK + 128 * wave;
+  const float lam = a.lambda;
+  constexpr int KSB = QK == QK_FP4 ? 4 : 8;  // scale bytes per Q/K row
+
+  // Q operand (B operand of S^T = K Q^T); an absent column reads column 0's row
+  v8i qop[2];
+  uint32_t qsc = 0;
+  v8bf qbf[8];
+  {
+    const int64_t qrow = (b * a.Hq + hq) * a.R + r;
+    const uint8_t* qp = a.q + qrow * 64;
+    if constexpr (QK == QK_FP4) {
+      qop[0] = v8_from4(*reinterpret_cast<const u4*>(qp + 16 * hh));
+      qop[1] = v8_from4(*reinterpret_cast<const u4*>(qp + 32 + 16 * hh));
+      qsc = *reinterpret_cast<const uint32_t*>(a.qs + qrow * 4) >> (8 * hh);
+    } else {
+      const u4 c0 = *reinterpret_cast<const u4*>(qp + 32 * hh), c1 = *reinterpret_cast<const u4*>(qp + 32 * hh + 16);
+      const uint32_t sw = *reinterpret_cast<const uint32_t*>(a.qs + qrow * 8 + 4 * hh);
+      const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+      for (int s = 0; s < 8; s++)
+        qbf[s] = __builtin_bit_cast(v8bf, dq8_bf16(cw[s], e4m3_value((sw >> (8 * (s >> 1))) & 0xFFu)));
+    }
+  }
+  const uint8_t* kc = a.k + (b * a.Hkv + hk) * a.N * 64;
+  const uint8_t* kscl = a.ks + (b * a.Hkv + hk) * a.N * KSB;
+  const int64_t vrow0 = (b * a.Hkv + hk) * 128;
+  const uint32_t np = (uint32_t)a.np;
+
+  // ---- the tile's operands, all requested before any is used: MFMA row ql of
+  // sub-tile bb reads key kt0 + key_of<true>(bb, (ql>>2)&1, 4(ql>>3) + (ql&3)), keys
+  // past N reading row N - 1 (masked); V^T rows are channels 32 db + ql, one byte per
+  // key (np, a multiple of 128, keeps a tile's bytes and its 4 scale bytes in the row)
+  u4 k0[4], k1[4], vlo[4][2], vhi[4][2];
+  uint32_t ks[4], vs[4];
+  v16f S[4];
+  float bm16[4], tmax = NEG_INF;
+  if (kt0 < (int)a.N) {
+#pragma unroll
+    for (int bb = 0; bb < 4; bb++) {
+      int key = kt0 + key_of<true>(bb, (ql >> 2) & 1, 4 * (ql >> 3) + (ql & 3));
+      key = key < (int)a.N ? key : (int)a.N - 1;
+      const uint8_t* kp = kc + (int64_t)key * 64;
+      if constexpr (QK == QK_FP4) {
+        k0[bb] = *reinterpret_cast<const u4*>(kp + 16 * hh);
+        k1[bb] = *reinterpret_cast<const u4*>(kp + 32 + 16 * hh);
+        ks[bb] = *reinterpret_cast<const uint32_t*>(kscl + (int64_t)key * 4);
+      } else {
+        k0[bb] = *reinterpret_cast<const u4*>(kp + 32 * hh);
+        k1[bb] = *reinterpret_cast<const u4*>(kp + 32 * hh + 16);
+        ks[bb] = *reinterpret_cast<const uint32_t*>(kscl + (int64_t)key * 8 + 4 * hh);
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < 4; db++) {
+      const int64_t vrow = vrow0 + 32 * db + ql;
+      const uint8_t* vp = a.v + vrow * np + kt0;
+#pragma unroll
+      for (int kcn = 0; kcn < 2; kcn++) {  // operand element n: key 64 kc + 32 (n / 16) + 16 h + n % 16
+        vlo[db][kcn] = *reinterpret_cast<const u4*>(vp + 64 * kcn + 16 * hh);
+        vhi[db][kcn] = *reinterpret_cast<const u4*>(vp + 64 * kcn + 32 + 16 * hh);
+      }
+      vs[db] = *reinterpret_cast<const uint32_t*>(a.vs + vrow * (np / 32) + kt0 / 32);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every read is in flight before the MFMAs
+  const int L = a.kv_len != nullptr ? a.kv_len[b] : (int)a.N;
+  const int pos = L - (int)a.R + r;  // keys <= pos are visible to this column
+  const bool live = kt0 < L;
+  if (live) {
+#pragma unroll
+    for (int bb = 0; bb < 4; bb++) {
+      v16f acc = zero16();
+      if constexpr (QK == QK_FP4) {
+        const uint32_t ks4 = ks[bb] >> (8 * hh);
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v8_from4(k0[bb]), qop[0], acc, 4, 4, 0, (int)ks4, 0,
+                                                              (int)qsc);
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v8_from4(k1[bb]), qop[1], acc, 4, 4, 2, (int)ks4, 2,
+                                                              (int)qsc);
+      } else {
+        const uint32_t kw[8] = {k0[bb].x, k0[bb].y, k0[bb].z, k0[bb].w, k1[bb].x, k1[bb].y, k1[bb].z, k1[bb].w};
+#pragma unroll
+        for (int s = 0; s < 8; s++)
+          acc = mfma_bf16(__builtin_bit_cast(v8bf, dq8_bf16(kw[s], e4m3_value((ks[bb] >> (8 * (s >> 1))) & 0xFFu))),
+                          qbf[s], acc);
+      }
+      S[bb] = acc;
+    }
+#pragma unroll
+    for (int bb = 0; bb < 4; bb++)
+#pragma unroll
+      for (int j = 0; j < 16; j++) {
+        const int key = kt0 + key_of<true>(bb, hh, j);
+        S[bb][j] = (cvalid && key <= pos) ? S[bb][j] : NEG_INF;  // pos < L
+      }
+#pragma unroll
+    for (int bb = 0; bb < 4; bb++) {
+      float x = S[bb][0];
+#pragma unroll
+      for (int j = 1; j < 16; j++) x = fmaxn(x, S[bb][j]);
+      bm16[bb] = x;
+    }
+    tmax = halves_max(fmaxn(fmaxn(bm16[0], bm16[1]), fmaxn(bm16[2], bm16[3])));
+  }
+
+  // ---- the running maximum before this tile (the split's second tile starts from
+  // the first tile's maximum)
+  __shared__ float smax[4][32];
+  if (hh == 0) smax[wave][ql] = tmax;
+  __syncthreads();
+  const float m0 = (wave & 1) ? smax[wave - 1][ql] : NEG_INF;
+
+  float m = m0, l = 0.0f;
+  v16f O[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) O[i] = zero16();
+  if (live) {
+    const float mnew = fmaxn(m0, tmax);
+    const float ms = mnew == NEG_INF ? 0.0f : mnew * lam;
+    m = mnew;
+    float lsum = 0.0f;
+    v8i bp[2];
+#pragma unroll
+    for (int bb = 0; bb < 4; bb++)
+#pragma unroll
+      for (int dw = 0; dw < 4; dw++) {  // c = E4M3(448 P~), four codes per dword
+        float y[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          y[u] = exp2_hw(__builtin_fmaf(S[bb][4 * dw + u], lam, -ms));
+          lsum += y[u];
+        }
+        int x = __builtin_amdgcn_cvt_pk_fp8_f32(448.0f * y[0], 448.0f * y[1], 0, false);
+        x = __builtin_amdgcn_cvt_pk_fp8_f32(448.0f * y[2], 448.0f * y[3], x, true);
+        bp[bb >> 1][4 * (bb & 1) + dw] = x;
+      }
+#pragma unroll
+    for (int db = 0; db < 4; db++) {
+      const uint32_t vs4 = vs[db] >> (8 * hh);
+#pragma unroll
+      for (int kcn = 0; kcn < 2; kcn++) {
+        const u4 lo = vlo[db][kcn], hi = vhi[db][kcn];
+        const v8i av = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        if (kcn == 0)
+          O[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bp[0], O[db], 0, 0, 0, (int)vs4, 0, 127);
+        else
+          O[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bp[1], O[db], 0, 0, 2, (int)vs4, 0, 127);
+      }
+    }
+    l = halves_sum(lsum);
+  }
+
+  // ---- the tile's normalized output (O / 448 / l) and log-sum-exp, merged per chunk
+  const float inv = l > 0.0f ? 1.0f / l / 448.0f : 0.0f;
+  extern __shared__ float so[];
+  __shared__ float slse[4][32];
+  if (cvalid)
+#pragma unroll
+    for (int db = 0; db < 4; db++)
+#pragma unroll
+      for (int j = 0; j < 16; j++)
+        so[(wave * ncol + ql) * 129 + 32 * db + 8 * (j >> 2) + 4 * hh + (j & 3)] = O[db][j] * inv;
+  if (hh == 0) slse[wave][ql] = l > 0.0f ? __logf(l) + m * a.sm_scale : NEG_INF;
+  __syncthreads();
+  merge_chunk(a, so, slse, ncol, b, hk, gsz, chunk);
+}
+
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 // The same decode for up to 16 query columns on the 16x16x128 block-scaled MFMA.  A
@@ -529,7 +719,10 @@ hipError_t launch_decode(int pmode, const DecArgs& a, hipStream_t st) {
   auto pick = [&](auto k32, auto k16) { return (a.Hq / a.Hkv) * a.R <= 16 ? run(k16) : run(k32); };
   hipError_t e0;
   const bool vt = a.vtiled != 0;
-  if (pmode == PM_DIRECT)
+  if (pmode == PM_FP8_FIXED) {  // QK4PV8: an FP8 V in role V, 32 columns at most
+    if (vt) return hipErrorNotSupported;
+    e0 = a.qk_fp4 ? run(decode_q4p8_kernel<QK_FP4>) : run(decode_q4p8_kernel<QK_BF16>);
+  } else if (pmode == PM_DIRECT)
     e0 = vt ? pick(decode_kernel<PM_DIRECT, true>, decode16_kernel<PM_DIRECT, true>)
             : pick(decode_kernel<PM_DIRECT, false>, decode16_kernel<PM_DIRECT, false>);
   else if (pmode == PM_PNQ)

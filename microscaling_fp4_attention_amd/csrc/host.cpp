@@ -370,18 +370,27 @@ static int decode_impl(const mxattn_qtensor* q, const mxattn_qtensor* k, const m
   if (q->d != 128 || k->d != 128 || v->d != 128) return MXATTN_E_UNSUPPORTED;
   if (q->B != k->B || q->B != v->B || k->N != v->N || k->H != v->H || v->ndocs != 1) return MXATTN_E_INVALID;
   if (q->H <= 0 || k->H <= 0 || q->H % k->H != 0) return MXATTN_E_INVALID;
+  if (v->n_padded != v_padded(v->N, 1, v->fmt.block)) return MXATTN_E_INVALID;  // the kernels read by it
   if (!p->causal || p->kv_tile != 128 || p->score_bias != nullptr || p->vkey != nullptr) return MXATTN_E_INVALID;
   if (!(p->sm_scale > 0.0f) || !isfinite(p->sm_scale)) return MXATTN_E_INVALID;
   if (p->exp_mode != MXATTN_EXP_EXACT) return p->exp_mode == MXATTN_EXP_MITCHELL || p->exp_mode == MXATTN_EXP_SCHRAUDOLPH
                                                  ? MXATTN_E_UNSUPPORTED : MXATTN_E_INVALID;
   const int64_t B = q->B, Hq = q->H, Hkv = k->H, R = q->N, N = k->N;
   if (R <= 0 || R > N || (Hq / Hkv) * R > 32) return MXATTN_E_UNSUPPORTED;
-  if (!same_fmt(q->fmt, k->fmt) || !is_mxfp4(q->fmt) || !is_mxfp4(v->fmt)) return MXATTN_E_UNSUPPORTED;
-  if (p->pmode != MXATTN_P_DIRECT && p->pmode != MXATTN_P_PNQ && p->pmode != MXATTN_P_TWO_LEVEL)
-    return MXATTN_E_UNSUPPORTED;
-  int prc = check_fmt(&p->pfmt, MXATTN_ROLE_V);
-  if (prc != MXATTN_OK) return prc;
-  if (!is_mxfp4(p->pfmt)) return MXATTN_E_UNSUPPORTED;
+  const bool q4p8 = p->pmode == MXATTN_P_FP8_FIXED;
+  if (!same_fmt(q->fmt, k->fmt)) return MXATTN_E_UNSUPPORTED;
+  if (q4p8) {
+    // QK4PV8: NVFP4 (or MXFP4) Q/K, an FP8 V in role V, P = E4M3(448 P~)
+    if (!(is_nvfp4(q->fmt) || is_mxfp4(q->fmt)) || !is_fp8v(v->fmt) || v->role != MXATTN_ROLE_V)
+      return MXATTN_E_UNSUPPORTED;
+  } else {
+    if (!is_mxfp4(q->fmt) || !is_mxfp4(v->fmt)) return MXATTN_E_UNSUPPORTED;
+    if (p->pmode != MXATTN_P_DIRECT && p->pmode != MXATTN_P_PNQ && p->pmode != MXATTN_P_TWO_LEVEL)
+      return p->pmode == MXATTN_P_NONE ? MXATTN_E_UNSUPPORTED : MXATTN_E_INVALID;
+    int prc = check_fmt(&p->pfmt, MXATTN_ROLE_V);
+    if (prc != MXATTN_OK) return prc;
+    if (!is_mxfp4(p->pfmt)) return MXATTN_E_UNSUPPORTED;
+  }
   if (N > (int64_t(1) << 24)) return MXATTN_E_UNSUPPORTED;
   if (B == 0) return MXATTN_OK;
   if (!q->codes || !q->scales || !k->codes || !k->scales || !v->codes || !v->scales || !out) return MXATTN_E_INVALID;
@@ -419,6 +428,7 @@ static int decode_impl(const mxattn_qtensor* q, const mxattn_qtensor* k, const m
   a.np = v->n_padded;
   a.kv_len = kv_len;
   a.vtiled = v->role == MXATTN_ROLE_VT ? 1 : 0;
+  a.qk_fp4 = is_mxfp4(q->fmt) ? 1 : 0;
   a.lambda = (float)((double)p->sm_scale * 1.4426950408889634);
   a.sm_scale = p->sm_scale;
   a.prule = make_rule(&p->pfmt);

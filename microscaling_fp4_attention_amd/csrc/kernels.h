@@ -128,6 +128,7 @@ struct DecArgs {
   int64_t B, Hq, Hkv, R, N, np;
   const int32_t* kv_len;  // device [B] keys of each request, or null (N each)
   int vtiled;             // V is role VT (tile-major)
+  int qk_fp4;             // FP8 V route: Q/K MXFP4 (1) or NVFP4 (0, scales [..][8], E4M3 per 16)
   float lambda, sm_scale;
   E8m0Rule prule;
   int64_t nsplit;  // 512-key chunks of the longest history: ceil(N / 512)

@@ -1,7 +1,8 @@
 """GPU split-key decode (mxattn_decode) against the oracle's split decode ("MpFA ...",
 section 5.3): the same quantized bytes, splits of 256 keys merged by log-sum-exp,
 |dO| <= 2e-3 max|O| + the merged flip budget; ragged histories, several newest rows,
-packed GQA groups, and a 32:8 GQA decode over 32K keys.  Up to 16 packed query columns
+packed GQA groups, and a 32:8 GQA decode over 32K keys, for the MXFP4 routes and the
+QK4PV8 route (NVFP4 Q/K, FP8 P and V).  Up to 16 packed query columns
 (query heads per KV head x newest rows) run on the 16-column kernel, 17 to 32 on the
 32-column one; both are covered for every P mode."""
 import numpy as np
@@ -10,11 +11,12 @@ import pytest
 import oracle
 import synth
 from helpers import (PM_ORACLE, TOL, gpu_available, gpu_codes_qk, gpu_codes_v, oracle_quant_qk, oracle_quant_v,
-                     FRAGILE_CAP, record_parity)
+                     FRAGILE_CAP, record_parity, score_rounds)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
-FMT = {"direct": ("mxfp4", "mxfp4"), "pnq": ("mxfp4_uos", "mxfp4_uos"), "two_level": ("mxfp4", "mxfp4")}
+FMT = {"direct": ("mxfp4", "mxfp4"), "pnq": ("mxfp4_uos", "mxfp4_uos"), "two_level": ("mxfp4", "mxfp4"),
+       "fp8": ("nvfp4", "fp8v")}  # QK4PV8: NVFP4 Q/K, P = E4M3(448 P~), FP8 V
 
 
 def _bf16(shape, seed, stream, shift=0.0):
@@ -22,10 +24,12 @@ def _bf16(shape, seed, stream, shift=0.0):
     return synth.f32_to_bf16(x.astype(np.float32))
 
 
-def run_decode(pm, B, Hq, Hkv, R, N, kv_len, seed):
+def run_decode(pm, B, Hq, Hkv, R, N, kv_len, seed, qfmt=None):
     import torch
     import microscaling_fp4_attention_amd as mx
     qf_, vf_ = FMT[pm]
+    qf_ = qfmt or qf_
+    pf_ = None if pm == "fp8" else qf_
     q, k, v = _bf16((B, Hq, R, 128), seed, 1), _bf16((B, Hkv, N, 128), seed, 2, 0.3), _bf16((B, Hkv, N, 128), seed, 3)
     dev = "cuda:0"
     t = {n: torch.from_numpy(a.astype(np.int16)).view(torch.bfloat16).to(dev) for n, a in (("q", q), ("k", k), ("v", v))}
@@ -34,7 +38,7 @@ def run_decode(pm, B, Hq, Hkv, R, N, kv_len, seed):
     V = mx.quantize(t["v"], mx.ROLE_V, vf_)
     kl = None if kv_len is None else torch.tensor(kv_len, dtype=torch.int32, device=dev)
     lse = torch.empty((B, Hq, R), dtype=torch.float32, device=dev)
-    out = mx.decode(Q, K, V, mx.fwd_params(pm, qf_, causal=True, out_fp32=True), kv_len=kl, lse=lse)
+    out = mx.decode(Q, K, V, mx.fwd_params(pm, pf_, causal=True, out_fp32=True), kv_len=kl, lse=lse)
     torch.cuda.synchronize()
     qc, qs, qd = oracle_quant_qk(synth.bf16_to_f32(q), qf_)
     kc, ks, kd = oracle_quant_qk(synth.bf16_to_f32(k), qf_)
@@ -43,13 +47,13 @@ def run_decode(pm, B, Hq, Hkv, R, N, kv_len, seed):
     gc, gs = gpu_codes_v(V, N, None)
     assert np.array_equal(gc, vc) and np.array_equal(gs, vs)
     kvl = np.full(B, N, np.int32) if kv_len is None else np.asarray(kv_len, np.int32)
-    O_ref, lse_ref, fb = oracle.decode(qd, kd, vd, kvl, PM_ORACLE[pm], qf_, split=256)
+    O_ref, lse_ref, fb = oracle.decode(qd, kd, vd, kvl, PM_ORACLE[pm], pf_, split=256, score_rounds=score_rounds(qf_))
     O_gpu = out.cpu().numpy()
     bound = TOL * np.abs(O_ref).max() + fb[..., None]
     ratio = float((np.abs(O_gpu - O_ref) / bound).max())
     lse_err = float(np.abs(lse.cpu().numpy() - lse_ref).max())
-    print(f"decode {pm} B{B} Hq{Hq} Hkv{Hkv} R{R} N{N}: max |dO|/bound {ratio:.3f}, |dlse| {lse_err:.2e}")
-    record_parity(f"decode {pm} B{B} Hq{Hq} Hkv{Hkv} R{R} N{N}", ratio, fb / (TOL * np.abs(O_ref).max()),
+    print(f"decode {pm} {qf_} B{B} Hq{Hq} Hkv{Hkv} R{R} N{N}: max |dO|/bound {ratio:.3f}, |dlse| {lse_err:.2e}")
+    record_parity(f"decode {pm} {qf_} B{B} Hq{Hq} Hkv{Hkv} R{R} N{N}", ratio, fb / (TOL * np.abs(O_ref).max()),
                   None if N > 4096 else FRAGILE_CAP)
     assert np.all(np.isfinite(O_gpu))
     assert ratio <= 1.0
@@ -75,6 +79,16 @@ def test_decode_column_forms(pm, Hq, Hkv, R):
     run_decode(pm, B=2, Hq=Hq, Hkv=Hkv, R=R, N=1100, kv_len=[1100, 517], seed=66)
 
 
+@pytest.mark.parametrize("qf", ["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("Hq,Hkv,R,N,kv_len", [(8, 2, 1, 700, [700, 333]), (8, 1, 3, 1100, [1100, 517]),
+                                               (4, 1, 8, 1300, None), (2, 2, 2, 260, [2, 257])])
+def test_decode_qk4pv8(qf, Hq, Hkv, R, N, kv_len):
+    """The QK4PV8 route ("MpFA", sections 4.1 and 5.3): NVFP4 (or MXFP4) Q/K, an FP8 V,
+    P = E4M3(448 P~): ragged histories, several newest rows, up to 32 packed columns"""
+    run_decode("fp8", B=2 if kv_len is not None and len(kv_len) == 2 else 1, Hq=Hq, Hkv=Hkv, R=R, N=N, kv_len=kv_len,
+               seed=71, qfmt=qf)
+
+
 def test_decode_minimal_history():
     run_decode("direct", B=3, Hq=2, Hkv=2, R=2, N=260, kv_len=[2, 130, 257], seed=63)
 
@@ -88,6 +102,10 @@ def test_decode_short_histories(N, kv_len):
 
 def test_decode_gqa_32_8_long():
     run_decode("two_level", B=1, Hq=32, Hkv=8, R=1, N=32768, kv_len=None, seed=64)
+
+
+def test_decode_qk4pv8_gqa_32_8_long():
+    run_decode("fp8", B=1, Hq=32, Hkv=8, R=1, N=32768, kv_len=None, seed=67)
 
 
 @pytest.mark.parametrize("pm,B,Hq,Hkv,R,N,kv_len", [("direct", 2, 8, 2, 1, 700, [700, 333]),
@@ -130,4 +148,10 @@ def test_decode_refused():
     Q1 = mx.quantize(q[:, :1], mx.ROLE_QK, "mxfp4")
     with pytest.raises(mx.MxattnError):  # decode rows are the newest tokens: causal only
         mx.decode(Q1, K, V, mx.fwd_params("direct", "mxfp4", causal=False))
+    with pytest.raises(mx.MxattnError) as e:  # FP8 P takes an FP8 V
+        mx.decode(Q1, K, V, mx.fwd_params("fp8", None, causal=True))
+    assert e.value.status == -2
+    with pytest.raises(mx.MxattnError) as e:  # an FP8 V has no tile-major form here
+        mx.decode(Q1, K, mx.quantize(k, mx.ROLE_VT, "mxfp4"), mx.fwd_params("fp8", None, causal=True))
+    assert e.value.status == -2
     torch.cuda.synchronize()

@@ -146,7 +146,13 @@ def test_decode_checks(mx):
     assert dec(mx, q, k, v, params(mx, causal=1, exp_mode=mx.EXP_MITCHELL)) == UNSUPPORTED
     assert dec(mx, qt(mx, mx.ROLE_QK, H=8, N=9), k, v, p) == UNSUPPORTED    # 4 heads x 9 rows > 32 columns
     assert dec(mx, qt(mx, mx.ROLE_QK, H=8, N=4097), k, v, p) == UNSUPPORTED  # more rows than keys
-    assert dec(mx, q, k, v, params(mx, "fp8", causal=1)) == UNSUPPORTED
+    assert dec(mx, q, k, v, params(mx, "fp8", causal=1)) == UNSUPPORTED      # FP8 P needs an FP8 V
+    nq, nk = qt(mx, mx.ROLE_QK, "nvfp4", H=8, N=1), qt(mx, mx.ROLE_QK, "nvfp4", H=2, N=4096)
+    assert dec(mx, nq, nk, v, params(mx, "fp8", causal=1)) == UNSUPPORTED    # ... also with NVFP4 Q/K
+    assert dec(mx, nq, nk, qt(mx, mx.ROLE_VT, "fp8v", H=2, N=4096), params(mx, "fp8", causal=1)) in (UNSUPPORTED,
+                                                                                                     INVALID)
+    assert dec(mx, nq, k, qt(mx, mx.ROLE_V, "fp8v", H=2, N=4096), params(mx, "fp8", causal=1)) == UNSUPPORTED
+    assert dec(mx, nq, nk, v, p) == UNSUPPORTED                              # NVFP4 Q/K decode with 4-bit P
     assert dec(mx, q, k, v, params(mx, pfmt="nvfp4", causal=1)) == UNSUPPORTED
     assert dec(mx, q, k, qt(mx, mx.ROLE_V, H=2, N=4096, ndocs=2), p) == INVALID
     need = mx.lib().mxattn_decode_workspace_bytes(1, 8, 1, 4096)
