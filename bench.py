@@ -225,9 +225,9 @@ def bench_decode(args, torch, mx):
     """Split-key decode step: quantize the new tokens' Q, then mxattn_decode over the cached,
     already quantized history.  Inputs are seeded normal bf16 drawn on the device."""
     B, Hq, Hkv, R, N = 4, 32, 8, 1, args.decode
-    q4p8 = args.decode_route == "qk4pv8"  # NVFP4 Q/K, FP8 P and V (V in role V only)
+    q4p8 = args.decode_route == "qk4pv8"  # NVFP4 Q/K, FP8 P and V
     qkf, vf = ("nvfp4", "fp8v") if q4p8 else ("mxfp4", "mxfp4")
-    layout = "v" if q4p8 else args.decode_layout
+    layout = args.decode_layout
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev)
     g.manual_seed(0)
@@ -310,8 +310,7 @@ def main():
                     help="layout of the decode's quantized V history: tile-major (role VT, the decode's own) or "
                          "role V (the prefill's)")
     ap.add_argument("--decode-route", default="mxfp4", choices=["mxfp4", "qk4pv8"],
-                    help="operand route of the decode: MXFP4 Q/K/V with two-level P, or NVFP4 Q/K with FP8 P and V "
-                         "(role V)")
+                    help="operand route of the decode: MXFP4 Q/K/V with two-level P, or NVFP4 Q/K with FP8 P and V")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (for scaling HBM byte counters)")
     args = ap.parse_args()

@@ -90,7 +90,7 @@ typedef enum {
                           key decode (mxattn_decode): each 128-key tile of V^T is
                           one contiguous run, so the decode reads the history tile
                           by tile instead of 128 pieces one channel row apart.  No
-                          documents; E2M1 with E8M0 scales per 32 keys only        */
+                          documents; E2M1 or E4M3 with E8M0 scales per 32 keys     */
 } mxattn_role;
 
 /* how the softmax operand P is quantized inside the attention loop */
@@ -137,7 +137,7 @@ typedef struct {
  *   role QK: codes  [B][H][N][d * bits / 8]        scales [B][H][N][d / block]
  *   role V : codes  [B][H][d][n_padded * bits / 8] scales [B][H][d][n_padded / block]
  *   BF16 (either role): codes [B][H][N][d] bf16, no scales, n_padded = N
- *   role VT: codes  [B][H][n_padded / 128][d][64]    scales [B][H][n_padded / 128][d][4]
+ *   role VT: codes  [B][H][n_padded / 128][d][128 * bits / 8]  scales [B][H][n_padded / 128][d][4]
  *            (role V's bytes of key tile t and channel c moved to [t][c])
  * bits = 4 (E2M1) or 8 (E4M3).  For role V the key axis is padded: each document
  * (the whole sequence when there are no documents) occupies ceil(L / block) whole
@@ -221,7 +221,7 @@ int mxattn_qtensor_bytes(const mxattn_qfmt* fmt, int role, int64_t B, int64_t H,
  *   role V : per channel, blocks of fmt->block consecutive tokens inside one
  *            document, written transposed (see mxattn_qtensor).
  *   role VT: as role V without documents, written tile-major (see mxattn_qtensor);
- *            E2M1 with E8M0 scales per 32 keys only.
+ *            E2M1 or E4M3 elements with E8M0 scales per 32 keys only.
  * Per block with maximum magnitude M ("MXAttention" section 2; blog "NVFP4, not
  * MXFP4"):
  *   E8M0 scale: exponent by fmt->rule, clamped to [-127, 127]; M = 0 gives 2^0.
@@ -236,7 +236,7 @@ int mxattn_qtensor_bytes(const mxattn_qfmt* fmt, int role, int64_t B, int64_t H,
  *   the sizes from mxattn_qtensor_bytes(); the library fills the other fields.
  * Errors: MXATTN_E_INVALID (also role VT with documents), MXATTN_E_UNSUPPORTED
  *   (d != 128, block not 16/32, E4M3 elements with an E4M3 scale, role VT in any
- *   format but E2M1 with E8M0 per 32, role QK with B*H*N >= 2^30), MXATTN_E_ALIGN,
+ *   format but E2M1 or E4M3 with E8M0 per 32, role QK with B*H*N >= 2^30), MXATTN_E_ALIGN,
  *   MXATTN_E_HIP.
  */
 int mxattn_quantize(const void* x_bf16, const int64_t x_strides[4], int64_t B, int64_t H, int64_t N,
@@ -380,9 +380,9 @@ int mxattn_fwd(const mxattn_qtensor* q, const mxattn_qtensor* k, const mxattn_qt
  *   Formats: MXFP4 Q/K/V (E2M1 with E8M0 per 32, any E8M0 rule) with P modes
  *   DIRECT, PNQ and TWO_LEVEL and P in E2M1 with E8M0 per 32; or the QK4PV8 route
  *   ("MpFA" sections 4.1 and 5.3): NVFP4 (or MXFP4) Q/K, V in E4M3 with E8M0 per 32
- *   keys in role V (not VT), P mode FP8_FIXED (P = E4M3(448 P~), the row sum from
- *   P~).  v->n_padded must be role V's padded length for N.  score_bias and vkey
- *   must be NULL.
+ *   keys (role V or VT), P mode FP8_FIXED (P = E4M3(448 P~), the row sum from P~).
+ *   v->n_padded must be role V's padded length for N.  score_bias and vkey must be
+ *   NULL.
  *   kv_len: DEVICE int32 [B] with R <= kv_len[b] <= N, or NULL (every history has N
  *   keys); the host does not read it.
  *   out: [B][Hq][R][d] with element strides out_strides (out_strides[3] == 1),

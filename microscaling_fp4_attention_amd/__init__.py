@@ -161,7 +161,7 @@ class QTensor:
 
     def codes_view(self) -> torch.Tensor:
         """role QK: [B, H, N, d*bits/8]; role V: [B, H, d, n_padded*bits/8];
-        role VT: [B, H, n_padded/128, d, 64]."""
+        role VT: [B, H, n_padded/128, d, 128*bits/8]."""
         d = self.desc
         if d.fmt.elem == ELEM_BF16:  # the values, [B, H, N, d]
             return self.codes.view(torch.bfloat16).view(d.B, d.H, d.N, d.d)
@@ -169,7 +169,7 @@ class QTensor:
         if d.role == ROLE_QK:
             return self.codes.view(d.B, d.H, d.N, d.d * bits // 8)
         if d.role == ROLE_VT:
-            return self.codes.view(d.B, d.H, d.n_padded // 128, d.d, 64)
+            return self.codes.view(d.B, d.H, d.n_padded // 128, d.d, 128 * bits // 8)
         return self.codes.view(d.B, d.H, d.d, d.n_padded * bits // 8)
 
     def scales_view(self) -> torch.Tensor:

@@ -280,8 +280,10 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecArgs a) {
 //   * P = E4M3(448 P~) (the oracle's FP8_FIXED), O^T = V^T P^T on the scaled FP8 MFMA
 //     with V's E8M0 scale per 32 keys and P's unit scale, the row sum from P~, and O
 //     divided by 448 with it; K rows are read in the FP8 operand's key order
-//     (key_of<true>), so the P codes built in registers are the PV B operand.
-template <int QK>
+//     (key_of<true>), so the P codes built in registers are the PV B operand;
+//   * V in role V (channel rows) or VT (tile-major: a tile's 128 channels x 128 bytes
+//     one contiguous run).
+template <int QK, bool VT>
 __global__ __launch_bounds__(256, 2) void decode_q4p8_kernel(DecArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, ql = lane & 31, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -349,13 +351,16 @@ __global__ __launch_bounds__(256, 2) void decode_q4p8_kernel(DecArgs a) {
 #pragma unroll
     for (int db = 0; db < 4; db++) {
       const int64_t vrow = vrow0 + 32 * db + ql;
-      const uint8_t* vp = a.v + vrow * np + kt0;
+      // slot of (tile, channel) in the tile-major form (role VT: 128 code bytes each)
+      const int64_t tslot = (int64_t)(kt0 / 128) * 128 + 32 * db + ql;
+      const uint8_t* vp = VT ? a.v + vrow0 * np + tslot * 128 : a.v + vrow * np + kt0;
 #pragma unroll
       for (int kcn = 0; kcn < 2; kcn++) {  // operand element n: key 64 kc + 32 (n / 16) + 16 h + n % 16
         vlo[db][kcn] = *reinterpret_cast<const u4*>(vp + 64 * kcn + 16 * hh);
         vhi[db][kcn] = *reinterpret_cast<const u4*>(vp + 64 * kcn + 32 + 16 * hh);
       }
-      vs[db] = *reinterpret_cast<const uint32_t*>(a.vs + vrow * (np / 32) + kt0 / 32);
+      vs[db] = *reinterpret_cast<const uint32_t*>(VT ? a.vs + vrow0 * (np / 32) + tslot * 4
+                                                     : a.vs + vrow * (np / 32) + kt0 / 32);
     }
   }
   __builtin_amdgcn_sched_barrier(0);  // every read is in flight before the MFMAs
@@ -719,9 +724,9 @@ hipError_t launch_decode(int pmode, const DecArgs& a, hipStream_t st) {
   auto pick = [&](auto k32, auto k16) { return (a.Hq / a.Hkv) * a.R <= 16 ? run(k16) : run(k32); };
   hipError_t e0;
   const bool vt = a.vtiled != 0;
-  if (pmode == PM_FP8_FIXED) {  // QK4PV8: an FP8 V in role V, 32 columns at most
-    if (vt) return hipErrorNotSupported;
-    e0 = a.qk_fp4 ? run(decode_q4p8_kernel<QK_FP4>) : run(decode_q4p8_kernel<QK_BF16>);
+  if (pmode == PM_FP8_FIXED) {  // QK4PV8: an FP8 V, 32 columns at most
+    if (vt) e0 = a.qk_fp4 ? run(decode_q4p8_kernel<QK_FP4, true>) : run(decode_q4p8_kernel<QK_BF16, true>);
+    else e0 = a.qk_fp4 ? run(decode_q4p8_kernel<QK_FP4, false>) : run(decode_q4p8_kernel<QK_BF16, false>);
   } else if (pmode == PM_DIRECT)
     e0 = vt ? pick(decode_kernel<PM_DIRECT, true>, decode16_kernel<PM_DIRECT, true>)
             : pick(decode_kernel<PM_DIRECT, false>, decode16_kernel<PM_DIRECT, false>);

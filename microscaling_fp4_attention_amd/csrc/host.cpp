@@ -51,13 +51,13 @@ int check_fmt(const mxattn_qfmt* f, int role) {
     return MXATTN_E_INVALID;
   if (role == MXATTN_ROLE_VKEY && (f->elem != MXATTN_ELEM_E2M1 || f->scale != MXATTN_SCALE_E8M0))
     return MXATTN_E_UNSUPPORTED;
-  if (role == MXATTN_ROLE_VT && (f->elem != MXATTN_ELEM_E2M1 || f->scale != MXATTN_SCALE_E8M0 || f->block != 32))
+  if (role == MXATTN_ROLE_VT && (f->scale != MXATTN_SCALE_E8M0 || f->block != 32))  // MXFP4 or FP8 V
     return MXATTN_E_UNSUPPORTED;
   if (f->scale == MXATTN_SCALE_E8M0) {
     if (f->rule != MXATTN_RULE_OCP && f->rule != MXATTN_RULE_CEIL) return MXATTN_E_INVALID;
     if (f->rule == MXATTN_RULE_CEIL && !(f->qmax >= 1.0f && f->qmax <= 448.0f)) return MXATTN_E_INVALID;
   }
-  if (f->elem == MXATTN_ELEM_E4M3 && (f->scale != MXATTN_SCALE_E8M0 || role != MXATTN_ROLE_V))
+  if (f->elem == MXATTN_ELEM_E4M3 && (f->scale != MXATTN_SCALE_E8M0 || (role != MXATTN_ROLE_V && role != MXATTN_ROLE_VT)))
     return MXATTN_E_UNSUPPORTED;
   return MXATTN_OK;
 }
@@ -380,9 +380,8 @@ static int decode_impl(const mxattn_qtensor* q, const mxattn_qtensor* k, const m
   const bool q4p8 = p->pmode == MXATTN_P_FP8_FIXED;
   if (!same_fmt(q->fmt, k->fmt)) return MXATTN_E_UNSUPPORTED;
   if (q4p8) {
-    // QK4PV8: NVFP4 (or MXFP4) Q/K, an FP8 V in role V, P = E4M3(448 P~)
-    if (!(is_nvfp4(q->fmt) || is_mxfp4(q->fmt)) || !is_fp8v(v->fmt) || v->role != MXATTN_ROLE_V)
-      return MXATTN_E_UNSUPPORTED;
+    // QK4PV8: NVFP4 (or MXFP4) Q/K, an FP8 V (role V or VT), P = E4M3(448 P~)
+    if (!(is_nvfp4(q->fmt) || is_mxfp4(q->fmt)) || !is_fp8v(v->fmt)) return MXATTN_E_UNSUPPORTED;
   } else {
     if (!is_mxfp4(q->fmt) || !is_mxfp4(v->fmt)) return MXATTN_E_UNSUPPORTED;
     if (p->pmode != MXATTN_P_DIRECT && p->pmode != MXATTN_P_PNQ && p->pmode != MXATTN_P_TWO_LEVEL)

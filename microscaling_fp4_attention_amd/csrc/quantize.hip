@@ -168,8 +168,8 @@ __device__ __forceinline__ const int32_t* stage_offsets(const int32_t* cu, int n
 }
 constexpr int VQ_KT = 8;              // most key tiles of 128 slots per workgroup
 
-// TILED (role VT, MXFP4 only): the same bytes tile-major, key tile t of channel c at
-// [t][c] (64 code bytes, 4 scale bytes).
+// TILED (role VT, MXFP4 or an FP8 V, E8M0 per 32): the same bytes tile-major, key
+// tile t of channel c at [t][c] (64 or 128 code bytes, 4 scale bytes).
 template <int ELEM, int SCALE, int BLOCK, bool TILED = false>
 __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict__ x, int64_t sB, int64_t sH,
                                                       int64_t sN, int64_t H, int64_t N, int64_t np,
@@ -291,7 +291,8 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
           out[(e * BPE) / 32] |= c << ((e * BPE) % 32);
         }
       }
-      uint8_t* cdst = codes + crow * (np * BPE / 8) + (t0 + sub * 64) * BPE / 8;
+      uint8_t* cdst = TILED ? codes + ((bh * ntiles + t0 / 128) * 128 + ch) * (128 * BPE / 8) + sub * 64 * BPE / 8
+                            : codes + crow * (np * BPE / 8) + (t0 + sub * 64) * BPE / 8;
 #pragma unroll
       for (int i = 0; i < 64 * BPE / 128; i++)
         reinterpret_cast<uint4*>(cdst)[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
@@ -468,10 +469,16 @@ hipError_t launch_quant_v(const QuantArgs& a, hipStream_t st) {
 #define MXQV(E, S, BL)                                                                                   \
   quant_v_kernel<E, S, BL><<<grid, 256, 0, st>>>(x, a.sB, a.sH, a.sN, a.H, a.N, a.np, a.cu, a.ndocs, a.rule, \
                                                  c, s, kt)
-  if (a.tiled) {  // role VT: MXFP4 only (checked by the host)
-    if (a.elem != ELEM_E2M1 || a.scale != SCALE_E8M0 || a.block != 32) return hipErrorInvalidValue;
-    quant_v_kernel<ELEM_E2M1, SCALE_E8M0, 32, true><<<grid, 256, 0, st>>>(x, a.sB, a.sH, a.sN, a.H, a.N, a.np, a.cu,
-                                                                         a.ndocs, a.rule, c, s, kt);
+  if (a.tiled) {  // role VT: MXFP4 or an FP8 V with E8M0 per 32 (checked by the host)
+    if (a.scale != SCALE_E8M0 || a.block != 32) return hipErrorInvalidValue;
+    if (a.elem == ELEM_E2M1)
+      quant_v_kernel<ELEM_E2M1, SCALE_E8M0, 32, true><<<grid, 256, 0, st>>>(x, a.sB, a.sH, a.sN, a.H, a.N, a.np,
+                                                                           a.cu, a.ndocs, a.rule, c, s, kt);
+    else if (a.elem == ELEM_E4M3)
+      quant_v_kernel<ELEM_E4M3, SCALE_E8M0, 32, true><<<grid, 256, 0, st>>>(x, a.sB, a.sH, a.sN, a.H, a.N, a.np,
+                                                                           a.cu, a.ndocs, a.rule, c, s, kt);
+    else
+      return hipErrorInvalidValue;
     return hipGetLastError();
   }
   if (a.elem == ELEM_E2M1 && a.scale == SCALE_E8M0 && a.block == 32) MXQV(ELEM_E2M1, SCALE_E8M0, 32);

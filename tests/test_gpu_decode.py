@@ -112,25 +112,37 @@ def test_decode_qk4pv8_gqa_32_8_long():
                                                       ("pnq", 1, 4, 1, 8, 1300, None),
                                                       ("two_level", 2, 4, 2, 1, 129, [129, 128]),
                                                       ("two_level", 1, 32, 8, 1, 32768, None),
-                                                      ("two_level", 2, 8, 1, 3, 1100, [1100, 517])])
+                                                      ("two_level", 2, 8, 1, 3, 1100, [1100, 517]),
+                                                      ("fp8", 2, 8, 2, 1, 700, [700, 333]),
+                                                      ("fp8", 1, 32, 8, 1, 32768, None),
+                                                      ("fp8", 2, 8, 1, 3, 1100, [1100, 517])])
 def test_decode_vt_equals_v(pm, B, Hq, Hkv, R, N, kv_len):
-    """The decode over role VT (V tile-major) gives exactly the decode over role V."""
+    """The decode over role VT (V tile-major) gives exactly the decode over role V, and
+    role VT holds role V's bytes moved tile by tile."""
     import torch
     import microscaling_fp4_attention_amd as mx
     qf_, vf_ = FMT[pm]
+    pf_ = None if pm == "fp8" else qf_
     q, k, v = _bf16((B, Hq, R, 128), 71, 1), _bf16((B, Hkv, N, 128), 71, 2, 0.3), _bf16((B, Hkv, N, 128), 71, 3)
     dev = "cuda:0"
     t = {n: torch.from_numpy(a.astype(np.int16)).view(torch.bfloat16).to(dev) for n, a in (("q", q), ("k", k), ("v", v))}
     Q, K = mx.quantize(t["q"], mx.ROLE_QK, qf_), mx.quantize(t["k"], mx.ROLE_QK, qf_)
     kl = None if kv_len is None else torch.tensor(kv_len, dtype=torch.int32, device=dev)
-    p = mx.fwd_params(pm, qf_, causal=True, out_fp32=True)
-    res = []
+    p = mx.fwd_params(pm, pf_, causal=True, out_fp32=True)
+    res, vq = [], []
     for role in (mx.ROLE_V, mx.ROLE_VT):
         lse = torch.empty((B, Hq, R), dtype=torch.float32, device=dev)
-        out = mx.decode(Q, K, mx.quantize(t["v"], role, vf_), p, kv_len=kl, lse=lse)
+        V = mx.quantize(t["v"], role, vf_)
+        out = mx.decode(Q, K, V, p, kv_len=kl, lse=lse)
         res.append((out, lse))
+        vq.append(V)
     torch.cuda.synchronize()
     assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+    cv, ct = vq[0].codes_view(), vq[1].codes_view()  # [B,H,d,np*b/8] and [B,H,np/128,d,128*b/8]
+    nt = ct.shape[2]
+    assert torch.equal(cv.reshape(B, Hkv, 128, nt, -1).permute(0, 1, 3, 2, 4), ct)
+    sv, st = vq[0].scales_view(), vq[1].scales_view()
+    assert torch.equal(sv.reshape(B, Hkv, 128, nt, 4).permute(0, 1, 3, 2, 4), st)
 
 
 def test_decode_refused():

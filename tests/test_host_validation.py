@@ -149,8 +149,6 @@ def test_decode_checks(mx):
     assert dec(mx, q, k, v, params(mx, "fp8", causal=1)) == UNSUPPORTED      # FP8 P needs an FP8 V
     nq, nk = qt(mx, mx.ROLE_QK, "nvfp4", H=8, N=1), qt(mx, mx.ROLE_QK, "nvfp4", H=2, N=4096)
     assert dec(mx, nq, nk, v, params(mx, "fp8", causal=1)) == UNSUPPORTED    # ... also with NVFP4 Q/K
-    assert dec(mx, nq, nk, qt(mx, mx.ROLE_VT, "fp8v", H=2, N=4096), params(mx, "fp8", causal=1)) in (UNSUPPORTED,
-                                                                                                     INVALID)
     assert dec(mx, nq, k, qt(mx, mx.ROLE_V, "fp8v", H=2, N=4096), params(mx, "fp8", causal=1)) == UNSUPPORTED
     assert dec(mx, nq, nk, v, p) == UNSUPPORTED                              # NVFP4 Q/K decode with 4-bit P
     assert dec(mx, q, k, v, params(mx, pfmt="nvfp4", causal=1)) == UNSUPPORTED
@@ -163,15 +161,15 @@ def test_decode_checks(mx):
 
 
 def test_role_vt_checks(mx):
-    # the tile-major V of the decode: role V's sizes, no documents, MXFP4 (E8M0 per 32) only
+    # the tile-major V of the decode: role V's sizes, no documents, E8M0 per 32 (MXFP4 or FP8 V)
     assert mx.qtensor_bytes("mxfp4_uos", mx.ROLE_VT, 2, 3, 1000) == mx.qtensor_bytes("mxfp4_uos", mx.ROLE_V, 2, 3, 1000)
     with pytest.raises(mx.MxattnError) as e:
         mx.qtensor_bytes("mxfp4", mx.ROLE_VT, 1, 2, 1000, ndocs=3)
     assert e.value.status == INVALID
-    for fmt in ("nvfp4", "fp8v"):
-        with pytest.raises(mx.MxattnError) as e:
-            mx.qtensor_bytes(fmt, mx.ROLE_VT, 1, 2, 1000)
-        assert e.value.status == UNSUPPORTED
+    with pytest.raises(mx.MxattnError) as e:  # E4M3 block scales have no tile-major form
+        mx.qtensor_bytes("nvfp4", mx.ROLE_VT, 1, 2, 1000)
+    assert e.value.status == UNSUPPORTED
+    assert mx.qtensor_bytes("fp8v", mx.ROLE_VT, 2, 3, 1000) == mx.qtensor_bytes("fp8v", mx.ROLE_V, 2, 3, 1000)
     # the prefill takes role V only
     q, k, v, p, _ = base(mx)
     assert fwd(mx, q, k, qt(mx, mx.ROLE_VT, H=2), p) == INVALID
