@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MXATTN_ABI_VERSION 7
+#define MXATTN_ABI_VERSION 8
 
 typedef enum {
   MXATTN_OK = 0,
@@ -189,8 +189,11 @@ int mxattn_abi_version(void);
 const char* mxattn_status_str(int status);
 
 /* Text of the last MXATTN_E_HIP failure on the calling thread, or of the last
- * MXATTN_E_WORKSPACE of mxattn_decode_noalloc() ("" if none). */
+ * MXATTN_E_WORKSPACE of mxattn_decode_noalloc() ("" if none).  Thread-local; the
+ * pointer stays valid until the thread's next failing call.  mxattn_last_hip_error()
+ * is the same function under the name of the HIP failure it reports. */
 const char* mxattn_last_error(void);
+const char* mxattn_last_hip_error(void);
 
 /*
  * Test hook of the error path: the next `count` device submissions made by library

@@ -27,7 +27,7 @@ P_NONE, P_DIRECT, P_TWO_LEVEL, P_PNQ, P_FP8_FIXED = 0, 1, 2, 3, 4
 EXP_EXACT, EXP_MITCHELL, EXP_SCHRAUDOLPH = 0, 1, 2
 
 
-ABI_VERSION = 7  # MXATTN_ABI_VERSION of include/mxattn.h
+ABI_VERSION = 8  # MXATTN_ABI_VERSION of include/mxattn.h
 DECODE_SCRATCH_BYTES = 32 << 20  # MXATTN_DECODE_SCRATCH_BYTES
 
 
@@ -96,6 +96,7 @@ def _lib():
         L.mxattn_status_str.restype = ctypes.c_char_p
         L.mxattn_status_str.argtypes = [i32]
         L.mxattn_last_error.restype = ctypes.c_char_p
+        L.mxattn_last_hip_error.restype = ctypes.c_char_p
         L.mxattn_debug_fail_launches.restype = i32
         L.mxattn_debug_fail_launches.argtypes = [i32]
         L.mxattn_qtensor_bytes.restype = i32

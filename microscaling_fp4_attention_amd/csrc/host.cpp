@@ -130,6 +130,7 @@ const char* mxattn_status_str(int s) {
 }
 
 const char* mxattn_last_error(void) { return g_err; }
+const char* mxattn_last_hip_error(void) { return g_err; }
 
 int mxattn_debug_fail_launches(int count) {
   const int prev = g_fail_launches;

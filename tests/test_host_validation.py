@@ -215,6 +215,7 @@ def test_forced_launch_failure_reports_hip_error(mx):
             assert fwd(mx, q, k, v, p) == -5
             err = L.mxattn_last_error().decode()
             assert "mxattn_fwd launch" in err, err
+            assert L.mxattn_last_hip_error().decode() == err  # the same text under both names
             assert L.mxattn_debug_fail_launches(0) == 0  # the one forced failure was used
             # the plan builder's copy takes the same path
             cu = (ctypes.c_int32 * 3)(0, 500, 1000)
