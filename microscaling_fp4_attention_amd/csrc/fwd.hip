@@ -1161,7 +1161,11 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
 #pragma unroll
       for (int bb = 0; bb < 4; bb++) {
         const float pm = PMODE == PM_TWO_LEVEL && LOGOFF ? pexp(bm16[bb], c1, cm) : pmax(bm16[bb], ms, cm, msub) * k1;
-        const float sv = e4m3_value(e4m3_mag(div6(pm)));
+        // E4M3_rne_sat(fl32(M / 6)) by the hardware FP8 convert and back: the same code
+        // as the integer encoder for every float below 464 (checked on all of them), and
+        // M / 6 <= 2688 (1 + 2^-20) / 6 stays below it
+        const float q6 = div6(pm);
+        const float sv = __builtin_amdgcn_cvt_f32_fp8(__builtin_amdgcn_cvt_pk_fp8_f32(q6, q6, 0, false), 0);
         sc16[bb] = 1.0f;
         sv16[bb] = sv;
         ki16[bb] = sv > 0.0f ? __builtin_amdgcn_rcpf(sv) : 0.0f;
@@ -1446,7 +1450,8 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     } else {  // PV_BF16: E4M3 scale per 16 keys
 #pragma unroll
       for (int bb = 0; bb < 4; bb++) {
-        const float sv = e4m3_value(e4m3_mag(div6(pm16[bb] * k1)));
+        const float q6 = div6(pm16[bb] * k1);  // E4M3_rne_sat(fl32(M / 6)) as in phase_v_pre
+        const float sv = __builtin_amdgcn_cvt_f32_fp8(__builtin_amdgcn_cvt_pk_fp8_f32(q6, q6, 0, false), 0);
         const float ki = sv > 0.0f ? __builtin_amdgcn_rcpf(sv) : 0.0f;
         float z[16];
 #pragma unroll
