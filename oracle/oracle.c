@@ -340,9 +340,10 @@ static int grain_exp(float v) {
  *     product with the two-level pre-scale and the element's product with it,
  *     against this oracle's single division: 4 u): 2^-20 covers both.
  *   - fold: with the exact exponential an implementation may apply the multiplier
- *     of the P quantization (the two-level 1/s1, an E4M3 block scale's 1/s) as an
- *     offset of the argument instead of a product: P~/s1 = 2^(lambda (s - t) + L)
- *     with t the tile's largest score and L = log2(448 * 6), and 1/s as -log2 s.
+ *     of the P quantization (the two-level 1/s1, an E4M3 block scale's 1/s, FP8's
+ *     448) as an offset of the argument instead of a product: P~/s1 =
+ *     2^(lambda (s - t) + L) with t the tile's largest score and L = log2(448 * 6),
+ *     1/s as -log2 s, and 448 P~ = 2^(lambda (s - m) + log2 448).
  *     Its offsets are rounded to FP32 once or twice more and log2 s comes from a
  *     hardware logarithm within 2^-20 for every E4M3 value (measured); attn_row_bias
  *     passes these terms, an absolute change of the argument, as fold.
@@ -504,7 +505,12 @@ static int attn_row_bias(const float* q, const float* K, const float* V, const f
        * offset fl(lambda t - L) and L's own rounding, an E4M3 scale's offset added to it
        * (or to fl(lambda m)) and its logarithm, and the larger argument */
       double fold = 0.0;
-      if (p->exp_mode == ORC_EXP_EXACT && p->pmode != ORC_P_FP8_FIXED && mt != -INFINITY) {
+      if (p->exp_mode == ORC_EXP_EXACT && p->pmode == ORC_P_FP8_FIXED && mt != -INFINITY) {
+        /* 448 P~ as 2^(lambda s - fl(lambda m) + log2 448): the offset's rounding, the
+         * rounding of log2 448 and the larger argument */
+        const double u = 0x1p-24, L8 = log2(448.0);
+        fold = u * (lam * fabs((double)mnew) + 2.5 * L8);
+      } else if (p->exp_mode == ORC_EXP_EXACT && mt != -INFINITY) {
         const double u = 0x1p-24, L = log2(448.0 * 6.0);
         const double c1 = p->pmode == ORC_P_TWO_LEVEL ? fabs(lam * (double)mt - L) : lam * fabs((double)mnew);
         if (p->pmode == ORC_P_TWO_LEVEL) fold = u * (c1 + 1.5 * L);
