@@ -1033,15 +1033,16 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   const uint32_t soff = (uint32_t)(512 * hh + 4 * ql);  // this lane's scale dword of a 32-row group
   bp[0] = bp[1] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
 
-  // The multiplier of the P quantization -- the two-level 1/s1 and an E4M3 group
-  // scale's 1/s -- enters the exact exponential as an offset of its argument instead
-  // of a product per element: P~/s1 = 2^(lambda (S - tmax) + log2 2688), since s1 is
-  // the tile's largest P~ over 2688, and 1/s as -log2 s (the hardware logarithm, within
-  // 2^-20 of log2 s for every E4M3 value).  One FMA per element instead of an FMA and a
+  // The multiplier of the P quantization -- the two-level 1/s1, an E4M3 group scale's
+  // 1/s, FP8 P's 448 -- enters the exact exponential as an offset of its argument
+  // instead of a product per element: P~/s1 = 2^(lambda (S - tmax) + log2 2688), since
+  // s1 is the tile's largest P~ over 2688, 1/s as -log2 s (the hardware logarithm,
+  // within 2^-20 of log2 s for every E4M3 value), 448 P~ = 2^(lambda S - ms + log2 448).  One FMA per element instead of an FMA and a
   // product (two-level E8M0 at N = 32K 8%, packed documents 6% faster).
   constexpr bool PFOLD = PV == PV_BF16 && PSC != SCALE_E8M0;
-  constexpr bool LOGOFF = !EXPB && (PMODE == PM_TWO_LEVEL || PFOLD);
+  constexpr bool LOGOFF = !EXPB && (PMODE == PM_TWO_LEVEL || PFOLD || PV == PV_FP8);
   constexpr float LOG2_2688 = 0x1.6c8ddep+3f;  // log2(448 * 6) rounded to FP32
+  constexpr float LOG2_448 = 0x1.19d5dap+3f;   // log2(448): FP8 P = E4M3(448 P~)
 
   // P of sub-tile bb (16 keys per lane) from its scores in S[bb]: the exponentials, this
   // lane's share of the row sum (returned), and the quantized operand written in place
@@ -1070,8 +1071,9 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     } else if constexpr (PV == PV_FP8) {  // c = E4M3(448 P~): 4 dwords per sub-tile
 #pragma unroll
       for (int dw = 0; dw < 4; dw++) {
-        int x = __builtin_amdgcn_cvt_pk_fp8_f32(448.0f * y[4 * dw], 448.0f * y[4 * dw + 1], 0, false);
-        x = __builtin_amdgcn_cvt_pk_fp8_f32(448.0f * y[4 * dw + 2], 448.0f * y[4 * dw + 3], x, true);
+        constexpr float F = LOGOFF ? 1.0f : 448.0f;  // LOGOFF: y is 448 P~ already
+        int x = __builtin_amdgcn_cvt_pk_fp8_f32(F * y[4 * dw], F * y[4 * dw + 1], 0, false);
+        x = __builtin_amdgcn_cvt_pk_fp8_f32(F * y[4 * dw + 2], F * y[4 * dw + 3], x, true);
         bp[bb >> 1][4 * (bb & 1) + dw] = x;
       }
     } else {
@@ -1177,7 +1179,13 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
         }
       }
     }
-    if constexpr (LOGOFF && !PFOLD) {
+    if constexpr (LOGOFF && PV == PV_FP8) {  // 448 P~ = 2^(lambda S - ms + log2 448)
+#pragma unroll
+      for (int bb = 0; bb < 4; bb++) {
+        vp_cg[bb] = ms - LOG2_448;
+        vp_lk[bb] = 1.0f / 448.0f;
+      }
+    } else if constexpr (LOGOFF && !PFOLD) {
 #pragma unroll
       for (int bb = 0; bb < 4; bb++) {
         vp_cg[bb] = c1;
