@@ -39,7 +39,7 @@ TRAFFIC_FILES = {"c3": "profiles/fwd_pp_kernel_c3_video_dit_32k_traffic.txt",
 KERNEL_SOURCES = ["microscaling_fp4_attention_amd/csrc/fwd.hip", "microscaling_fp4_attention_amd/csrc/device_util.h",
                   "microscaling_fp4_attention_amd/csrc/formats.h", "microscaling_fp4_attention_amd/csrc/kernels.h"]
 # the same for the split-key decode at 128K keys (V tile-major), its main kernel
-DECODE_TRAFFIC_FILE = "profiles/decode_kernel_gqa_128k_traffic.txt"
+DECODE_TRAFFIC_FILE = "profiles/decode_kernel_gqa_128k.txt"
 DECODE_SOURCES = ["microscaling_fp4_attention_amd/csrc/decode.hip"] + KERNEL_SOURCES[1:]
 
 
