@@ -272,11 +272,13 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecArgs a) {
 
 // The QK4PV8 route ("MpFA", sections 4.1 and 5.3: NVFP4 Q and K, FP8 P and V): the
 // same split-key decode, 32 query columns at most, with
-//   * S^T = K Q^T on the bf16 MFMA after exact dequantization (an E2M1 value times an
-//     E4M3 block scale has at most 6 significant bits); the contraction slot j of lane
-//     half h in step s holds channel 64 h + 8 s + j, so a lane reads one contiguous
-//     half of each K row (32 code bytes) and its 4 block scales (one dword), and Q the
-//     same half (MXFP4 Q and K take the scaled FP4 MFMA instead);
+//   * S^T = K Q^T on the f16 MFMA after exact dequantization (an E2M1 value times an
+//     E4M3 block scale has at most 6 significant bits and lies in [2^-10, 2688]: exact
+//     in f16, formed by the FP4-to-f16 convert and one packed multiply per pair); the
+//     contraction slot j of lane half h in step s holds channel 64 h + 8 s + j, so a
+//     lane reads one contiguous half of each K row (32 code bytes) and its 4 block
+//     scales (one dword), and Q the same half (MXFP4 Q and K take the scaled FP4 MFMA
+//     instead);
 //   * P = E4M3(448 P~) (the oracle's FP8_FIXED), O^T = V^T P^T on the scaled FP8 MFMA
 //     with V's E8M0 scale per 32 keys and P's unit scale, the row sum from P~, and O
 //     divided by 448 with it; K rows are read in the FP8 operand's key order
@@ -302,7 +304,7 @@ __global__ __launch_bounds__(256, 2) void decode_q4p8_kernel(DecArgs a) {
   // Q operand (B operand of S^T = K Q^T); an absent column reads column 0's row
   v8i qop[2];
   uint32_t qsc = 0;
-  v8bf qbf[8];
+  v8h qh[8];
   {
     const int64_t qrow = (b * a.Hq + hq) * a.R + r;
     const uint8_t* qp = a.q + qrow * 64;
@@ -315,8 +317,10 @@ __global__ __launch_bounds__(256, 2) void decode_q4p8_kernel(DecArgs a) {
       const uint32_t sw = *reinterpret_cast<const uint32_t*>(a.qs + qrow * 8 + 4 * hh);
       const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
-      for (int s = 0; s < 8; s++)
-        qbf[s] = __builtin_bit_cast(v8bf, dq8_bf16(cw[s], e4m3_value((sw >> (8 * (s >> 1))) & 0xFFu)));
+      for (int s = 0; s < 8; s++) {
+        const _Float16 sh = (_Float16)e4m3_value((sw >> (8 * (s >> 1))) & 0xFFu);  // exact in f16
+        qh[s] = dq8_f16(cw[s], v2h{sh, sh});
+      }
     }
   }
   const uint8_t* kc = a.k + (b * a.Hkv + hk) * a.N * 64;
@@ -380,9 +384,10 @@ __global__ __launch_bounds__(256, 2) void decode_q4p8_kernel(DecArgs a) {
       } else {
         const uint32_t kw[8] = {k0[bb].x, k0[bb].y, k0[bb].z, k0[bb].w, k1[bb].x, k1[bb].y, k1[bb].z, k1[bb].w};
 #pragma unroll
-        for (int s = 0; s < 8; s++)
-          acc = mfma_bf16(__builtin_bit_cast(v8bf, dq8_bf16(kw[s], e4m3_value((ks[bb] >> (8 * (s >> 1))) & 0xFFu))),
-                          qbf[s], acc);
+        for (int s = 0; s < 8; s++) {
+          const _Float16 sk = (_Float16)e4m3_value((ks[bb] >> (8 * (s >> 1))) & 0xFFu);
+          acc = mfma_f16(dq8_f16(kw[s], v2h{sk, sk}), qh[s], acc);
+        }
       }
       S[bb] = acc;
     }
