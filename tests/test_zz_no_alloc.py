@@ -19,15 +19,16 @@ def _case(mx, torch, B, Hq, Hkv, R, N, kv_len, pm, seed):
         a = synth.f32_to_bf16(synth.gaussian(seed, k, shape).astype(np.float32))
         return torch.from_numpy(a.astype(np.int16)).view(torch.bfloat16).to(dev)
 
-    Q = mx.quantize(bf((B, Hq, R, 128), 1), mx.ROLE_QK, "mxfp4")
-    K = mx.quantize(bf((B, Hkv, N, 128), 2), mx.ROLE_QK, "mxfp4")
-    V = mx.quantize(bf((B, Hkv, N, 128), 3), mx.ROLE_VT, "mxfp4")
+    qkf, vf, pf = ("nvfp4", "fp8v", None) if pm == "fp8" else ("mxfp4", "mxfp4", "mxfp4")  # fp8: QK4PV8
+    Q = mx.quantize(bf((B, Hq, R, 128), 1), mx.ROLE_QK, qkf)
+    K = mx.quantize(bf((B, Hkv, N, 128), 2), mx.ROLE_QK, qkf)
+    V = mx.quantize(bf((B, Hkv, N, 128), 3), mx.ROLE_VT, vf)
     kl = torch.tensor(kv_len, dtype=torch.int32, device=dev)
-    p = mx.fwd_params(pm, "mxfp4", causal=True, out_fp32=True)
+    p = mx.fwd_params(pm, pf, causal=True, out_fp32=True)
     return Q, K, V, kl, p
 
 
-@pytest.mark.parametrize("pm", ["pnq", "two_level"])
+@pytest.mark.parametrize("pm", ["pnq", "two_level", "fp8"])
 def test_decode_noalloc_equals_decode(pm):
     import torch
     import microscaling_fp4_attention_amd as mx
