@@ -709,13 +709,11 @@ struct PpLds {
   static constexpr int KSC = BOFF + (BIAS ? 512 : 0);
   static constexpr int VSC = KSC + (QK == QK_FP4 ? 1024 : 0);
   static constexpr int STAGE = VSC + (PV == PV_BF16 ? 0 : 1024);
-  // after the 3 stages, with causally safe V scales: the per-key form of the two
-  // diagonal tiles of the workgroup (128 channel rows of 80 bytes, E2M1 codes, then
-  // the 128 per-key E8M0 bytes in key order)
-  static constexpr int KEYR = 3 * STAGE;
-  static constexpr int KEYX = 128 * 80;
-  static constexpr int KEYT = KEYX + 128;
-  static constexpr int BYTES = KEYR + (SAFE ? 2 * KEYT : 0);
+  // after the 3 stages, with causally safe V scales: the per-key E8M0 bytes of the
+  // workgroup's two diagonal key tiles, 128 per tile in key order (their E2M1 codes
+  // come through the stages)
+  static constexpr int KEYX = 3 * STAGE;
+  static constexpr int BYTES = KEYX + (SAFE ? 256 : 0);
 };
 
 template <int QK, int PV, int PMODE, int PSC, bool BIAS, bool SAFE, bool EXPB>
@@ -849,6 +847,10 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   const uint32_t np = (uint32_t)a.np, vrow_bytes = PV == PV_FP8 ? np : np / 2;
   const uint32_t nvb = np / 32;  // V scale blocks per channel row
   const uint8_t* hv_codes = a.v + vrow0 * vrow_bytes;
+  // causally safe V: the workgroup's two diagonal key tiles, 2 qt and 2 qt + 1, are
+  // staged from the per-key form (E2M1 codes in the same channel-row layout, unit
+  // block scales); its per-key exponents go into P in the V phase
+  const uint8_t* hvk_codes = SAFE ? a.vk + vrow0 * vrow_bytes : nullptr;
   const uint8_t* hv_sbase = a.vs + vrow0 * nvb;
   const uint32_t vblk0 = (uint32_t)(vstart >> 5) & ~3u, vsh = (uint32_t)(vstart >> 5) & 3u;
   const uint32_t o_v = (uint32_t)kr * vrow_bytes, o_vs = (uint32_t)sr * nvb + vblk0;
@@ -938,6 +940,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       rks = *reinterpret_cast<const uint16_t*>(hk_scales + ((uint32_t)key * 8 + 2 * part));
     }
     const uint32_t key0 = (uint32_t)vstart + (uint32_t)t * 128;  // first padded key slot (< np)
+    const bool pk = SAFE && (t >> 1) == (int)qt;                  // per-key form (wave-uniform)
     if constexpr (PV == PV_FP8) {  // two chunks of 16 keys: parts gt%4 and gt%4 + 4
       const uint32_t k1 = __builtin_elementwise_min(key0 + 16 * part, np - 16);
       const uint32_t k2 = __builtin_elementwise_min(key0 + 16 * (part + 4), np - 16);
@@ -945,11 +948,11 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       rv1 = *reinterpret_cast<const u4*>(hv_codes + (o_v + k2));
     } else {
       const uint32_t k1 = __builtin_elementwise_min(key0 + 32 * part, np - 32);
-      rv0 = *reinterpret_cast<const u4*>(hv_codes + (o_v + k1 / 2));
+      rv0 = *reinterpret_cast<const u4*>((pk ? hvk_codes : hv_codes) + (o_v + k1 / 2));
     }
     if constexpr (PV == PV_BF16) {  // the chunk's own block scale
       const uint32_t blk = __builtin_elementwise_min((key0 + 32 * part) / 32, nvb - 1);
-      rvs = hv_sbase[(uint32_t)kr * nvb + blk];
+      rvs = pk ? 127u : (uint32_t)hv_sbase[(uint32_t)kr * nvb + blk];
     } else if (gt >= 64 && gt < 128) {  // a channel's 4 block scales (wave-uniform)
       // the group of 4 after the tile's first one lies past the row only when the
       // tile's keys do (vblk0 + 4t <= nvb - 4 since key0 < np and nvb % 4 == 0)
@@ -957,6 +960,10 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       const uint32_t hi = vblk0 + 4 * (uint32_t)t + 4 < nvb ? lo + 4 : lo;
       rvs = *reinterpret_cast<const uint32_t*>(hv_sbase + lo);
       rvs_hi = *reinterpret_cast<const uint32_t*>(hv_sbase + hi);
+      if constexpr (SAFE) {  // unit scales on the per-key tiles
+        rvs = pk ? 0x7F7F7F7Fu : rvs;
+        rvs_hi = pk ? 0x7F7F7F7Fu : rvs_hi;
+      }
     }
   };
   auto store_half = [&](uint32_t so) __attribute__((always_inline)) {
@@ -1015,9 +1022,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
 
   // ---------------- state ----------------
   float m = NEG_INF, lpart = 0.0f, s1prev = 1.0f;
-  float lfix = 0.0f;  // PNQ with causally safe V: this lane's share of the folded tile's row sum
-  // causally safe V: the key tile holding this group's rows (256-row query tile qt)
-  const int tdiag = SAFE ? 2 * (int)qt + grp : -1;
+  float lfix = 0.0f;  // PNQ with causally safe V: this lane's share of the folded tiles' row sum
   v16f O[4], Lacc, S[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) O[i] = zero16();
@@ -1208,16 +1213,15 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   // its mask and maxima
   auto phase_m = [&](int t, uint32_t sk, uint32_t sv, bool can_fold) __attribute__((always_inline)) {
     if (t >= 1) {
-      // the folded tile takes the per-key form of V (unit block scales)
-      const bool fold = SAFE && can_fold && t - 1 == tdiag;
+      // a folded tile (a diagonal tile under causally safe V) is staged in the per-key
+      // form of V, with unit block scales
+      const bool fold = SAFE && can_fold && ((t - 1) >> 1) == (int)qt;
       const uint8_t* Vs = smem + sv + KV;
       if constexpr (PV == PV_FP4) {
-        const uint8_t* Vr = fold ? smem + L::KEYR + grp * L::KEYT : Vs;
 #pragma unroll
         for (int db = 0; db < 4; db++) {
-          const uint8_t* rp = Vr + (32 * db + ql) * 80;
-          uint32_t vs4 = *reinterpret_cast<const uint32_t*>(smem + sv + L::VSC + 128 * db + soff);
-          if constexpr (SAFE) vs4 = fold ? 0x7F7F7F7Fu : vs4;
+          const uint8_t* rp = Vs + (32 * db + ql) * 80;
+          const uint32_t vs4 = *reinterpret_cast<const uint32_t*>(smem + sv + L::VSC + 128 * db + soff);
           v8i a0 = v8_from4(*reinterpret_cast<const u4*>(rp + 16 * hh));
           v8i a1 = v8_from4(*reinterpret_cast<const u4*>(rp + 32 + 16 * hh));
           O[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, bp[0], O[db], 4, 4, 0, (int)vs4, 0, (int)pscw);
@@ -1274,28 +1278,14 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
           const int bb = 2 * (s >> 2) + ((s & 3) >> 1);
           pb[s] = __builtin_bit_cast(v8bf, dq8_bf16(pc[2 * bb + ((s & 3) & 1)], pdq[bb]));
         }
-        if (SAFE && fold) {  // per-key E2M1 codes, dequantized (unit scale) on the fly
-          const uint8_t* Kr = smem + L::KEYR + grp * L::KEYT;
 #pragma unroll
-          for (int db = 0; db < 4; db++) {
-            const uint8_t* rp = Kr + (32 * db + ql) * 80;
+        for (int db = 0; db < 4; db++) {
+          const uint8_t* rp = Vs + (32 * db + ql) * 256;
 #pragma unroll
-            for (int s = 0; s < 8; s++) {
-              const int lc = 8 * (s >> 2) + 4 * hh + (s & 3);  // keys 8 lc + [0, 8)
-              v8bf av = __builtin_bit_cast(v8bf, dq8_bf16(*reinterpret_cast<const uint32_t*>(rp + 4 * lc), 1.0f));
-              O[db] = mfma_bf16(av, pb[s], O[db]);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int db = 0; db < 4; db++) {
-            const uint8_t* rp = Vs + (32 * db + ql) * 256;
-#pragma unroll
-            for (int s = 0; s < 8; s++) {
-              const int chunk = (8 * (s >> 2) + 4 * hh + (s & 3)) ^ (ql & 15);
-              v8bf av = *reinterpret_cast<const v8bf*>(rp + chunk * 16);
-              O[db] = mfma_bf16(av, pb[s], O[db]);
-            }
+          for (int s = 0; s < 8; s++) {
+            const int chunk = (8 * (s >> 2) + 4 * hh + (s & 3)) ^ (ql & 15);
+            v8bf av = *reinterpret_cast<const v8bf*>(rp + chunk * 16);
+            O[db] = mfma_bf16(av, pb[s], O[db]);
           }
         }
       }
@@ -1348,7 +1338,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
         bm16[bb] = fmaxn(y0, y1);
       }
       tmax = halves_max(fmaxn(fmaxn(bm16[0], bm16[1]), fmaxn(bm16[2], bm16[3])));
-      if (PRE_IN_M && !(SAFE && can_fold && t == tdiag)) phase_v_pre();
+      if (PRE_IN_M && !(SAFE && can_fold)) phase_v_pre();
     }
   };
 
@@ -1368,10 +1358,13 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     if constexpr (PMODE != PM_PNQ || PV != PV_FP4) lpart = vp_alpha * lpart + lsum;
   };
 
-  // V phase of the group's diagonal tile with causally safe V scales ("FLAMIA" section
-  // 3.2): P'_j = P~_j 2^e_j with the key's per-key exponent (exact ldexp), quantized as
-  // P is; block maxima and the two-level row maximum come from the P' values.  The row
-  // sum takes P~ (DIRECT, TWO_LEVEL) or deq(P^'_j) 2^-e_j (PNQ).
+  // V phase of a diagonal tile with causally safe V scales ("FLAMIA" section 3.2): the
+  // causal boundary of the 256-row query tile qt runs through key tiles 2 qt and
+  // 2 qt + 1, which are staged in the per-key form of V.  P'_j = P~_j 2^e_j with the
+  // key's per-key exponent (exact ldexp), quantized as P is; block maxima and the
+  // two-level row maximum come from the P' values.  The row sum takes P~ (DIRECT,
+  // TWO_LEVEL) or deq(P^'_j) 2^-e_j (PNQ).  (Group A's rows see no key of tile
+  // 2 qt + 1: there every P' is 0.)
   auto phase_v_fold = [&](int t) __attribute__((always_inline)) {
     const float mnew = fmaxn(m, tmax);
     const float ms = mnew == NEG_INF ? 0.0f : mnew * lam;
@@ -1379,7 +1372,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     const float cm = pexp_c(ms);
     const float alpha = m == mnew ? 1.0f : exp2_diff(m, mnew, lam);
     m = mnew;
-    const uint8_t* kx = smem + L::KEYR + grp * L::KEYT + L::KEYX;  // per-key bytes, key order
+    const uint8_t* kx = smem + L::KEYX + 128 * (t - 2 * (int)qt);  // per-key bytes, key order
     // exponent of the lane's key j of sub-tile bb (re-read where needed, not held)
     auto kexp = [&](int bb, int j) __attribute__((always_inline)) -> int {
       return (int)kx[key_of<false>(bb, hh, 0) + j] - 127;
@@ -1494,22 +1487,12 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   // Stage offsets rotate through 0, STAGE, 2 STAGE as scalars: sk holds tile t, sv
   // tile t-1, ss the tile this group stores next (t+1+grp).
   if constexpr (SAFE) {
-    // the per-key form of key tiles 2 qt and 2 qt + 1 (the groups' diagonal tiles):
-    // 512 threads copy the 128 x 64 code bytes of a tile, 32 of them its 128 exponents
-    const uint8_t* hvk = a.vk + vrow0 * (int64_t)(np / 2);
-    const uint8_t* hvks = a.vks + (b * a.Hkv + hk) * (int64_t)np;
-    const int row = tid >> 2, part = tid & 3;
-#pragma unroll
-    for (int g = 0; g < 2; g++) {
-      const uint32_t ks0 = (uint32_t)vstart + 128u * (uint32_t)(2 * qt + g);
-      const uint32_t k1 = __builtin_elementwise_min(ks0 + 32u * part, np - 32);
-      const u4 c = *reinterpret_cast<const u4*>(hvk + ((uint32_t)row * (np / 2) + k1 / 2));
-      *reinterpret_cast<u4*>(smem + L::KEYR + g * L::KEYT + row * 80 + part * 16) = c;
-      if (tid < 32) {
-        const uint32_t s0 = __builtin_elementwise_min(ks0 + 4u * tid, np - 4);
-        *reinterpret_cast<uint32_t*>(smem + L::KEYR + g * L::KEYT + L::KEYX + 4 * tid) =
-            *reinterpret_cast<const uint32_t*>(hvks + s0);
-      }
+    // the per-key exponents of key tiles 2 qt and 2 qt + 1, 256 bytes in key order
+    // (dwords past the padded row repeat its last one: those keys are masked)
+    if (tid < 64) {
+      const uint8_t* hvks = a.vks + (b * a.Hkv + hk) * (int64_t)np;
+      const uint32_t s0 = __builtin_elementwise_min((uint32_t)vstart + 256u * (uint32_t)qt + 4u * tid, np - 4);
+      *reinterpret_cast<uint32_t*>(smem + L::KEYX + 4 * tid) = *reinterpret_cast<const uint32_t*>(hvks + s0);
     }
   }
   load_half(0);
@@ -1523,8 +1506,9 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   if (grp == 1) __syncthreads();
   auto rot = [](uint32_t o) { return o == 2 * STAGE ? 0u : o + STAGE; };
   uint32_t sk = 0, sv = 2 * STAGE, ss = grp == 0 ? STAGE : 2 * STAGE;
-  // one M phase and one V phase; can_fold (a constant at each call) compiles the
-  // per-key fold in, which only the group's diagonal tile 2 qt + grp needs
+  // one M phase and one V phase; can_fold (a constant at each call) selects the
+  // per-key fold, which the diagonal tiles 2 qt and 2 qt + 1 take: their V phases are
+  // all fold phases, and the M phase that follows each skips the matrix-core row sum
   // Issue priority: the SIMD issues the older wave first, so a phase of the younger
   // group waits behind the co-resident wave's stream.  Where one phase's stream is the
   // one that holds up the pair, it runs at raised priority (s_setprio): the M phase
@@ -1551,7 +1535,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
         load_half(nt < nkt ? nt : nkt - 1);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (SAFE && can_fold && t == tdiag) phase_v_fold(t);
+      if (SAFE && can_fold) phase_v_fold(t);
       else phase_v(t);
       if constexpr (VPRIO) __builtin_amdgcn_s_setprio(0);
       if constexpr (!STAGE_FIRST) {

@@ -32,7 +32,7 @@ class Fmt(ctypes.Structure):
 class AttnParams(ctypes.Structure):
     _fields_ = [("pmode", ctypes.c_int), ("pfmt", Fmt), ("causal", ctypes.c_int),
                 ("sm_scale", ctypes.c_float), ("kv_tile", ctypes.c_int), ("exp_mode", ctypes.c_int),
-                ("score_rounds", ctypes.c_int)]
+                ("score_rounds", ctypes.c_int), ("q_tile", ctypes.c_int)]
 
 
 # named formats (the presets of the pages)
@@ -208,12 +208,13 @@ def dequant_cols(codes, scales, f, doc_off=None):
 
 
 def attention(Q, K, V, pmode, pfmt=None, causal=False, sm_scale=None, kv_tile=128, doc_off=None,
-              rows=None, bias=None, vkey=None, vkey_exp=None, exp_mode="exact", score_rounds=2):
+              rows=None, bias=None, vkey=None, vkey_exp=None, exp_mode="exact", score_rounds=2, q_tile=256):
     """Q [B,Hq,N,d], K/V [B,Hkv,N,d] float32 (dequantized); bias: None or float32 [B,Hq,N]
     added to each key's scores; vkey [B,Hkv,N,d] / vkey_exp [B,Hkv,N]: the per-key form
-    of V used on each row's diagonal tile (causal only); exp_mode: "exact", "mitchell"
-    or "schraudolph" (the exponential of P~); score_rounds: FP32 roundings in the score
-    sums of the implementation under test (flip-budget window only).
+    of V used on each row's diagonal tiles (causal only): the key tiles that start inside
+    the row's query tile of q_tile rows; exp_mode: "exact", "mitchell" or "schraudolph"
+    (the exponential of P~); score_rounds: FP32 roundings in the score sums of the
+    implementation under test (flip-budget window only).
     Returns (O [nrows,d], lse, fb)."""
     Q = np.ascontiguousarray(Q, dtype=np.float32)
     K = np.ascontiguousarray(K, dtype=np.float32)
@@ -223,7 +224,8 @@ def attention(Q, K, V, pmode, pfmt=None, causal=False, sm_scale=None, kv_tile=12
     if sm_scale is None:
         sm_scale = 1.0 / np.sqrt(d)
     pf = fmt(pfmt) if pfmt is not None else Fmt(0, 0, 32, 0, 0.0)
-    p = AttnParams(pmode, pf, int(bool(causal)), float(sm_scale), kv_tile, EXP_MODES[exp_mode], score_rounds)
+    p = AttnParams(pmode, pf, int(bool(causal)), float(sm_scale), kv_tile, EXP_MODES[exp_mode], score_rounds,
+                   q_tile)
     r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
     nrows = B * Hq * N if r is None else len(r)
     O = np.zeros((nrows, d), dtype=np.float32)

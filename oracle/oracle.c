@@ -411,7 +411,7 @@ static float p_exp(const orc_attn_params* p, double x) {
 /* ascending order; P blocks are consecutive keys aligned to the tile.     */
 /* ------------------------------------------------------------------------ */
 static int attn_row_bias(const float* q, const float* K, const float* V, const float* sbias,
-                         const float* Vk, const int* ek, int diag_t0, int nk, int vis, int d,
+                         const float* Vk, const int* ek, int diag_lo, int nk, int vis, int d,
                          const orc_attn_params* p, float* o, float* lse, double* fb);
 
 int orc_attn_row(const float* q, const float* K, const float* V, int nk, int vis, int d,
@@ -421,16 +421,18 @@ int orc_attn_row(const float* q, const float* K, const float* V, int nk, int vis
 
 /* sbias: NULL, or the score bias of keys 0..nk-1 of this range ([MPFA] Eq. 10: added
  * to the exact dot product before the mask and the running maximum).
- * Vk, ek, diag_t0: causally safe V scales ([FLAMIA] section 3.2): on the tile that
- * starts at key diag_t0 the row uses the per-key form of V -- E2M1 values Vk[j][c]
- * with unit scale and a power-of-two scale 2^ek[j] per key -- and folds that scale
- * into P, P'_j = P~_j * 2^ek[j] (exact float ldexp), which is then quantized as P
- * normally is; O takes P^' Vk, and the PNQ row sum takes deq(P^'_j) 2^-ek[j].
+ * Vk, ek, diag_lo: causally safe V scales ([FLAMIA] section 3.2): on the tiles that
+ * start at keys diag_lo .. diag_lo + q_tile - 1 (the row's diagonal tiles) the row
+ * uses the per-key form of V -- E2M1 values Vk[j][c] with unit scale and a
+ * power-of-two scale 2^ek[j] per key -- and folds that scale into P,
+ * P'_j = P~_j * 2^ek[j] (exact float ldexp), which is then quantized as P normally
+ * is; O takes P^' Vk, and the PNQ row sum takes deq(P^'_j) 2^-ek[j].
  * Vk == NULL: no tile uses the per-key form. */
 static int attn_row_bias(const float* q, const float* K, const float* V, const float* sbias,
-                         const float* Vk, const int* ek, int diag_t0, int nk, int vis, int d,
+                         const float* Vk, const int* ek, int diag_lo, int nk, int vis, int d,
                          const orc_attn_params* p, float* o, float* lse, double* fb) {
   int T = p->kv_tile;
+  const int QT = p->q_tile > 0 ? p->q_tile : T;
   float m = -INFINITY, l = 0.0f;
   float* acc = (float*)calloc((size_t)d, sizeof(float));
   float* s = (float*)malloc(sizeof(float) * (size_t)T);
@@ -523,7 +525,7 @@ static int attn_row_bias(const float* q, const float* K, const float* V, const f
       }
     }
     /* per-key fold of the diagonal tile: the quantizer sees P' = P~ 2^ek */
-    const int fold = Vk != NULL && t0 == diag_t0;
+    const int fold = Vk != NULL && t0 >= diag_lo && t0 < diag_lo + QT;
     float* pq = pt;
     if (fold) {
       for (int j = 0; j < tl; j++) x2[j] = ldexpf(pt[j], ek[t0 + j]);
@@ -656,7 +658,9 @@ int orc_attention_ex(const float* Q, const float* K, const float* V, const float
                      const orc_attn_params* p, const int64_t* rows, int64_t nrows, float* O, float* lse,
                      double* fb) {
   int64_t total = (int64_t)B * Hq * N;
+  const int QT = p->q_tile > 0 ? p->q_tile : p->kv_tile;
   if (Vk && !p->causal) return -3; /* the per-key form serves causal diagonal tiles */
+  if (Vk && QT % p->kv_tile != 0) return -5;
   if (p->exp_mode < ORC_EXP_EXACT || p->exp_mode > ORC_EXP_SCHRAUDOLPH) return -4;
   if (!rows) nrows = total;
   if (doc_off && ndocs > 0 && B != 1) return -1;
@@ -681,8 +685,9 @@ int orc_attention_ex(const float* Q, const float* K, const float* V, const float
     vis = p->causal ? (i - ks + 1) : nk;
     const float* vkb = Vk ? Vk + ((b * Hkv + hk) * (int64_t)N + ks) * d : NULL;
     const int* ekb = ek ? ek + (b * Hkv + hk) * (int64_t)N + ks : NULL;
-    /* the row's diagonal tile: the kv_tile keys from kv_tile * floor((i - ks) / kv_tile) */
-    int diag = Vk ? ((i - ks) / p->kv_tile) * p->kv_tile : -1;
+    /* the row's diagonal tiles: those starting in its query tile's rows,
+     * [QT floor((i - ks) / QT), + QT) */
+    int diag = Vk ? ((i - ks) / QT) * QT : -1;
     attn_row_bias(Q + r * d, kb + (int64_t)ks * d, vb + (int64_t)ks * d,
                   bias ? bias + (b * Hq + h) * (int64_t)N + ks : NULL, vkb, ekb, diag, nk, vis, d, p,
                   O + idx * d, lse ? lse + idx : NULL, fb ? fb + idx : NULL);

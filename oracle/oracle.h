@@ -77,6 +77,9 @@ typedef struct {
                   /* factor between tiles stays exact)              */
   int score_rounds; /* flip budget only: FP32 roundings in the score   */
                   /* sums of the implementation under test (0: 2)   */
+  int q_tile;     /* query rows per tile, from the sequence or      */
+                  /* document start (0: kv_tile); with the per-key  */
+                  /* V form it fixes a row's diagonal tiles         */
 } orc_attn_params;
 
 /* ---- bit-level exponentials ([FLAMIA] section 3.7, appendix C) ----
@@ -147,11 +150,14 @@ int orc_attention_bias(const float* Q, const float* K, const float* V, const flo
 
 /* As orc_attention_bias, plus the causally safe form of a 4-bit V ([FLAMIA] section
  * 3.2): Vk [B][Hkv][N][d] holds the E2M1 values of V's per-key form (unit scale)
- * and ek [B][Hkv][N] its per-key exponents (orc_quantize_keys).  On each row's
- * diagonal tile -- the kv_tile keys from kv_tile * floor((i - start) / kv_tile) of
- * its sequence or document -- P~_j is multiplied by 2^ek[j] before it is quantized
- * and multiplies Vk; every other tile uses V.  Requires a causal mask (returns -3
- * otherwise); Vk/ek NULL: as orc_attention_bias. */
+ * and ek [B][Hkv][N] its per-key exponents (orc_quantize_keys).  Queries are taken
+ * in tiles of q_tile rows from the start of their sequence or document; the causal
+ * boundary of a query tile runs through the key tiles that start inside its rows'
+ * span, [q_tile floor((i - start) / q_tile), + q_tile) -- the row's diagonal tiles.
+ * On them P~_j is multiplied by 2^ek[j] before it is quantized and multiplies Vk;
+ * every other tile uses V.  Requires a causal mask (returns -3 otherwise) and a
+ * q_tile that is a multiple of kv_tile (returns -5); Vk/ek NULL: as
+ * orc_attention_bias. */
 int orc_attention_ex(const float* Q, const float* K, const float* V, const float* bias, const float* Vk,
                      const int* ek, int B, int Hq, int Hkv, int N, int d, const int* doc_off, int ndocs,
                      const orc_attn_params* p, const int64_t* rows, int64_t nrows, float* O, float* lse,

@@ -82,3 +82,32 @@ def test_fold_requires_causal(orc):
     with pytest.raises(ValueError):
         orc.attention(q, k, v, orc.P_DIRECT, "mxfp4", causal=False, vkey=orc.e2m1_values(kc)[None, None],
                       vkey_exp=ek[None, None])
+
+
+def test_diagonal_tiles_are_the_query_tiles(orc):
+    """The per-key form covers exactly the key tiles that start inside a row's query
+    tile.  A different grouped V on keys 0..255 then reaches no row of the first query
+    tile and every row after it: with 256-row query tiles rows 0..255 never read the
+    grouped V below key 256; with 128-row query tiles rows 128..255 read it on key
+    tile 0."""
+    q, k, v = _case(34, N=600)
+    vc, vs = orc.quantize_cols(v[0, 0], "mxfp4")
+    vd = orc.dequant_cols(vc, vs, "mxfp4")[None, None]
+    kc, ek = orc.quantize_keys(v[0, 0], "mxfp4")
+    kw = dict(vkey=orc.e2m1_values(kc)[None, None], vkey_exp=ek[None, None])
+    vd2 = vd.copy()
+    vd2[..., :256, :] = -3.0 * vd2[..., :256, :] + 0.5
+    for qt in (256, 128):
+        a = orc.attention(q, k, vd, orc.P_DIRECT, "mxfp4", causal=True, q_tile=qt, **kw)[0]
+        b = orc.attention(q, k, vd2, orc.P_DIRECT, "mxfp4", causal=True, q_tile=qt, **kw)[0]
+        same = np.all(a == b, axis=1)
+        assert same[:qt].all(), qt
+        assert not same[qt:].any(), qt
+
+
+def test_query_tile_must_hold_whole_key_tiles(orc):
+    q, k, v = _case(35, N=64)
+    kc, ek = orc.quantize_keys(v[0, 0], "mxfp4")
+    with pytest.raises(ValueError):
+        orc.attention(q, k, v, orc.P_DIRECT, "mxfp4", causal=True, q_tile=192, vkey=orc.e2m1_values(kc)[None, None],
+                      vkey_exp=ek[None, None])
