@@ -100,18 +100,19 @@ CONFIGS = {
 }
 
 
-def route_peak(qf, vf, pm, pf, causal_safe=False):
+def route_peak(qf, vf, pm, pf):
     """MFMA types of the forward's two products and their combined dense peak (TFLOP/s):
     MXFP4 Q/K run on the FP4 MFMA, NVFP4 Q/K on bf16 after exact dequantization; PV runs
     on FP8 for FP8 P, on FP4 for E8M0-scaled P with an MXFP4 V, on f16 for other P with an
-    MXFP4 V (V's channels shifted into f16 range), on bf16 otherwise (same peak as f16)"""
+    MXFP4 V (V's channels shifted into f16 range; under causally safe V the two diagonal
+    key tiles of each query tile take bf16 products, at the same peak), on bf16 otherwise"""
     qk = ("fp4", FP4_PEAK_TFLOPS) if qf.startswith("mxfp4") else ("bf16", BF16_PEAK_TFLOPS)
     if pm == "fp8":
         pv = ("fp8", FP8_PEAK_TFLOPS)
     elif pf is not None and pf.startswith("mxfp4") and vf.startswith("mxfp4"):
         pv = ("fp4", FP4_PEAK_TFLOPS)
     else:
-        pv = ("f16" if vf.startswith("mxfp4") and not causal_safe else "bf16", BF16_PEAK_TFLOPS)
+        pv = ("f16" if vf.startswith("mxfp4") else "bf16", BF16_PEAK_TFLOPS)
     return f"QK {qk[0]}, PV {pv[0]}", 1.0 / (0.5 / qk[1] + 0.5 / pv[1])
 
 
@@ -420,7 +421,7 @@ def main():
     log(f"[bench] step {t_step * 1e3:.3f} ms (wall {wall / args.steps * 1e3:.3f} ms), fwd {t_fwd * 1e3:.3f} ms")
 
     flop = counted_flop(B, Hq, N, 128, causal, doc_off)
-    route, rpeak = route_peak(qf, vf, pm, pf, args.causal_safe)
+    route, rpeak = route_peak(qf, vf, pm, pf)
     tops = flop / t_step / 1e12
     fwd_tflops = flop / t_fwd / 1e12
     peak = FP4_PEAK_TFLOPS

@@ -713,7 +713,9 @@ struct PpLds {
   // workgroup's two diagonal key tiles, 128 per tile in key order (their E2M1 codes
   // come through the stages)
   static constexpr int KEYX = 3 * STAGE;
-  static constexpr int BYTES = KEYX + (SAFE ? 256 : 0);
+  // then, with causally safe V, the Q operand rows (80-byte rows, 256 query rows)
+  static constexpr int QOFF = KEYX + 256;
+  static constexpr int BYTES = KEYX + (SAFE ? 256 + (QK == QK_FP4 ? 256 * 80 : 0) : 0);
 };
 
 template <int QK, int PV, int PMODE, int PSC, bool BIAS, bool SAFE, bool EXPB>
@@ -724,8 +726,9 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[L::BYTES];
   constexpr int STAGE = L::STAGE, KV = L::KV;
   constexpr bool SPLIT16 = PV == PV_FP8;
-  // E4M3-scaled P with MXFP4 V: the PV product in f16 (the per-key V form keeps bf16)
-  constexpr bool H16 = PV == PV_BF16 && !SAFE;
+  // E4M3-scaled P with MXFP4 V: the PV product in f16 (a tile staged from the per-key
+  // form of V takes bf16 products on the same accumulator)
+  constexpr bool H16 = PV == PV_BF16;
   const int tid = threadIdx.x, lane = tid & 63, ql = lane & 31, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int grp = wave >> 2;  // 0: group A, 1: group B
@@ -821,6 +824,10 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     qsc = *reinterpret_cast<const uint32_t*>(a.qs + qrow * 4) >> (8 * hh);
     qop[0] = v8_from4(*reinterpret_cast<const u4*>(qp + 16 * hh));
     qop[1] = v8_from4(*reinterpret_cast<const u4*>(qp + 32 + 16 * hh));
+    if constexpr (SAFE) {  // kept in LDS instead (the registers go to the per-key steps)
+      *reinterpret_cast<u4*>(smem + L::QOFF + (32 * wave + ql) * 80 + 16 * hh) = mk4(qop[0][0], qop[0][1], qop[0][2], qop[0][3]);
+      *reinterpret_cast<u4*>(smem + L::QOFF + (32 * wave + ql) * 80 + 32 + 16 * hh) = mk4(qop[1][0], qop[1][1], qop[1][2], qop[1][3]);
+    }
   } else {
     const uint8_t* qp = a.q + qrow * 64;
     u2 s8 = *reinterpret_cast<const u2*>(a.qs + qrow * 8);
@@ -859,6 +866,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   const int bkey = 64 * grp + (gt & 63);
   u4 rk, rv0, rv1;
   uint32_t rks = 0, rvs = 0, rvs_hi = 0;
+  bool rpk = false;  // the staged tile comes from the per-key form
   float rb = 0.0f;
   // f16 PV: each channel row c of V is staged as V 2^vshift_c, which places the largest
   // E8M0 exponent among the row's blocks this workgroup reads at 13 (6 2^13 < 65504).
@@ -872,7 +880,15 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   // block lies more than 36 binades below it, the zero blocks are told apart by their
   // codes and left out.
   int vshift = 0;
+  // causally safe V on the f16 route: the per-key tiles' P operand carries 2^sigma and
+  // their V 2^(vshift - sigma) in bf16, sigma = max(0, largest vshift - 125), so every
+  // staged value stays below 2^128 (a bf16 E2M1 value with 2 significant bits is exact
+  // down to 2^-133; vshift - sigma >= -127 for bf16 inputs, whose E8M0 block exponents
+  // stay at or below 125) and P^' 2^sigma <= 2688 2^15
+  int psig = 0;
+  float psig_f = 1.0f, pks = 1.0f;
   __shared__ int vshift_lds[H16 ? 128 : 1];
+  __shared__ int vsh_wmax[H16 && SAFE ? 8 : 1];
   if constexpr (H16) {
     const uint32_t b0 = (uint32_t)(vstart >> 5);
     const uint32_t bk = (uint32_t)((vstart + klen + 31) >> 5);       // past the range's keys
@@ -921,6 +937,21 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     }
     vshift = 140 - (int)mx;  // biased byte mx -> exponent 13
     if ((tid & 3) == 0) vshift_lds[row] = vshift;
+    if constexpr (SAFE) {
+      int w = vshift;  // the same in the 4 lanes of a row
+      w = __builtin_elementwise_max(w, __shfl_xor(w, 4));
+      w = __builtin_elementwise_max(w, __shfl_xor(w, 8));
+      w = __builtin_elementwise_max(w, __shfl_xor(w, 16));
+      w = __builtin_elementwise_max(w, __shfl_xor(w, 32));
+      if (lane == 0) vsh_wmax[wave] = w;
+      __syncthreads();
+      int mxs = vsh_wmax[0];
+#pragma unroll
+      for (int i = 1; i < 8; i++) mxs = __builtin_elementwise_max(mxs, vsh_wmax[i]);
+      psig = mxs > 125 ? mxs - 125 : 0;
+      psig_f = __builtin_ldexpf(1.0f, psig);
+      pks = __builtin_ldexpf(1.0f, vshift - psig);
+    }
   }
   auto load_half = [&](int t) __attribute__((always_inline)) {
     if constexpr (BIAS) {
@@ -941,6 +972,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     }
     const uint32_t key0 = (uint32_t)vstart + (uint32_t)t * 128;  // first padded key slot (< np)
     const bool pk = SAFE && (t >> 1) == (int)qt;                  // per-key form (wave-uniform)
+    if constexpr (SAFE) rpk = pk;
     if constexpr (PV == PV_FP8) {  // two chunks of 16 keys: parts gt%4 and gt%4 + 4
       const uint32_t k1 = __builtin_elementwise_min(key0 + 16 * part, np - 16);
       const uint32_t k2 = __builtin_elementwise_min(key0 + 16 * (part + 4), np - 16);
@@ -1001,22 +1033,22 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
         *reinterpret_cast<uint32_t*>(base + L::VSC + 4 * sr) = w;
         *reinterpret_cast<uint32_t*>(base + L::VSC + 512 + 4 * sr) = w >> 8;
       }
-    } else if constexpr (H16) {  // f16 row of 128 keys (V 2^vshift), chunk = key / 8, swizzled
-      // scale 2^(e + vshift) as the convert's operand: biased exponent byte + vshift
-      // (140 at most inside the scanned blocks, clamped there outside them); blocks more
-      // than 139 binades below the largest become 0
-      const int be = __builtin_elementwise_min((int)rvs + vshift, 140);
-      const float sc = u2f((uint32_t)(be > 1 ? be : 1) << 23);
+    } else {  // a row of 128 keys of 2-byte values, chunk = key / 8, swizzled by the channel
       const uint32_t w4[4] = {rv0.x, rv0.y, rv0.z, rv0.w};
+      if (SAFE && rpk) {  // per-key form: bf16 Vk 2^(vshift - sigma), exact
 #pragma unroll
-      for (int u = 0; u < 4; u++)
-        *reinterpret_cast<u4*>(vb + kr * 256 + (((4 * part + u) ^ (kr & 15)) * 16)) = dq8_f16_pow2(w4[u], sc);
-    } else {  // bf16 row of 128 keys, chunk = key / 8, swizzled by the channel
-      const float sv = scale_value(rvs, SCALE_E8M0);
-      const uint32_t w4[4] = {rv0.x, rv0.y, rv0.z, rv0.w};
+        for (int u = 0; u < 4; u++)
+          *reinterpret_cast<u4*>(vb + kr * 256 + (((4 * part + u) ^ (kr & 15)) * 16)) = dq8_bf16(w4[u], pks);
+      } else {  // f16 V 2^vshift
+        // scale 2^(e + vshift) as the convert's operand: biased exponent byte + vshift
+        // (140 at most inside the scanned blocks, clamped there outside them); blocks
+        // more than 139 binades below the largest become 0
+        const int be = __builtin_elementwise_min((int)rvs + vshift, 140);
+        const float sc = u2f((uint32_t)(be > 1 ? be : 1) << 23);
 #pragma unroll
-      for (int u = 0; u < 4; u++)
-        *reinterpret_cast<u4*>(vb + kr * 256 + (((4 * part + u) ^ (kr & 15)) * 16)) = dq8_bf16(w4[u], sv);
+        for (int u = 0; u < 4; u++)
+          *reinterpret_cast<u4*>(vb + kr * 256 + (((4 * part + u) ^ (kr & 15)) * 16)) = dq8_f16_pow2(w4[u], sc);
+      }
     }
   };
 
@@ -1211,11 +1243,11 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   };
   // M(t): PV of tile t-1 (stage offset sv), then S^T of tile t (stage offset sk) with
   // its mask and maxima
-  auto phase_m = [&](int t, uint32_t sk, uint32_t sv, bool can_fold) __attribute__((always_inline)) {
+  // mfold: tile t-1 is a diagonal tile under causally safe V, staged in the per-key form
+  // of V (unit block scales); vfold: the V phase that follows folds (no set-up here)
+  auto phase_m = [&](int t, uint32_t sk, uint32_t sv, bool mfold, bool vfold) __attribute__((always_inline)) {
     if (t >= 1) {
-      // a folded tile (a diagonal tile under causally safe V) is staged in the per-key
-      // form of V, with unit block scales
-      const bool fold = SAFE && can_fold && ((t - 1) >> 1) == (int)qt;
+      const bool fold = SAFE && mfold;
       const uint8_t* Vs = smem + sv + KV;
       if constexpr (PV == PV_FP4) {
 #pragma unroll
@@ -1249,7 +1281,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
             else O[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bp[1], O[db], 0, 0, 2, (int)vs4, 0, 127);
           }
         }
-      } else if constexpr (H16) {
+      } else if (!(SAFE && fold)) {
         // P^ of step s (keys 64(s/4) + 32h + 8(s%4) + [0, 8) = sub-tile 2(s/4) + (s%4)/2,
         // entries 8((s%4)%2) + [0, 8)) dequantized exactly to f16 from its codes
         v8h pb[8];
@@ -1270,13 +1302,13 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
           }
         }
       } else {
-        // P^ of step s (keys 64(s/4) + 32h + 8(s%4) + [0, 8) = sub-tile 2(s/4) + (s%4)/2,
-        // entries 8((s%4)%2) + [0, 8)) dequantized exactly to bf16 from its codes
+        // a tile staged from the per-key form: bf16 P^' 2^sigma against bf16
+        // Vk 2^(vshift - sigma), the same product scaled by 2^vshift, both exact
         v8bf pb[8];
 #pragma unroll
         for (int s = 0; s < 8; s++) {
           const int bb = 2 * (s >> 2) + ((s & 3) >> 1);
-          pb[s] = __builtin_bit_cast(v8bf, dq8_bf16(pc[2 * bb + ((s & 3) & 1)], pdq[bb]));
+          pb[s] = __builtin_bit_cast(v8bf, dq8_bf16(pc[2 * bb + ((s & 3) & 1)], pdq[bb] * psig_f));
         }
 #pragma unroll
         for (int db = 0; db < 4; db++) {
@@ -1292,6 +1324,12 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     }
     if (t < nkt) {
       const uint8_t* Ks = smem + sk;
+      // the Q operand: held in registers, or with causally safe V read from LDS here
+      v8i qo0 = qop[0], qo1 = qop[1];
+      if constexpr (SAFE && QK == QK_FP4) {
+        qo0 = v8_from4(*reinterpret_cast<const u4*>(smem + L::QOFF + (32 * wave + ql) * 80 + 16 * hh));
+        qo1 = v8_from4(*reinterpret_cast<const u4*>(smem + L::QOFF + (32 * wave + ql) * 80 + 32 + 16 * hh));
+      }
 #pragma unroll
       for (int bb = 0; bb < 4; bb++) {
         if constexpr (QK == QK_FP4) {
@@ -1300,8 +1338,8 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
           v8i a0 = v8_from4(*reinterpret_cast<const u4*>(rp + koffk));
           v8i a1 = v8_from4(*reinterpret_cast<const u4*>(rp + koffk + 32));
           v16f acc = BIAS ? bias16(Ks + L::BOFF + 4 * key_of<SPLIT16>(bb, hh, 0)) : zero16();
-          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, qop[0], acc, 4, 4, 0, (int)ks4, 0, (int)qsc);
-          S[bb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, qop[1], acc, 4, 4, 2, (int)ks4, 2, (int)qsc);
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, qo0, acc, 4, 4, 0, (int)ks4, 0, (int)qsc);
+          S[bb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, qo1, acc, 4, 4, 2, (int)ks4, 2, (int)qsc);
         } else {
           const uint8_t* rp = Ks + (32 * bb + ql) * 256;
           v16f acc = BIAS ? bias16(Ks + L::BOFF + 4 * key_of<SPLIT16>(bb, hh, 0)) : zero16();
@@ -1338,7 +1376,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
         bm16[bb] = fmaxn(y0, y1);
       }
       tmax = halves_max(fmaxn(fmaxn(bm16[0], bm16[1]), fmaxn(bm16[2], bm16[3])));
-      if (PRE_IN_M && !(SAFE && can_fold)) phase_v_pre();
+      if (PRE_IN_M && !(SAFE && vfold)) phase_v_pre();
     }
   };
 
@@ -1506,9 +1544,10 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   if (grp == 1) __syncthreads();
   auto rot = [](uint32_t o) { return o == 2 * STAGE ? 0u : o + STAGE; };
   uint32_t sk = 0, sv = 2 * STAGE, ss = grp == 0 ? STAGE : 2 * STAGE;
-  // one M phase and one V phase; can_fold (a constant at each call) selects the
-  // per-key fold, which the diagonal tiles 2 qt and 2 qt + 1 take: their V phases are
-  // all fold phases, and the M phase that follows each skips the matrix-core row sum
+  // one M phase and one V phase; mfold and vfold (constants at each call) select the
+  // forms of the diagonal tiles 2 qt and 2 qt + 1 under causally safe V: their V phases
+  // fold the per-key exponents into P, and the M phases that follow take their PV from
+  // the per-key form
   // Issue priority: the SIMD issues the older wave first, so a phase of the younger
   // group waits behind the co-resident wave's stream.  Where one phase's stream is the
   // one that holds up the pair, it runs at raised priority (s_setprio): the M phase
@@ -1518,9 +1557,9 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   // documents 2-3% faster); the FP8 PV route measured best without.
   constexpr int MPRIO = QK == QK_FP4 && PV == PV_FP4 ? 1 : 0;
   constexpr int VPRIO = QK == QK_FP4 && PV == PV_BF16 ? 1 : 0;
-  auto step = [&](int t, bool can_fold) __attribute__((always_inline)) {
+  auto step = [&](int t, bool mfold, bool vfold) __attribute__((always_inline)) {
     if constexpr (MPRIO) __builtin_amdgcn_s_setprio(MPRIO);
-    phase_m(t, sk, sv, can_fold);
+    phase_m(t, sk, sv, mfold, vfold);
     __builtin_amdgcn_sched_barrier(0);  // keep the phase's MFMAs on this side of the barrier
     if constexpr (MPRIO) __builtin_amdgcn_s_setprio(0);
     __syncthreads();
@@ -1535,7 +1574,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
         load_half(nt < nkt ? nt : nkt - 1);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (SAFE && can_fold) phase_v_fold(t);
+      if (SAFE && vfold) phase_v_fold(t);
       else phase_v(t);
       if constexpr (VPRIO) __builtin_amdgcn_s_setprio(0);
       if constexpr (!STAGE_FIRST) {
@@ -1549,12 +1588,15 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
     sk = __builtin_amdgcn_readfirstlane(rot(sk));
     ss = __builtin_amdgcn_readfirstlane(rot(ss));
   };
-  // tiles before 2 qt need no fold (the loop without it keeps its registers); the
-  // rest run with it
+  // tiles before 2 qt need no fold; step 2 qt folds in its V phase only, the steps
+  // after it in both phases (each copy of the step holds one form of each phase, which
+  // keeps the register allocation of the main loop)
   const int tsplit = SAFE ? (2 * (int)qt < nkt + 1 ? 2 * (int)qt : nkt + 1) : nkt + 1;
-  for (int t = 0; t < tsplit; t++) step(t, false);
-  if constexpr (SAFE)
-    for (int t = tsplit; t <= nkt; t++) step(t, true);
+  for (int t = 0; t < tsplit; t++) step(t, false, false);
+  if constexpr (SAFE) {
+    if (tsplit <= nkt) step(tsplit, false, true);
+    for (int t = tsplit + 1; t <= nkt; t++) step(t, true, true);
+  }
   if (grp == 0) __syncthreads();
 
   // ---------------- epilogue ----------------

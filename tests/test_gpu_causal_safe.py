@@ -50,6 +50,22 @@ def test_fwd_causal_safe_with_centering():
     _check(res, "causal safe + centering")
 
 
+@pytest.mark.parametrize("route", ["mxfp4_two_level_e4m3", "mxfp4_pnq_e4m3p"])
+def test_fwd_causal_safe_tiny_channel(route):
+    """One V channel 2^-118 times the others: its f16 shift exceeds 125, so the per-key
+    tiles' bf16 products split the shift between the two operands (V 2^(vshift - sigma),
+    P^' 2^sigma with sigma > 0).  A sigma missing on either side would scale every
+    channel's diagonal-tile contribution by 2^sigma."""
+    q, v, pm, pf = SAFE_ROUTES[route]
+    x = synth.make_inputs("outlier", 1, 2, 2, 600, 128, 46)
+    vf = synth.bf16_to_f32(x["v"])
+    vf[..., 7] *= 2.0 ** -118
+    assert np.abs(vf[..., 7]).max() < 2.0 ** -110  # largest E8M0 block exponent below -112
+    x = dict(x, v=synth.f32_to_bf16(vf))
+    res = run_case(q, v, pm, pf, 1, 2, 2, 600, causal=True, inputs=x, safe=True)
+    _check(res, route + " causal safe tiny channel")
+
+
 @pytest.mark.parametrize("route", ["mxfp4_direct", "mxfp4_two_level_e4m3"])
 def test_leak_probe(route):
     """Scaling the values of keys >= 200 (inside the V block of keys 192..223) changes
