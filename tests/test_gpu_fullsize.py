@@ -8,14 +8,15 @@ import pytest
 
 import oracle
 import synth
-from helpers import (PM_ORACLE, TOL, gpu_available, gpu_codes_qk, gpu_codes_v, oracle_quant_qk, oracle_quant_v,
-                     record_parity, score_rounds)
+from helpers import (PM_ORACLE, TOL, gpu_available, gpu_codes_qk, gpu_codes_v, gpu_codes_vkey, oracle_quant_qk,
+                     oracle_quant_v, oracle_vkey, record_parity, score_rounds)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
 # case -> (workload, Q/K format, V format, P mode, P format), as bench.py runs them; the
 # two-level cases at N = 32K take the video-DiT inputs with both readings of the
-# level-2 block format (E4M3 per 16 keys, E8M0 per 32 keys)
+# level-2 block format (E4M3 per 16 keys, E8M0 per 32 keys); "_safe": with causally
+# safe V scales (bench.py --causal-safe)
 CASES = {
     "c1_single_head": ("c1_single_head", "mxfp4", "mxfp4", "two_level", "nvfp4"),
     "c2_mha_4k": ("c2_mha_4k", "mxfp4", "mxfp4", "two_level", "nvfp4"),
@@ -24,6 +25,7 @@ CASES = {
     "c5_varlen_causal_64k": ("c5_varlen_causal_64k", "mxfp4", "mxfp4", "two_level", "nvfp4"),
     "two_level_e4m3_32k": ("c3_video_dit_32k", "mxfp4", "mxfp4", "two_level", "nvfp4"),
     "two_level_e8m0_32k": ("c3_video_dit_32k", "mxfp4", "mxfp4", "two_level", "mxfp4"),
+    "c5_varlen_causal_64k_safe": ("c5_varlen_causal_64k", "mxfp4", "mxfp4", "two_level", "nvfp4"),
 }
 
 
@@ -51,11 +53,13 @@ def test_fullsize_sampled_rows(name):
     Q = mx.quantize(t["q"], mx.ROLE_QK, qf)
     K = mx.quantize(t["k"], mx.ROLE_QK, qf)
     V = mx.quantize(t["v"], mx.ROLE_V, vf, cu_seqlens=cu)
+    safe = name.endswith("_safe")
+    Vk = mx.quantize(t["v"], mx.ROLE_VKEY, vf, cu_seqlens=cu) if safe else None
     ws, nd = None, 0
     if doc_off is not None:
         ws = mx.fwd_plan(doc_off, N, causal)
         nd = len(doc_off) - 1
-    out = mx.fwd(Q, K, V, mx.fwd_params(pm, pf, causal=causal, out_fp32=True), workspace=ws, ndocs=nd)
+    out = mx.fwd(Q, K, V, mx.fwd_params(pm, pf, causal=causal, out_fp32=True, vkey=Vk), workspace=ws, ndocs=nd)
     torch.cuda.synchronize()
 
     rng = np.random.default_rng(12345)
@@ -63,6 +67,8 @@ def test_fullsize_sampled_rows(name):
     rows = _sample_rows(N, doc_off, rng)
     qcodes, kcodes = gpu_codes_qk(Q), gpu_codes_qk(K)
     vcodes, vscales = gpu_codes_v(V, N, doc_off)
+    if safe:
+        gkc, gke = gpu_codes_vkey(Vk, N, doc_off)
     worst, fbt = 0.0, []
     for h in heads:
         hk = h * Hkv // Hq
@@ -75,8 +81,13 @@ def test_fullsize_sampled_rows(name):
         assert np.array_equal(qcodes[0, h], qc[0, 0]) and np.array_equal(Q.scales_view()[0, h].cpu().numpy(), qs[0, 0])
         assert np.array_equal(kcodes[0, hk], kc[0, 0]) and np.array_equal(K.scales_view()[0, hk].cpu().numpy(), ks[0, 0])
         assert np.array_equal(vcodes[0, hk], vc[0, 0]) and np.array_equal(vscales[0, hk], vs[0, 0])
+        vk_vals = vk_exp = None
+        if safe:
+            vk_codes, vk_vals, vk_exp = oracle_vkey(vh, vf)
+            assert np.array_equal(gkc[0, hk], vk_codes[0, 0]) and np.array_equal(gke[0, hk], vk_exp[0, 0])
         O_ref, _, fb = oracle.attention(qd, kd, vd, PM_ORACLE[pm], pf, causal=causal, doc_off=doc_off,
-                                        rows=np.array(rows, np.int64), score_rounds=score_rounds(qf))
+                                        rows=np.array(rows, np.int64), score_rounds=score_rounds(qf),
+                                        vkey=vk_vals, vkey_exp=vk_exp)
         O_gpu = out[0, h].cpu().numpy()[rows]
         # the bound uses max|O| of the sampled rows of this head
         bound = TOL * np.abs(O_ref).max() + fb[:, None]
