@@ -637,6 +637,184 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecArgs a) {
   merge_chunk(a, so, slse, ncol, b, hk, gsz, chunk);
 }
 
+// The QK4PV8 decode for up to 16 query columns, in the lane layout of decode16_kernel
+// (lane l: column or operand row l % 16, contraction block l / 16), which halves the
+// score and output accumulators of the 32-column form, so more waves (and more of the
+// history) are in flight:
+//   * an 8-bit operand of the 16x16x128 MFMA gives the lane of block g (lane / 16)
+//     elements n = 0..31 at contraction index 64 (n / 16) + 16 g + n % 16, and the E8M0
+//     scale of block g covers indices [32 g, 32 g + 32).  With the key as the index, a
+//     lane's V^T row holds keys 16 g + [0, 16) and 64 + 16 g + [0, 16) (two 16-byte
+//     reads) and the scale of V's block g is the lane's own;
+//   * S^T = K Q^T per 16-key sub-tile st (8 per tile), MFMA row r reading key
+//     64 (st / 4) + 16 (r / 4) + 4 (st % 4) + r % 4, so the lane of (column c, block g)
+//     holds, as element n = 4 st + i, the score of key 64 (n / 16) + 16 g + n % 16: the
+//     keys of its own P operand elements, whose codes need no other lane.  NVFP4 Q and
+//     K run on the f16 16x16x32 MFMA after exact dequantization: in step s the 8
+//     contraction slots of block g hold channels 32 g + 8 s + [0, 8), so a lane reads 16
+//     contiguous code bytes of its K row and the two E4M3 scales that cover them; MXFP4
+//     Q and K take the scaled FP4 16x16x128 MFMA;
+//   * O^T = V^T P^T on the scaled FP8 MFMA with P = E4M3(448 P~) and P's unit scale.
+template <int QK, bool VT>
+__global__ __launch_bounds__(256, 2) void decode16_q4p8_kernel(DecArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63, qc = lane & 15, kb = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t nchunk = (a.N + DEC_CHUNK - 1) / DEC_CHUNK;
+  const int64_t chunk = blockIdx.x % nchunk, bhk = blockIdx.x / nchunk;
+  const int64_t b = bhk / a.Hkv, hk = bhk % a.Hkv;
+  const int gsz = (int)(a.Hq / a.Hkv);
+  const int ncol = gsz * (int)a.R;  // <= 16
+  const bool cvalid = qc < ncol;
+  const int g = cvalid ? qc / (int)a.R : 0, r = cvalid ? qc % (int)a.R : 0;
+  const int64_t hq = hk * gsz + g;
+  const int kt0 = (int)chunk * DEC_CHUNK + 128 * wave;
+  const float lam = a.lambda;
+  constexpr int KSB = QK == QK_FP4 ? 4 : 8;  // scale bytes per Q/K row
+
+  // Q operand (B of S^T = K Q^T): column qc, channels [32 kb, 32 kb + 32); an absent
+  // column reads column 0's row (its scores are masked)
+  v8i qop = {0, 0, 0, 0, 0, 0, 0, 0};
+  uint32_t qsc = 0;
+  v8h qh[4];
+  {
+    const int64_t qrow = (b * a.Hq + hq) * a.R + r;
+    const u4 c = *reinterpret_cast<const u4*>(a.q + qrow * 64 + 16 * kb);
+    if constexpr (QK == QK_FP4) {
+      qop = v8_from4(c);
+      qsc = *reinterpret_cast<const uint32_t*>(a.qs + qrow * 4) >> (8 * kb);
+    } else {
+      const uint32_t sw = *reinterpret_cast<const uint32_t*>(a.qs + qrow * 8 + 4 * (kb >> 1)) >> (16 * (kb & 1));
+      const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+      for (int s = 0; s < 4; s++) {
+        const _Float16 sh = (_Float16)e4m3_value((sw >> (8 * (s >> 1))) & 0xFFu);  // exact in f16
+        qh[s] = dq8_f16(cw[s], v2h{sh, sh});
+      }
+    }
+  }
+  const uint8_t* kc = a.k + (b * a.Hkv + hk) * a.N * 64;
+  const uint8_t* kscl = a.ks + (b * a.Hkv + hk) * a.N * KSB;
+  const int64_t vrow0 = (b * a.Hkv + hk) * 128;
+  const uint32_t np = (uint32_t)a.np;
+
+  // ---- every operand of the tile requested before any is used; keys past N read row
+  // N - 1 (masked).  V has one byte per key and np is a multiple of 128, so a tile's
+  // bytes and its 4 scale bytes lie inside the row and the scale dword is aligned.
+  u4 kq[8], vlo[8], vhi[8];
+  uint32_t ks[8], vs[8];
+  if (kt0 < (int)a.N) {
+#pragma unroll
+    for (int st = 0; st < 8; st++) {
+      int key = kt0 + 64 * (st >> 2) + 16 * (qc >> 2) + 4 * (st & 3) + (qc & 3);
+      key = key < (int)a.N ? key : (int)a.N - 1;
+      kq[st] = *reinterpret_cast<const u4*>(kc + (int64_t)key * 64 + 16 * kb);
+      if constexpr (QK == QK_FP4) ks[st] = *reinterpret_cast<const uint32_t*>(kscl + (int64_t)key * 4) >> (8 * kb);
+      else ks[st] = *reinterpret_cast<const uint32_t*>(kscl + (int64_t)key * 8 + 4 * (kb >> 1)) >> (16 * (kb & 1));
+    }
+#pragma unroll
+    for (int db = 0; db < 8; db++) {
+      const int64_t vrow = vrow0 + 16 * db + qc;
+      // slot of (tile, channel) in the tile-major form (role VT: 128 code bytes each)
+      const int64_t tslot = (int64_t)(kt0 / 128) * 128 + 16 * db + qc;
+      const uint8_t* vp = (VT ? a.v + vrow0 * np + tslot * 128 : a.v + vrow * np + kt0) + 16 * kb;
+      vlo[db] = *reinterpret_cast<const u4*>(vp);
+      vhi[db] = *reinterpret_cast<const u4*>(vp + 64);
+      vs[db] = *reinterpret_cast<const uint32_t*>(VT ? a.vs + vrow0 * (np / 32) + tslot * 4
+                                                     : a.vs + vrow * (np / 32) + kt0 / 32) >> (8 * kb);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every read is in flight before the MFMAs
+  const int L = a.kv_len != nullptr ? a.kv_len[b] : (int)a.N;
+  const int pos = L - (int)a.R + r;  // keys <= pos are visible to this column's query
+  const bool live = kt0 < L;
+  float y[32];  // the lane's 32 scores, key kt0 + 64 (j / 16) + 16 kb + j % 16
+  float tmax = NEG_INF;
+  if (live) {
+#pragma unroll
+    for (int st = 0; st < 8; st++) {
+      v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (QK == QK_FP4) {
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(v8_from4(kq[st]), qop, acc, 4, 4, 0, (int)ks[st], 0,
+                                                               (int)qsc);
+      } else {
+        const uint32_t kw[4] = {kq[st].x, kq[st].y, kq[st].z, kq[st].w};
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+          const _Float16 sk = (_Float16)e4m3_value((ks[st] >> (8 * (s >> 1))) & 0xFFu);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dq8_f16(kw[s], v2h{sk, sk}), qh[s], acc, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; i++) y[4 * st + i] = acc[i];
+    }
+    float bmax = NEG_INF;
+#pragma unroll
+    for (int j = 0; j < 32; j++) {
+      const int key = kt0 + 64 * (j >> 4) + 16 * kb + (j & 15);
+      y[j] = (cvalid && key <= pos) ? y[j] : NEG_INF;  // pos < L
+      bmax = fmaxn(bmax, y[j]);
+    }
+    tmax = fmaxn(bmax, __shfl_xor(bmax, 16));
+    tmax = fmaxn(tmax, __shfl_xor(tmax, 32));
+  }
+
+  // ---- the running maximum before this tile: the split's first tile starts from
+  // -inf, its second from the first tile's maximum
+  __shared__ float smax[4][32];
+  if (kb == 0) smax[wave][qc] = tmax;
+  __syncthreads();
+  const float m0 = (wave & 1) ? smax[wave - 1][qc] : NEG_INF;
+
+  float m = m0, l = 0.0f;
+  v4f O[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) O[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  if (live) {
+    // ---- P = E4M3(448 P~), element n (byte n % 4 of dword n / 4) for score n; the row
+    // sum from P~
+    const float mnew = fmaxn(m0, tmax);
+    const float ms = mnew == NEG_INF ? 0.0f : mnew * lam;
+    m = mnew;
+    float lsum = 0.0f;
+    v8i bp;
+#pragma unroll
+    for (int dw = 0; dw < 8; dw++) {
+      float p4[4];
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        p4[u] = exp2_hw(__builtin_fmaf(y[4 * dw + u], lam, -ms));
+        lsum += p4[u];
+      }
+      int x = __builtin_amdgcn_cvt_pk_fp8_f32(448.0f * p4[0], 448.0f * p4[1], 0, false);
+      x = __builtin_amdgcn_cvt_pk_fp8_f32(448.0f * p4[2], 448.0f * p4[3], x, true);
+      bp[dw] = x;
+    }
+
+    // ---- O^T = V^T P^T: channel rows 16 db + qc, keys kt0 + [0, 128)
+#pragma unroll
+    for (int db = 0; db < 8; db++) {
+      const v8i av = {(int)vlo[db].x, (int)vlo[db].y, (int)vlo[db].z, (int)vlo[db].w,
+                      (int)vhi[db].x, (int)vhi[db].y, (int)vhi[db].z, (int)vhi[db].w};
+      O[db] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bp, O[db], 0, 0, 0, (int)vs[db], 0, 127);
+    }
+    lsum += __shfl_xor(lsum, 16);
+    l = lsum + __shfl_xor(lsum, 32);
+  }
+
+  // ---- the tile's normalized output (O / 448 / l) and log-sum-exp, merged per chunk
+  const float inv = l > 0.0f ? 1.0f / l / 448.0f : 0.0f;
+  extern __shared__ float so[];  // [tile][column < ncol][channel], rows padded to 129
+  __shared__ float slse[4][32];
+  if (cvalid)
+#pragma unroll
+    for (int db = 0; db < 8; db++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) so[(wave * ncol + qc) * 129 + 16 * db + 4 * kb + i] = O[db][i] * inv;
+  if (kb == 0) slse[wave][qc] = l > 0.0f ? __logf(l) + m * a.sm_scale : NEG_INF;
+  __syncthreads();
+  merge_chunk(a, so, slse, ncol, b, hk, gsz, chunk);
+}
+
 // merge of the chunk states of one (request, query head, row) by their log-sum-exp.
 // Workgroup = (row, quarter of the 128 channels); its 8 groups of 32 threads (thread =
 // channel) take every 8th chunk in one pass, 8 chunk states in flight, keeping a running
@@ -730,8 +908,12 @@ hipError_t launch_decode(int pmode, const DecArgs& a, hipStream_t st) {
   hipError_t e0;
   const bool vt = a.vtiled != 0;
   if (pmode == PM_FP8_FIXED) {  // QK4PV8: an FP8 V, 32 columns at most
-    if (vt) e0 = a.qk_fp4 ? run(decode_q4p8_kernel<QK_FP4, true>) : run(decode_q4p8_kernel<QK_BF16, true>);
-    else e0 = a.qk_fp4 ? run(decode_q4p8_kernel<QK_FP4, false>) : run(decode_q4p8_kernel<QK_BF16, false>);
+    if (vt)
+      e0 = a.qk_fp4 ? pick(decode_q4p8_kernel<QK_FP4, true>, decode16_q4p8_kernel<QK_FP4, true>)
+                    : pick(decode_q4p8_kernel<QK_BF16, true>, decode16_q4p8_kernel<QK_BF16, true>);
+    else
+      e0 = a.qk_fp4 ? pick(decode_q4p8_kernel<QK_FP4, false>, decode16_q4p8_kernel<QK_FP4, false>)
+                    : pick(decode_q4p8_kernel<QK_BF16, false>, decode16_q4p8_kernel<QK_BF16, false>);
   } else if (pmode == PM_DIRECT)
     e0 = vt ? pick(decode_kernel<PM_DIRECT, true>, decode16_kernel<PM_DIRECT, true>)
             : pick(decode_kernel<PM_DIRECT, false>, decode16_kernel<PM_DIRECT, false>);

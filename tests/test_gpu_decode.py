@@ -81,10 +81,12 @@ def test_decode_column_forms(pm, Hq, Hkv, R):
 
 @pytest.mark.parametrize("qf", ["nvfp4", "mxfp4"])
 @pytest.mark.parametrize("Hq,Hkv,R,N,kv_len", [(8, 2, 1, 700, [700, 333]), (8, 1, 3, 1100, [1100, 517]),
-                                               (4, 1, 8, 1300, None), (2, 2, 2, 260, [2, 257])])
+                                               (4, 1, 8, 1300, None), (2, 2, 2, 260, [2, 257]),
+                                               (16, 1, 1, 900, [900, 450])])
 def test_decode_qk4pv8(qf, Hq, Hkv, R, N, kv_len):
     """The QK4PV8 route ("MpFA", sections 4.1 and 5.3): NVFP4 (or MXFP4) Q/K, an FP8 V,
-    P = E4M3(448 P~): ragged histories, several newest rows, up to 32 packed columns"""
+    P = E4M3(448 P~): ragged histories, several newest rows, up to 32 packed columns
+    (16 at most on the 16-column kernel, which the 2-, 4- and 16-column cases take)"""
     run_decode("fp8", B=2 if kv_len is not None and len(kv_len) == 2 else 1, Hq=Hq, Hkv=Hkv, R=R, N=N, kv_len=kv_len,
                seed=71, qfmt=qf)
 
