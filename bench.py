@@ -39,17 +39,45 @@ TRAFFIC_FILES = {"c3": "profiles/fwd_pp_kernel_c3_video_dit_32k_traffic.txt",
 KERNEL_SOURCES = ["microscaling_fp4_attention_amd/csrc/fwd.hip", "microscaling_fp4_attention_amd/csrc/device_util.h",
                   "microscaling_fp4_attention_amd/csrc/formats.h", "microscaling_fp4_attention_amd/csrc/kernels.h"]
 # the same for the split-key decode at 128K keys (V tile-major), its main kernel
-DECODE_TRAFFIC_FILE = "profiles/decode_kernel_gqa_128k.txt"
+# decode at 128K keys, role VT: the MXFP4 route's profile and the QK4PV8 route's
+DECODE_TRAFFIC_FILES = {False: "profiles/decode_kernel_gqa_128k.txt", True: "profiles/decode_qk4pv8_gqa_128k.txt"}
 DECODE_SOURCES = ["microscaling_fp4_attention_amd/csrc/decode.hip"] + KERNEL_SOURCES[1:]
 
 
+def _code_only(text):
+    """C/C++ source without its comments, trailing blanks and empty lines (string and
+    character literals kept as written)"""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":  # a literal: copy through its closing quote
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = (ln.rstrip() for ln in "".join(out).split("\n"))
+    return "\n".join(ln for ln in lines if ln)
+
+
 def kernel_source_sha256(sources=None):
-    """SHA-256 over a kernel's source files (the forward's by default), in list order"""
+    """SHA-256 over a kernel's source files (the forward's by default), in list order,
+    taken over their code only: an edit of comments or blank lines keeps the hash, so a
+    profile stays tied to the code it measured"""
     import hashlib
     h = hashlib.sha256()
     for rel in sources or KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 
@@ -281,8 +309,8 @@ def bench_decode(args, torch, mx):
            "tokens_per_s": round(B * R / t_step, 1),
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
                         "frac": round(gbs / 8000.0, 4),
-                        "traffic": read_traffic(DECODE_TRAFFIC_FILE, DECODE_SOURCES)
-                        if (N, layout, q4p8) == (131072, "vt", False) else None,
+                        "traffic": read_traffic(DECODE_TRAFFIC_FILES[q4p8], DECODE_SOURCES)
+                        if (N, layout) == (131072, "vt") else None,
                         "kernel": "split-key decode (mxattn_decode)"}}
     print(json.dumps(res), flush=True)
 

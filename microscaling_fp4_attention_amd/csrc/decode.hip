@@ -637,10 +637,10 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecArgs a) {
   merge_chunk(a, so, slse, ncol, b, hk, gsz, chunk);
 }
 
-// The QK4PV8 decode for up to 16 query columns, in the lane layout of decode16_kernel
-// (lane l: column or operand row l % 16, contraction block l / 16), which halves the
-// score and output accumulators of the 32-column form, so more waves (and more of the
-// history) are in flight:
+// The QK4PV8 decode ("MpFA", sections 4.1 and 5.3) for up to 16 query columns, in the
+// lane layout of decode16_kernel (lane l: column or operand row l % 16, contraction
+// block l / 16), which halves the score and output accumulators of the 32-column form,
+// so more waves (and more of the history) are in flight:
 //   * an 8-bit operand of the 16x16x128 MFMA gives the lane of block g (lane / 16)
 //     elements n = 0..31 at contraction index 64 (n / 16) + 16 g + n % 16, and the E8M0
 //     scale of block g covers indices [32 g, 32 g + 32).  With the key as the index, a
