@@ -130,11 +130,12 @@ CONFIGS = {
 
 def route_peak(qf, vf, pm, pf):
     """MFMA types of the forward's two products and their combined dense peak (TFLOP/s):
-    MXFP4 Q/K run on the FP4 MFMA, NVFP4 Q/K on bf16 after exact dequantization; PV runs
+    MXFP4 Q/K run on the FP4 MFMA, NVFP4 Q/K on f16 after exact dequantization (bf16 in
+    the single-buffer kernel of the routes with an E4M3-scaled V, at the same peak); PV runs
     on FP8 for FP8 P, on FP4 for E8M0-scaled P with an MXFP4 V, on f16 for other P with an
     MXFP4 V (V's channels shifted into f16 range; under causally safe V the two diagonal
     key tiles of each query tile take bf16 products, at the same peak), on bf16 otherwise"""
-    qk = ("fp4", FP4_PEAK_TFLOPS) if qf.startswith("mxfp4") else ("bf16", BF16_PEAK_TFLOPS)
+    qk = ("fp4", FP4_PEAK_TFLOPS) if qf.startswith("mxfp4") else ("f16", BF16_PEAK_TFLOPS)
     if pm == "fp8":
         pv = ("fp8", FP8_PEAK_TFLOPS)
     elif pf is not None and pf.startswith("mxfp4") and vf.startswith("mxfp4"):

@@ -818,7 +818,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
   // ---------------- Q operand ----------------
   v8i qop[2];
   uint32_t qsc = 0;
-  v8bf qbf[8];
+  v8h qh16[8];
   if constexpr (QK == QK_FP4) {
     const uint8_t* qp = a.q + qrow * 64;
     qsc = *reinterpret_cast<const uint32_t*>(a.qs + qrow * 4) >> (8 * hh);
@@ -828,14 +828,16 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       *reinterpret_cast<u4*>(smem + L::QOFF + (32 * wave + ql) * 80 + 16 * hh) = mk4(qop[0][0], qop[0][1], qop[0][2], qop[0][3]);
       *reinterpret_cast<u4*>(smem + L::QOFF + (32 * wave + ql) * 80 + 32 + 16 * hh) = mk4(qop[1][0], qop[1][1], qop[1][2], qop[1][3]);
     }
-  } else {
+  } else {  // NVFP4: each element dequantized exactly to f16 (an E2M1 value times an
+             // E4M3 scale has at most 6 significant bits in [2^-10, 2688]); the scale
+             // byte by the hardware E4M3 convert
     const uint8_t* qp = a.q + qrow * 64;
     u2 s8 = *reinterpret_cast<const u2*>(a.qs + qrow * 8);
 #pragma unroll
     for (int s = 0; s < 8; s++) {
       uint32_t w = *reinterpret_cast<const uint32_t*>(qp + 8 * s + 4 * hh);
-      uint32_t sb = ((s < 4 ? s8.x : s8.y) >> (8 * (s & 3))) & 0xFF;
-      qbf[s] = __builtin_bit_cast(v8bf, dq8_bf16(w, e4m3_value(sb)));
+      const _Float16 sh = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)((s < 4 ? s8.x : s8.y) >> (8 * (s & 3))), 0);
+      qh16[s] = dq8_f16(w, v2h{sh, sh});
     }
   }
 
@@ -1009,13 +1011,14 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
         *reinterpret_cast<uint32_t*>(base + L::KSC + 4 * kpos_s) = rks;
         *reinterpret_cast<uint32_t*>(base + L::KSC + 512 + 4 * kpos_s) = rks >> 8;
       }
-    } else {  // channels 32 part + [0, 32), E4M3 blocks 2 part and 2 part + 1
-      const float s0 = e4m3_value(rks & 0xFF), s1 = e4m3_value((rks >> 8) & 0xFF);
+    } else {  // NVFP4 as exact f16: channels 32 part + [0, 32), E4M3 blocks 2 part, 2 part + 1
+      const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)rks, 0);
+      const _Float16 s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)rks, 1);
       const uint32_t w4[4] = {rk.x, rk.y, rk.z, rk.w};
 #pragma unroll
       for (int u = 0; u < 4; u++)
-        *reinterpret_cast<u4*>(base + kpos_r * 256 + (((4 * part + u) ^ (kpos_r & 15)) * 16)) =
-            dq8_bf16(w4[u], u < 2 ? s0 : s1);
+        *reinterpret_cast<v8h*>(base + kpos_r * 256 + (((4 * part + u) ^ (kpos_r & 15)) * 16)) =
+            dq8_f16(w4[u], u < 2 ? v2h{s0, s0} : v2h{s1, s1});
     }
     uint8_t* vb = base + KV;
     if constexpr (PV == PV_FP4) {
@@ -1346,7 +1349,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
 #pragma unroll
           for (int s = 0; s < 8; s++) {
             const int chunk = (2 * s + hh) ^ (ql & 15);
-            acc = mfma_bf16(*reinterpret_cast<const v8bf*>(rp + chunk * 16), qbf[s], acc);
+            acc = mfma_f16(*reinterpret_cast<const v8h*>(rp + chunk * 16), qh16[s], acc);
           }
           S[bb] = acc;
         }
