@@ -34,7 +34,9 @@ FP4_MEASURED_TFLOPS = 8200.0  # the same MFMA measured back to back on one MI355
 # plain-copy calibration; read from the committed profile summaries, which record the
 # SHA-256 of the kernel source they were taken on (None when absent or stale)
 TRAFFIC_FILES = {"c3": "profiles/fwd_pp_kernel_c3_video_dit_32k_traffic.txt",
-                 "c4": "profiles/fwd_pp_kernel_c4_gqa_causal_32k_traffic.txt"}
+                 "c4": "profiles/fwd_pp_kernel_c4_gqa_causal_32k_traffic.txt",
+                 "c5": "profiles/fwd_pp_kernel_c5_varlen_causal_64k_traffic.txt",
+                 "c2": "profiles/fwd_pp_kernel_c2_mha_4k_traffic.txt"}
 # the forward kernel's source: the kernel file and the headers it includes
 KERNEL_SOURCES = ["microscaling_fp4_attention_amd/csrc/fwd.hip", "microscaling_fp4_attention_amd/csrc/device_util.h",
                   "microscaling_fp4_attention_amd/csrc/formats.h", "microscaling_fp4_attention_amd/csrc/kernels.h"]
