@@ -449,6 +449,19 @@ def main():
     fwd_ms = np.array([a.elapsed_time(b) for _, a, b in ev])
     quant_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
     t_fwd = float(np.mean(fwd_ms)) / 1e3
+    # the quantize pass's bandwidth against a plain device copy (read + write) of 1 GiB,
+    # four times the 256 MB Infinity Cache, timed after the steps on the same stream
+    src = torch.empty(1 << 29, dtype=torch.int16, device=q.device)
+    cp = torch.empty_like(src)
+    cp.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(3):
+        cp.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 3 * 2 * 2 * src.numel() / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, cp
     log(f"[bench] step {t_step * 1e3:.3f} ms (wall {wall / args.steps * 1e3:.3f} ms), fwd {t_fwd * 1e3:.3f} ms")
 
     flop = counted_flop(B, Hq, N, 128, causal, doc_off)
@@ -480,6 +493,7 @@ def main():
         "t_quant_median_ms": round(float(np.median(quant_ms)), 4),
         # the quantize pass reads bf16 Q, K, V and writes their codes and scales
         "quant_gbs": round(quant_bytes / (float(np.median(quant_ms)) * 1e-3) / 1e9, 1) if args.preproc == "none" else None,
+        "copy_gbs": round(copy_gbs, 1),  # torch copy_ of 1 GiB, read + write
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(fwd_tflops / peak, 4),
                      "traffic": profiled_traffic(args.config)
