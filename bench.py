@@ -330,8 +330,9 @@ def main():
                     help="outlier pre-processing of Q and K inside the step: smooth-K (K mean), sequence centering "
                          "with the compensation bias, and/or the normalized Hadamard rotation")
     ap.add_argument("--causal-safe", action="store_true",
-                    help="causally safe V scales: quantize the per-key form of V in the step and use it on each "
-                         "row's diagonal tile (causal workloads with a 4-bit V)")
+                    help="causally safe V scales: quantize the per-key form of V in the step and use it on the "
+                         "two key tiles of each 256-row query tile the causal boundary runs through (causal "
+                         "workloads with a 4-bit V)")
     ap.add_argument("--exp", default="exact", choices=["exact", "mitchell", "schraudolph"],
                     help="exponential of P~: exact (hardware exp), or the bit-level Mitchell-P / Schraudolph "
                          "approximations for inference (ping-pong kernel routes)")

@@ -171,13 +171,14 @@ typedef struct {
                               aligned                                                  */
   const mxattn_qtensor* vkey; /* causally safe V scales ("FLAMIA" section 3.2), or NULL: a
                         mxattn_qtensor of role VKEY quantized from the same V with the
-                        same documents.  On the key tile that holds a row's own
-                        position (the 128 keys from 128 floor(i / 128) of its sequence
-                        or document) the row uses this per-key form and multiplies
-                        P~_j by the key's scale 2^e_j before quantizing P; every other
-                        tile uses v.  Needs a causal mask and a V in E2M1 with E8M0
-                        scales per 32 keys (an FP8 V with round-up exponents needs no
-                        per-key form).                                                 */
+                        same documents.  Queries go in tiles of 256 rows from the start
+                        of their sequence or document; on the key tiles that start
+                        inside a row's query tile (the 256 keys from 256 floor(i / 256),
+                        the tiles its causal boundary runs through) the row uses this
+                        per-key form and multiplies P~_j by the key's scale 2^e_j before
+                        quantizing P; every other tile uses v.  Needs a causal mask and
+                        a V in E2M1 with E8M0 scales per 32 keys (an FP8 V with round-up
+                        exponents needs no per-key form).                              */
   int32_t exp_mode; /* mxattn_exp_mode.  The bit-level modes need a V with E8M0 scales
                        per 32 keys (E2M1 or E4M3) and are refused by mxattn_decode() */
 } mxattn_fwd_params;

@@ -1,8 +1,9 @@
 """GPU causally safe V scales ("FLAMIA ...", section 3.2) against the oracle: the
 per-key form of V (bytes bit-exact, with and without documents), the forward with the
-per-key fold on each row's diagonal tile for every 4-bit-V route of the ping-pong
-kernel (parity), a leak probe (future keys leave earlier rows bit-identical), and the
-refused combinations."""
+per-key fold on each row's diagonal tiles (the key tiles inside its 256-row query tile)
+for every 4-bit-V route of the ping-pong kernel (parity), a channel small enough to
+split the f16 shift between the bf16 operands, a leak probe (future keys leave earlier
+rows bit-identical), and the refused combinations."""
 import numpy as np
 import pytest
 
