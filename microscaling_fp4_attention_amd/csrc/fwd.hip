@@ -1359,19 +1359,20 @@ __global__ __launch_bounds__(512, 1) void fwd_pp_kernel(FwdArgs a) {
       const int k0 = t * 128;
       if ((k0 + 128 > klen) || (a.causal && k0 + 127 > (int)qt * 256 + 32 * wave)) {
         // keys below lim are visible (the tail, and under the causal mask the row's own
-        // position); a lane's 16 keys of sub-tile bb are consecutive, so one count each
-        // and a compare per element (packed documents 1.5% faster).  The FP8 P route
-        // keeps the per-key test: the count form measured 5% slower there (GQA causal
-        // 32K), its schedule shifting with the registers it frees.
+        // position); a lane's 16 keys of sub-tile bb are consecutive, so on the f16 P route
+        // one count each and a compare per element (packed documents 2.5% faster).  The
+        // FP4 and FP8 P routes keep the per-key test: there the count form measured
+        // slower (video-DiT 32K 1.4%, GQA causal 32K 5%, neither of which masks most of
+        // its tiles), the main loop's schedule shifting with it.
         const int lim = a.causal && qloc + 1 < klen ? qloc + 1 : klen;
 #pragma unroll
         for (int bb = 0; bb < 4; bb++) {
           const int n = lim - (k0 + key_of<SPLIT16>(bb, hh, 0));
 #pragma unroll
           for (int j = 0; j < 16; j++) {
-            const bool vis = PV == PV_FP8 ? k0 + key_of<SPLIT16>(bb, hh, j) < klen &&
-                                                (!a.causal || k0 + key_of<SPLIT16>(bb, hh, j) <= qloc)
-                                          : j < n;
+            const bool vis = PV != PV_BF16 ? k0 + key_of<SPLIT16>(bb, hh, j) < klen &&
+                                                 (!a.causal || k0 + key_of<SPLIT16>(bb, hh, j) <= qloc)
+                                           : j < n;
             S[bb][j] = vis ? S[bb][j] : NEG_INF;
           }
         }
