@@ -47,8 +47,9 @@ def record_parity(name, ratio, fb_over_tol, cap_share=FRAGILE_CAP):
 
 def score_rounds(qfmt) -> int:
     """FP32 roundings in the HIP path's score sums: two chained FP4 MFMAs (64 channels
-    each) for MXFP4 Q/K, eight bf16 MFMAs (16 channels each) for NVFP4 Q/K; the oracle
-    widens the window of every decision by what they can move a score."""
+    each) for MXFP4 Q/K, at most eight chained f16 (or, in the single-buffer kernel, bf16)
+    MFMAs (16 channels each; four of 32 in the 16-column decode) for NVFP4 Q/K; the
+    oracle widens the window of every decision by what they can move a score."""
     return 8 if str(qfmt).startswith("nvfp4") else 2
 
 
