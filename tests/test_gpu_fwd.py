@@ -75,6 +75,19 @@ def test_fwd_small_and_degenerate_shapes():
         _check(res, f"N={N}")
 
 
+@pytest.mark.parametrize("case", [("mxfp4_two_level_e4m3", False), ("mxfp4_two_level_e4m3", True),
+                                  ("qk4pv8", False), ("mxfp4_uos_pnq", True)])
+def test_fwd_boundary_lengths(case):
+    """Causal lengths at the edges of the 128-key tiles and of the 256-row query tiles
+    (the causally safe form folds on a query tile's two key tiles, the second of which
+    may be partial or absent)"""
+    route, safe = case
+    q, v, pm, pf = ROUTES[route]
+    for N in (1, 2, 127, 128, 129, 255, 256, 257):
+        res = run_case(q, v, pm, pf, B=1, Hq=2, Hkv=1, N=N, causal=True, kind="outlier", seed=6, safe=safe)
+        _check(res, f"{route}{' safe' if safe else ''} causal N={N}")
+
+
 def test_fwd_deterministic():
     import torch
     import microscaling_fp4_attention_amd as mx
