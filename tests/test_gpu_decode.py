@@ -11,7 +11,7 @@ import pytest
 import oracle
 import synth
 from helpers import (PM_ORACLE, TOL, gpu_available, gpu_codes_qk, gpu_codes_v, oracle_quant_qk, oracle_quant_v,
-                     FRAGILE_CAP, record_parity, score_rounds)
+                     FRAGILE_CAP, record_parity, score_rounds, unpack_nibbles)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
@@ -147,6 +147,52 @@ def test_decode_vt_equals_v(pm, B, Hq, Hkv, R, N, kv_len):
     assert torch.equal(sv.reshape(B, Hkv, 128, nt, 4).permute(0, 1, 3, 2, 4), st)
 
 
+@pytest.mark.parametrize("pm", ["two_level", "fp8"])
+def test_decode_bench_size(pm):
+    """The decode in the shape bench.py times: 4 requests, GQA 32:8, one new token each
+    over 131072 keys (256 chunk states per row to merge), V tile-major (role VT).  The
+    four requests hold one history and one query, so request 0 is checked against the
+    oracle and the others must equal it bit for bit."""
+    import torch
+    import microscaling_fp4_attention_amd as mx
+    B, Hq, Hkv, N = 4, 32, 8, 131072
+    qf_, vf_ = FMT[pm]
+    pf_ = None if pm == "fp8" else qf_
+    q, k, v = _bf16((1, Hq, 1, 128), 68, 1), _bf16((1, Hkv, N, 128), 68, 2, 0.3), _bf16((1, Hkv, N, 128), 68, 3)
+    dev = "cuda:0"
+    t = {n: torch.from_numpy(a.astype(np.int16)).view(torch.bfloat16).to(dev).repeat(B, 1, 1, 1)
+         for n, a in (("q", q), ("k", k), ("v", v))}
+    Q, K = mx.quantize(t["q"], mx.ROLE_QK, qf_), mx.quantize(t["k"], mx.ROLE_QK, qf_)
+    V = mx.quantize(t["v"], mx.ROLE_VT, vf_)
+    lse = torch.empty((B, Hq, 1), dtype=torch.float32, device=dev)
+    out = mx.decode(Q, K, V, mx.fwd_params(pm, pf_, causal=True, out_fp32=True), lse=lse)
+    torch.cuda.synchronize()
+    assert all(torch.equal(out[b], out[0]) and torch.equal(lse[b], lse[0]) for b in range(1, B))
+    qc, qs, qd = oracle_quant_qk(synth.bf16_to_f32(q), qf_)
+    kc, ks, kd = oracle_quant_qk(synth.bf16_to_f32(k), qf_)
+    vc, vs, vd = oracle_quant_v(synth.bf16_to_f32(v), vf_)
+    assert np.array_equal(gpu_codes_qk(Q)[:1], qc) and np.array_equal(gpu_codes_qk(K)[:1], kc)
+    # role VT [B, H, tile, d, 128 keys] holds role V's channel rows [B, H, d, keys] tile by tile
+    ct, st = V.codes_view()[:1], V.scales_view()[:1]
+    gc = ct.permute(0, 1, 3, 2, 4).reshape(1, Hkv, 128, -1).cpu().numpy()
+    gs = st.permute(0, 1, 3, 2, 4).reshape(1, Hkv, 128, -1).cpu().numpy()
+    if V.desc.fmt.elem == 0:
+        gc = unpack_nibbles(gc)
+    assert np.array_equal(gc[..., :N], vc) and np.array_equal(gs[..., :vs.shape[-1]], vs)
+    O_ref, lse_ref, fb = oracle.decode(qd, kd, vd, np.array([N], np.int32), PM_ORACLE[pm], pf_, split=256,
+                                       score_rounds=score_rounds(qf_))
+    O_gpu = out[:1].cpu().numpy()
+    bound = TOL * np.abs(O_ref).max() + fb[..., None]
+    ratio = float((np.abs(O_gpu - O_ref) / bound).max())
+    lse_err = float(np.abs(lse[:1].cpu().numpy() - lse_ref).max())
+    name = f"decode {pm} {qf_} B{B} Hq{Hq} Hkv{Hkv} R1 N{N} VT"
+    print(f"{name}: max |dO|/bound {ratio:.3f}, |dlse| {lse_err:.2e}")
+    record_parity(name, ratio, fb / (TOL * np.abs(O_ref).max()), None)
+    assert np.all(np.isfinite(O_gpu))
+    assert ratio <= 1.0
+    assert lse_err <= 1e-3 * max(1.0, float(np.abs(lse_ref).max()))
+
+
 def test_decode_refused():
     import torch
     import microscaling_fp4_attention_amd as mx
@@ -165,7 +211,7 @@ def test_decode_refused():
     with pytest.raises(mx.MxattnError) as e:  # FP8 P takes an FP8 V
         mx.decode(Q1, K, V, mx.fwd_params("fp8", None, causal=True))
     assert e.value.status == -2
-    with pytest.raises(mx.MxattnError) as e:  # an FP8 V has no tile-major form here
+    with pytest.raises(mx.MxattnError) as e:  # FP8 P takes an FP8 V in the tile-major form too
         mx.decode(Q1, K, mx.quantize(k, mx.ROLE_VT, "mxfp4"), mx.fwd_params("fp8", None, causal=True))
     assert e.value.status == -2
     torch.cuda.synchronize()
