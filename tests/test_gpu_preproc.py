@@ -179,3 +179,60 @@ def test_fullsize_gqa_causal_centered():
     print(f"c4 centered: heads {heads}, {len(rows)} rows, max |dO|/bound = {worst:.2e}")
     record_parity("full size c4 centered", worst, np.concatenate(fbt), None)
     assert worst <= 1.0
+
+
+def test_fullsize_varlen_causal_centered():
+    """The packed-document causal 64K workload (MXFP4 Q/K/V, two-level P with E4M3/16
+    level 2) with per-document centering and the compensation bias, in the launch shape
+    bench.py times, on sampled rows of a few heads (each document's first and last row
+    among them); means bit-exact, compensation within one ulp, bytes bit-exact."""
+    import torch
+    import microscaling_fp4_attention_amd as mx
+    from helpers import PM_ORACLE, oracle_quant_v, gpu_codes_v
+
+    x = synth.workload("c5_varlen_causal_64k")
+    B, Hq, Hkv, N, doc_off = x["B"], x["Hq"], x["Hkv"], x["N"], x["doc_off"]
+    nd = len(doc_off) - 1
+    cu = torch.tensor(doc_off, dtype=torch.int32, device="cuda:0")
+    qg, kg, vg = _dev(x["q"]), _dev(x["k"]), _dev(x["v"])
+    qm, km = mx.channel_mean(qg, cu), mx.channel_mean(kg, cu)
+    Q = mx.quantize(qg, mx.ROLE_QK, "mxfp4", cu_seqlens=cu, mean=qm)
+    K = mx.quantize(kg, mx.ROLE_QK, "mxfp4", cu_seqlens=cu, mean=km)
+    V = mx.quantize(vg, mx.ROLE_V, "mxfp4", cu_seqlens=cu)
+    delta = mx.center_comp(qm, kg, km, cu)
+    ws = mx.fwd_plan(doc_off, N, True)
+    out = mx.fwd(Q, K, V, mx.fwd_params("two_level", "nvfp4", causal=True, out_fp32=True, score_bias=delta),
+                 workspace=ws, ndocs=nd)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+    heads = sorted({0, Hq - 1, int(rng.integers(0, Hq))})
+    starts, ends = doc_off[:-1], doc_off[1:] - 1
+    rows = sorted({0, N - 1, *map(int, starts[:4]), *map(int, ends[:4]), *map(int, rng.integers(0, N, 8))})
+    qcodes, kcodes = gpu_codes_qk(Q), gpu_codes_qk(K)
+    gvc, gvs = gpu_codes_v(V, N, doc_off)
+    dg = delta.cpu().numpy()
+    worst, fbt = 0.0, []
+    for h in heads:
+        hk = h * Hkv // Hq
+        qf = synth.bf16_to_f32(x["q"][:1, h:h + 1])
+        kf = synth.bf16_to_f32(x["k"][:1, hk:hk + 1])
+        vf = synth.bf16_to_f32(x["v"][:1, hk:hk + 1])
+        qmean, qy = oracle_preproc(qf, doc_off, True, False)
+        kmean, ky = oracle_preproc(kf, doc_off, True, False)
+        assert np.array_equal(qm[0, h].cpu().numpy(), qmean[0, 0]) and np.array_equal(km[0, hk].cpu().numpy(), kmean[0, 0])
+        qc, qs, qd = oracle_quant_qk(qy, "mxfp4")
+        kc, ks, kd = oracle_quant_qk(ky, "mxfp4")
+        assert np.array_equal(qcodes[0, h], qc[0, 0]) and np.array_equal(kcodes[0, hk], kc[0, 0])
+        vc, vs, vd = oracle_quant_v(vf, "mxfp4", doc_off)
+        assert np.array_equal(gvc[0, hk], vc[0, 0]) and np.array_equal(gvs[0, hk], vs[0, 0])
+        bias = oracle_comp(qmean, kf, kmean, 1, doc_off)
+        assert ulp_diff(dg[0, h], bias[0, 0]) <= 1
+        O_ref, _, fb = oracle.attention(qd, kd, vd, PM_ORACLE["two_level"], "nvfp4", causal=True, doc_off=doc_off,
+                                        rows=np.array(rows, np.int64), bias=bias, score_rounds=score_rounds("mxfp4"))
+        O_gpu = out[0, h].cpu().numpy()[rows]
+        bound = TOL * np.abs(O_ref).max() + fb[:, None]
+        worst = max(worst, float((np.abs(O_gpu - O_ref) / bound).max()))
+        fbt.append(fb / (TOL * np.abs(O_ref).max()))
+    print(f"c5 centered: {nd} documents, heads {heads}, {len(rows)} rows, max |dO|/bound = {worst:.2e}")
+    record_parity("full size c5 centered", worst, np.concatenate(fbt), None)
+    assert worst <= 1.0
