@@ -181,10 +181,11 @@ def test_fullsize_gqa_causal_centered():
     assert worst <= 1.0
 
 
-def test_fullsize_varlen_causal_centered():
+@pytest.mark.parametrize("had", [False, True])
+def test_fullsize_varlen_causal_centered(had):
     """The packed-document causal 64K workload (MXFP4 Q/K/V, two-level P with E4M3/16
-    level 2) with per-document centering and the compensation bias, in the launch shape
-    bench.py times, on sampled rows of a few heads (each document's first and last row
+    level 2) with per-document centering and the compensation bias, with and without the
+    normalized Hadamard rotation of the centered Q and K, in the launch shape bench.py times, on sampled rows of a few heads (each document's first and last row
     among them); means bit-exact, compensation within one ulp, bytes bit-exact."""
     import torch
     import microscaling_fp4_attention_amd as mx
@@ -196,8 +197,8 @@ def test_fullsize_varlen_causal_centered():
     cu = torch.tensor(doc_off, dtype=torch.int32, device="cuda:0")
     qg, kg, vg = _dev(x["q"]), _dev(x["k"]), _dev(x["v"])
     qm, km = mx.channel_mean(qg, cu), mx.channel_mean(kg, cu)
-    Q = mx.quantize(qg, mx.ROLE_QK, "mxfp4", cu_seqlens=cu, mean=qm)
-    K = mx.quantize(kg, mx.ROLE_QK, "mxfp4", cu_seqlens=cu, mean=km)
+    Q = mx.quantize(qg, mx.ROLE_QK, "mxfp4", cu_seqlens=cu, mean=qm, hadamard=had)
+    K = mx.quantize(kg, mx.ROLE_QK, "mxfp4", cu_seqlens=cu, mean=km, hadamard=had)
     V = mx.quantize(vg, mx.ROLE_V, "mxfp4", cu_seqlens=cu)
     delta = mx.center_comp(qm, kg, km, cu)
     ws = mx.fwd_plan(doc_off, N, True)
@@ -217,8 +218,8 @@ def test_fullsize_varlen_causal_centered():
         qf = synth.bf16_to_f32(x["q"][:1, h:h + 1])
         kf = synth.bf16_to_f32(x["k"][:1, hk:hk + 1])
         vf = synth.bf16_to_f32(x["v"][:1, hk:hk + 1])
-        qmean, qy = oracle_preproc(qf, doc_off, True, False)
-        kmean, ky = oracle_preproc(kf, doc_off, True, False)
+        qmean, qy = oracle_preproc(qf, doc_off, True, had)
+        kmean, ky = oracle_preproc(kf, doc_off, True, had)
         assert np.array_equal(qm[0, h].cpu().numpy(), qmean[0, 0]) and np.array_equal(km[0, hk].cpu().numpy(), kmean[0, 0])
         qc, qs, qd = oracle_quant_qk(qy, "mxfp4")
         kc, ks, kd = oracle_quant_qk(ky, "mxfp4")
@@ -233,6 +234,7 @@ def test_fullsize_varlen_causal_centered():
         bound = TOL * np.abs(O_ref).max() + fb[:, None]
         worst = max(worst, float((np.abs(O_gpu - O_ref) / bound).max()))
         fbt.append(fb / (TOL * np.abs(O_ref).max()))
-    print(f"c5 centered: {nd} documents, heads {heads}, {len(rows)} rows, max |dO|/bound = {worst:.2e}")
-    record_parity("full size c5 centered", worst, np.concatenate(fbt), None)
+    name = "full size c5 centered" + (" + Hadamard" if had else "")
+    print(f"{name}: {nd} documents, heads {heads}, {len(rows)} rows, max |dO|/bound = {worst:.2e}")
+    record_parity(name, worst, np.concatenate(fbt), None)
     assert worst <= 1.0
