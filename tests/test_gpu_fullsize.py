@@ -26,6 +26,8 @@ CASES = {
     "two_level_e4m3_32k": ("c3_video_dit_32k", "mxfp4", "mxfp4", "two_level", "nvfp4"),
     "two_level_e8m0_32k": ("c3_video_dit_32k", "mxfp4", "mxfp4", "two_level", "mxfp4"),
     "c5_varlen_causal_64k_safe": ("c5_varlen_causal_64k", "mxfp4", "mxfp4", "two_level", "nvfp4"),
+    # the same with the bit-level Mitchell-P exponential (bench.py --causal-safe --exp mitchell)
+    "c5_varlen_causal_64k_safe_mitchell": ("c5_varlen_causal_64k", "mxfp4", "mxfp4", "two_level", "nvfp4"),
 }
 
 
@@ -53,13 +55,15 @@ def test_fullsize_sampled_rows(name):
     Q = mx.quantize(t["q"], mx.ROLE_QK, qf)
     K = mx.quantize(t["k"], mx.ROLE_QK, qf)
     V = mx.quantize(t["v"], mx.ROLE_V, vf, cu_seqlens=cu)
-    safe = name.endswith("_safe")
+    exp_mode = "mitchell" if name.endswith("_mitchell") else "exact"
+    safe = name.endswith("_safe") or name.endswith("_safe_mitchell")
     Vk = mx.quantize(t["v"], mx.ROLE_VKEY, vf, cu_seqlens=cu) if safe else None
     ws, nd = None, 0
     if doc_off is not None:
         ws = mx.fwd_plan(doc_off, N, causal)
         nd = len(doc_off) - 1
-    out = mx.fwd(Q, K, V, mx.fwd_params(pm, pf, causal=causal, out_fp32=True, vkey=Vk), workspace=ws, ndocs=nd)
+    out = mx.fwd(Q, K, V, mx.fwd_params(pm, pf, causal=causal, out_fp32=True, vkey=Vk, exp_mode=exp_mode),
+                 workspace=ws, ndocs=nd)
     torch.cuda.synchronize()
 
     rng = np.random.default_rng(12345)
@@ -87,7 +91,7 @@ def test_fullsize_sampled_rows(name):
             assert np.array_equal(gkc[0, hk], vk_codes[0, 0]) and np.array_equal(gke[0, hk], vk_exp[0, 0])
         O_ref, _, fb = oracle.attention(qd, kd, vd, PM_ORACLE[pm], pf, causal=causal, doc_off=doc_off,
                                         rows=np.array(rows, np.int64), score_rounds=score_rounds(qf),
-                                        vkey=vk_vals, vkey_exp=vk_exp)
+                                        vkey=vk_vals, vkey_exp=vk_exp, exp_mode=exp_mode)
         O_gpu = out[0, h].cpu().numpy()[rows]
         # the bound uses max|O| of the sampled rows of this head
         bound = TOL * np.abs(O_ref).max() + fb[:, None]
