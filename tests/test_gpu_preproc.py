@@ -132,6 +132,17 @@ def test_fwd_other_preprocessing(pre):
     _check(res, f"pre={pre}")
 
 
+@pytest.mark.parametrize("route", [("mxfp4", "mxfp4", "two_level", "nvfp4"), ("mxfp4_uos", "mxfp4_uos", "pnq", "mxfp4_uos"),
+                                   ("nvfp4", "fp8v", "fp8", None), ("nvfp4", "nvfp4", "direct", "nvfp4")])
+def test_fwd_smoothk_packed_causal(route):
+    """smooth-K alone (each document's K mean, no compensation: a row's visible keys all
+    share it) under the causal mask with packed documents, on both forward kernels"""
+    doc_off = np.array([0, 1, 300, 301, 777], np.int32)
+    res = run_case(*route, B=1, Hq=4, Hkv=2, N=777, causal=True, kind="outlier", seed=24, doc_off=doc_off,
+                   pre={"smoothk": True})
+    _check(res, f"smooth-K docs causal {route[2]} {route[0]}")
+
+
 def test_fullsize_gqa_causal_centered():
     """The GQA causal 32K workload (NVFP4 Q/K, FP8 P and V) with sequence centering
     and the compensation bias, in the launch shape bench.py times, on sampled rows
